@@ -1,0 +1,126 @@
+"""ctypes front end of the CPU oracle (oracle/spmm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the package smoke check and by
+the benchmark's CPU-baseline leg.  The product path never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+SUM, MEAN, MAX = 0, 1, 2
+REDUCE = {"sum": SUM, "mean": MEAN, "max": MAX}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            from . import build as _b
+            _b.build(out=path)
+        lib = ctypes.CDLL(path)
+        lib.oracle_spmm.argtypes = [_p, _p, _p, _i64, _i64, _p, _i64, ctypes.c_int,
+                                    ctypes.c_int, _p, _i64, _p, _p]
+        lib.oracle_spmm.restype = ctypes.c_int
+        lib.oracle_sumabs.argtypes = [_p, _p, _p, _i64, _p, _i64, _p, _i64, _p]
+        lib.oracle_sumabs.restype = ctypes.c_int
+        lib.oracle_validate.argtypes = [_p, _p, _i64, _i64]
+        lib.oracle_validate.restype = _i64
+        lib.oracle_descriptors.argtypes = [_p, _i64, _p, _p]
+        lib.oracle_descriptors.restype = None
+        lib.oracle_partition.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p]
+        lib.oracle_partition.restype = ctypes.c_int
+        lib.oracle_mac_gap.argtypes = [_i64, _i64, _i64]
+        lib.oracle_mac_gap.restype = _i64
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _csr(rowptr, col, val):
+        rowptr = np.ascontiguousarray(rowptr, dtype=np.int64)
+        col = np.ascontiguousarray(col, dtype=np.int64)
+        val = None if val is None else np.ascontiguousarray(val, dtype=np.float32)
+        return rowptr, col, val
+
+    def spmm(self, rowptr, col, val, M, K, B, reduce="sum", fused=False, rows=None):
+        """Returns C [nrows, N] fp32 and, for max, argmax [nrows, N] int64."""
+        rowptr, col, val = self._csr(rowptr, col, val)
+        B = np.ascontiguousarray(B, dtype=np.float32)
+        N = B.shape[1]
+        red = REDUCE[reduce] if isinstance(reduce, str) else int(reduce)
+        rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = M if rows_a is None else rows_a.size
+        C = np.empty((nrows, N), dtype=np.float32)
+        arg = np.empty((nrows, N), dtype=np.int64) if red == MAX else None
+        rc = self.lib.oracle_spmm(_ptr(rowptr), _ptr(col), _ptr(val), M, K, _ptr(B), N, red,
+                                  int(bool(fused)), _ptr(rows_a), nrows, _ptr(C), _ptr(arg))
+        if rc != 0:
+            raise ValueError("oracle_spmm rejected its arguments")
+        return (C, arg) if red == MAX else C
+
+    def sumabs(self, rowptr, col, val, M, B, rows=None):
+        rowptr, col, val = self._csr(rowptr, col, val)
+        B = np.ascontiguousarray(B, dtype=np.float32)
+        N = B.shape[1]
+        rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = M if rows_a is None else rows_a.size
+        S = np.empty((nrows, N), dtype=np.float64)
+        rc = self.lib.oracle_sumabs(_ptr(rowptr), _ptr(col), _ptr(val), M, _ptr(B), N,
+                                    _ptr(rows_a), nrows, _ptr(S))
+        if rc != 0:
+            raise ValueError("oracle_sumabs rejected its arguments")
+        return S
+
+    def validate(self, rowptr, col, M, K) -> int:
+        rowptr, col, _ = self._csr(rowptr, col, None)
+        return int(self.lib.oracle_validate(_ptr(rowptr), _ptr(col), M, K))
+
+    def descriptors(self, rowptr, M):
+        rowptr = np.ascontiguousarray(rowptr, dtype=np.int64)
+        ints = np.zeros(3, dtype=np.int64)
+        dbl = np.zeros(2, dtype=np.float64)
+        self.lib.oracle_descriptors(_ptr(rowptr), M, _ptr(ints), _ptr(dbl))
+        return dict(nnz=int(ints[0]), dmax=int(ints[1]), n_empty=int(ints[2]),
+                    mean=float(dbl[0]), cv=float(dbl[1]))
+
+    def partition(self, rowptr, M, T, L):
+        rowptr = np.ascontiguousarray(rowptr, dtype=np.int64)
+        counts = np.zeros(3, dtype=np.int64)
+        z = np.zeros(0, dtype=np.int64)
+        rc = self.lib.oracle_partition(_ptr(rowptr), M, T, L, _ptr(z), _ptr(z), _ptr(z), 0,
+                                       _ptr(z), 0, _ptr(counts))
+        if rc != 0:
+            raise ValueError("oracle_partition rejected its arguments")
+        n_seg, n_light = int(counts[1]), int(counts[2])
+        sr = np.empty(n_seg, np.int64)
+        sb = np.empty(n_seg, np.int64)
+        se = np.empty(n_seg, np.int64)
+        light = np.empty(n_light, np.int64)
+        self.lib.oracle_partition(_ptr(rowptr), M, T, L, _ptr(sr), _ptr(sb), _ptr(se), n_seg,
+                                  _ptr(light), n_light, _ptr(counts))
+        return dict(n_heavy=int(counts[0]), seg_row=sr, seg_begin=sb, seg_end=se, light=light)
+
+    def mac_gap(self, dim, F, omega) -> int:
+        return int(self.lib.oracle_mac_gap(dim, F, omega))
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

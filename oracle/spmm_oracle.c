@@ -1,0 +1,229 @@
+/*
+ * CPU oracle for CSR sparse x dense products with sum / mean / max+argmax
+ * reductions (GNN neighbour aggregation).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference: it is
+ * built and called by the test suite, by the package smoke check and by the
+ * benchmark's CPU-baseline leg, never by the product path.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * Plain, slow, single-threaded, fp32 as the pages fix ("fp32 only", "fp32
+ * summation order": graph-spmm kernel card, sections "Requirements and
+ * limits" and "Correctness").  Build with -O2 -ffp-contract=off so that the
+ * compiler never fuses a multiply into an add unless asked to (fused = 1).
+ *
+ * Definitions followed (sources are the pages' titles and sections):
+ *  - CSR: row i owns entries rowPtr[i] .. rowPtr[i+1]-1 (ParamSpMM, section 2
+ *    "Background", CSR format).
+ *  - sum: C[i][k] accumulates a_p * B[col_p][k] over the row's entries in
+ *    stored order, writing C once at the end (ParamSpMM section 2, Algorithm 1;
+ *    GE-SpMM section III-A).
+ *  - mean: row-wise mean, empty rows give 0 (graph-spmm card, API table:
+ *    spmm_mean).  The divisor is the number of stored entries of the row.
+ *  - max: (values, argmax) with the winning neighbour's column id; empty rows
+ *    give (0, -1) (graph-spmm card, API table: spmm_max, and "Method").  Ties go
+ *    to the first entry in stored order (strict greater-than).
+ *  - val == NULL: every stored entry is 1 and no value is read (graph-spmm card,
+ *    API table: spmm_sum with val=None; "Method").
+ *  - duplicates are not merged: each stored entry counts (graph-spmm card,
+ *    "Correctness").
+ *  - descriptors: M, mean degree nnz/M and the coefficient of variation of the
+ *    row degree (RA-SpMM, abstract and "Structural taxonomy").
+ *  - row split: rows longer than a threshold are cut into fixed-length pieces
+ *    processed separately (ParamSpMM section 3.2 "workload balancing", PCSR
+ *    TRow in section 4.2; graph-spmm card, "Requirements and limits").
+ *  - MAC-job gap of thread coarsening (ParamSpMM section 3.3, eq. 1, read with
+ *    Table 2: the gap is zero when dim is a multiple of F * omega).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define RED_SUM 0
+#define RED_MEAN 1
+#define RED_MAX 2
+
+/* One product a_p * b: a single fp32 rounding, or none of its own when fused. */
+static float product(const float *val, int64_t p, float b) {
+    if (val == NULL) return b;
+    return val[p] * b;
+}
+
+/*
+ * C[r][k] for r over `rows` (all rows when rows == NULL), k in [0, N).
+ * C (and argmax, for max) are [nrows, N] row-major, one row per listed row.
+ * fused = 0: acc = acc + (a*b), two roundings per entry (the plain definition).
+ * fused = 1: acc = fmaf(a, b, acc), one rounding per entry.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_spmm(const int64_t *rowptr, const int64_t *col, const float *val,
+                int64_t M, int64_t K, const float *B, int64_t N, int reduce,
+                int fused, const int64_t *rows, int64_t nrows, float *C,
+                int64_t *argmax) {
+    if (M < 0 || K < 0 || N <= 0 || reduce < RED_SUM || reduce > RED_MAX)
+        return -1;
+    if (rows == NULL) nrows = M;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= M) return -1;
+        int64_t first = rowptr[i];
+        int64_t last = rowptr[i + 1];
+        int64_t deg = last - first;
+        for (int64_t k = 0; k < N; ++k) {
+            float out;
+            int64_t arg = -1;
+            if (reduce == RED_MAX) {
+                if (deg == 0) {
+                    out = 0.0f;
+                } else {
+                    float best = product(val, first, B[col[first] * N + k]);
+                    arg = col[first];
+                    for (int64_t p = first + 1; p < last; ++p) {
+                        float t = product(val, p, B[col[p] * N + k]);
+                        if (t > best) {
+                            best = t;
+                            arg = col[p];
+                        }
+                    }
+                    out = best;
+                }
+                argmax[r * N + k] = arg;
+            } else {
+                float acc = 0.0f;
+                for (int64_t p = first; p < last; ++p) {
+                    float b = B[col[p] * N + k];
+                    if (fused && val != NULL)
+                        acc = fmaf(val[p], b, acc);
+                    else
+                        acc = acc + product(val, p, b);
+                }
+                if (reduce == RED_MEAN)
+                    out = (deg == 0) ? 0.0f : acc / (float)deg;
+                else
+                    out = acc;
+            }
+            C[r * N + k] = out;
+        }
+    }
+    return 0;
+}
+
+/* S[r][k] = sum over the row's entries of |a_p * B[col_p][k]|, in double. */
+int oracle_sumabs(const int64_t *rowptr, const int64_t *col, const float *val,
+                  int64_t M, const float *B, int64_t N, const int64_t *rows,
+                  int64_t nrows, double *S) {
+    if (M < 0 || N <= 0) return -1;
+    if (rows == NULL) nrows = M;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= M) return -1;
+        for (int64_t k = 0; k < N; ++k) {
+            double s = 0.0;
+            for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+                double a = val ? (double)val[p] : 1.0;
+                s += fabs(a * (double)B[col[p] * N + k]);
+            }
+            S[r * N + k] = s;
+        }
+    }
+    return 0;
+}
+
+/*
+ * CSR well-formedness: rowptr[0] == 0, rowptr non-decreasing, every column in
+ * [0, K).  Returns -1 when valid, else the first row that breaks a rule
+ * (row i for a decrease rowptr[i+1] < rowptr[i] or a bad column in row i;
+ * row 0 when rowptr[0] != 0).
+ */
+int64_t oracle_validate(const int64_t *rowptr, const int64_t *col, int64_t M,
+                        int64_t K) {
+    if (rowptr[0] != 0) return 0;
+    for (int64_t i = 0; i < M; ++i)
+        if (rowptr[i + 1] < rowptr[i]) return i;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p)
+            if (col[p] < 0 || col[p] >= K) return i;
+    return -1;
+}
+
+/*
+ * Row-degree descriptors.  ints = {nnz, dmax, n_empty}; dbl = {mean, cv}
+ * with mean = nnz / M and cv = population standard deviation / mean
+ * (two-pass: mean first, then the mean squared deviation).  M == 0 or a zero
+ * mean gives cv = 0.
+ */
+void oracle_descriptors(const int64_t *rowptr, int64_t M, int64_t *ints,
+                        double *dbl) {
+    int64_t nnz = 0, dmax = 0, n_empty = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t d = rowptr[i + 1] - rowptr[i];
+        nnz += d;
+        if (d > dmax) dmax = d;
+        if (d == 0) n_empty += 1;
+    }
+    double mean = (M > 0) ? (double)nnz / (double)M : 0.0;
+    double var = 0.0;
+    for (int64_t i = 0; i < M; ++i) {
+        double dev = (double)(rowptr[i + 1] - rowptr[i]) - mean;
+        var += dev * dev;
+    }
+    var = (M > 0) ? var / (double)M : 0.0;
+    ints[0] = nnz;
+    ints[1] = dmax;
+    ints[2] = n_empty;
+    dbl[0] = mean;
+    dbl[1] = (mean > 0.0) ? sqrt(var) / mean : 0.0;
+}
+
+/*
+ * Row split.  Heavy rows are those with degree > T, taken in ascending order;
+ * heavy row i is cut into pieces [rowptr[i] + s*L, min(rowptr[i] + (s+1)*L,
+ * rowptr[i+1])) for s = 0, 1, ...  Pieces are listed by (row, s).  Every other
+ * row is light, listed in ascending order.  Writes at most `cap` pieces and
+ * `light_cap` light rows; counts = {n_heavy, n_pieces, n_light}.
+ * Returns 0, or -1 for T < 0 or L <= 0.
+ */
+int oracle_partition(const int64_t *rowptr, int64_t M, int64_t T, int64_t L,
+                     int64_t *seg_row, int64_t *seg_begin, int64_t *seg_end,
+                     int64_t cap, int64_t *light, int64_t light_cap,
+                     int64_t *counts) {
+    if (T < 0 || L <= 0) return -1;
+    int64_t n_heavy = 0, n_seg = 0, n_light = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t deg = rowptr[i + 1] - rowptr[i];
+        if (deg > T) {
+            n_heavy += 1;
+            for (int64_t b = rowptr[i]; b < rowptr[i + 1]; b += L) {
+                int64_t e = b + L;
+                if (e > rowptr[i + 1]) e = rowptr[i + 1];
+                if (n_seg < cap) {
+                    seg_row[n_seg] = i;
+                    seg_begin[n_seg] = b;
+                    seg_end[n_seg] = e;
+                }
+                n_seg += 1;
+            }
+        } else {
+            if (n_light < light_cap) light[n_light] = i;
+            n_light += 1;
+        }
+    }
+    counts[0] = n_heavy;
+    counts[1] = n_seg;
+    counts[2] = n_light;
+    return 0;
+}
+
+/*
+ * MAC-job gap of a warp that produces F*omega columns per pass over a row,
+ * for a dense width dim: the ideal job count min(dim, F*omega) minus the
+ * residual warp's job count dim mod (F*omega), taken as 0 when the residual is
+ * 0 (no residual warp).
+ */
+int64_t oracle_mac_gap(int64_t dim, int64_t F, int64_t omega) {
+    int64_t span = F * omega;
+    int64_t tn = dim < span ? dim : span;
+    int64_t tr = dim % span;
+    if (tr == 0) return 0;
+    return tn - tr;
+}

@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with something the pages or the mathematics fix:
+
+* brute-force dense float64 products (duplicates accumulated into the dense
+  matrix) and scipy's CSR product, both within Higham's recursive-summation
+  bound gamma_n * sum|a*b|;
+* identity adjacency returns B bit for bit, argmax = own index;
+* B = ones returns the (weighted) row degree; mean * deg recovers sum;
+* empty rows reduce to 0 and (0, -1) (graph-spmm card, API table);
+* max / argmax from numpy's max and first-occurrence argmax over the stored
+  entries, with ties forced by small-integer features (graph-spmm card,
+  "Correctness": per-row reference built from the CSR entries);
+* val = NULL equals an explicit all-ones weight array bit for bit (card,
+  "Correctness");
+* the row split against a hand-enumerated case and its tiling invariants;
+* degree descriptors against closed forms and numpy's population std;
+* the MAC-job gap against ParamSpMM Table 2.
+
+tests/test_oracle.py runs every pin on the real oracle; tests/test_oracle_mutants.py
+runs them on oracle builds with a planted mistake and requires some pin to fail.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U = 2.0 ** -24          # fp32 unit roundoff
+
+
+def gamma(n):
+    n = np.asarray(n, dtype=np.float64)
+    return n * U / (1.0 - n * U)
+
+
+def _dense(g: W.Graph) -> np.ndarray:
+    A = np.zeros((g.M, g.K), dtype=np.float64)
+    rows = np.repeat(np.arange(g.M), g.degrees())
+    vals = np.ones(g.nnz) if g.val is None else g.val.astype(np.float64)
+    np.add.at(A, (rows, g.col), vals)            # duplicates accumulate
+    return A
+
+
+def _small_graphs():
+    rng = np.random.default_rng(20240601)
+    out = []
+    for it in range(8):
+        M = int(rng.integers(1, 65))
+        K = int(rng.integers(1, 65))
+        out.append(W.random_csr(rng, M, K, mean_deg=float(rng.uniform(0.5, 12)),
+                                empty_frac=0.15, dup_frac=0.2 if it % 2 else 0.0,
+                                shuffle_rows=bool(it % 3 == 0), weighted=bool(it % 4 != 1)))
+    return out
+
+
+def _bound_check(C, ref, S, deg, what, mean=False):
+    n = np.maximum(deg, 1)[:, None]
+    if mean:
+        tol = (gamma(n + 2) * S) / n
+    else:
+        tol = gamma(n + 1) * S
+    err = np.abs(C.astype(np.float64) - ref)
+    bad = err > tol + 1e-300
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries outside the recursive-summation bound"
+
+
+def pin_dense_bruteforce(orc):
+    rng = np.random.default_rng(7)
+    for g in _small_graphs():
+        N = int(rng.integers(1, 9))
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        ref = _dense(g) @ B.astype(np.float64)
+        Sabs = np.abs(_dense_abs(g)) @ np.abs(B.astype(np.float64))
+        deg = g.degrees()
+        for fused in (False, True):
+            C = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "sum", fused=fused)
+            _bound_check(C, ref, Sabs, deg, f"sum fused={fused}")
+            Cm = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "mean", fused=fused)
+            refm = np.where(deg[:, None] > 0, ref / np.maximum(deg, 1)[:, None], 0.0)
+            _bound_check(Cm, refm, Sabs, deg, f"mean fused={fused}", mean=True)
+
+
+def _dense_abs(g: W.Graph) -> np.ndarray:
+    A = np.zeros((g.M, g.K), dtype=np.float64)
+    rows = np.repeat(np.arange(g.M), g.degrees())
+    vals = np.ones(g.nnz) if g.val is None else np.abs(g.val.astype(np.float64))
+    np.add.at(A, (rows, g.col), vals)
+    return A
+
+
+def pin_scipy_product(orc):
+    import scipy.sparse as sp
+    rng = np.random.default_rng(11)
+    g = W.random_csr(rng, 300, 250, mean_deg=9.0, empty_frac=0.05, dup_frac=0.1)
+    for N in (1, 5, 33):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        A = sp.csr_matrix((g.val.astype(np.float64), g.col, g.rowptr), shape=(g.M, g.K))
+        ref = np.asarray(A @ B.astype(np.float64))
+        Aabs = sp.csr_matrix((np.abs(g.val.astype(np.float64)), g.col, g.rowptr), shape=(g.M, g.K))
+        S = np.asarray(Aabs @ np.abs(B.astype(np.float64)))
+        C = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "sum")
+        _bound_check(C, ref, S, g.degrees(), f"scipy N={N}")
+        S2 = orc.sumabs(g.rowptr, g.col, g.val, g.M, B)
+        assert np.allclose(S2, S, rtol=1e-12, atol=0), "sumabs differs from |A| @ |B|"
+
+
+def pin_identity(orc):
+    rng = np.random.default_rng(3)
+    M = 37
+    B = rng.standard_normal((M, 7)).astype(np.float32)
+    rowptr = np.arange(M + 1, dtype=np.int64)
+    col = np.arange(M, dtype=np.int64)
+    for val in (None, np.ones(M, np.float32)):
+        for red in ("sum", "mean"):
+            C = orc.spmm(rowptr, col, val, M, M, B, red)
+            assert np.array_equal(C.view(np.uint32), B.view(np.uint32)), f"identity {red}"
+        C, arg = orc.spmm(rowptr, col, val, M, M, B, "max")
+        assert np.array_equal(C.view(np.uint32), B.view(np.uint32)), "identity max"
+        assert np.array_equal(arg, np.repeat(np.arange(M)[:, None], 7, axis=1)), "identity argmax"
+
+
+def pin_ones(orc):
+    rng = np.random.default_rng(5)
+    g = W.random_csr(rng, 120, 90, mean_deg=6.0, empty_frac=0.1, dup_frac=0.1, weighted=False)
+    B = np.ones((g.K, 4), np.float32)
+    deg = g.degrees().astype(np.float32)
+    C = orc.spmm(g.rowptr, g.col, None, g.M, g.K, B, "sum")
+    assert np.array_equal(C, np.repeat(deg[:, None], 4, axis=1)), "unweighted ones -> degree"
+    gw = W.random_csr(rng, 120, 90, mean_deg=6.0, empty_frac=0.1, dup_frac=0.1, weighted=True)
+    Cw = orc.spmm(gw.rowptr, gw.col, gw.val, gw.M, gw.K, B, "sum")
+    for i in range(gw.M):
+        a, b = gw.rowptr[i], gw.rowptr[i + 1]
+        exact = math.fsum(float(v) for v in gw.val[a:b])
+        tol = float(gamma(b - a + 1)) * math.fsum(abs(float(v)) for v in gw.val[a:b])
+        assert np.all(np.abs(Cw[i].astype(np.float64) - exact) <= tol), f"weighted degree row {i}"
+    Cm = orc.spmm(g.rowptr, g.col, None, g.M, g.K, B, "mean")
+    nz = deg > 0
+    assert np.all(Cm[nz] == 1.0) and np.all(Cm[~nz] == 0.0), "unweighted ones mean -> 1"
+
+
+def pin_empty_rows(orc):
+    rowptr = np.array([0, 0, 2, 2, 3, 3], np.int64)
+    col = np.array([1, 0, 2], np.int64)
+    val = np.array([0.5, -2.0, 3.0], np.float32)
+    B = np.array([[1.0, -1.0], [2.0, 4.0], [-3.0, 0.25]], np.float32)
+    M, K = 5, 3
+    empty = np.array([True, False, True, False, True])
+    for red in ("sum", "mean"):
+        C = orc.spmm(rowptr, col, val, M, K, B, red)
+        assert np.all(C[empty].view(np.uint32) == 0), f"{red}: empty rows must be +0"
+    C, arg = orc.spmm(rowptr, col, val, M, K, B, "max")
+    assert np.all(C[empty].view(np.uint32) == 0) and np.all(arg[empty] == -1), "max empty -> (0,-1)"
+    # row 1: entries (col 1, 0.5) and (col 0, -2.0); row 3: (col 2, 3.0)
+    assert np.array_equal(C[1], np.float32([max(0.5 * 2.0, -2.0 * 1.0), max(0.5 * 4.0, -2.0 * -1.0)]))
+    assert np.array_equal(arg[1], [1, 1]), "first maximum wins (0.5*4 == -2*-1)"
+    assert np.array_equal(C[3], np.float32([-9.0, 0.75])) and np.array_equal(arg[3], [2, 2])
+    Cs = orc.spmm(rowptr, col, val, M, K, B, "sum")
+    assert np.array_equal(Cs[1], np.float32([1.0 - 2.0, 2.0 + 2.0]))
+    Cm = orc.spmm(rowptr, col, val, M, K, B, "mean")
+    assert np.array_equal(Cm[1], np.float32([-0.5, 2.0]))
+
+
+def pin_max_numpy(orc):
+    rng = np.random.default_rng(13)
+    for it in range(6):
+        g = W.random_csr(rng, 80, 60, mean_deg=7.0, empty_frac=0.1, dup_frac=0.25,
+                         shuffle_rows=bool(it % 2), weighted=bool(it % 3))
+        if g.val is not None and it % 2:
+            g.val = rng.choice(np.float32([0.0, 0.5, 1.0, -1.0]), size=g.nnz).astype(np.float32)
+        N = 6
+        B = rng.integers(0, 3, size=(g.K, N)).astype(np.float32)       # ties everywhere
+        if it >= 3:
+            B = rng.standard_normal((g.K, N)).astype(np.float32)
+        C, arg = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "max")
+        for i in range(g.M):
+            a, b = g.rowptr[i], g.rowptr[i + 1]
+            if a == b:
+                continue
+            cols = g.col[a:b]
+            t = B[cols]                                                  # [deg, N] fp32
+            if g.val is not None:
+                t = (g.val[a:b, None] * t).astype(np.float32)
+            j = np.argmax(t, axis=0)                                     # first occurrence
+            first_max = t[j, np.arange(N)]                               # its exact bits (+0 vs -0)
+            assert np.array_equal(C[i].view(np.uint32), first_max.view(np.uint32)), f"max row {i}"
+            assert np.array_equal(arg[i], cols[j]), f"argmax row {i}"
+
+
+def pin_val_null_is_ones(orc):
+    rng = np.random.default_rng(17)
+    g = W.random_csr(rng, 200, 150, mean_deg=9.0, dup_frac=0.1, weighted=False)
+    B = rng.standard_normal((g.K, 12)).astype(np.float32)
+    ones = np.ones(g.nnz, np.float32)
+    for red in ("sum", "mean"):
+        for fused in (False, True):
+            a = orc.spmm(g.rowptr, g.col, None, g.M, g.K, B, red, fused=fused)
+            b = orc.spmm(g.rowptr, g.col, ones, g.M, g.K, B, red, fused=fused)
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"val=NULL {red}"
+    a, ia = orc.spmm(g.rowptr, g.col, None, g.M, g.K, B, "max")
+    b, ib = orc.spmm(g.rowptr, g.col, ones, g.M, g.K, B, "max")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)) and np.array_equal(ia, ib)
+
+
+def pin_mean_sum_relation(orc):
+    rng = np.random.default_rng(19)
+    g = W.random_csr(rng, 150, 100, mean_deg=5.0, empty_frac=0.2)
+    B = rng.standard_normal((g.K, 9)).astype(np.float32)
+    S = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "sum")
+    Mn = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "mean")
+    deg = g.degrees()
+    for i in range(g.M):
+        if deg[i] == 0:
+            assert np.all(Mn[i] == 0)
+        else:
+            assert np.array_equal(Mn[i], (S[i] / np.float32(deg[i])).astype(np.float32)), f"mean row {i}"
+
+
+def pin_row_subset(orc):
+    rng = np.random.default_rng(23)
+    g = W.random_csr(rng, 90, 70, mean_deg=6.0, dup_frac=0.1)
+    B = rng.standard_normal((g.K, 5)).astype(np.float32)
+    rows = np.array([89, 0, 17, 17, 42], np.int64)
+    for red in ("sum", "mean"):
+        full = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, red)
+        sub = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, red, rows=rows)
+        assert np.array_equal(full[rows], sub), f"row subset {red}"
+    full, fa = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "max")
+    sub, sa = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "max", rows=rows)
+    assert np.array_equal(full[rows], sub) and np.array_equal(fa[rows], sa)
+
+
+def _read_partition_golden():
+    segs, light = [], []
+    with open(os.path.join(GOLDEN, "partition_hand.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if not line:
+                continue
+            if line[0] == "seg":
+                segs.append(tuple(int(x) for x in line[1:4]))
+            elif line[0] == "light":
+                light.append(int(line[1]))
+    return segs, light
+
+
+def pin_partition(orc):
+    rowptr = np.array([0, 0, 5, 1205, 1718], np.int64)
+    segs, light = _read_partition_golden()
+    p = orc.partition(rowptr, 4, 512, 512)
+    got = list(zip(p["seg_row"].tolist(), p["seg_begin"].tolist(), p["seg_end"].tolist()))
+    assert got == segs, f"hand partition: {got}"
+    assert p["light"].tolist() == light and p["n_heavy"] == 2
+    # T = 0: every non-empty row is heavy; L = 1: one piece per entry
+    q = orc.partition(rowptr, 4, 0, 1)
+    assert q["n_heavy"] == 3 and len(q["seg_row"]) == 1718 and q["light"].tolist() == [0]
+    assert np.array_equal(q["seg_begin"], np.arange(1718)) and np.array_equal(q["seg_end"], np.arange(1, 1719))
+    # tiling invariants on a skewed random graph
+    rng = np.random.default_rng(29)
+    g = W.random_csr(rng, 500, 500, mean_deg=4.0, heavy_rows=7, heavy_deg=777)
+    deg = g.degrees()
+    for T, L in ((16, 16), (100, 64), (776, 777), (777, 1)):
+        r = orc.partition(g.rowptr, g.M, T, L)
+        heavy = np.nonzero(deg > T)[0]
+        assert np.array_equal(r["light"], np.nonzero(deg <= T)[0])
+        assert r["n_heavy"] == heavy.size
+        sr, sb, se = r["seg_row"], r["seg_begin"], r["seg_end"]
+        assert np.all(np.diff(sr) >= 0) and np.all(se > sb) and np.all(se - sb <= L)
+        for h in heavy:
+            m = sr == h
+            assert sb[m][0] == g.rowptr[h] and se[m][-1] == g.rowptr[h + 1]
+            assert np.array_equal(sb[m][1:], se[m][:-1])
+            assert np.all((se[m] - sb[m])[:-1] == L)
+        assert set(sr.tolist()) == set(heavy.tolist())
+
+
+def pin_descriptors(orc):
+    def rp(deg):
+        return np.concatenate([[0], np.cumsum(deg)]).astype(np.int64)
+    d = orc.descriptors(rp([10] * 50), 50)
+    assert d["mean"] == 10.0 and d["cv"] == 0.0 and d["dmax"] == 10 and d["n_empty"] == 0
+    d = orc.descriptors(rp([0, 2]), 2)
+    assert d["mean"] == 1.0 and abs(d["cv"] - 1.0) < 1e-15 and d["n_empty"] == 1 and d["nnz"] == 2
+    d = orc.descriptors(rp([1, 2, 3, 4]), 4)
+    assert abs(d["cv"] - math.sqrt(1.25) / 2.5) < 1e-15 and d["dmax"] == 4
+    d = orc.descriptors(rp([]), 0)
+    assert d["mean"] == 0.0 and d["cv"] == 0.0 and d["nnz"] == 0
+    rng = np.random.default_rng(31)
+    deg = rng.zipf(2.1, size=5000).clip(0, 100000)
+    d = orc.descriptors(rp(deg), deg.size)
+    assert abs(d["cv"] - deg.std() / deg.mean()) <= 1e-12 * d["cv"]
+    assert d["dmax"] == deg.max() and d["n_empty"] == int((deg == 0).sum())
+
+
+def pin_validate(orc):
+    assert orc.validate(np.array([0, 2, 3], np.int64), np.array([0, 1, 1], np.int64), 2, 2) == -1
+    assert orc.validate(np.array([1, 2, 3], np.int64), np.array([0, 1, 1], np.int64), 2, 2) == 0
+    assert orc.validate(np.array([0, 2, 1], np.int64), np.array([0, 1, 1], np.int64), 2, 2) == 1
+    assert orc.validate(np.array([0, 2, 3], np.int64), np.array([0, 1, 2], np.int64), 2, 2) == 1
+    assert orc.validate(np.array([0, 2, 3], np.int64), np.array([0, -1, 1], np.int64), 2, 2) == 0
+    assert orc.validate(np.array([0, 0, 0], np.int64), np.zeros(0, np.int64), 2, 0) == -1
+
+
+def pin_mac_gap(orc):
+    with open(os.path.join(GOLDEN, "paramspmm_table2_mac_gap.txt")) as f:
+        rows = [line.split() for line in f if line.strip() and not line.startswith("#")]
+    assert len(rows) == 14
+    for dim, F, omega, gap in rows:
+        got = orc.mac_gap(int(dim), int(F), int(omega))
+        assert got == int(gap), f"gap(dim={dim}, F={F}) = {got}, Table 2 prints {gap}"
+
+
+def pin_tiny_config(orc):
+    """The full tiny regime against dense float64 products."""
+    w = W.make("tiny")
+    g = w.graph
+    B = w.B
+    ref = _dense(g) @ B.astype(np.float64)
+    S = _dense_abs(g) @ np.abs(B.astype(np.float64))
+    C = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "sum")
+    _bound_check(C, ref, S, g.degrees(), "tiny sum")
+    S2 = orc.sumabs(g.rowptr, g.col, g.val, g.M, B)
+    assert np.allclose(S2, S, rtol=1e-12, atol=0)
+
+
+ALL_PINS = [
+    pin_dense_bruteforce, pin_scipy_product, pin_identity, pin_ones, pin_empty_rows,
+    pin_max_numpy, pin_val_null_is_ones, pin_mean_sum_relation, pin_row_subset,
+    pin_partition, pin_descriptors, pin_validate, pin_mac_gap, pin_tiny_config,
+]

@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in copies of the oracle and require the pins to notice.
+
+Each mutant is a one-line textual change to oracle/spmm_oracle.c (a dropped
+term, a wrong sign, a transposed operand, a wrong tie rule, an off-by-one in
+the row split, ...), compiled with gcc into a temporary library.  The test
+passes only if at least one pin in tests/oracle_pins.py fails on it, which is
+evidence that the pins constrain every part of the oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "spmm_oracle.c")
+
+MUTANTS = {
+    "dropped_last_term": ("for (int64_t p = first; p < last; ++p) {\n                    float b",
+                          "for (int64_t p = first; p < last - 1; ++p) {\n                    float b"),
+    "wrong_sign": ("acc = acc + product(val, p, b);", "acc = acc - product(val, p, b);"),
+    "transposed_B": ("float b = B[col[p] * N + k];", "float b = B[k * K + col[p]];"),
+    "weight_ignored": ("return val[p] * b;", "return b;"),
+    "later_tie_wins": ("if (t > best) {", "if (t >= best) {"),
+    "argmax_is_position": ("arg = col[p];", "arg = p;"),
+    "empty_max_arg_zero": ("int64_t arg = -1;", "int64_t arg = 0;"),
+    "mean_divisor_off": ("acc / (float)deg", "acc / (float)(deg + 1)"),
+    "max_skips_first": ("float best = product(val, first, B[col[first] * N + k]);",
+                        "float best = -1e30f;"),
+    "heavy_threshold_ge": ("if (deg > T) {", "if (deg >= T) {"),
+    "piece_overlap": ("int64_t e = b + L;", "int64_t e = b + L + 1;"),
+    "sample_variance": ("var = (M > 0) ? var / (double)M : 0.0;",
+                        "var = (M > 1) ? var / (double)(M - 1) : 0.0;"),
+    "gap_as_printed": ("if (tr == 0) return 0;", ""),
+    "validate_skips_last_row": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t p",
+                                "for (int64_t i = 0; i + 1 < M; ++i)\n        for (int64_t p"),
+    "sumabs_signed": ("s += fabs(a * (double)B[col[p] * N + k]);", "s += a * (double)B[col[p] * N + k];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(before) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(before, after))
+    lib = obuild.build(str(src), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,16 @@
+"""Seeded synthetic inputs for CSR sparse x dense products (GNN neighbour aggregation).
+
+This module only builds inputs: graph structure (CSR), edge weights and the dense
+feature matrix.  It holds none of the product's arithmetic, so both the HIP path
+and the CPU oracle can be fed from it without sharing any computation.
+"""
+from .graphs import (  # noqa: F401
+    CONFIGS,
+    Graph,
+    Workload,
+    make,
+    make_graph,
+    make_features,
+    random_csr,
+    csr_from_pairs,
+)
