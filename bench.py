@@ -1,0 +1,303 @@
+"""Benchmark of the CSR SpMM hot path on one MI355X.
+
+One step = one spmm_run (all kernels of the product: light rows, split
+pieces and their combine when the plan has them) over the headline workload:
+the road-like graph (M = K = 1,000,000, Poisson(3) degrees, neighbours within
++-256 rows, unweighted) times B [1M, 64] fp32, sum reduction.  Inputs and the
+plan are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout (rank 0).  `value` is GFLOP/s = 2*nnz*N / t over
+the K timed back-to-back steps.  Alongside: effective HBM GB/s on the
+compulsory-byte model, the row kernel's roofline (achieved GB/s from HIP events
+on the launch stream, against the 8 TB/s HBM peak), the CPU oracle timed on
+this host, and per-regime results for the other synthetic graphs (warm
+back-to-back and cache-flushed medians).
+
+Byte model (compulsory bytes, per product): rowptr (M+1)*4 + nnz*(4 + 4 if
+weighted) + K*N*4 (B) + M*N*4 (C) [+ M*N*8 argmax for max]; the plan stores
+int32 indexes, so 4 bytes per index are what the kernels read.  Gather bytes
+nnz*N*4 are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SpMM GFLOP/s (2·nnz·N) + effective HBM GB/s as % of MI355X peak, per regime"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/spmm_internal.h"]
+
+REGIME_TEXT = {
+    "tiny": "tiny random graph M=K=2,000, Poisson(8) degrees, 1% empty rows, weighted, N=16",
+    "road": "road-like M=K=1,000,000, Poisson(3) degrees, neighbours within +-256 rows, unweighted, N=64",
+    "powerlaw": "power-law M=K=2,000,000, degree exponent 2.1 rescaled to mean 25, max 50,000, "
+                "uniform columns, GCN weights, N=128",
+    "diffusion": "diffusion M=K=1,000,000, exactly 10 neighbours (Gaussian offsets sigma 500), "
+                 "unweighted, N=16",
+    "community": "community M=K=500,000 in 256-node blocks, Bernoulli(0.1) inside + 2 outside, "
+                 "weighted, N=512",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def byte_model(g, N, reduce):
+    idx = 4
+    comp = (g.M + 1) * idx + g.nnz * (idx + (4 if g.val is not None else 0)) + g.K * N * 4 + g.M * N * 4
+    if reduce == "max":
+        comp += g.M * N * 8
+    return comp, g.nnz * N * 4
+
+
+def read_traffic(workload: str):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"row_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Runner:
+    def __init__(self, name, M=None):
+        import torch
+
+        import gnn_sparse_dense_amd as G
+        import workloads as W
+        self.torch, self.G = torch, G
+        t0 = time.time()
+        self.w = W.make(name, M=M)
+        self.gen_s = time.time() - t0
+        g = self.w.graph
+        self.g = g
+        dev = torch.device("cuda:0")
+        self.rowptr = torch.from_numpy(g.rowptr).to(dev)
+        self.col = torch.from_numpy(g.col).to(dev)
+        self.val = None if g.val is None else torch.from_numpy(g.val).to(dev)
+        self.B = torch.from_numpy(self.w.B).to(dev)
+        self.C = torch.empty((g.M, self.w.N), dtype=torch.float32, device=dev)
+        self.arg = None
+        t0 = time.time()
+        self.plan = G.spmm_plan_create(self.rowptr, self.col, self.val, g.M, g.K)
+        self.plan_s = time.time() - t0
+        self.info = G.spmm_plan_info(self.plan)
+
+    def step(self, reduce):
+        if reduce == "max" and self.arg is None:
+            self.arg = self.torch.empty((self.g.M, self.w.N), dtype=self.torch.int64, device=self.C.device)
+        self.G.spmm_run(self.plan, self.B, self.C, self.arg if reduce == "max" else None,
+                        self.w.N, reduce, None)
+
+    def time_steps(self, reduce, steps, warmup, flush=None):
+        """Per-step durations (ms) from HIP events on the launch stream, plus the
+        wall time of the whole back-to-back loop (ms) when flush is None."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(reduce)
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush()
+            starts[i].record()
+            self.step(reduce)
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall_ms
+
+    def close(self):
+        self.G.spmm_plan_destroy(self.plan)
+
+
+def make_flush():
+    import torch
+    buf = torch.ones(512 * 1024 * 1024 // 4 * 2, dtype=torch.float32, device="cuda:0")   # 1 GiB
+
+    def flush():
+        buf.sum()          # reads 1 GiB: evicts L2 and the 256 MB Infinity Cache
+    return flush
+
+
+def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
+    """The CPU oracle (single-threaded C, as built) on the headline workload."""
+    import oracle
+    g = w.graph
+    orc = oracle.default()
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps:
+        t0 = time.perf_counter()
+        orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s:
+            break
+    t = statistics.median(times)
+    return t, len(times)
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def regime_result(r, reduce, steps, warmup, flush):
+    g, N = r.g, r.w.N
+    warm, _ = r.time_steps(reduce, steps, warmup)
+    cold, _ = r.time_steps(reduce, steps, 2, flush=flush)
+    comp, gather = byte_model(g, N, reduce)
+    med_c = statistics.median(cold)
+    med_w = statistics.median(warm)
+    return {
+        "reduce": reduce, "M": g.M, "nnz": g.nnz, "N": N,
+        "ms_flushed_median": round(med_c, 5), "ms_flushed_min": round(min(cold), 5),
+        "ms_flushed_p90": round(percentile(cold, 0.9), 5),
+        "ms_warm_median": round(med_w, 5),
+        "gflops_flushed": round(2.0 * g.nnz * N / (med_c * 1e-3) / 1e9, 1),
+        "effective_GBps_flushed": round(comp / (med_c * 1e-3) / 1e9, 1),
+        "frac_hbm_peak_flushed": round(comp / (med_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "gather_GBps_flushed": round(gather / (med_c * 1e-3) / 1e9, 1),
+        "compulsory_MB": round(comp / 1e6, 1), "gather_MB": round(gather / 1e6, 1),
+        "route": {k: r.info[k] for k in ("route_lanes", "route_vec", "route_coarsen",
+                                         "route_rows_per_wave", "route_slices")},
+        "split": {"T": r.info["split_T"], "L": r.info["split_L"], "n_heavy": r.info["n_heavy"],
+                  "n_seg": r.info["n_seg"]},
+        "plan_ms": round(r.info["plan_ms"], 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--headline-only", action="store_true", help="skip the other regimes")
+    ap.add_argument("--regimes", default="tiny,diffusion,community,powerlaw")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows would shard with a per-layer halo exchange of B; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    headline, reduce = "road", "sum"
+    r = Runner(headline)
+    g, N = r.g, r.w.N
+    print(f"[bench] {headline}: M={g.M} nnz={g.nnz} N={N} gen={r.gen_s:.1f}s plan={r.info['plan_ms']:.1f}ms",
+          file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    durations, wall_ms = r.time_steps(reduce, args.steps, args.warmup)
+    ms_per_step = wall_ms / args.steps
+    avg_launch_ms = sum(durations) / len(durations)
+    comp, gather = byte_model(g, N, reduce)
+    flops = 2.0 * g.nnz * N
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    achieved = comp / (avg_launch_ms * 1e-3) / 1e9
+    traffic = read_traffic(headline)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": REGIME_TEXT[headline] + ", sum reduction", "M": g.M, "K": g.K,
+                   "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32},
+        "effective_GBps": round(comp / (ms_per_step * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(comp / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "gather_GBps": round(gather / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": "row_kernel_t (lanes=%d vec=%d coarsen=%d)" % (
+                r.info["route_lanes"], r.info["route_vec"], r.info["route_coarsen"]),
+            "bytes_per_launch": comp, "avg_launch_ms": round(avg_launch_ms, 5),
+        },
+    }
+
+    if not args.no_cpu:
+        t_cpu, reps = cpu_oracle_baseline(r.w, reduce)
+        result["cpu_baseline"] = {
+            "value": round(flops / t_cpu / 1e9, 3), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {headline} graph and B, {reduce}, median of {reps} single-threaded "
+                      f"oracle runs ({t_cpu * 1e3:.1f} ms each)",
+        }
+
+    if not args.headline_only:
+        flush = make_flush()
+        regimes = {}
+        regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush)
+                             for red in r.w.reduces]
+        r.close()
+        del r
+        torch.cuda.empty_cache()
+        for name in [x for x in args.regimes.split(",") if x]:
+            rr = Runner(name)
+            print(f"[bench] {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N} gen={rr.gen_s:.1f}s",
+                  file=sys.stderr, flush=True)
+            regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush)
+                             for red in rr.w.reduces]
+            rr.close()
+            del rr
+            torch.cuda.empty_cache()
+        result["regimes"] = regimes
+    else:
+        r.close()
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

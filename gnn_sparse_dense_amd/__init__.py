@@ -1,0 +1,222 @@
+"""Python binding of the gfx950 CSR SpMM library (include/spmm.h).
+
+Argument marshalling only: every step of the product runs in the HIP library
+libgnn_spmm.so next to this file.  PyTorch supplies device memory and the
+current stream.  Importing this package fails loudly when the library has not
+been built; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgnn_spmm.so")
+
+SPMM_SUM, SPMM_MEAN, SPMM_MAX = 0, 1, 2
+REDUCE = {"sum": SPMM_SUM, "mean": SPMM_MEAN, "max": SPMM_MAX}
+
+SPMM_OK = 0
+SPMM_E_INVALID_ARG = -1
+SPMM_E_BAD_CSR = -2
+SPMM_E_OOM = -3
+SPMM_E_HIP = -4
+SPMM_E_UNSUPPORTED = -5
+
+SPMM_OPT_SPLIT_T = 1
+SPMM_OPT_SPLIT_L = 2
+SPMM_OPT_SPLIT_MODE = 3
+SPMM_OPT_LANES = 4
+SPMM_OPT_COARSEN = 5
+SPMM_OPT_VEC = 6
+SPMM_OPT_XCD_REMAP = 7
+SPMM_OPT_NT_STORE = 8
+
+EXPORTED = (
+    "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
+    "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
+)
+
+
+class SpmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("nnz", ctypes.c_int64),
+        ("dmax", ctypes.c_int64), ("n_empty", ctypes.c_int64),
+        ("mean_deg", ctypes.c_double), ("cv_deg", ctypes.c_double),
+        ("split_T", ctypes.c_int64), ("split_L", ctypes.c_int64),
+        ("n_heavy", ctypes.c_int64), ("n_seg", ctypes.c_int64),
+        ("split_ratio", ctypes.c_double),
+        ("has_val", ctypes.c_int32), ("index_bits", ctypes.c_int32),
+        ("plan_ms", ctypes.c_double),
+        ("route_N", ctypes.c_int64),
+        ("route_lanes", ctypes.c_int32), ("route_vec", ctypes.c_int32),
+        ("route_coarsen", ctypes.c_int32), ("route_rows_per_wave", ctypes.c_int32),
+        ("route_slices", ctypes.c_int32), ("route_xcd_remap", ctypes.c_int32),
+        ("route_nt_store", ctypes.c_int32), ("route_split", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.spmm_plan_create.argtypes = [p, p, p, i64, i64]
+    lib.spmm_plan_create.restype = p
+    lib.spmm_run.argtypes = [p, p, p, p, i64, i32, p]
+    lib.spmm_run.restype = i32
+    lib.spmm_plan_destroy.argtypes = [p]
+    lib.spmm_plan_destroy.restype = i32
+    lib.spmm_plan_info.argtypes = [p, ctypes.POINTER(_Info)]
+    lib.spmm_plan_info.restype = i32
+    lib.spmm_plan_route.argtypes = [p, i64, i32]
+    lib.spmm_plan_route.restype = i32
+    lib.spmm_plan_partition.argtypes = [p, p, p, p, i64, p, i64, p]
+    lib.spmm_plan_partition.restype = i32
+    lib.spmm_plan_set_option.argtypes = [p, i32, i64]
+    lib.spmm_plan_set_option.restype = i32
+    lib.spmm_last_error.argtypes = [ctypes.c_char_p, i64]
+    lib.spmm_last_error.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def spmm_last_error():
+    buf = ctypes.create_string_buffer(512)
+    st = _lib.spmm_last_error(buf, 512)
+    return st, buf.value.decode(errors="replace")
+
+
+def _check(status: int):
+    if status != SPMM_OK:
+        st, msg = spmm_last_error()
+        raise SpmmError(status, msg)
+
+
+def _addr(t) -> Optional[int]:
+    """Device address of a tensor (or None), without touching its data."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def spmm_plan_create(rowptr, col, val, M: int, K: int) -> int:
+    """Plan handle for the CSR (rowptr int64 [M+1], col int64 [nnz], val fp32 or None)."""
+    for name, t, dt in (("rowptr", rowptr, "int64"), ("col", col, "int64"), ("val", val, "float32")):
+        if t is not None and not isinstance(t, int):
+            if str(t.dtype).split(".")[-1] != dt or not t.is_contiguous():
+                raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    h = _lib.spmm_plan_create(_addr(rowptr), _addr(col), _addr(val), int(M), int(K))
+    if not h:
+        st, msg = spmm_last_error()
+        raise SpmmError(st, msg)
+    return h
+
+
+def spmm_run(plan: int, B, C, argmax, N: int, reduce, stream=None) -> None:
+    """Enqueue C = reduce(A . B) (argmax for 'max' only) on `stream`
+    (an int handle, a torch stream, or None for torch's current stream)."""
+    red = REDUCE[reduce] if isinstance(reduce, str) else int(reduce)
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(_lib.spmm_run(plan, _addr(B), _addr(C), _addr(argmax), int(N), red, stream))
+
+
+def spmm_plan_destroy(plan: int) -> None:
+    _check(_lib.spmm_plan_destroy(plan))
+
+
+def spmm_plan_info(plan: int) -> dict:
+    info = _Info()
+    _check(_lib.spmm_plan_info(plan, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in _Info._fields_}
+
+
+def spmm_plan_route(plan: int, N: int, reduce) -> dict:
+    red = REDUCE[reduce] if isinstance(reduce, str) else int(reduce)
+    _check(_lib.spmm_plan_route(plan, int(N), red))
+    return spmm_plan_info(plan)
+
+
+def spmm_plan_partition(plan: int):
+    """Row split as host numpy arrays: dict(n_heavy, seg_row, seg_begin, seg_end, light)."""
+    import numpy as np
+    counts = np.zeros(3, dtype=np.int64)
+    z = ctypes.c_void_p(0)
+    _check(_lib.spmm_plan_partition(plan, z, z, z, 0, z, 0, counts.ctypes.data))
+    ns, nl = int(counts[1]), int(counts[2])
+    sr = np.empty(ns, np.int64)
+    sb = np.empty(ns, np.int64)
+    se = np.empty(ns, np.int64)
+    light = np.empty(nl, np.int64)
+    _check(_lib.spmm_plan_partition(plan, sr.ctypes.data, sb.ctypes.data, se.ctypes.data, ns,
+                                    light.ctypes.data, nl, counts.ctypes.data))
+    return dict(n_heavy=int(counts[0]), seg_row=sr, seg_begin=sb, seg_end=se, light=light)
+
+
+def spmm_plan_set_option(plan: int, option: int, value: int) -> None:
+    _check(_lib.spmm_plan_set_option(plan, int(option), int(value)))
+
+
+class SparseAdj:
+    """A CSR adjacency held once on the GPU and applied many times
+    (graph-spmm card, "Usage": build the CSR once, apply it per layer)."""
+
+    def __init__(self, rowptr, col, val=None, num_cols: Optional[int] = None):
+        self.M = int(rowptr.numel()) - 1
+        self.K = int(num_cols if num_cols is not None else self.M)
+        self.device = rowptr.device
+        self._plan = spmm_plan_create(rowptr, col, val, self.M, self.K)
+
+    @property
+    def plan(self) -> int:
+        return self._plan
+
+    def info(self) -> dict:
+        return spmm_plan_info(self._plan)
+
+    def set_option(self, option: int, value: int) -> None:
+        spmm_plan_set_option(self._plan, option, value)
+
+    def reduce(self, B, reduce: str = "sum", out=None, argmax=None, stream=None):
+        import torch
+        N = int(B.shape[1])
+        if out is None:
+            out = torch.empty((self.M, N), dtype=torch.float32, device=B.device)
+        if reduce == "max" and argmax is None:
+            argmax = torch.empty((self.M, N), dtype=torch.int64, device=B.device)
+        spmm_run(self._plan, B, out, argmax if reduce == "max" else None, N, reduce, stream)
+        return (out, argmax) if reduce == "max" else out
+
+    def __matmul__(self, B):
+        return self.reduce(B, "sum")
+
+    def close(self) -> None:
+        if self._plan:
+            spmm_plan_destroy(self._plan)
+            self._plan = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

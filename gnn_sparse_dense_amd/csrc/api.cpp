@@ -1,0 +1,672 @@
+// C ABI of the CSR SpMM library: plan construction (validation, descriptors,
+// narrowing, row split), the rule router and the per-call launches.
+#include <algorithm>
+#include <chrono>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "spmm_internal.h"
+
+#define SPMM_API extern "C" __attribute__((visibility("default")))
+
+namespace gspmm {
+int64_t colscan_blocks(int64_t nnz);
+}
+
+using namespace gspmm;
+
+namespace {
+
+thread_local int t_status = SPMM_OK;
+thread_local char t_msg[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(t_msg, sizeof(t_msg), fmt, ap);
+    va_end(ap);
+    t_status = status;
+    return status;
+}
+
+int succeed() {
+    t_status = SPMM_OK;
+    t_msg[0] = '\0';
+    return SPMM_OK;
+}
+
+int fail_hip(hipError_t e, const char *what) {
+    (void)hipGetLastError();
+    return fail(SPMM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_device_ptr(const void *p) {
+    if (p == nullptr) return false;
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    const hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+template <typename T>
+int dev_alloc(T **p, int64_t count, const char *what) {
+    *p = nullptr;
+    if (count <= 0) return SPMM_OK;
+    const hipError_t e = hipMalloc(reinterpret_cast<void **>(p), (size_t)count * sizeof(T));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return fail(SPMM_E_OOM, "device allocation of %s (%lld bytes) failed: %s", what,
+                    (long long)(count * (int64_t)sizeof(T)), hipGetErrorString(e));
+    }
+    return SPMM_OK;
+}
+
+template <typename T>
+void dev_free(T *&p) {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+}
+
+void free_split(spmm_plan *p) {
+    dev_free(p->heavy_rows);
+    dev_free(p->seg_first);
+    dev_free(p->seg_begin);
+    dev_free(p->seg_end);
+    dev_free(p->light_rows);
+    dev_free(p->partial);
+    dev_free(p->part_arg);
+    p->split = false;
+    p->n_heavy = p->n_seg = 0;
+    p->n_light = p->M;
+}
+
+void free_plan(spmm_plan *p) {
+    if (!p) return;
+    free_split(p);
+    dev_free(p->rowptr);
+    dev_free(p->col);
+    dev_free(p->val);
+    delete p;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+        else prev = -1;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+// Default split parameters.  ParamSpMM's split granularity (section 5.1,
+// eq. 3) is the mean non-empty row length rounded up to a multiple of the
+// wave width; with wave64 and GNN-typical degrees that is 64, which would cut
+// thousands of ordinary rows.  The threshold and piece length are therefore
+// max(that granularity, 512): rows above 512 entries take more than ~20x the
+// work of a typical row and are the ones that stall a wave-per-row schedule.
+void auto_split_params(const spmm_plan *p, int64_t *T, int64_t *L) {
+    const int64_t nonempty = p->M - p->n_empty;
+    const double dhat = nonempty > 0 ? (double)p->nnz / (double)nonempty : 0.0;
+    const int64_t sg = (int64_t)std::ceil(dhat / 64.0) * 64;
+    const int64_t base = std::max<int64_t>(sg, 512);
+    *T = p->opt_T >= 0 ? p->opt_T : base;
+    *L = p->opt_L > 0 ? p->opt_L : base;
+}
+
+int build_split(spmm_plan *p) {
+    free_split(p);
+    int64_t T, L;
+    auto_split_params(p, &T, &L);
+    p->T = T;
+    p->L = L;
+    const bool enabled =
+        p->opt_split == 1 || (p->opt_split == -1 && p->dmax > T && p->cv_deg > 1.0);
+    if (!enabled || p->M == 0) return SPMM_OK;
+
+    const int64_t nblocks = (p->M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
+    PartCount *d_counts = nullptr;
+    int st = dev_alloc(&d_counts, nblocks, "split counts");
+    if (st) return st;
+    hipError_t e = launch_part_count(p->rowptr, p->M, T, L, d_counts, nblocks, nullptr);
+    std::vector<PartCount> counts((size_t)nblocks);
+    if (e == hipSuccess)
+        e = hipMemcpy(counts.data(), d_counts, sizeof(PartCount) * nblocks, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+        dev_free(d_counts);
+        return fail_hip(e, "row split count");
+    }
+    PartCount run{0, 0, 0};
+    for (auto &c : counts) {            // exclusive scan in block order
+        const PartCount here = c;
+        c = run;
+        run.n_heavy += here.n_heavy;
+        run.n_seg += here.n_seg;
+        run.n_light += here.n_light;
+    }
+    if (run.n_heavy == 0) {
+        dev_free(d_counts);
+        return SPMM_OK;
+    }
+    if (run.n_seg >= INT_MAX || run.n_seg * (int64_t)kPartialWidth < 0) {
+        dev_free(d_counts);
+        return fail(SPMM_E_UNSUPPORTED, "row split would create %lld pieces", (long long)run.n_seg);
+    }
+    p->n_heavy = run.n_heavy;
+    p->n_seg = run.n_seg;
+    p->n_light = run.n_light;
+    if ((st = dev_alloc(&p->heavy_rows, p->n_heavy, "heavy rows")) ||
+        (st = dev_alloc(&p->seg_first, p->n_heavy + 1, "piece index")) ||
+        (st = dev_alloc(&p->seg_begin, p->n_seg, "piece begin")) ||
+        (st = dev_alloc(&p->seg_end, p->n_seg, "piece end")) ||
+        (st = dev_alloc(&p->light_rows, std::max<int64_t>(p->n_light, 1), "light rows")) ||
+        (st = dev_alloc(&p->partial, p->n_seg * kPartialWidth, "partial sums")) ||
+        (st = dev_alloc(&p->part_arg, p->n_seg * kPartialWidth, "partial argmax"))) {
+        dev_free(d_counts);
+        free_split(p);
+        return st;
+    }
+    e = hipMemcpy(d_counts, counts.data(), sizeof(PartCount) * nblocks, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = launch_part_write(p->rowptr, p->M, T, L, d_counts, p->heavy_rows, p->seg_first,
+                              p->seg_begin, p->seg_end, p->light_rows, nblocks, nullptr);
+    const int nseg32 = (int)p->n_seg;
+    if (e == hipSuccess)
+        e = hipMemcpy(p->seg_first + p->n_heavy, &nseg32, sizeof(int), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    dev_free(d_counts);
+    if (e != hipSuccess) {
+        free_split(p);
+        return fail_hip(e, "row split write");
+    }
+    p->split = true;
+    return SPMM_OK;
+}
+
+int pow2_ceil(int64_t x) {
+    int g = 1;
+    while (g < x && g < 64) g <<= 1;
+    return g;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Rule router: vector width from N and alignment, lanes per row from the
+// number of vector columns (a row's group spans the feature width once, so
+// narrow N packs several rows per wave), coarsening when one pass of 64
+// lanes does not cover the row.  Forced options override each rule.
+Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, const void *argmax) {
+    Route r;
+    const bool a16 = aligned(B, 16) && aligned(C, 16) && (!argmax || aligned(argmax, 16));
+    const bool a8 = aligned(B, 8) && aligned(C, 8) && (!argmax || aligned(argmax, 16));
+    int vec = (N % 4 == 0 && a16) ? 4 : (N % 2 == 0 && a8) ? 2 : 1;
+    if (p->opt_vec == 4 && N % 4 == 0 && a16) vec = 4;
+    else if (p->opt_vec == 2 && N % 2 == 0 && a8) vec = 2;
+    else if (p->opt_vec == 1) vec = 1;
+    const int64_t W = N / vec;
+    int G = std::max(4, pow2_ceil(W));
+    int F = W > G ? 2 : 1;
+    if (p->opt_lanes) G = p->opt_lanes;
+    if (p->opt_coarsen) F = p->opt_coarsen;
+    r.vec = vec;
+    r.lanes = G;
+    r.coarsen = F;
+    r.slices = (int)((W + (int64_t)G * F - 1) / ((int64_t)G * F));
+    r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 1;
+    r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
+    r.split = p->split;
+    return r;
+}
+
+// Launch the row kernel over tasks [0, ntasks), in several dispatches when
+// one grid would exceed the 2^32 work-item limit of a dispatch dimension.
+hipError_t launch_rows(RowKernelFn fn, RowArgs a, int rows_per_wave, int slices, hipStream_t s) {
+    const int64_t per_block = (int64_t)rows_per_wave * kWaves;
+    const int64_t max_blocks = (int64_t)(UINT32_MAX / kBlock);
+    const int64_t end = a.ntasks;
+    for (int64_t base = 0; base < end; base += max_blocks * per_block) {
+        const int64_t n = std::min(end - base, max_blocks * per_block);
+        a.task_base = base;
+        a.ntasks = base + n;
+        void *args[] = {&a};
+        const dim3 grid((unsigned)((n + per_block - 1) / per_block), (unsigned)slices);
+        const hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, dim3(kBlock), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+SPMM_API int spmm_last_error(char *buf, int64_t cap) {
+    if (buf && cap > 0) {
+        std::strncpy(buf, t_msg, (size_t)cap - 1);
+        buf[cap - 1] = '\0';
+    }
+    return t_status;
+}
+
+SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const float *val,
+                                      int64_t M, int64_t K) {
+    const auto t0 = std::chrono::steady_clock::now();
+    if (M < 0 || K < 0) {
+        fail(SPMM_E_INVALID_ARG, "negative size (M=%lld, K=%lld)", (long long)M, (long long)K);
+        return nullptr;
+    }
+    if (M >= INT_MAX || K >= INT_MAX) {
+        fail(SPMM_E_UNSUPPORTED, "M and K must be below 2^31 - 1");
+        return nullptr;
+    }
+    if (!rowptr) {
+        fail(SPMM_E_INVALID_ARG, "rowptr is NULL");
+        return nullptr;
+    }
+    if (!is_device_ptr(rowptr)) {
+        fail(SPMM_E_INVALID_ARG, "rowptr is not device memory");
+        return nullptr;
+    }
+    hipError_t e = hipDeviceSynchronize();   // inputs may still be in flight on other streams
+    if (e != hipSuccess) {
+        fail_hip(e, "synchronise before plan creation");
+        return nullptr;
+    }
+    int64_t ends[2] = {0, 0};
+    e = hipMemcpy(&ends[0], rowptr, sizeof(int64_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(&ends[1], rowptr + M, sizeof(int64_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+        fail_hip(e, "read rowptr[0] and rowptr[M]");
+        return nullptr;
+    }
+    if (ends[0] != 0) {
+        fail(SPMM_E_BAD_CSR, "invalid CSR: first bad row 0 (rowptr[0] = %lld, expected 0)",
+             (long long)ends[0]);
+        return nullptr;
+    }
+    const int64_t nnz = ends[1];
+    if (nnz < 0) {
+        fail(SPMM_E_BAD_CSR, "invalid CSR: rowptr[M] = %lld is negative", (long long)nnz);
+        return nullptr;
+    }
+    if (nnz >= INT_MAX) {
+        fail(SPMM_E_UNSUPPORTED, "nnz = %lld must be below 2^31 - 1", (long long)nnz);
+        return nullptr;
+    }
+    if (nnz > 0 && K == 0) {
+        fail(SPMM_E_BAD_CSR, "invalid CSR: %lld entries with K = 0", (long long)nnz);
+        return nullptr;
+    }
+    if (nnz > 0 && !is_device_ptr(col)) {
+        fail(SPMM_E_INVALID_ARG, "col is NULL or not device memory");
+        return nullptr;
+    }
+    if (val && nnz > 0 && !is_device_ptr(val)) {
+        fail(SPMM_E_INVALID_ARG, "val is not device memory");
+        return nullptr;
+    }
+
+    spmm_plan *p = new (std::nothrow) spmm_plan();
+    if (!p) {
+        fail(SPMM_E_OOM, "host allocation of the plan failed");
+        return nullptr;
+    }
+    (void)hipGetDevice(&p->device);
+    p->M = M;
+    p->K = K;
+    p->nnz = nnz;
+    p->n_light = M;
+
+    int st;
+    if ((st = dev_alloc(&p->rowptr, M + 1, "rowptr")) || (st = dev_alloc(&p->col, nnz, "col")) ||
+        (val && (st = dev_alloc(&p->val, nnz, "val")))) {
+        free_plan(p);
+        return nullptr;
+    }
+
+    // rowptr: validation, descriptors, int32 copy
+    const int64_t rblocks = (M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
+    RowScanOut *d_rows = nullptr;
+    if ((st = dev_alloc(&d_rows, std::max<int64_t>(rblocks, 1), "row scan"))) {
+        free_plan(p);
+        return nullptr;
+    }
+    if (M == 0) e = hipMemset(p->rowptr, 0, sizeof(int));
+    else e = launch_rowscan(rowptr, M, p->rowptr, d_rows, rblocks, nullptr);
+    std::vector<RowScanOut> rs((size_t)rblocks);
+    if (e == hipSuccess && rblocks > 0)
+        e = hipMemcpy(rs.data(), d_rows, sizeof(RowScanOut) * rblocks, hipMemcpyDeviceToHost);
+    dev_free(d_rows);
+    if (e != hipSuccess) {
+        fail_hip(e, "row scan");
+        free_plan(p);
+        return nullptr;
+    }
+    int64_t bad_row = INT64_MAX, sum_deg = 0, sum_deg2 = 0, dmax = 0, n_empty = 0;
+    for (const auto &r : rs) {
+        bad_row = std::min(bad_row, r.bad_row);
+        sum_deg += r.sum_deg;
+        sum_deg2 += r.sum_deg2;
+        dmax = std::max(dmax, r.dmax);
+        n_empty += r.n_empty;
+    }
+    if (bad_row != INT64_MAX) {
+        fail(SPMM_E_BAD_CSR, "invalid CSR: first bad row %lld (rowptr decreases)", (long long)bad_row);
+        free_plan(p);
+        return nullptr;
+    }
+
+    // col: range check, int32 copy
+    if (nnz > 0) {
+        const int64_t cblocks = colscan_blocks(nnz);
+        int64_t *d_bad = nullptr;
+        if ((st = dev_alloc(&d_bad, cblocks, "col scan"))) {
+            free_plan(p);
+            return nullptr;
+        }
+        e = launch_colscan(col, nnz, K, p->col, d_bad, cblocks, nullptr);
+        std::vector<int64_t> bad((size_t)cblocks);
+        if (e == hipSuccess)
+            e = hipMemcpy(bad.data(), d_bad, sizeof(int64_t) * cblocks, hipMemcpyDeviceToHost);
+        dev_free(d_bad);
+        if (e != hipSuccess) {
+            fail_hip(e, "column scan");
+            free_plan(p);
+            return nullptr;
+        }
+        const int64_t bad_pos = *std::min_element(bad.begin(), bad.end());
+        if (bad_pos != INT64_MAX) {
+            // locate the row owning entry bad_pos (error path only)
+            std::vector<int64_t> h_rowptr((size_t)M + 1);
+            int64_t row = -1;
+            if (hipMemcpy(h_rowptr.data(), rowptr, sizeof(int64_t) * (M + 1), hipMemcpyDeviceToHost) ==
+                hipSuccess)
+                row = (int64_t)(std::upper_bound(h_rowptr.begin(), h_rowptr.end(), bad_pos) -
+                                h_rowptr.begin()) - 1;
+            fail(SPMM_E_BAD_CSR, "invalid CSR: first bad row %lld (entry %lld has a column outside [0, %lld))",
+                 (long long)row, (long long)bad_pos, (long long)K);
+            free_plan(p);
+            return nullptr;
+        }
+        if (val) {
+            e = hipMemcpy(p->val, val, sizeof(float) * nnz, hipMemcpyDeviceToDevice);
+            if (e != hipSuccess) {
+                fail_hip(e, "copy val");
+                free_plan(p);
+                return nullptr;
+            }
+        }
+    }
+
+    // descriptors (RA-SpMM: M, mean degree, coefficient of variation)
+    p->dmax = dmax;
+    p->n_empty = n_empty;
+    p->sum_deg2 = sum_deg2;
+    p->mean_deg = M > 0 ? (double)sum_deg / (double)M : 0.0;
+    if (M > 0 && sum_deg > 0) {
+        const __int128 num = (__int128)M * (__int128)sum_deg2 - (__int128)sum_deg * (__int128)sum_deg;
+        const double var = (double)num / ((double)M * (double)M);
+        p->cv_deg = std::sqrt(std::max(var, 0.0)) / p->mean_deg;
+    }
+
+    if ((st = build_split(p))) {
+        free_plan(p);
+        return nullptr;
+    }
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        fail_hip(e, "plan creation");
+        free_plan(p);
+        return nullptr;
+    }
+    p->plan_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    succeed();
+    return p;
+}
+
+SPMM_API int spmm_plan_destroy(spmm_plan_t plan) {
+    if (!plan) return succeed();
+    DeviceGuard dg(plan->device);
+    free_plan(plan);
+    return succeed();
+}
+
+SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
+    if (!p) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
+    DeviceGuard dg(p->device);
+    switch (option) {
+        case SPMM_OPT_SPLIT_T:
+            if (value < -1) return fail(SPMM_E_INVALID_ARG, "split threshold must be >= -1");
+            p->opt_T = value;
+            break;
+        case SPMM_OPT_SPLIT_L:
+            if (value == 0 || value < -1) return fail(SPMM_E_INVALID_ARG, "piece length must be > 0 or -1");
+            p->opt_L = value;
+            break;
+        case SPMM_OPT_SPLIT_MODE:
+            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "split mode must be -1, 0 or 1");
+            p->opt_split = value;
+            break;
+        case SPMM_OPT_LANES:
+            if (!(value == 0 || value == 4 || value == 8 || value == 16 || value == 32 || value == 64))
+                return fail(SPMM_E_INVALID_ARG, "lanes per row must be 0, 4, 8, 16, 32 or 64");
+            p->opt_lanes = (int)value;
+            return succeed();
+        case SPMM_OPT_COARSEN:
+            if (value < 0 || value > 2) return fail(SPMM_E_INVALID_ARG, "coarsening must be 0, 1 or 2");
+            p->opt_coarsen = (int)value;
+            return succeed();
+        case SPMM_OPT_VEC:
+            if (!(value == 0 || value == 1 || value == 2 || value == 4))
+                return fail(SPMM_E_INVALID_ARG, "vector width must be 0, 1, 2 or 4");
+            p->opt_vec = (int)value;
+            return succeed();
+        case SPMM_OPT_XCD_REMAP:
+            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "XCD remap must be -1, 0 or 1");
+            p->opt_xcd = (int)value;
+            return succeed();
+        case SPMM_OPT_NT_STORE:
+            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
+            p->opt_nt = (int)value;
+            return succeed();
+        default:
+            return fail(SPMM_E_INVALID_ARG, "unknown option %d", option);
+    }
+    const hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(e, "synchronise before rebuilding the split");
+    const int st = build_split(p);
+    if (st) return st;
+    return succeed();
+}
+
+SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
+    if (!p || !out) return fail(SPMM_E_INVALID_ARG, "plan or output is NULL");
+    struct spmm_plan_info info;
+    std::memset(&info, 0, sizeof(info));
+    info.M = p->M;
+    info.K = p->K;
+    info.nnz = p->nnz;
+    info.dmax = p->dmax;
+    info.n_empty = p->n_empty;
+    info.mean_deg = p->mean_deg;
+    info.cv_deg = p->cv_deg;
+    info.split_T = p->T;
+    info.split_L = p->L;
+    info.n_heavy = p->split ? p->n_heavy : 0;
+    info.n_seg = p->split ? p->n_seg : 0;
+    info.split_ratio = p->M > 0 ? (double)(p->split ? p->n_light + p->n_seg : p->M) / (double)p->M : 1.0;
+    info.has_val = p->val != nullptr;
+    info.index_bits = 32;
+    info.plan_ms = p->plan_ms;
+    info.route_N = p->route_N;
+    info.route_lanes = p->route.lanes;
+    info.route_vec = p->route.vec;
+    info.route_coarsen = p->route.coarsen;
+    info.route_rows_per_wave = 64 / p->route.lanes;
+    info.route_slices = p->route.slices;
+    info.route_xcd_remap = p->route.xcd_remap;
+    info.route_nt_store = p->route.nt_store;
+    info.route_split = p->route.split ? 1 : 0;
+    *out = info;
+    return succeed();
+}
+
+SPMM_API int spmm_plan_route(spmm_plan_t p, int64_t N, int reduce) {
+    if (!p) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
+    if (N <= 0) return fail(SPMM_E_INVALID_ARG, "N must be positive");
+    if (reduce < SPMM_SUM || reduce > SPMM_MAX) return fail(SPMM_E_INVALID_ARG, "unknown reduce %d", reduce);
+    static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+    p->route = route_for(p, N, dummy, dummy, nullptr);
+    p->route_N = N;
+    return succeed();
+}
+
+SPMM_API int spmm_plan_partition(spmm_plan_t p, int64_t *seg_row, int64_t *seg_begin, int64_t *seg_end,
+                                 int64_t seg_cap, int64_t *light, int64_t light_cap, int64_t *counts) {
+    if (!p || !counts) return fail(SPMM_E_INVALID_ARG, "plan or counts is NULL");
+    if (seg_cap < 0 || light_cap < 0) return fail(SPMM_E_INVALID_ARG, "negative capacity");
+    if ((seg_cap > 0 && (!seg_row || !seg_begin || !seg_end)) || (light_cap > 0 && !light))
+        return fail(SPMM_E_INVALID_ARG, "output array is NULL");
+    DeviceGuard dg(p->device);
+    const int64_t nh = p->split ? p->n_heavy : 0;
+    const int64_t ns = p->split ? p->n_seg : 0;
+    const int64_t nl = p->split ? p->n_light : p->M;
+    counts[0] = nh;
+    counts[1] = ns;
+    counts[2] = nl;
+    hipError_t e = hipSuccess;
+    if (ns > 0 && seg_cap > 0) {
+        std::vector<int> hr((size_t)nh), sf((size_t)nh + 1), sb((size_t)ns), se((size_t)ns);
+        e = hipMemcpy(hr.data(), p->heavy_rows, sizeof(int) * nh, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipMemcpy(sf.data(), p->seg_first, sizeof(int) * (nh + 1), hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipMemcpy(sb.data(), p->seg_begin, sizeof(int) * ns, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipMemcpy(se.data(), p->seg_end, sizeof(int) * ns, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "copy row split");
+        for (int64_t h = 0; h < nh; ++h)
+            for (int64_t s = sf[h]; s < sf[h + 1] && s < seg_cap; ++s) seg_row[s] = hr[h];
+        for (int64_t s = 0; s < ns && s < seg_cap; ++s) {
+            seg_begin[s] = sb[s];
+            seg_end[s] = se[s];
+        }
+    }
+    if (light_cap > 0) {
+        if (p->split) {
+            std::vector<int> lr((size_t)nl);
+            if (nl > 0) e = hipMemcpy(lr.data(), p->light_rows, sizeof(int) * nl, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return fail_hip(e, "copy light rows");
+            for (int64_t i = 0; i < nl && i < light_cap; ++i) light[i] = lr[i];
+        } else {
+            for (int64_t i = 0; i < nl && i < light_cap; ++i) light[i] = i;
+        }
+    }
+    return succeed();
+}
+
+SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, int64_t N, int reduce,
+                      void *stream) {
+    if (!p) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
+    if (N <= 0) return fail(SPMM_E_INVALID_ARG, "N must be positive (got %lld)", (long long)N);
+    if (reduce < SPMM_SUM || reduce > SPMM_MAX) return fail(SPMM_E_INVALID_ARG, "unknown reduce %d", reduce);
+    if (argmax && reduce != SPMM_MAX) return fail(SPMM_E_INVALID_ARG, "argmax is only produced by SPMM_MAX");
+    if (N >= INT_MAX) return fail(SPMM_E_UNSUPPORTED, "N must be below 2^31 - 1");
+    if (p->M == 0) return succeed();
+    if (!is_device_ptr(C)) return fail(SPMM_E_INVALID_ARG, "C is NULL or not device memory");
+    if (p->K > 0 && !is_device_ptr(B)) return fail(SPMM_E_INVALID_ARG, "B is NULL or not device memory");
+    if (argmax && !is_device_ptr(argmax)) return fail(SPMM_E_INVALID_ARG, "argmax is not device memory");
+    {
+        const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(p->K * N) * sizeof(float);
+        const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(p->M * N) * sizeof(float);
+        const uintptr_t a0 = (uintptr_t)argmax, a1 = a0 + (uintptr_t)(p->M * N) * sizeof(int64_t);
+        if (B && b0 < c1 && c0 < b1) return fail(SPMM_E_INVALID_ARG, "B overlaps C");
+        if (B && argmax && b0 < a1 && a0 < b1) return fail(SPMM_E_INVALID_ARG, "B overlaps argmax");
+        if (argmax && c0 < a1 && a0 < c1) return fail(SPMM_E_INVALID_ARG, "C overlaps argmax");
+    }
+    DeviceGuard dg(p->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool is_max = reduce == SPMM_MAX;
+    const bool has_val = p->val != nullptr;
+
+    Route r = route_for(p, N, B, C, argmax);
+    RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false};
+    RowKernelFn fn = row_kernel(key);
+    if (!fn) return fail(SPMM_E_UNSUPPORTED, "no kernel for lanes=%d vec=%d coarsen=%d", r.lanes, r.vec, r.coarsen);
+    if (r.slices > 65535) return fail(SPMM_E_UNSUPPORTED, "N = %lld needs too many column slices", (long long)N);
+    p->route = r;
+    p->route_N = N;
+
+    RowArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.rowptr = p->rowptr;
+    a.rows = p->split ? p->light_rows : nullptr;
+    a.col = p->col;
+    a.val = p->val;
+    a.B = B;
+    a.out = C;
+    a.argmax = argmax;
+    a.ldo = N;
+    a.N = N;
+    a.c_begin = 0;
+    a.c_end = N;
+    a.ntasks = p->split ? p->n_light : p->M;
+    a.mean = reduce == SPMM_MEAN;
+    a.xcd_remap = r.xcd_remap;
+    a.nt_store = r.nt_store;
+    hipError_t e = launch_rows(fn, a, 64 / r.lanes, r.slices, s);
+    if (e != hipSuccess) return fail_hip(e, "row kernel launch");
+
+    if (p->split && p->n_seg > 0) {
+        for (int64_t w0 = 0; w0 < N; w0 += kPartialWidth) {
+            const int64_t w1 = std::min<int64_t>(N, w0 + kPartialWidth);
+            const int64_t Wv = (w1 - w0) / r.vec;
+            const int F = Wv > 64 ? 2 : 1;
+            const int slices = (int)((Wv + 64 * F - 1) / (64 * F));
+            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true});
+            if (!pf) return fail(SPMM_E_UNSUPPORTED, "no piece kernel for vec=%d", r.vec);
+            RowArgs pa;
+            std::memset(&pa, 0, sizeof(pa));
+            pa.seg_begin = p->seg_begin;
+            pa.seg_end = p->seg_end;
+            pa.col = p->col;
+            pa.val = p->val;
+            pa.B = B;
+            pa.out = p->partial;
+            pa.part_arg = p->part_arg;
+            pa.ldo = kPartialWidth;
+            pa.N = N;
+            pa.c_begin = w0;
+            pa.c_end = w1;
+            pa.ntasks = p->n_seg;
+            pa.xcd_remap = 0;
+            pa.nt_store = 0;
+            e = launch_rows(pf, pa, 1, slices, s);
+            if (e != hipSuccess) return fail_hip(e, "piece kernel launch");
+            CombineArgs ca;
+            ca.heavy_rows = p->heavy_rows;
+            ca.seg_first = p->seg_first;
+            ca.rowptr = p->rowptr;
+            ca.partial = p->partial;
+            ca.part_arg = p->part_arg;
+            ca.C = C;
+            ca.argmax = argmax;
+            ca.N = N;
+            ca.c_begin = w0;
+            ca.c_end = w1;
+            ca.n_heavy = p->n_heavy;
+            ca.mean = reduce == SPMM_MEAN;
+            e = launch_combine(ca, is_max, s);
+            if (e != hipSuccess) return fail_hip(e, "combine launch");
+        }
+    }
+    return succeed();
+}

@@ -1,0 +1,217 @@
+// Plan-time kernels: CSR validation, degree descriptors, index narrowing and
+// the row split.  All are single passes over rowptr or col (O(M) / O(nnz)),
+// run once per graph and amortised over every later product (RA-SpMM,
+// abstract and "Matched lifecycle timing": descriptors come from one O(M)
+// pass over the row pointer; formats are built once and reused).
+//
+// Each block reduces its slice to one record; the host folds the records in
+// block order, so every result is exact and independent of scheduling.
+#include <climits>
+
+#include "spmm_internal.h"
+
+namespace gspmm {
+
+namespace {
+
+__device__ __forceinline__ void block_reduce5(int64_t &mn, uint64_t &s1, uint64_t &s2, int64_t &mx,
+                                              int64_t &ne) {
+    __shared__ int64_t sh_mn[kBlock], sh_mx[kBlock], sh_ne[kBlock];
+    __shared__ uint64_t sh_s1[kBlock], sh_s2[kBlock];
+    const int t = threadIdx.x;
+    sh_mn[t] = mn; sh_s1[t] = s1; sh_s2[t] = s2; sh_mx[t] = mx; sh_ne[t] = ne;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (t < o) {
+            sh_mn[t] = min(sh_mn[t], sh_mn[t + o]);
+            sh_s1[t] += sh_s1[t + o];
+            sh_s2[t] += sh_s2[t + o];
+            sh_mx[t] = max(sh_mx[t], sh_mx[t + o]);
+            sh_ne[t] += sh_ne[t + o];
+        }
+        __syncthreads();
+    }
+    mn = sh_mn[0]; s1 = sh_s1[0]; s2 = sh_s2[0]; mx = sh_mx[0]; ne = sh_ne[0];
+}
+
+// Rows [b*kRowsPerScanBlock, ...): monotonicity (and rowptr[0] == 0), degree
+// sums, largest degree, empty rows; also writes the int32 copy of rowptr.
+// Callers guarantee rowptr[M] < 2^31.
+__global__ __launch_bounds__(kBlock) void rowscan_kernel(const int64_t *__restrict__ rowptr, int64_t M,
+                                                         int *__restrict__ rowptr32,
+                                                         RowScanOut *__restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock;
+    int64_t bad = INT64_MAX, mx = 0, ne = 0;
+    uint64_t s1 = 0, s2 = 0;
+    for (int j = threadIdx.x; j < kRowsPerScanBlock; j += kBlock) {
+        const int64_t i = base + j;
+        if (i >= M) break;
+        const int64_t a0 = rowptr[i];
+        const int64_t a1 = rowptr[i + 1];
+        const int64_t d = a1 - a0;
+        if (d < 0 || (i == 0 && a0 != 0)) bad = min(bad, i);
+        rowptr32[i] = (int)a0;
+        if (i == M - 1) rowptr32[M] = (int)a1;
+        const uint64_t du = (uint64_t)d;
+        s1 += du;
+        s2 += du * du;
+        mx = max(mx, d);
+        ne += (d == 0);
+    }
+    block_reduce5(bad, s1, s2, mx, ne);
+    if (threadIdx.x == 0) out[blockIdx.x] = RowScanOut{bad, (int64_t)s1, (int64_t)s2, mx, ne};
+}
+
+constexpr int kColsPerThread = 8;
+constexpr int kColsPerBlock = kBlock * kColsPerThread;
+
+// Column range check and int32 narrowing; one record per block: the first bad
+// entry position or INT64_MAX.
+__global__ __launch_bounds__(kBlock) void colscan_kernel(const int64_t *__restrict__ col, int64_t nnz,
+                                                         int64_t K, int *__restrict__ col32,
+                                                         int64_t *__restrict__ bad_pos) {
+    const int64_t base = (int64_t)blockIdx.x * kColsPerBlock;
+    int64_t bad = INT64_MAX;
+#pragma unroll
+    for (int j = 0; j < kColsPerThread; ++j) {
+        const int64_t p = base + j * kBlock + threadIdx.x;
+        if (p < nnz) {
+            const int64_t c = col[p];
+            if (c < 0 || c >= K) bad = min(bad, p);
+            col32[p] = (int)c;
+        }
+    }
+    __shared__ int64_t sh[kBlock];
+    sh[threadIdx.x] = bad;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] = min(sh[threadIdx.x], sh[threadIdx.x + o]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) bad_pos[blockIdx.x] = sh[0];
+}
+
+constexpr int kRowsPerThread = kRowsPerScanBlock / kBlock;   // consecutive rows per thread
+
+__device__ __forceinline__ int64_t pieces_of(int64_t deg, int64_t L) { return (deg + L - 1) / L; }
+
+__global__ __launch_bounds__(kBlock) void part_count_kernel(const int *__restrict__ rowptr, int64_t M,
+                                                            int64_t T, int64_t L,
+                                                            PartCount *__restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock + (int64_t)threadIdx.x * kRowsPerThread;
+    int64_t nh = 0, ns = 0, nl = 0;
+    for (int j = 0; j < kRowsPerThread; ++j) {
+        const int64_t i = base + j;
+        if (i >= M) break;
+        const int64_t d = rowptr[i + 1] - rowptr[i];
+        if (d > T) {
+            nh += 1;
+            ns += pieces_of(d, L);
+        } else {
+            nl += 1;
+        }
+    }
+    __shared__ int64_t sh[3][kBlock];
+    sh[0][threadIdx.x] = nh; sh[1][threadIdx.x] = ns; sh[2][threadIdx.x] = nl;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o)
+            for (int c = 0; c < 3; ++c) sh[c][threadIdx.x] += sh[c][threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = PartCount{sh[0][0], sh[1][0], sh[2][0]};
+}
+
+// Ordered compaction: thread t of block b owns kRowsPerThread consecutive
+// rows, so a block-wide exclusive scan of per-thread counts plus the block's
+// global offset gives every heavy row, piece and light row its final index.
+__global__ __launch_bounds__(kBlock) void part_write_kernel(
+    const int *__restrict__ rowptr, int64_t M, int64_t T, int64_t L,
+    const PartCount *__restrict__ block_off, int *__restrict__ heavy_rows, int *__restrict__ seg_first,
+    int *__restrict__ seg_begin, int *__restrict__ seg_end, int *__restrict__ light_rows) {
+    const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock + (int64_t)threadIdx.x * kRowsPerThread;
+    int64_t cnt[3] = {0, 0, 0};
+    for (int j = 0; j < kRowsPerThread; ++j) {
+        const int64_t i = base + j;
+        if (i >= M) break;
+        const int64_t d = rowptr[i + 1] - rowptr[i];
+        if (d > T) {
+            cnt[0] += 1;
+            cnt[1] += pieces_of(d, L);
+        } else {
+            cnt[2] += 1;
+        }
+    }
+    __shared__ int64_t sh[3][kBlock];
+    for (int c = 0; c < 3; ++c) sh[c][threadIdx.x] = cnt[c];
+    __syncthreads();
+    for (int o = 1; o < kBlock; o <<= 1) {        // inclusive Hillis-Steele scan
+        int64_t y[3];
+        for (int c = 0; c < 3; ++c) y[c] = threadIdx.x >= o ? sh[c][threadIdx.x - o] : 0;
+        __syncthreads();
+        for (int c = 0; c < 3; ++c) sh[c][threadIdx.x] += y[c];
+        __syncthreads();
+    }
+    const PartCount bo = block_off[blockIdx.x];
+    int64_t ho = bo.n_heavy + sh[0][threadIdx.x] - cnt[0];
+    int64_t so = bo.n_seg + sh[1][threadIdx.x] - cnt[1];
+    int64_t lo = bo.n_light + sh[2][threadIdx.x] - cnt[2];
+    for (int j = 0; j < kRowsPerThread; ++j) {
+        const int64_t i = base + j;
+        if (i >= M) break;
+        const int64_t r0 = rowptr[i], r1 = rowptr[i + 1];
+        if (r1 - r0 > T) {
+            heavy_rows[ho] = (int)i;
+            seg_first[ho] = (int)so;
+            ho += 1;
+            for (int64_t b = r0; b < r1; b += L) {
+                seg_begin[so] = (int)b;
+                seg_end[so] = (int)min(b + L, r1);
+                so += 1;
+            }
+        } else if (light_rows) {
+            light_rows[lo] = (int)i;
+            lo += 1;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rowscan(const int64_t *rowptr, int64_t M, int *rowptr32, RowScanOut *out,
+                          int64_t nblocks, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rowscan_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr, M,
+                       rowptr32, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_colscan(const int64_t *col, int64_t nnz, int64_t K, int *col32, int64_t *bad_pos,
+                          int64_t nblocks, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(colscan_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, col, nnz, K,
+                       col32, bad_pos);
+    return hipGetLastError();
+}
+
+int64_t colscan_blocks(int64_t nnz) { return (nnz + kColsPerBlock - 1) / kColsPerBlock; }
+
+hipError_t launch_part_count(const int *rowptr32, int64_t M, int64_t T, int64_t L, PartCount *out,
+                             int64_t nblocks, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(part_count_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr32, M,
+                       T, L, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t L,
+                             const PartCount *offsets, int *heavy_rows, int *seg_first,
+                             int *seg_begin, int *seg_end, int *light_rows, int64_t nblocks,
+                             hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(part_write_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr32, M, T,
+                       L, offsets, heavy_rows, seg_first, seg_begin, seg_end, light_rows);
+    return hipGetLastError();
+}
+
+}  // namespace gspmm

@@ -1,0 +1,352 @@
+// Row kernel of the CSR SpMM: G lanes per output row, 64/G rows per wave64.
+//
+// Mapping (ParamSpMM section 2, Algorithm 1: a worker owns a segment of one C
+// row and walks that row's entries; graph-spmm card, "Method": lanes hold
+// strided slices of the feature columns, each output reduces privately in a
+// register, nothing is shared between waves, so no atomics):
+//   * lane g of a row's group owns columns c0 + (f*G + g)*VEC .. +VEC-1 for
+//     f < F (F = coarsening factor, ParamSpMM section 3.3 / GE-SpMM section
+//     III-C "coarse-grained warp merging"), so for each entry the group's B
+//     access is one contiguous, coalesced run of G*VEC floats per f;
+//   * the wave's entries (all of its rows together) are staged kChunk at a
+//     time in LDS with coalesced loads and then read back by every lane of the
+//     owning group (GE-SpMM section III-B "coalesced row caching");
+//   * several rows per wave when G < 64 serve narrow N and low degree
+//     (DualGCN section 3.3, sparse path: a warp handles a subset of rows);
+//   * each lane walks its row's entries in stored order with one accumulator
+//     per output (fused multiply-add for sum/mean, strict '>' for max), so
+//     every variant produces the same bits for a given row.
+// Piece mode runs the same loop over pieces of split rows and writes partial
+// results (plus int32 partial argmax) for the ordered combine.
+#pragma once
+
+#include <cmath>
+
+#include "spmm_internal.h"
+
+namespace gspmm {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+
+// Block id permutation giving each XCD a contiguous range of logical blocks.
+// The hardware hands consecutive block ids to the 8 XCDs round-robin; this
+// maps the j-th block that lands on XCD x to logical block start(x) + j.
+__device__ __forceinline__ int64_t xcd_remap_block(int64_t b, int64_t nb) {
+    const int64_t per = nb / kXcds, rem = nb % kXcds;
+    const int64_t x = b % kXcds, j = b / kXcds;
+    return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// Orders this wave's LDS writes before its later LDS reads (and reads before
+// the next overwrite).  A wave's LDS operations execute in program order, so
+// only compiler reordering has to be prevented.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float *p, float (&x)[VEC]) {
+    if constexpr (VEC == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else if constexpr (VEC == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2 *>(p);
+        x[0] = v.x; x[1] = v.y;
+    } else {
+        x[0] = *p;
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool nt) {
+    if constexpr (VEC == 4) {
+        const f32x4 v = {x[0], x[1], x[2], x[3]};
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+        else *reinterpret_cast<f32x4 *>(p) = v;
+    } else if constexpr (VEC == 2) {
+        const f32x2 v = {x[0], x[1]};
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(p));
+        else *reinterpret_cast<f32x2 *>(p) = v;
+    } else {
+        if (nt) __builtin_nontemporal_store(x[0], p);
+        else *p = x[0];
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC]) {
+    if constexpr (VEC == 4) {
+        reinterpret_cast<i64x2 *>(p)[0] = i64x2{x[0], x[1]};
+        reinterpret_cast<i64x2 *>(p)[1] = i64x2{x[2], x[3]};
+    } else if constexpr (VEC == 2) {
+        *reinterpret_cast<i64x2 *>(p) = i64x2{x[0], x[1]};
+    } else {
+        *p = x[0];
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
+    if constexpr (VEC == 4) *reinterpret_cast<i32x4 *>(p) = i32x4{x[0], x[1], x[2], x[3]};
+    else if constexpr (VEC == 2) *reinterpret_cast<i32x2 *>(p) = i32x2{x[0], x[1]};
+    else *p = x[0];
+}
+
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
+__global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
+    static_assert(G >= 4 && G <= 64 && (64 % G) == 0, "lanes per row");
+    constexpr int R = 64 / G;          // rows (or pieces) per wave
+    constexpr int SL = G * VEC * F;    // columns per slice
+    constexpr int U = 4;               // entries whose loads are issued together
+    constexpr int NT = kChunk / 64;    // staging loads per lane per chunk
+
+    __shared__ int s_col[kWaves][kChunk];
+    __shared__ float s_val[kWaves][HAS_VAL ? kChunk : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int sub = lane / G;
+    const int g = lane - sub * G;
+
+    const int64_t gx = gridDim.x;
+    int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
+    const int64_t bx = lin % gx;
+    const int64_t by = lin / gx;
+
+    const int64_t task0 = a.task_base + (bx * kWaves + wv) * R;
+    if (task0 >= a.ntasks) return;                     // uniform per wave
+    const int64_t c0 = a.c_begin + by * SL;
+
+    const int64_t v = task0 + sub;
+    const bool live = v < a.ntasks;
+    int beg = 0, end = 0;
+    int64_t orow = 0;
+    if (live) {
+        if constexpr (PIECES) {
+            beg = a.seg_begin[v];
+            end = a.seg_end[v];
+            orow = v;
+        } else {
+            const int r = a.rows ? a.rows[v] : (int)v;
+            beg = a.rowptr[r];
+            end = a.rowptr[r + 1];
+            orow = r;
+        }
+    }
+    const int deg = end - beg;
+
+    // Position of this group's entries in the wave's concatenated entry list.
+    const int beg0 = __builtin_amdgcn_readfirstlane(beg);
+    int off = 0, total = 0;
+    bool contiguous = true;
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+        const int ds = __builtin_amdgcn_readlane(deg, s * G);
+        const int bs = __builtin_amdgcn_readlane(beg, s * G);
+        off += (s < sub) ? ds : 0;
+        contiguous = contiguous && (ds == 0 || bs == beg0 + total);
+        total += ds;
+    }
+
+    int colf[F];
+    bool ok[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        colf[f] = (int)(c0 + (f * G + g) * VEC);
+        ok[f] = (c0 + (int64_t)(f * G + g) * VEC) < a.c_end;
+    }
+
+    float acc[F][VEC];
+    int arg[F][VEC];
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            acc[f][e] = IS_MAX ? -INFINITY : 0.0f;
+            arg[f][e] = -1;
+        }
+
+    const float *__restrict__ Bp = a.B;
+    const int64_t N = a.N;
+
+    for (int cb = 0; cb < total; cb += kChunk) {
+        const int cn = min(kChunk, total - cb);
+        const int nt = (cn + 63) >> 6;
+        int cr[NT];
+        float vr[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+                const int q = cb + min(t * 64 + lane, cn - 1);
+                int p;
+                if (contiguous) {
+                    p = beg0 + q;
+                } else {
+                    p = 0;
+                    int o = 0;
+#pragma unroll
+                    for (int s = 0; s < R; ++s) {
+                        const int ds = __builtin_amdgcn_readlane(deg, s * G);
+                        const int bs = __builtin_amdgcn_readlane(beg, s * G);
+                        p = (q >= o && q < o + ds) ? bs + (q - o) : p;
+                        o += ds;
+                    }
+                }
+                cr[t] = a.col[p];
+                if constexpr (HAS_VAL) vr[t] = a.val[p];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+                s_col[wv][t * 64 + lane] = cr[t];
+                if constexpr (HAS_VAL) s_val[wv][t * 64 + lane] = vr[t];
+            }
+        }
+        wave_lds_sync();
+
+        const int lo = max(off, cb) - cb;
+        const int hi = min(off + deg, cb + cn) - cb;
+        int k = lo;
+        for (; k + U <= hi; k += U) {
+            int cidx[U];
+            float w[U];
+            float bv[U][F][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                cidx[u] = s_col[wv][k + u];
+                w[u] = HAS_VAL ? s_val[wv][k + u] : 1.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int f = 0; f < F; ++f) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) bv[u][f][e] = 0.0f;
+                    if (ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        if constexpr (IS_MAX) {
+                            const float t = HAS_VAL ? w[u] * bv[u][f][e] : bv[u][f][e];
+                            if (arg[f][e] < 0 || t > acc[f][e]) {
+                                acc[f][e] = t;
+                                arg[f][e] = cidx[u];
+                            }
+                        } else {
+                            acc[f][e] = HAS_VAL ? __builtin_fmaf(w[u], bv[u][f][e], acc[f][e])
+                                                : acc[f][e] + bv[u][f][e];
+                        }
+                    }
+        }
+        for (; k < hi; ++k) {
+            const int ci = s_col[wv][k];
+            const float wi = HAS_VAL ? s_val[wv][k] : 1.0f;
+            float bv[F][VEC];
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) bv[f][e] = 0.0f;
+                if (ok[f]) load_vec<VEC>(Bp + (int64_t)ci * N + colf[f], bv[f]);
+            }
+#pragma unroll
+            for (int f = 0; f < F; ++f)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    if constexpr (IS_MAX) {
+                        const float t = HAS_VAL ? wi * bv[f][e] : bv[f][e];
+                        if (arg[f][e] < 0 || t > acc[f][e]) {
+                            acc[f][e] = t;
+                            arg[f][e] = ci;
+                        }
+                    } else {
+                        acc[f][e] = HAS_VAL ? __builtin_fmaf(wi, bv[f][e], acc[f][e])
+                                            : acc[f][e] + bv[f][e];
+                    }
+                }
+        }
+        wave_lds_sync();
+    }
+
+    if (!live) return;
+    float *orow_p = a.out + orow * a.ldo;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        if (!ok[f]) continue;
+        const int64_t cc = (int64_t)colf[f] - a.c_begin;
+        float res[VEC];
+        int ar[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (IS_MAX) {
+                res[e] = deg > 0 ? acc[f][e] : 0.0f;
+                ar[e] = deg > 0 ? arg[f][e] : -1;
+            } else if constexpr (PIECES) {
+                res[e] = acc[f][e];
+            } else {
+                res[e] = (a.mean && deg > 0) ? acc[f][e] / (float)deg : acc[f][e];
+            }
+        }
+        store_vec<VEC>(orow_p + cc, res, a.nt_store != 0);
+        if constexpr (IS_MAX) {
+            if constexpr (PIECES) store_arg32<VEC>(a.part_arg + orow * a.ldo + cc, ar);
+            else if (a.argmax) store_arg64<VEC>(a.argmax + orow * a.ldo + cc, ar);
+        }
+    }
+}
+
+// Lookup of one instantiated kernel; G = 64 also gets the piece-mode kernels.
+template <int G, int VEC, int F>
+RowKernelFn pick_row_kernel(const RowKernelKey &k) {
+    if (k.pieces) {
+        if constexpr (G == 64) {
+            if (k.is_max)
+                return k.has_val ? row_kernel_t<G, VEC, F, true, true, true>
+                                 : row_kernel_t<G, VEC, F, false, true, true>;
+            return k.has_val ? row_kernel_t<G, VEC, F, true, false, true>
+                             : row_kernel_t<G, VEC, F, false, false, true>;
+        } else {
+            return nullptr;
+        }
+    }
+    if (k.is_max)
+        return k.has_val ? row_kernel_t<G, VEC, F, true, true, false>
+                         : row_kernel_t<G, VEC, F, false, true, false>;
+    return k.has_val ? row_kernel_t<G, VEC, F, true, false, false>
+                     : row_kernel_t<G, VEC, F, false, false, false>;
+}
+
+template <int VEC>
+RowKernelFn pick_row_kernel_vec(const RowKernelKey &k) {
+    if (k.coarsen == 1) {
+        switch (k.lanes) {
+            case 4: return pick_row_kernel<4, VEC, 1>(k);
+            case 8: return pick_row_kernel<8, VEC, 1>(k);
+            case 16: return pick_row_kernel<16, VEC, 1>(k);
+            case 32: return pick_row_kernel<32, VEC, 1>(k);
+            case 64: return pick_row_kernel<64, VEC, 1>(k);
+        }
+    } else if (k.coarsen == 2) {
+        switch (k.lanes) {
+            case 4: return pick_row_kernel<4, VEC, 2>(k);
+            case 8: return pick_row_kernel<8, VEC, 2>(k);
+            case 16: return pick_row_kernel<16, VEC, 2>(k);
+            case 32: return pick_row_kernel<32, VEC, 2>(k);
+            case 64: return pick_row_kernel<64, VEC, 2>(k);
+        }
+    }
+    return nullptr;
+}
+
+}  // namespace gspmm

@@ -1,0 +1,133 @@
+// Internal declarations of the gfx950 CSR SpMM library: plan layout, kernel
+// arguments and the launch table shared by the HIP translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/spmm.h"
+
+namespace gspmm {
+
+constexpr int kBlock = 256;             // threads per block: 4 wave64s
+constexpr int kWaves = kBlock / 64;
+constexpr int kChunk = 256;             // col/val entries a wave stages in LDS at once
+constexpr int kPartialWidth = 256;      // columns per pass of the split path
+constexpr int kRowsPerScanBlock = 1024; // rows per block of the plan-time scans
+constexpr int kXcds = 8;                // MI355X: 8 XCDs, 32 CUs each
+
+// Arguments of the row kernel (light rows or split pieces).
+struct RowArgs {
+    const int *rowptr;     // int32 [M+1]                     (row mode)
+    const int *rows;       // int32 row list or nullptr        (row mode)
+    const int *seg_begin;  // int32 [n_seg]                    (piece mode)
+    const int *seg_end;    // int32 [n_seg]                    (piece mode)
+    const int *col;        // int32 [nnz]
+    const float *val;      // fp32 [nnz] or nullptr
+    const float *B;        // fp32 [K, N]
+    float *out;            // C (row mode) or the partial buffer (piece mode)
+    int64_t *argmax;       // int64 [M, N] or nullptr          (row mode, max)
+    int *part_arg;         // int32 partial argmax             (piece mode, max)
+    int64_t ldo;           // row stride of out / argmax / part_arg, in elements
+    int64_t N;             // columns of B (row stride of B)
+    int64_t c_begin;       // first column handled by this launch
+    int64_t c_end;         // one past the last column handled
+    int64_t task_base;     // first task of this launch
+    int64_t ntasks;        // rows (row mode) or pieces (piece mode): tasks end here
+    int mean;              // divide by the row degree (row mode)
+    int xcd_remap;         // give each XCD a contiguous range of tasks
+    int nt_store;          // non-temporal output stores
+};
+
+// Arguments of the ordered combine of split pieces.
+struct CombineArgs {
+    const int *heavy_rows;   // int32 [n_heavy]
+    const int *seg_first;    // int32 [n_heavy+1]: pieces of heavy row h
+    const int *rowptr;       // int32 [M+1]
+    const float *partial;    // fp32 [n_seg, kPartialWidth]
+    const int *part_arg;     // int32 [n_seg, kPartialWidth] (max only)
+    float *C;                // fp32 [M, N]
+    int64_t *argmax;         // int64 [M, N] or nullptr
+    int64_t N;
+    int64_t c_begin, c_end;  // columns of this pass (c_end - c_begin <= kPartialWidth)
+    int64_t n_heavy;
+    int mean;
+};
+
+struct RowKernelKey {
+    int lanes;    // G: lanes per row (4..64); 64 / G rows per wave
+    int vec;      // floats per lane access (1, 2, 4)
+    int coarsen;  // F: accesses per lane per entry
+    bool has_val;
+    bool is_max;
+    bool pieces;  // piece mode (split rows) instead of row mode
+};
+
+typedef void (*RowKernelFn)(RowArgs);
+
+// Looks up a compiled row kernel; nullptr when the combination is not built.
+RowKernelFn row_kernel_v1(const RowKernelKey &k);
+RowKernelFn row_kernel_v2(const RowKernelKey &k);
+RowKernelFn row_kernel_v4(const RowKernelKey &k);
+RowKernelFn row_kernel(const RowKernelKey &k);
+
+hipError_t launch_combine(const CombineArgs &a, bool is_max, hipStream_t s);
+
+// ---- plan-time kernels (plan_kernels.hip) ----
+struct RowScanOut {        // one record per scan block
+    int64_t bad_row;       // first row breaking monotonicity, or INT64_MAX
+    int64_t sum_deg;
+    int64_t sum_deg2;
+    int64_t dmax;
+    int64_t n_empty;
+};
+hipError_t launch_rowscan(const int64_t *rowptr, int64_t M, int *rowptr32, RowScanOut *out,
+                          int64_t nblocks, hipStream_t s);
+hipError_t launch_colscan(const int64_t *col, int64_t nnz, int64_t K, int *col32,
+                          int64_t *bad_pos, int64_t nblocks, hipStream_t s);
+
+struct PartCount {         // one record per scan block
+    int64_t n_heavy, n_seg, n_light;
+};
+hipError_t launch_part_count(const int *rowptr32, int64_t M, int64_t T, int64_t L,
+                             PartCount *out, int64_t nblocks, hipStream_t s);
+hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t L,
+                             const PartCount *offsets, int *heavy_rows, int *seg_first,
+                             int *seg_begin, int *seg_end, int *light_rows, int64_t nblocks,
+                             hipStream_t s);
+
+// ---- the plan ----
+struct Route {
+    int lanes = 64, vec = 4, coarsen = 1, slices = 1;
+    int xcd_remap = 1, nt_store = 0;
+    bool split = false;
+};
+
+}  // namespace gspmm
+
+struct spmm_plan {
+    int device = 0;
+    int64_t M = 0, K = 0, nnz = 0;
+    // descriptors
+    int64_t dmax = 0, n_empty = 0, sum_deg2 = 0;
+    double mean_deg = 0, cv_deg = 0, plan_ms = 0;
+    // narrowed CSR (device)
+    int *rowptr = nullptr;
+    int *col = nullptr;
+    float *val = nullptr;
+    // row split (device)
+    bool split = false;
+    int64_t T = 0, L = 0, n_heavy = 0, n_seg = 0, n_light = 0;
+    int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
+    int *light_rows = nullptr;
+    float *partial = nullptr;
+    int *part_arg = nullptr;
+    // options (-1 / 0 = automatic)
+    int64_t opt_T = -1, opt_L = -1, opt_split = -1;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1;
+    // last routing decision
+    int64_t route_N = 0;
+    gspmm::Route route;
+};

@@ -1,0 +1,163 @@
+/*
+ * spmm.h -- C ABI of the MI355X (gfx950) CSR sparse x dense product library
+ * for GNN neighbour aggregation: C = A . B with sum, mean or max (+argmax)
+ * reductions over each row's stored entries.
+ *
+ * The interface follows the problem statement shared by the pages:
+ *  - A is a fixed graph in CSR form, built once and applied once per layer
+ *    (graph-spmm kernel card, "Usage" and the SparseAdj row of its API table;
+ *    RA-SpMM, "SpMM formulation": A fixed per graph, B changes per layer, the
+ *    feature width N is known only at call time).
+ *  - rowptr [M+1] and col [nnz] are int64, the dense operand is fp32
+ *    (graph-spmm card, API table footnote and "Requirements and limits").
+ *  - B and C are row-major (GE-SpMM, section II-A: GNN feature matrices are
+ *    row-major, unlike a column-major vendor product).
+ *  - reductions sum / mean / max with the winning neighbour's index, empty rows
+ *    giving 0 and (0, -1), val == NULL meaning every stored entry is 1
+ *    (graph-spmm card, API table and "Method").
+ *
+ * Semantics of one output element, for row i with stored entries p in
+ * [rowptr[i], rowptr[i+1]) taken in stored order, t_p = a_p * B[col_p][k]
+ * (a_p = val[p], or 1 when val == NULL):
+ *   SUM  : fp32 sum of t_p.  Rows processed whole are summed in stored order
+ *          with one fused multiply-add per entry; rows longer than the split
+ *          threshold are summed piece by piece, pieces combined in order.
+ *   MEAN : SUM / (number of stored entries), one IEEE fp32 division; 0 if empty.
+ *   MAX  : largest t_p (strict '>', so the first of equal values wins) and the
+ *          column id col_p of that entry; (0, -1) if the row is empty.
+ * Duplicated (row, col) entries each count; columns need not be sorted.
+ * Results are bitwise reproducible from run to run: no atomics are used.
+ *
+ * All functions return a status (or NULL for plan creation) and never abort
+ * or throw.  spmm_last_error() returns the calling thread's last status and
+ * a message.
+ */
+#ifndef GNN_SPMM_H
+#define GNN_SPMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spmm_plan *spmm_plan_t;
+
+/* Reductions. */
+enum spmm_reduce { SPMM_SUM = 0, SPMM_MEAN = 1, SPMM_MAX = 2 };
+
+/* Status codes. */
+enum spmm_status {
+    SPMM_OK = 0,
+    SPMM_E_INVALID_ARG = -1, /* null / host pointer, negative size, bad enum  */
+    SPMM_E_BAD_CSR = -2,     /* rowptr not monotone from 0, or col outside [0,K) */
+    SPMM_E_OOM = -3,         /* device allocation failed                        */
+    SPMM_E_HIP = -4,         /* a HIP runtime call or kernel launch failed      */
+    SPMM_E_UNSUPPORTED = -5  /* size beyond the library's 32-bit index limits   */
+};
+
+/* Options for spmm_plan_set_option (value 0 / -1 = automatic where noted). */
+enum spmm_option {
+    SPMM_OPT_SPLIT_T = 1,      /* rows with more than T entries are split; -1 auto */
+    SPMM_OPT_SPLIT_L = 2,      /* piece length of split rows; -1 auto             */
+    SPMM_OPT_SPLIT_MODE = 3,   /* -1 auto (split only skewed graphs), 0 off, 1 on */
+    SPMM_OPT_LANES = 4,        /* lanes per row G in {4,8,16,32,64}; 0 auto       */
+    SPMM_OPT_COARSEN = 5,      /* vectors per lane F in {1,2}; 0 auto             */
+    SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto            */
+    SPMM_OPT_XCD_REMAP = 7,    /* -1 auto, 0 off, 1 on: contiguous rows per XCD  */
+    SPMM_OPT_NT_STORE = 8      /* -1 auto, 0 off, 1 on: non-temporal C stores    */
+};
+
+/* Descriptors of a plan and of its last routing decision. */
+struct spmm_plan_info {
+    int64_t M, K, nnz;
+    int64_t dmax, n_empty;       /* largest row degree, number of empty rows     */
+    double mean_deg;             /* nnz / M (0 when M == 0)                      */
+    double cv_deg;               /* population std of row degree / mean_deg      */
+    int64_t split_T, split_L;    /* row-split threshold and piece length in use  */
+    int64_t n_heavy, n_seg;      /* split rows and pieces (0 when not split)     */
+    double split_ratio;          /* (light rows + pieces) / M, ParamSpMM's SR    */
+    int32_t has_val;             /* 1 if the plan holds edge values              */
+    int32_t index_bits;          /* width of the plan's stored indexes (32)      */
+    double plan_ms;              /* wall time of spmm_plan_create                */
+    /* routing of the most recent spmm_run / spmm_plan_route call */
+    int64_t route_N;
+    int32_t route_lanes, route_vec, route_coarsen, route_rows_per_wave;
+    int32_t route_slices, route_xcd_remap, route_nt_store, route_split;
+};
+
+/*
+ * Build a plan for the CSR matrix A [M, K] held on the current HIP device.
+ *   rowptr : device int64 [M+1], rowptr[0] == 0, non-decreasing.
+ *   col    : device int64 [nnz], values in [0, K); may be NULL when nnz == 0.
+ *   val    : device fp32 [nnz], or NULL for an unweighted graph (all ones).
+ * nnz is read from rowptr[M].  M, K and nnz must each be below 2^31.
+ * The call is synchronous.  It validates the CSR on the GPU, computes the
+ * degree descriptors (mean degree and its coefficient of variation, RA-SpMM
+ * abstract), narrows indexes to int32, and builds the row split when the
+ * graph is skewed.  It copies everything it needs: the caller may free or
+ * change its arrays once it returns.  The plan owns its device memory until
+ * spmm_plan_destroy.
+ * Returns NULL on error (INVALID_ARG, BAD_CSR with the first bad row in the
+ * message, OOM, HIP, UNSUPPORTED; see spmm_last_error).
+ */
+spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const float *val,
+                             int64_t M, int64_t K);
+
+/*
+ * C = reduce(A . B) on `stream` (a hipStream_t; NULL = the null stream).
+ *   B      : device fp32 [K, N] row-major (may be NULL only when K == 0).
+ *   C      : device fp32 [M, N] row-major, fully overwritten.
+ *   argmax : device int64 [M, N] or NULL; only allowed with SPMM_MAX, where it
+ *            receives the column id of each maximum (-1 for empty rows).
+ *   N      : feature width, N >= 1.
+ * Asynchronous: it validates its arguments, picks a kernel from the plan's
+ * descriptors and N, enqueues the kernels and returns without waiting.  It
+ * allocates nothing.  B must not overlap C or argmax.  Runs on one plan must
+ * be ordered on one stream (the plan's split buffer is shared); use one plan
+ * per stream for concurrency.  Kernel faults surface at the caller's next
+ * synchronisation, as usual in HIP.
+ * Returns SPMM_OK, INVALID_ARG, UNSUPPORTED or HIP.  M == 0 is a no-op.
+ */
+int spmm_run(spmm_plan_t plan, const float *B, float *C, int64_t *argmax, int64_t N,
+             int reduce, void *stream);
+
+/* Free a plan and its device memory.  No run on it may still be in flight.
+ * NULL is accepted (no-op). */
+int spmm_plan_destroy(spmm_plan_t plan);
+
+/* Copy the plan's descriptors and last routing decision into *out (host). */
+int spmm_plan_info(spmm_plan_t plan, struct spmm_plan_info *out);
+
+/* Fill the routing fields of the plan's info for width N and `reduce`
+ * without running anything (B and C assumed 16-byte aligned). */
+int spmm_plan_route(spmm_plan_t plan, int64_t N, int reduce);
+
+/*
+ * Copy the row split to host arrays.  Pieces are ordered by (row, piece) and
+ * piece s of a split row i covers entries [rowptr[i] + s*L, min(rowptr[i] +
+ * (s+1)*L, rowptr[i+1])) (ParamSpMM section 3.2 workload balancing, PCSR TRow
+ * of section 4.2).  Light rows are the rows that are not split, ascending.
+ *   seg_row/seg_begin/seg_end : host int64 [seg_cap] (may be NULL if seg_cap 0)
+ *   light                     : host int64 [light_cap] (may be NULL if 0)
+ *   counts                    : host int64 [3] = {n_heavy, n_seg, n_light}
+ * At most seg_cap / light_cap entries are written.  Synchronous.
+ */
+int spmm_plan_partition(spmm_plan_t plan, int64_t *seg_row, int64_t *seg_begin,
+                        int64_t *seg_end, int64_t seg_cap, int64_t *light,
+                        int64_t light_cap, int64_t *counts);
+
+/* Set an option (enum spmm_option).  Changing the split parameters rebuilds
+ * the split synchronously; other options apply to later runs.  The caller
+ * must not have runs on this plan in flight. */
+int spmm_plan_set_option(spmm_plan_t plan, int option, int64_t value);
+
+/* The calling thread's last status; copies its message (NUL-terminated,
+ * truncated to cap bytes) into buf when buf != NULL and cap > 0. */
+int spmm_last_error(char *buf, int64_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNN_SPMM_H */

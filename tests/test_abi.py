@@ -1,0 +1,109 @@
+"""C ABI of the HIP library, without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spmm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spmm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_calls():
+    names = _declared_functions()
+    for required in ("spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
+                     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option",
+                     "spmm_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    import gnn_sparse_dense_amd as G
+    lib = G.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(G.EXPORTED) == _declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (spmm_\w+)", out)))
+    assert exported == _declared_functions(), "exported C symbols differ from the header"
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_header_struct_layout_matches_binding():
+    import gnn_sparse_dense_amd as G
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "spmm.h"\n'
+           'int main(void){printf("%zu %zu %zu\\n", sizeof(struct spmm_plan_info),'
+           ' offsetof(struct spmm_plan_info, plan_ms), offsetof(struct spmm_plan_info, route_split));return 0;}\n')
+    tmp = os.path.join(ROOT, "_work")
+    os.makedirs(tmp, exist_ok=True)
+    c = os.path.join(tmp, "layout_probe.c")
+    exe = os.path.join(tmp, "layout_probe")
+    open(c, "w").write(src)
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+    size, off_ms, off_split = map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split())
+    assert size == ctypes.sizeof(G._Info)
+    assert off_ms == G._Info.plan_ms.offset and off_split == G._Info.route_split.offset
+
+
+def _err():
+    import gnn_sparse_dense_amd as G
+    return G.spmm_last_error()
+
+
+def test_argument_errors_without_gpu():
+    import gnn_sparse_dense_amd as G
+    lib = G.lib()
+    # plan creation: negative sizes and a NULL row pointer fail before any HIP call
+    assert lib.spmm_plan_create(None, None, None, -1, 5) is None
+    assert _err()[0] == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_plan_create(None, None, None, 4, 4) is None
+    st, msg = _err()
+    assert st == G.SPMM_E_INVALID_ARG and "rowptr" in msg
+    assert lib.spmm_plan_create(None, None, None, 2**31, 4) is None
+    assert _err()[0] == G.SPMM_E_UNSUPPORTED
+    # runs on a NULL plan, bad N, bad reduce
+    assert lib.spmm_run(None, None, None, None, 8, 0, None) == G.SPMM_E_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: checks come first
+    assert lib.spmm_run(fake, None, None, None, 0, 0, None) == G.SPMM_E_INVALID_ARG
+    assert "N must be positive" in _err()[1]
+    assert lib.spmm_run(fake, None, None, None, 8, 7, None) == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_run(fake, None, None, fake, 8, G.SPMM_SUM, None) == G.SPMM_E_INVALID_ARG
+    assert "argmax" in _err()[1]
+    assert lib.spmm_plan_info(None, None) == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_plan_set_option(None, 1, 5) == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_plan_route(None, 8, 0) == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_plan_partition(None, None, None, None, 0, None, 0, None) == G.SPMM_E_INVALID_ARG
+    assert lib.spmm_plan_destroy(None) == G.SPMM_OK
+    assert _err()[0] == G.SPMM_OK
+
+
+def test_last_error_truncates():
+    import gnn_sparse_dense_amd as G
+    lib = G.lib()
+    lib.spmm_run(None, None, None, None, 8, 0, None)
+    buf = ctypes.create_string_buffer(6)
+    assert lib.spmm_last_error(buf, 6) == G.SPMM_E_INVALID_ARG
+    assert len(buf.value) == 5
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The HIP package and its sources never import or link the oracle."""
+    pkg = os.path.join(ROOT, "gnn_sparse_dense_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sum and mean: |GPU - oracle| <= 1e-5 * sum|a*b| + 1e-6 per element; rows walked
+whole are also bit-exact against the oracle's fused mode.  Max and argmax:
+bit-exact.  Row split pieces: bit-exact against the oracle's partition.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gnn_sparse_dense_amd as G
+    from tests.gpu_helpers import DEV, check, gpu_run, log, make_plan, to_dev
+
+
+@functools.lru_cache(maxsize=2)
+def _workload(name, M=None):
+    return W.make(name, M=M)
+
+
+def _light_rows(plan, M):
+    return G.spmm_plan_partition(plan)["light"]
+
+
+def test_tiny_config_all_reductions(orc):
+    w = _workload("tiny")
+    g = w.graph
+    log(f"tiny: M={g.M} nnz={g.nnz} N={w.N}")
+    plan = make_plan(g)
+    _, _, _, Bd = to_dev(g, w.B)
+    for red in ("sum", "mean", "max"):
+        C, arg = gpu_run(plan, g.M, Bd, red)
+        check(orc, g, w.B, red, C, arg, exact_rows=np.arange(g.M), what=f"tiny {red}")
+    G.spmm_plan_destroy(plan)
+
+
+VARIANTS = [(lanes, coarsen, vec) for lanes in (4, 8, 16, 32, 64) for coarsen in (1, 2) for vec in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("weighted", [True, False])
+def test_forced_variants_agree_bitwise(orc, weighted):
+    rng = np.random.default_rng(101)
+    g = W.random_csr(rng, 3001, 2500, mean_deg=9.0, empty_frac=0.05, dup_frac=0.1,
+                     shuffle_rows=True, weighted=weighted, zero_frac=0.05)
+    for N in (16, 64, 100):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        for red in ("sum", "mean", "max"):
+            ref_out = None
+            for lanes, coarsen, vec in VARIANTS:
+                if N % vec:
+                    continue
+                what = f"N={N} {red} lanes={lanes} F={coarsen} vec={vec} w={weighted}"
+                log(what)
+                plan = make_plan(g, [(G.SPMM_OPT_LANES, lanes), (G.SPMM_OPT_COARSEN, coarsen),
+                                     (G.SPMM_OPT_VEC, vec)])
+                C, arg = gpu_run(plan, g.M, Bd, red)
+                info = G.spmm_plan_info(plan)
+                assert (info["route_lanes"], info["route_coarsen"], info["route_vec"]) == (lanes, coarsen, vec)
+                if ref_out is None:
+                    check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=what)
+                    ref_out = (C, arg)
+                else:
+                    assert np.array_equal(C.view(np.uint32), ref_out[0].view(np.uint32)), what
+                    if arg is not None:
+                        assert np.array_equal(arg, ref_out[1]), what
+                G.spmm_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("N", [1, 3, 17, 63, 65, 100, 130, 257, 300, 1030])
+def test_ragged_widths(orc, N):
+    rng = np.random.default_rng(200 + N)
+    g = W.random_csr(rng, 1500, 1200, mean_deg=7.0, empty_frac=0.1, dup_frac=0.05)
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    plan = make_plan(g)
+    _, _, _, Bd = to_dev(g, B)
+    for red in ("sum", "mean", "max"):
+        log(f"ragged N={N} {red}")
+        C, arg = gpu_run(plan, g.M, Bd, red)
+        check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=f"N={N} {red}")
+    # an offset (8-byte but not 16-byte aligned) view of B forces narrower vectors
+    if N % 4 == 0:
+        Bbig = torch.empty(g.K * N + 2, dtype=torch.float32, device=DEV)
+        Bv = Bbig[2:].view(g.K, N)
+        Bv.copy_(Bd)
+        C, _ = gpu_run(plan, g.M, Bv, "sum")
+        assert G.spmm_plan_info(plan)["route_vec"] == 2
+        check(orc, g, B, "sum", C, None, exact_rows=np.arange(g.M), what=f"N={N} misaligned B")
+    G.spmm_plan_destroy(plan)
+
+
+def test_ties_and_signed_zeros(orc):
+    rng = np.random.default_rng(7)
+    for weighted in (False, True):
+        g = W.random_csr(rng, 2000, 300, mean_deg=12.0, empty_frac=0.1, dup_frac=0.3,
+                         shuffle_rows=True, weighted=weighted)
+        if weighted:
+            g.val = rng.choice(np.float32([0.0, -0.0, 0.5, 1.0, -1.0]), size=g.nnz).astype(np.float32)
+        B = rng.integers(-1, 2, size=(g.K, 24)).astype(np.float32)
+        B[rng.random(B.shape) < 0.2] = -0.0
+        plan = make_plan(g)
+        _, _, _, Bd = to_dev(g, B)
+        for red in ("max", "sum", "mean"):
+            C, arg = gpu_run(plan, g.M, Bd, red)
+            check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=f"ties {red} w={weighted}")
+        G.spmm_plan_destroy(plan)
+
+
+def test_degenerate_shapes(orc):
+    rng = np.random.default_rng(9)
+    cases = [
+        ("all empty", W.Graph("e", 50, 40, np.zeros(51, np.int64), np.zeros(0, np.int64), None)),
+        ("K=0", W.Graph("k0", 7, 0, np.zeros(8, np.int64), np.zeros(0, np.int64), None)),
+        ("one row", W.random_csr(rng, 1, 500, mean_deg=300.0, empty_frac=0.0)),
+        ("one long row", W.random_csr(rng, 3, 100, mean_deg=2.0, empty_frac=0.0, heavy_rows=1,
+                                      heavy_deg=5000)),
+        ("identity", W.Graph("i", 333, 333, np.arange(334, dtype=np.int64), np.arange(333, dtype=np.int64),
+                             None)),
+    ]
+    for what, g in cases:
+        N = 20
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        log(f"degenerate: {what}")
+        plan = make_plan(g)
+        if g.K == 0:
+            Bd = torch.empty((0, N), dtype=torch.float32, device=DEV)
+        else:
+            _, _, _, Bd = to_dev(g, B)
+        for red in ("sum", "mean", "max"):
+            C, arg = gpu_run(plan, g.M, Bd, red)
+            if g.K == 0:
+                assert np.all(C.view(np.uint32) == 0) and (arg is None or np.all(arg == -1))
+                continue
+            check(orc, g, B, red, C, arg, exact_rows=None, what=f"{what} {red}")
+        G.spmm_plan_destroy(plan)
+    # M = 0: a no-op
+    g0 = W.Graph("m0", 0, 5, np.zeros(1, np.int64), np.zeros(0, np.int64), None)
+    plan = make_plan(g0)
+    Bd = torch.zeros((5, 4), dtype=torch.float32, device=DEV)
+    C = torch.empty((0, 4), dtype=torch.float32, device=DEV)
+    G.spmm_run(plan, Bd, C, None, 4, "sum")
+    torch.cuda.synchronize()
+    G.spmm_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("T,L", [(64, 64), (100, 37), (0, 1000), (513, 512)])
+def test_row_split(orc, T, L):
+    rng = np.random.default_rng(T * 7 + L)
+    g = W.random_csr(rng, 4000, 3000, mean_deg=6.0, empty_frac=0.05, heavy_rows=25, heavy_deg=2100,
+                     dup_frac=0.05, shuffle_rows=True)
+    plan = make_plan(g, [(G.SPMM_OPT_SPLIT_T, T), (G.SPMM_OPT_SPLIT_L, L), (G.SPMM_OPT_SPLIT_MODE, 1)])
+    part = G.spmm_plan_partition(plan)
+    ref = orc.partition(g.rowptr, g.M, T, L)
+    log(f"split T={T} L={L}: heavy={part['n_heavy']} pieces={len(part['seg_row'])}")
+    assert part["n_heavy"] == ref["n_heavy"] > 0
+    for k in ("seg_row", "seg_begin", "seg_end", "light"):
+        assert np.array_equal(part[k], ref[k]), k
+    info = G.spmm_plan_info(plan)
+    assert info["split_T"] == T and info["split_L"] == L and info["n_seg"] == len(ref["seg_row"])
+    for N in (48, 130, 300):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        for red in ("sum", "mean", "max"):
+            C, arg = gpu_run(plan, g.M, Bd, red)
+            check(orc, g, B, red, C, arg, exact_rows=ref["light"], what=f"split T={T} L={L} N={N} {red}")
+    G.spmm_plan_destroy(plan)
+
+
+def test_determinism_bitwise(orc):
+    w = _workload("powerlaw", M=200_000)
+    g = w.graph
+    log(f"determinism: powerlaw M={g.M} nnz={g.nnz}")
+    plan = make_plan(g)
+    assert G.spmm_plan_info(plan)["n_heavy"] > 0
+    _, _, _, Bd = to_dev(g, w.B)
+    first = gpu_run(plan, g.M, Bd, "sum")[0]
+    for _ in range(4):
+        again = gpu_run(plan, g.M, Bd, "sum")[0]
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+    fm, fa = gpu_run(plan, g.M, Bd, "max")
+    for _ in range(2):
+        m, a = gpu_run(plan, g.M, Bd, "max")
+        assert np.array_equal(fm.view(np.uint32), m.view(np.uint32)) and np.array_equal(fa, a)
+    G.spmm_plan_destroy(plan)
+
+
+def test_descriptors_and_errors(orc):
+    rng = np.random.default_rng(3)
+    g = W.random_csr(rng, 5000, 4000, mean_deg=5.0, empty_frac=0.1, heavy_rows=3, heavy_deg=3000)
+    plan = make_plan(g)
+    info = G.spmm_plan_info(plan)
+    d = orc.descriptors(g.rowptr, g.M)
+    assert (info["M"], info["K"], info["nnz"]) == (g.M, g.K, d["nnz"])
+    assert info["dmax"] == d["dmax"] and info["n_empty"] == d["n_empty"]
+    assert abs(info["mean_deg"] - d["mean"]) <= 1e-12 * d["mean"]
+    assert abs(info["cv_deg"] - d["cv"]) <= 1e-12 * d["cv"]
+    G.spmm_plan_destroy(plan)
+
+    # invalid CSR: the first bad row matches the oracle's validator
+    rowptr = g.rowptr.copy()
+    col = g.col.copy()
+    bad_r = int(np.nonzero(g.degrees()[1234:] > 0)[0][0]) + 1234   # a non-empty row
+    col[rowptr[bad_r]] = g.K + 5
+    col[rowptr[bad_r + 700]] = -1
+    assert orc.validate(rowptr, col, g.M, g.K) == bad_r
+    rp, cl, vl, _ = to_dev(W.Graph("bad", g.M, g.K, rowptr, col, g.val))
+    with pytest.raises(G.SpmmError) as ei:
+        G.spmm_plan_create(rp, cl, vl, g.M, g.K)
+    assert ei.value.status == G.SPMM_E_BAD_CSR and f"first bad row {bad_r}" in str(ei.value)
+    rowptr2 = g.rowptr.copy()
+    rowptr2[2001] = rowptr2[2002] + 1          # row 2001 gets a negative length
+    bad2 = orc.validate(rowptr2, g.col, g.M, g.K)
+    rp2 = torch.from_numpy(rowptr2).to(DEV)
+    with pytest.raises(G.SpmmError) as ei:
+        G.spmm_plan_create(rp2, cl, vl, g.M, g.K)
+    assert ei.value.status == G.SPMM_E_BAD_CSR and f"first bad row {bad2}" in str(ei.value)
+
+    # host memory where device memory is required
+    host_rp = torch.from_numpy(g.rowptr)
+    with pytest.raises(G.SpmmError) as ei:
+        G.spmm_plan_create(host_rp, cl, vl, g.M, g.K)
+    assert ei.value.status == G.SPMM_E_INVALID_ARG
+    plan = make_plan(g)
+    Bh = torch.zeros((g.K, 8), dtype=torch.float32)
+    C = torch.empty((g.M, 8), dtype=torch.float32, device=DEV)
+    with pytest.raises(G.SpmmError) as ei:
+        G.spmm_run(plan, Bh, C, None, 8, "sum")
+    assert ei.value.status == G.SPMM_E_INVALID_ARG
+    with pytest.raises(G.SpmmError):
+        G.spmm_run(plan, C, C, None, 8, "sum")           # B overlaps C
+    G.spmm_plan_destroy(plan)
+
+
+def test_side_stream(orc):
+    w = _workload("tiny")
+    g = w.graph
+    plan = make_plan(g)
+    _, _, _, Bd = to_dev(g, w.B)
+    s = torch.cuda.Stream()
+    C = torch.empty((g.M, w.N), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(s):
+        G.spmm_run(plan, Bd, C, None, w.N, "mean", s)
+    s.synchronize()
+    check(orc, g, w.B, "mean", C.cpu().numpy(), None, exact_rows=np.arange(g.M), what="side stream")
+    G.spmm_plan_destroy(plan)
+
+
+MEDIUM = [("road", 60_000), ("powerlaw", 120_000), ("diffusion", 60_000), ("community", 12_000)]
+
+
+@pytest.mark.parametrize("name,M", MEDIUM, ids=[m[0] for m in MEDIUM])
+def test_regimes_medium_full_compare(orc, name, M):
+    w = _workload(name, M=M)
+    g = w.graph
+    log(f"medium {name}: M={g.M} nnz={g.nnz} N={w.N}")
+    plan = make_plan(g)
+    light = G.spmm_plan_partition(plan)["light"]
+    _, _, _, Bd = to_dev(g, w.B)
+    for red in sorted(set(w.reduces) | {"max"}):
+        C, arg = gpu_run(plan, g.M, Bd, red)
+        check(orc, g, w.B, red, C, arg, exact_rows=light, what=f"{name} {red}")
+    G.spmm_plan_destroy(plan)
+
+
+FULL = ["road", "diffusion", "community", "powerlaw"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_regimes_full_size_sampled(orc, name):
+    """Full-size regimes in the benchmark's launch configuration (automatic
+    routing), checked on a sample of rows: evenly spaced rows, the first and
+    last rows, and the longest rows (all split rows for the power-law graph)."""
+    w = _workload(name)
+    g = w.graph
+    log(f"full {name}: M={g.M} nnz={g.nnz} N={w.N}")
+    plan = make_plan(g)
+    info = G.spmm_plan_info(plan)
+    part = G.spmm_plan_partition(plan)
+    _, _, _, Bd = to_dev(g, w.B)
+    deg = g.degrees()
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(g.M - 64, g.M), rng.choice(g.M, size=3000, replace=False),
+        np.argsort(deg)[-400:], np.unique(part["seg_row"])[:2000],
+    ])).astype(np.int64)
+    light_set = np.setdiff1d(sample, np.unique(part["seg_row"]), assume_unique=False)
+    exact_idx = np.searchsorted(sample, light_set)
+    log(f"  split: heavy={info['n_heavy']} pieces={info['n_seg']} sample={sample.size}")
+    for red in w.reduces:
+        C, arg = gpu_run(plan, g.M, Bd, red, poison=True)
+        assert not np.isnan(C).any(), "unwritten output"
+        check(orc, g, w.B, red, C[sample], None if arg is None else arg[sample], rows=sample,
+              exact_rows=exact_idx, what=f"full {name} {red}")
+    G.spmm_plan_destroy(plan)
