@@ -147,6 +147,26 @@ def make_flush():
     return flush
 
 
+def copy_ceiling_gbps(reps=20):
+    """Bandwidth of a plain 1 GiB device-to-device copy (bytes read + written)."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / (statistics.median(times) * 1e-3) / 1e9
+
+
 def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
     """The CPU oracle (single-threaded C, as built) on the headline workload."""
     import oracle
@@ -173,6 +193,7 @@ def regime_result(r, reduce, steps, warmup, flush):
     g, N = r.g, r.w.N
     warm, _ = r.time_steps(reduce, steps, warmup)
     cold, _ = r.time_steps(reduce, steps, 2, flush=flush)
+    r.info = r.G.spmm_plan_info(r.plan)       # routing of the runs just timed
     comp, gather = byte_model(g, N, reduce)
     med_c = statistics.median(cold)
     med_w = statistics.median(warm)
@@ -222,15 +243,10 @@ def main():
     print(f"[bench] {headline}: M={g.M} nnz={g.nnz} N={N} gen={r.gen_s:.1f}s plan={r.info['plan_ms']:.1f}ms",
           file=sys.stderr, flush=True)
 
-    if args.calibrate_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_gbps = copy_ceiling_gbps(reps=3 if args.calibrate_copy else 20)
 
     durations, wall_ms = r.time_steps(reduce, args.steps, args.warmup)
+    r.info = r.G.spmm_plan_info(r.plan)       # routing of the runs just timed
     ms_per_step = wall_ms / args.steps
     avg_launch_ms = sum(durations) / len(durations)
     comp, gather = byte_model(g, N, reduce)
@@ -257,6 +273,8 @@ def main():
         "effective_GBps": round(comp / (ms_per_step * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(comp / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "gather_GBps": round(gather / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_copy_ceiling_GBps": round(copy_gbps, 1),
+        "frac_of_copy_ceiling": round(comp / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -82,7 +82,6 @@ void free_split(spmm_plan *p) {
     dev_free(p->seg_first);
     dev_free(p->seg_begin);
     dev_free(p->seg_end);
-    dev_free(p->light_rows);
     dev_free(p->partial);
     dev_free(p->part_arg);
     p->split = false;
@@ -171,7 +170,6 @@ int build_split(spmm_plan *p) {
         (st = dev_alloc(&p->seg_first, p->n_heavy + 1, "piece index")) ||
         (st = dev_alloc(&p->seg_begin, p->n_seg, "piece begin")) ||
         (st = dev_alloc(&p->seg_end, p->n_seg, "piece end")) ||
-        (st = dev_alloc(&p->light_rows, std::max<int64_t>(p->n_light, 1), "light rows")) ||
         (st = dev_alloc(&p->partial, p->n_seg * kPartialWidth, "partial sums")) ||
         (st = dev_alloc(&p->part_arg, p->n_seg * kPartialWidth, "partial argmax"))) {
         dev_free(d_counts);
@@ -181,7 +179,7 @@ int build_split(spmm_plan *p) {
     e = hipMemcpy(d_counts, counts.data(), sizeof(PartCount) * nblocks, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = launch_part_write(p->rowptr, p->M, T, L, d_counts, p->heavy_rows, p->seg_first,
-                              p->seg_begin, p->seg_end, p->light_rows, nblocks, nullptr);
+                              p->seg_begin, p->seg_end, nullptr, nblocks, nullptr);
     const int nseg32 = (int)p->n_seg;
     if (e == hipSuccess)
         e = hipMemcpy(p->seg_first + p->n_heavy, &nseg32, sizeof(int), hipMemcpyHostToDevice);
@@ -203,10 +201,23 @@ int pow2_ceil(int64_t x) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Rule router: vector width from N and alignment, lanes per row from the
-// number of vector columns (a row's group spans the feature width once, so
-// narrow N packs several rows per wave), coarsening when one pass of 64
-// lanes does not cover the row.  Forced options override each rule.
+// Rule router (first matching rule per decision; forced options override):
+//  * vector width: 4 floats when N and the pointers allow 16-byte accesses,
+//    else 2, else 1;
+//  * lanes per row: one pass of the row's group spans the W = N / vec vector
+//    columns (several rows per wave when W < 64; coarsening F = 2 when
+//    W > 64), following ParamSpMM's thread-coarsening analysis (section 3.3)
+//    with the MAC-job gap kept at zero wherever N allows;
+//  * low mean degree (< 8, RA-SpMM's sparse-uniform regime): half the lanes
+//    and F = 2, doubling the rows per wave so more rows' gathers are in
+//    flight per wave;
+//  * skewed degrees (CV > 1, RA-SpMM's sparse-skewed / extreme-skew regime),
+//    where neighbours carry no locality, with a B wider than 64 floats:
+//    64-column slices, so each pass over the graph touches a quarter-sized
+//    part of B that stays in the Infinity Cache longer;
+//  * XCD remap (contiguous rows per XCD, sharing B rows in one L2) except for
+//    those skewed graphs, which have no neighbour locality to keep.
+// The thresholds come from rocprofv3-timed sweeps on the five regimes.
 Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, const void *argmax) {
     Route r;
     const bool a16 = aligned(B, 16) && aligned(C, 16) && (!argmax || aligned(argmax, 16));
@@ -215,23 +226,32 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     if (p->opt_vec == 4 && N % 4 == 0 && a16) vec = 4;
     else if (p->opt_vec == 2 && N % 2 == 0 && a8) vec = 2;
     else if (p->opt_vec == 1) vec = 1;
-    const int64_t W = N / vec;
+    const int64_t W = (N + vec - 1) / vec;
     int G = std::max(4, pow2_ceil(W));
     int F = W > G ? 2 : 1;
+    const bool skewed = p->cv_deg > 1.0;
+    if (skewed && W >= 32) {
+        G = 16;
+        F = 1;
+    } else if (p->mean_deg < 8.0 && G >= 16 && W <= G) {
+        G /= 2;
+        F = 2;
+    }
     if (p->opt_lanes) G = p->opt_lanes;
     if (p->opt_coarsen) F = p->opt_coarsen;
     r.vec = vec;
     r.lanes = G;
     r.coarsen = F;
     r.slices = (int)((W + (int64_t)G * F - 1) / ((int64_t)G * F));
-    r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 1;
+    r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : (skewed ? 0 : 1);
     r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
     r.split = p->split;
     return r;
 }
 
-// Launch the row kernel over tasks [0, ntasks), in several dispatches when
-// one grid would exceed the 2^32 work-item limit of a dispatch dimension.
+// Launch the row kernel over tasks [0, ntasks), one task group per wave, in
+// several dispatches when one grid would exceed the 2^32 work-item limit of a
+// dispatch dimension.
 hipError_t launch_rows(RowKernelFn fn, RowArgs a, int rows_per_wave, int slices, hipStream_t s) {
     const int64_t per_block = (int64_t)rows_per_wave * kWaves;
     const int64_t max_blocks = (int64_t)(UINT32_MAX / kBlock);
@@ -480,6 +500,7 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
             return succeed();
+
         default:
             return fail(SPMM_E_INVALID_ARG, "unknown option %d", option);
     }
@@ -518,6 +539,7 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_xcd_remap = p->route.xcd_remap;
     info.route_nt_store = p->route.nt_store;
     info.route_split = p->route.split ? 1 : 0;
+
     *out = info;
     return succeed();
 }
@@ -562,10 +584,12 @@ SPMM_API int spmm_plan_partition(spmm_plan_t p, int64_t *seg_row, int64_t *seg_b
     }
     if (light_cap > 0) {
         if (p->split) {
-            std::vector<int> lr((size_t)nl);
-            if (nl > 0) e = hipMemcpy(lr.data(), p->light_rows, sizeof(int) * nl, hipMemcpyDeviceToHost);
-            if (e != hipSuccess) return fail_hip(e, "copy light rows");
-            for (int64_t i = 0; i < nl && i < light_cap; ++i) light[i] = lr[i];
+            std::vector<int> rp((size_t)p->M + 1);
+            e = hipMemcpy(rp.data(), p->rowptr, sizeof(int) * (p->M + 1), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return fail_hip(e, "copy rowptr");
+            int64_t n = 0;
+            for (int64_t i = 0; i < p->M && n < light_cap; ++i)
+                if (rp[i + 1] - rp[i] <= p->T) light[n++] = i;
         } else {
             for (int64_t i = 0; i < nl && i < light_cap; ++i) light[i] = i;
         }
@@ -608,7 +632,6 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     RowArgs a;
     std::memset(&a, 0, sizeof(a));
     a.rowptr = p->rowptr;
-    a.rows = p->split ? p->light_rows : nullptr;
     a.col = p->col;
     a.val = p->val;
     a.B = B;
@@ -618,7 +641,8 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.N = N;
     a.c_begin = 0;
     a.c_end = N;
-    a.ntasks = p->split ? p->n_light : p->M;
+    a.ntasks = p->M;
+    a.skip_above = p->split ? (int)std::min<int64_t>(p->T, INT_MAX) : INT_MAX;
     a.mean = reduce == SPMM_MEAN;
     a.xcd_remap = r.xcd_remap;
     a.nt_store = r.nt_store;

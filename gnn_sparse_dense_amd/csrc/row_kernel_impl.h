@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
     static_assert(G >= 4 && G <= 64 && (64 % G) == 0, "lanes per row");
     constexpr int R = 64 / G;          // rows (or pieces) per wave
     constexpr int SL = G * VEC * F;    // columns per slice
-    constexpr int U = 4;               // entries whose loads are issued together
+    constexpr int U = (F * VEC <= 4) ? 8 : 4;   // entries whose loads are issued together
     constexpr int NT = kChunk / 64;    // staging loads per lane per chunk
 
     __shared__ int s_col[kWaves][kChunk];
@@ -125,22 +125,24 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
     const int64_t c0 = a.c_begin + by * SL;
 
     const int64_t v = task0 + sub;
-    const bool live = v < a.ntasks;
+    bool live = v < a.ntasks;
     int beg = 0, end = 0;
     int64_t orow = 0;
     if (live) {
         if constexpr (PIECES) {
             beg = a.seg_begin[v];
             end = a.seg_end[v];
-            orow = v;
         } else {
-            const int r = a.rows ? a.rows[v] : (int)v;
-            beg = a.rowptr[r];
-            end = a.rowptr[r + 1];
-            orow = r;
+            beg = a.rowptr[v];
+            end = a.rowptr[v + 1];
         }
+        orow = v;
     }
-    const int deg = end - beg;
+    int deg = end - beg;
+    if (!PIECES && deg > a.skip_above) {   // split row: its pieces produce the output
+        deg = 0;
+        live = false;
+    }
 
     // Position of this group's entries in the wave's concatenated entry list.
     const int beg0 = __builtin_amdgcn_readfirstlane(beg);
@@ -214,15 +216,20 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
 
         const int lo = max(off, cb) - cb;
         const int hi = min(off + deg, cb + cn) - cb;
-        int k = lo;
-        for (; k + U <= hi; k += U) {
+        // Batches of U entries: all loads of a batch are issued before the
+        // first use, and a short row (or the tail of a long one) is one
+        // predicated batch rather than one round trip per entry.
+        for (int k = lo; k < hi; k += U) {
             int cidx[U];
             float w[U];
+            bool vld[U];
             float bv[U][F][VEC];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                cidx[u] = s_col[wv][k + u];
-                w[u] = HAS_VAL ? s_val[wv][k + u] : 1.0f;
+                vld[u] = k + u < hi;
+                const int kk = vld[u] ? k + u : lo;
+                cidx[u] = s_col[wv][kk];
+                w[u] = HAS_VAL ? s_val[wv][kk] : 1.0f;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -230,10 +237,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
                 for (int f = 0; f < F; ++f) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) bv[u][f][e] = 0.0f;
-                    if (ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                    if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
                 }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u) {
+                if (!vld[u]) continue;
 #pragma unroll
                 for (int f = 0; f < F; ++f)
 #pragma unroll
@@ -249,32 +257,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
                                                 : acc[f][e] + bv[u][f][e];
                         }
                     }
-        }
-        for (; k < hi; ++k) {
-            const int ci = s_col[wv][k];
-            const float wi = HAS_VAL ? s_val[wv][k] : 1.0f;
-            float bv[F][VEC];
-#pragma unroll
-            for (int f = 0; f < F; ++f) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) bv[f][e] = 0.0f;
-                if (ok[f]) load_vec<VEC>(Bp + (int64_t)ci * N + colf[f], bv[f]);
             }
-#pragma unroll
-            for (int f = 0; f < F; ++f)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    if constexpr (IS_MAX) {
-                        const float t = HAS_VAL ? wi * bv[f][e] : bv[f][e];
-                        if (arg[f][e] < 0 || t > acc[f][e]) {
-                            acc[f][e] = t;
-                            arg[f][e] = ci;
-                        }
-                    } else {
-                        acc[f][e] = HAS_VAL ? __builtin_fmaf(wi, bv[f][e], acc[f][e])
-                                            : acc[f][e] + bv[f][e];
-                    }
-                }
         }
         wave_lds_sync();
     }

@@ -21,7 +21,6 @@ constexpr int kXcds = 8;                // MI355X: 8 XCDs, 32 CUs each
 // Arguments of the row kernel (light rows or split pieces).
 struct RowArgs {
     const int *rowptr;     // int32 [M+1]                     (row mode)
-    const int *rows;       // int32 row list or nullptr        (row mode)
     const int *seg_begin;  // int32 [n_seg]                    (piece mode)
     const int *seg_end;    // int32 [n_seg]                    (piece mode)
     const int *col;        // int32 [nnz]
@@ -36,6 +35,7 @@ struct RowArgs {
     int64_t c_end;         // one past the last column handled
     int64_t task_base;     // first task of this launch
     int64_t ntasks;        // rows (row mode) or pieces (piece mode): tasks end here
+    int skip_above;        // row mode: rows longer than this are split, not written here
     int mean;              // divide by the row degree (row mode)
     int xcd_remap;         // give each XCD a contiguous range of tasks
     int nt_store;          // non-temporal output stores
@@ -121,7 +121,6 @@ struct spmm_plan {
     bool split = false;
     int64_t T = 0, L = 0, n_heavy = 0, n_seg = 0, n_light = 0;
     int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
-    int *light_rows = nullptr;
     float *partial = nullptr;
     int *part_arg = nullptr;
     // options (-1 / 0 = automatic)
