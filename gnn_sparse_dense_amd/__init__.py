@@ -32,6 +32,7 @@ SPMM_OPT_COARSEN = 5
 SPMM_OPT_VEC = 6
 SPMM_OPT_XCD_REMAP = 7
 SPMM_OPT_NT_STORE = 8
+SPMM_OPT_TILES = 9
 
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
@@ -60,6 +61,8 @@ class _Info(ctypes.Structure):
         ("route_coarsen", ctypes.c_int32), ("route_rows_per_wave", ctypes.c_int32),
         ("route_slices", ctypes.c_int32), ("route_xcd_remap", ctypes.c_int32),
         ("route_nt_store", ctypes.c_int32), ("route_split", ctypes.c_int32),
+        ("tiles", ctypes.c_int32), ("tile_cap", ctypes.c_int32),
+        ("route_tiled", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 

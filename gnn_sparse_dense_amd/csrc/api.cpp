@@ -89,9 +89,15 @@ void free_split(spmm_plan *p) {
     p->n_light = p->M;
 }
 
+void free_tiles(spmm_plan *p) {
+    dev_free(p->tiles);
+    p->tile_cap = p->tile_words = 0;
+}
+
 void free_plan(spmm_plan *p) {
     if (!p) return;
     free_split(p);
+    free_tiles(p);
     dev_free(p->rowptr);
     dev_free(p->col);
     dev_free(p->val);
@@ -193,6 +199,39 @@ int build_split(spmm_plan *p) {
     return SPMM_OK;
 }
 
+// Row-tile records for low, even degrees (RA-SpMM's sparse-uniform regime):
+// a record holds 8 row ends plus up to `cap` indexes (and values), with cap
+// sized to cover the mean tile plus four standard deviations of its entry
+// count.  Built when the mean degree is at most 16 and the degree CV at most
+// 1, and the graph is not split.
+int build_tiles(spmm_plan *p) {
+    free_tiles(p);
+    const double mt = kTileRows * p->mean_deg;
+    const double st = std::sqrt((double)kTileRows) * p->cv_deg * p->mean_deg;
+    int cap = (int)std::ceil((mt + 4.0 * st + 4.0) / 8.0) * 8;
+    cap = std::max(8, cap);
+    const bool fits = cap <= kTileMaxCap;
+    cap = std::min(cap, kTileMaxCap);
+    const bool enabled =
+        p->opt_tiles == 1 ||
+        (p->opt_tiles == -1 && !p->split && p->mean_deg <= 16.0 && p->cv_deg <= 1.0 && fits);
+    if (!enabled || p->M == 0 || p->split) return SPMM_OK;
+    const int rs = kTileRows + cap * (p->val ? 2 : 1);
+    const int64_t ntiles = (p->M + kTileRows - 1) / kTileRows;
+    int st2 = dev_alloc(&p->tiles, ntiles * rs, "row tiles");
+    if (st2) return st2;
+    hipError_t e = hipMemset(p->tiles, 0, sizeof(int) * ntiles * rs);
+    if (e == hipSuccess) e = launch_tile_build(p->rowptr, p->col, p->val, p->M, cap, rs, p->tiles, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_tiles(p);
+        return fail_hip(e, "row tile build");
+    }
+    p->tile_cap = cap;
+    p->tile_words = rs;
+    return SPMM_OK;
+}
+
 int pow2_ceil(int64_t x) {
     int g = 1;
     while (g < x && g < 64) g <<= 1;
@@ -246,6 +285,7 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : (skewed ? 0 : 1);
     r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
     r.split = p->split;
+    r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
     return r;
 }
 
@@ -440,7 +480,7 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
         p->cv_deg = std::sqrt(std::max(var, 0.0)) / p->mean_deg;
     }
 
-    if ((st = build_split(p))) {
+    if ((st = build_split(p)) || (st = build_tiles(p))) {
         free_plan(p);
         return nullptr;
     }
@@ -478,6 +518,15 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "split mode must be -1, 0 or 1");
             p->opt_split = value;
             break;
+        case SPMM_OPT_TILES: {
+            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "tiles must be -1, 0 or 1");
+            p->opt_tiles = value;
+            const hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail_hip(e, "synchronise before rebuilding the tiles");
+            const int st = build_tiles(p);
+            if (st) return st;
+            return succeed();
+        }
         case SPMM_OPT_LANES:
             if (!(value == 0 || value == 4 || value == 8 || value == 16 || value == 32 || value == 64))
                 return fail(SPMM_E_INVALID_ARG, "lanes per row must be 0, 4, 8, 16, 32 or 64");
@@ -506,7 +555,8 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
     }
     const hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail_hip(e, "synchronise before rebuilding the split");
-    const int st = build_split(p);
+    int st = build_split(p);
+    if (!st) st = build_tiles(p);
     if (st) return st;
     return succeed();
 }
@@ -539,6 +589,9 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_xcd_remap = p->route.xcd_remap;
     info.route_nt_store = p->route.nt_store;
     info.route_split = p->route.split ? 1 : 0;
+    info.tiles = p->tiles ? 1 : 0;
+    info.tile_cap = p->tile_cap;
+    info.route_tiled = p->route.tiled ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -622,7 +675,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     const bool has_val = p->val != nullptr;
 
     Route r = route_for(p, N, B, C, argmax);
-    RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false};
+    RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled};
     RowKernelFn fn = row_kernel(key);
     if (!fn) return fail(SPMM_E_UNSUPPORTED, "no kernel for lanes=%d vec=%d coarsen=%d", r.lanes, r.vec, r.coarsen);
     if (r.slices > 65535) return fail(SPMM_E_UNSUPPORTED, "N = %lld needs too many column slices", (long long)N);
@@ -634,6 +687,9 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.rowptr = p->rowptr;
     a.col = p->col;
     a.val = p->val;
+    a.tiles = p->tiles;
+    a.tile_cap = p->tile_cap;
+    a.tile_words = p->tile_words;
     a.B = B;
     a.out = C;
     a.argmax = argmax;
@@ -655,7 +711,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
             const int64_t Wv = (w1 - w0) / r.vec;
             const int F = Wv > 64 ? 2 : 1;
             const int slices = (int)((Wv + 64 * F - 1) / (64 * F));
-            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true});
+            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true, false});
             if (!pf) return fail(SPMM_E_UNSUPPORTED, "no piece kernel for vec=%d", r.vec);
             RowArgs pa;
             std::memset(&pa, 0, sizeof(pa));

@@ -176,7 +176,44 @@ __global__ __launch_bounds__(kBlock) void part_write_kernel(
     }
 }
 
+// One wave per row tile: header of cumulative row ends (or -1 in the last
+// word when the tile holds more than cap entries), then the tile's column ids
+// and, when weighted, their values as fp32 bit patterns.
+__global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restrict__ rowptr,
+                                                            const int *__restrict__ col,
+                                                            const float *__restrict__ val, int64_t M,
+                                                            int cap, int rs, int *__restrict__ tiles) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t ntiles = (M + kTileRows - 1) / kTileRows;
+    if (t >= ntiles) return;
+    const int64_t r0 = t * kTileRows;
+    const int rb = rowptr[r0];
+    const int re = rowptr[min(r0 + kTileRows, M)];
+    const int total = re - rb;
+    int *rec = tiles + t * rs;
+    if (total > cap) {
+        if (lane < kTileRows) rec[lane] = (lane == kTileRows - 1) ? -1 : 0;
+        return;
+    }
+    if (lane < kTileRows) rec[lane] = rowptr[min(r0 + lane + 1, M)] - rb;
+    for (int k = lane; k < total; k += 64) {
+        rec[kTileRows + k] = col[rb + k];
+        if (val) rec[kTileRows + cap + k] = __float_as_int(val[rb + k]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
+                             int *tiles, hipStream_t s) {
+    const int64_t ntiles = (M + kTileRows - 1) / kTileRows;
+    if (ntiles <= 0) return hipSuccess;
+    const int64_t blocks = (ntiles + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(tile_build_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, rowptr, col, val, M, cap,
+                       rs, tiles);
+    return hipGetLastError();
+}
 
 hipError_t launch_rowscan(const int64_t *rowptr, int64_t M, int *rowptr32, RowScanOut *out,
                           int64_t nblocks, hipStream_t s) {

@@ -98,75 +98,60 @@ __device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
     else *p = x[0];
 }
 
-template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
-__global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
-    static_assert(G >= 4 && G <= 64 && (64 % G) == 0, "lanes per row");
-    constexpr int R = 64 / G;          // rows (or pieces) per wave
-    constexpr int SL = G * VEC * F;    // columns per slice
-    constexpr int U = (F * VEC <= 4) ? 8 : 4;   // entries whose loads are issued together
-    constexpr int NT = kChunk / 64;    // staging loads per lane per chunk
-
-    __shared__ int s_col[kWaves][kChunk];
-    __shared__ float s_val[kWaves][HAS_VAL ? kChunk : 1];
-
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int sub = lane / G;
-    const int g = lane - sub * G;
-
-    const int64_t gx = gridDim.x;
-    int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
-    if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
-    const int64_t bx = lin % gx;
-    const int64_t by = lin / gx;
-
-    const int64_t task0 = a.task_base + (bx * kWaves + wv) * R;
-    if (task0 >= a.ntasks) return;                     // uniform per wave
-    const int64_t c0 = a.c_begin + by * SL;
-
-    const int64_t v = task0 + sub;
-    bool live = v < a.ntasks;
-    int beg = 0, end = 0;
-    int64_t orow = 0;
-    if (live) {
-        if constexpr (PIECES) {
-            beg = a.seg_begin[v];
-            end = a.seg_end[v];
-        } else {
-            beg = a.rowptr[v];
-            end = a.rowptr[v + 1];
+// Gathers and reduces entries [lo, hi) of the staged index list cp (values vp,
+// as fp32 bit patterns) into this lane's accumulators.  Batches of U entries:
+// all loads of a batch are issued before the first use, and a short row (or
+// the tail of a long one) is one predicated batch rather than one round trip
+// per entry.  Entries are folded in stored order with one accumulator per
+// output: fused multiply-add (plain add when unweighted) or strict '>'.
+template <int F, int VEC, bool HAS_VAL, bool IS_MAX>
+__device__ __forceinline__ void consume(const int *cp, const int *vp, int lo, int hi, const float *__restrict__ Bp,
+                                        int64_t N, const int (&colf)[F], const bool (&ok)[F],
+                                        float (&acc)[F][VEC], int (&arg)[F][VEC]) {
+    constexpr int U = (F * VEC <= 4) ? 8 : 4;
+    for (int k = lo; k < hi; k += U) {
+        int cidx[U];
+        float w[U];
+        bool vld[U];
+        float bv[U][F][VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vld[u] = k + u < hi;
+            const int kk = vld[u] ? k + u : lo;
+            cidx[u] = cp[kk];
+            w[u] = HAS_VAL ? __int_as_float(vp[kk]) : 1.0f;
         }
-        orow = v;
-    }
-    int deg = end - beg;
-    if (!PIECES && deg > a.skip_above) {   // split row: its pieces produce the output
-        deg = 0;
-        live = false;
-    }
-
-    // Position of this group's entries in the wave's concatenated entry list.
-    const int beg0 = __builtin_amdgcn_readfirstlane(beg);
-    int off = 0, total = 0;
-    bool contiguous = true;
 #pragma unroll
-    for (int s = 0; s < R; ++s) {
-        const int ds = __builtin_amdgcn_readlane(deg, s * G);
-        const int bs = __builtin_amdgcn_readlane(beg, s * G);
-        off += (s < sub) ? ds : 0;
-        contiguous = contiguous && (ds == 0 || bs == beg0 + total);
-        total += ds;
-    }
-
-    int colf[F];
-    bool ok[F];
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-        colf[f] = (int)(c0 + (f * G + g) * VEC);
-        ok[f] = (c0 + (int64_t)(f * G + g) * VEC) < a.c_end;
+            for (int f = 0; f < F; ++f) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) bv[u][f][e] = 0.0f;
+                if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!vld[u]) continue;
+#pragma unroll
+            for (int f = 0; f < F; ++f)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    if constexpr (IS_MAX) {
+                        const float t = HAS_VAL ? w[u] * bv[u][f][e] : bv[u][f][e];
+                        if (arg[f][e] < 0 || t > acc[f][e]) {
+                            acc[f][e] = t;
+                            arg[f][e] = cidx[u];
+                        }
+                    } else {
+                        acc[f][e] = HAS_VAL ? __builtin_fmaf(w[u], bv[u][f][e], acc[f][e]) : acc[f][e] + bv[u][f][e];
+                    }
+                }
+        }
     }
+}
 
-    float acc[F][VEC];
-    int arg[F][VEC];
+template <int F, int VEC, bool IS_MAX>
+__device__ __forceinline__ void init_acc(float (&acc)[F][VEC], int (&arg)[F][VEC]) {
 #pragma unroll
     for (int f = 0; f < F; ++f)
 #pragma unroll
@@ -174,95 +159,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
             acc[f][e] = IS_MAX ? -INFINITY : 0.0f;
             arg[f][e] = -1;
         }
+}
 
-    const float *__restrict__ Bp = a.B;
-    const int64_t N = a.N;
-
-    for (int cb = 0; cb < total; cb += kChunk) {
-        const int cn = min(kChunk, total - cb);
-        const int nt = (cn + 63) >> 6;
-        int cr[NT];
-        float vr[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-                const int q = cb + min(t * 64 + lane, cn - 1);
-                int p;
-                if (contiguous) {
-                    p = beg0 + q;
-                } else {
-                    p = 0;
-                    int o = 0;
-#pragma unroll
-                    for (int s = 0; s < R; ++s) {
-                        const int ds = __builtin_amdgcn_readlane(deg, s * G);
-                        const int bs = __builtin_amdgcn_readlane(beg, s * G);
-                        p = (q >= o && q < o + ds) ? bs + (q - o) : p;
-                        o += ds;
-                    }
-                }
-                cr[t] = a.col[p];
-                if constexpr (HAS_VAL) vr[t] = a.val[p];
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-                s_col[wv][t * 64 + lane] = cr[t];
-                if constexpr (HAS_VAL) s_val[wv][t * 64 + lane] = vr[t];
-            }
-        }
-        wave_lds_sync();
-
-        const int lo = max(off, cb) - cb;
-        const int hi = min(off + deg, cb + cn) - cb;
-        // Batches of U entries: all loads of a batch are issued before the
-        // first use, and a short row (or the tail of a long one) is one
-        // predicated batch rather than one round trip per entry.
-        for (int k = lo; k < hi; k += U) {
-            int cidx[U];
-            float w[U];
-            bool vld[U];
-            float bv[U][F][VEC];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                vld[u] = k + u < hi;
-                const int kk = vld[u] ? k + u : lo;
-                cidx[u] = s_col[wv][kk];
-                w[u] = HAS_VAL ? s_val[wv][kk] : 1.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int f = 0; f < F; ++f) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) bv[u][f][e] = 0.0f;
-                    if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
-                }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (!vld[u]) continue;
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        if constexpr (IS_MAX) {
-                            const float t = HAS_VAL ? w[u] * bv[u][f][e] : bv[u][f][e];
-                            if (arg[f][e] < 0 || t > acc[f][e]) {
-                                acc[f][e] = t;
-                                arg[f][e] = cidx[u];
-                            }
-                        } else {
-                            acc[f][e] = HAS_VAL ? __builtin_fmaf(w[u], bv[u][f][e], acc[f][e])
-                                                : acc[f][e] + bv[u][f][e];
-                        }
-                    }
-            }
-        }
-        wave_lds_sync();
-    }
-
-    if (!live) return;
+// Epilogue of one output row (or piece): mean division, empty-row values,
+// argmax as int64 column ids (int32 in piece mode).
+template <int F, int VEC, bool IS_MAX, bool PIECES>
+__device__ __forceinline__ void store_out(const RowArgs &a, int64_t orow, int deg, const int (&colf)[F],
+                                          const bool (&ok)[F], const float (&acc)[F][VEC],
+                                          const int (&arg)[F][VEC]) {
     float *orow_p = a.out + orow * a.ldo;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
@@ -289,9 +193,213 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
     }
 }
 
-// Lookup of one instantiated kernel; G = 64 also gets the piece-mode kernels.
+// Column ownership of lane g within its row group for the slice starting at c0.
+template <int G, int VEC, int F>
+__device__ __forceinline__ void lane_columns(const RowArgs &a, int64_t c0, int g, int (&colf)[F], bool (&ok)[F]) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        colf[f] = (int)(c0 + (f * G + g) * VEC);
+        ok[f] = (c0 + (int64_t)(f * G + g) * VEC) < a.c_end;
+    }
+}
+
+// Rows (or pieces) task0 .. task0 + 64/G - 1 of one wave from the CSR arrays:
+// row bounds, then the wave's index chunk staged in LDS, then the gathers.
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
+__device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int lane, int *s_col, int *s_val,
+                                         const int (&colf)[F], const bool (&ok)[F]) {
+    constexpr int R = 64 / G;
+    constexpr int NT = kChunk / 64;    // staging loads per lane per chunk
+    const int sub = lane / G;
+    const int64_t v = task0 + sub;
+    bool live = v < a.ntasks;
+    int beg = 0, end = 0;
+    if (live) {
+        if constexpr (PIECES) {
+            beg = a.seg_begin[v];
+            end = a.seg_end[v];
+        } else {
+            beg = a.rowptr[v];
+            end = a.rowptr[v + 1];
+        }
+    }
+    int deg = end - beg;
+    if (!PIECES && deg > a.skip_above) {   // split row: its pieces produce the output
+        deg = 0;
+        live = false;
+    }
+
+    // Position of this group's entries in the wave's concatenated entry list.
+    const int beg0 = __builtin_amdgcn_readfirstlane(beg);
+    int off = 0, total = 0;
+    bool contiguous = true;
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+        const int ds = __builtin_amdgcn_readlane(deg, s * G);
+        const int bs = __builtin_amdgcn_readlane(beg, s * G);
+        off += (s < sub) ? ds : 0;
+        contiguous = contiguous && (ds == 0 || bs == beg0 + total);
+        total += ds;
+    }
+
+    float acc[F][VEC];
+    int arg[F][VEC];
+    init_acc<F, VEC, IS_MAX>(acc, arg);
+
+    for (int cb = 0; cb < total; cb += kChunk) {
+        const int cn = min(kChunk, total - cb);
+        const int nt = (cn + 63) >> 6;
+        int cr[NT];
+        int vr[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+                const int q = cb + min(t * 64 + lane, cn - 1);
+                int p;
+                if (contiguous) {
+                    p = beg0 + q;
+                } else {
+                    p = 0;
+                    int o = 0;
+#pragma unroll
+                    for (int s = 0; s < R; ++s) {
+                        const int ds = __builtin_amdgcn_readlane(deg, s * G);
+                        const int bs = __builtin_amdgcn_readlane(beg, s * G);
+                        p = (q >= o && q < o + ds) ? bs + (q - o) : p;
+                        o += ds;
+                    }
+                }
+                cr[t] = a.col[p];
+                if constexpr (HAS_VAL) vr[t] = __float_as_int(a.val[p]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+                s_col[t * 64 + lane] = cr[t];
+                if constexpr (HAS_VAL) s_val[t * 64 + lane] = vr[t];
+            }
+        }
+        wave_lds_sync();
+        const int lo = max(off, cb) - cb;
+        const int hi = min(off + deg, cb + cn) - cb;
+        consume<F, VEC, HAS_VAL, IS_MAX>(s_col, s_val, lo, hi, a.B, a.N, colf, ok, acc, arg);
+        wave_lds_sync();
+    }
+
+    if (live) store_out<F, VEC, IS_MAX, PIECES>(a, v, deg, colf, ok, acc, arg);
+}
+
+// Block -> (first wave task, column slice), optionally XCD-aware.
+__device__ __forceinline__ void block_coords(const RowArgs &a, int64_t *bx, int64_t *by) {
+    const int64_t gx = gridDim.x;
+    int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
+    *bx = lin % gx;
+    *by = lin / gx;
+}
+
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
+__global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
+    static_assert(G >= 4 && G <= 64 && (64 % G) == 0, "lanes per row");
+    constexpr int R = 64 / G;          // rows (or pieces) per wave
+    constexpr int SL = G * VEC * F;    // columns per slice
+    __shared__ int s_col[kWaves][kChunk];
+    __shared__ int s_val[kWaves][HAS_VAL ? kChunk : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    int64_t bx, by;
+    block_coords(a, &bx, &by);
+    const int64_t task0 = a.task_base + (bx * kWaves + wv) * R;
+    if (task0 >= a.ntasks) return;                     // uniform per wave
+    int colf[F];
+    bool ok[F];
+    lane_columns<G, VEC, F>(a, a.c_begin + by * SL, lane % G, colf, ok);
+    row_task<G, VEC, F, HAS_VAL, IS_MAX, PIECES>(a, task0, lane, s_col[wv], s_val[wv], colf, ok);
+}
+
+// Row-tile kernel for low-degree graphs.  The plan stores every kTileRows-row
+// tile as one fixed-size record: kTileRows cumulative row ends, then up to
+// tile_cap column ids, then (weighted) as many values.  A wave reads its
+// 64/G / kTileRows records with one coalesced pass and has row bounds and
+// indexes together, so its gathers start one memory latency after launch
+// instead of two (bounds, then indexes).  Tiles longer than tile_cap carry an
+// end of -1 in their last header word and go through the CSR path.
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX>
+__global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
+    static_assert(G == 4 || G == 8, "a wave holds one or two row tiles");
+    constexpr int R = 64 / G;
+    constexpr int TPW = R / kTileRows;       // tiles per wave
+    constexpr int SL = G * VEC * F;
+    constexpr int NL = kTileLdsWords / 64;   // record loads per lane
+    __shared__ int s_rec[kWaves][kTileLdsWords];
+    __shared__ int s_col[kWaves][kChunk];
+    __shared__ int s_val[kWaves][HAS_VAL ? kChunk : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int sub = lane / G;
+    int64_t bx, by;
+    block_coords(a, &bx, &by);
+    const int64_t tile0 = a.task_base / kTileRows + (bx * kWaves + wv) * TPW;
+    const int64_t row0 = tile0 * kTileRows;
+    if (row0 >= a.ntasks) return;                      // uniform per wave
+    int colf[F];
+    bool ok[F];
+    lane_columns<G, VEC, F>(a, a.c_begin + by * SL, lane % G, colf, ok);
+
+    const int rs = a.tile_words;
+    const int64_t ntiles = (a.ntasks + kTileRows - 1) / kTileRows;
+    const int nwords = (int)min((int64_t)TPW, ntiles - tile0) * rs;
+    const int *rec = a.tiles + tile0 * rs;
+    int r[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        if (i * 64 < nwords) r[i] = rec[min(i * 64 + lane, nwords - 1)];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        if (i * 64 < nwords) s_rec[wv][i * 64 + lane] = r[i];
+    wave_lds_sync();
+
+    bool overflow = false;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        if (t * rs < nwords) overflow = overflow || s_rec[wv][t * rs + kTileRows - 1] < 0;
+    if (overflow) {                                     // uniform: CSR path for these rows
+        row_task<G, VEC, F, HAS_VAL, IS_MAX, false>(a, row0, lane, s_col[wv], s_val[wv], colf, ok);
+        return;
+    }
+
+    const int t = sub / kTileRows;
+    const int j = sub - t * kTileRows;
+    const int64_t orow = row0 + sub;
+    const bool live = orow < a.ntasks;
+    const int *hdr = s_rec[wv] + t * rs;
+    const int b = live ? (j ? hdr[j - 1] : 0) : 0;
+    const int deg = live ? hdr[j] - b : 0;
+    const int *cp = hdr + kTileRows + b;
+    float acc[F][VEC];
+    int arg[F][VEC];
+    init_acc<F, VEC, IS_MAX>(acc, arg);
+    consume<F, VEC, HAS_VAL, IS_MAX>(cp, cp + a.tile_cap, 0, deg, a.B, a.N, colf, ok, acc, arg);
+    if (live) store_out<F, VEC, IS_MAX, false>(a, orow, deg, colf, ok, acc, arg);
+}
+
+// Lookup of one instantiated kernel; G = 64 also gets the piece-mode kernels,
+// G = 4 and 8 the row-tile kernels.
 template <int G, int VEC, int F>
 RowKernelFn pick_row_kernel(const RowKernelKey &k) {
+    if (k.tiled) {
+        if constexpr (G == 4 || G == 8) {
+            if (k.pieces) return nullptr;
+            if (k.is_max)
+                return k.has_val ? tile_kernel_t<G, VEC, F, true, true> : tile_kernel_t<G, VEC, F, false, true>;
+            return k.has_val ? tile_kernel_t<G, VEC, F, true, false> : tile_kernel_t<G, VEC, F, false, false>;
+        } else {
+            return nullptr;
+        }
+    }
     if (k.pieces) {
         if constexpr (G == 64) {
             if (k.is_max)

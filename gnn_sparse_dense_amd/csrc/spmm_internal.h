@@ -7,7 +7,7 @@
 #include <cstdint>
 #include <string>
 
-#include "../../include/spmm.h"
+#include "spmm.h"
 
 namespace gspmm {
 
@@ -17,6 +17,9 @@ constexpr int kChunk = 256;             // col/val entries a wave stages in LDS 
 constexpr int kPartialWidth = 256;      // columns per pass of the split path
 constexpr int kRowsPerScanBlock = 1024; // rows per block of the plan-time scans
 constexpr int kXcds = 8;                // MI355X: 8 XCDs, 32 CUs each
+constexpr int kTileRows = 8;            // rows per row-tile record
+constexpr int kTileLdsWords = 512;      // LDS words per wave for row-tile records (2 records)
+constexpr int kTileMaxCap = 120;        // largest entries per row-tile record
 
 // Arguments of the row kernel (light rows or split pieces).
 struct RowArgs {
@@ -25,6 +28,9 @@ struct RowArgs {
     const int *seg_end;    // int32 [n_seg]                    (piece mode)
     const int *col;        // int32 [nnz]
     const float *val;      // fp32 [nnz] or nullptr
+    const int *tiles;      // row-tile records (tile kernels only)
+    int tile_cap;          // entries per record
+    int tile_words;        // record length in int32 words
     const float *B;        // fp32 [K, N]
     float *out;            // C (row mode) or the partial buffer (piece mode)
     int64_t *argmax;       // int64 [M, N] or nullptr          (row mode, max)
@@ -63,6 +69,7 @@ struct RowKernelKey {
     bool has_val;
     bool is_max;
     bool pieces;  // piece mode (split rows) instead of row mode
+    bool tiled;   // row-tile records instead of CSR row bounds
 };
 
 typedef void (*RowKernelFn)(RowArgs);
@@ -98,11 +105,15 @@ hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t 
                              int *seg_begin, int *seg_end, int *light_rows, int64_t nblocks,
                              hipStream_t s);
 
+hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
+                             int *tiles, hipStream_t s);
+
 // ---- the plan ----
 struct Route {
     int lanes = 64, vec = 4, coarsen = 1, slices = 1;
     int xcd_remap = 1, nt_store = 0;
     bool split = false;
+    bool tiled = false;
 };
 
 }  // namespace gspmm
@@ -123,8 +134,11 @@ struct spmm_plan {
     int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
     float *partial = nullptr;
     int *part_arg = nullptr;
+    // row-tile records (low-degree graphs)
+    int *tiles = nullptr;
+    int tile_cap = 0, tile_words = 0;
     // options (-1 / 0 = automatic)
-    int64_t opt_T = -1, opt_L = -1, opt_split = -1;
+    int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1;
     int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1;
     // last routing decision
     int64_t route_N = 0;

@@ -65,7 +65,9 @@ enum spmm_option {
     SPMM_OPT_COARSEN = 5,      /* vectors per lane F in {1,2}; 0 auto             */
     SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto            */
     SPMM_OPT_XCD_REMAP = 7,    /* -1 auto, 0 off, 1 on: contiguous rows per XCD  */
-    SPMM_OPT_NT_STORE = 8      /* -1 auto, 0 off, 1 on: non-temporal C stores    */
+    SPMM_OPT_NT_STORE = 8,     /* -1 auto, 0 off, 1 on: non-temporal C stores    */
+    SPMM_OPT_TILES = 9         /* -1 auto (low, even degrees), 0 off, 1 on: keep
+                                  8-row tile records with bounds + indexes    */
 };
 
 /* Descriptors of a plan and of its last routing decision. */
@@ -84,6 +86,8 @@ struct spmm_plan_info {
     int64_t route_N;
     int32_t route_lanes, route_vec, route_coarsen, route_rows_per_wave;
     int32_t route_slices, route_xcd_remap, route_nt_store, route_split;
+    int32_t tiles, tile_cap;     /* row-tile records built; entries per record   */
+    int32_t route_tiled, reserved;
 };
 
 /*

@@ -298,3 +298,33 @@ def test_regimes_full_size_sampled(orc, name):
         check(orc, g, w.B, red, C[sample], None if arg is None else arg[sample], rows=sample,
               exact_rows=exact_idx, what=f"full {name} {red}")
     G.spmm_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_row_tiles_match_csr_path(orc, weighted):
+    """Row-tile records (bounds + indexes in one record per 8 rows) give the same
+    bits as the CSR path, including tiles too long for a record (which take the
+    CSR path inside the tile kernel) and a ragged last tile."""
+    rng = np.random.default_rng(404 + weighted)
+    g = W.random_csr(rng, 20_003, 15_000, mean_deg=3.0, empty_frac=0.05, heavy_rows=40, heavy_deg=150,
+                     dup_frac=0.05, shuffle_rows=True, weighted=weighted)
+    for N in (16, 64, 32):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        on = make_plan(g, [(G.SPMM_OPT_TILES, 1)])
+        off = make_plan(g, [(G.SPMM_OPT_TILES, 0)])
+        info = G.spmm_plan_info(on)
+        assert info["tiles"] == 1 and info["tile_cap"] > 0
+        assert G.spmm_plan_info(off)["tiles"] == 0
+        for red in ("sum", "mean", "max"):
+            C1, a1 = gpu_run(on, g.M, Bd, red)
+            assert G.spmm_plan_info(on)["route_tiled"] == 1, f"N={N}: tile kernel not routed"
+            C0, a0 = gpu_run(off, g.M, Bd, red)
+            assert G.spmm_plan_info(off)["route_tiled"] == 0
+            log(f"tiles N={N} {red} cap={info['tile_cap']}")
+            assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), f"tiles vs CSR N={N} {red}"
+            if a1 is not None:
+                assert np.array_equal(a1, a0)
+            check(orc, g, B, red, C1, a1, exact_rows=np.arange(g.M), what=f"tiles N={N} {red}")
+        G.spmm_plan_destroy(on)
+        G.spmm_plan_destroy(off)
