@@ -220,8 +220,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="road", choices=sorted(REGIME_TEXT),
+                    help="regime timed for the JSON line (default: the road-like headline)")
+    ap.add_argument("--reduce", default=None, help="reduction for the JSON line (default: the regime's first)")
     ap.add_argument("--headline-only", action="store_true", help="skip the other regimes")
-    ap.add_argument("--regimes", default="tiny,diffusion,community,powerlaw")
+    ap.add_argument("--regimes", default="road,tiny,diffusion,community,powerlaw")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -237,8 +240,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    headline, reduce = "road", "sum"
+    headline = args.workload
     r = Runner(headline)
+    reduce = args.reduce or r.w.reduces[0]
     g, N = r.g, r.w.N
     print(f"[bench] {headline}: M={g.M} nnz={g.nnz} N={N} gen={r.gen_s:.1f}s plan={r.info['plan_ms']:.1f}ms",
           file=sys.stderr, flush=True)
@@ -268,7 +272,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": REGIME_TEXT[headline] + ", sum reduction", "M": g.M, "K": g.K,
+        "config": {"workload": REGIME_TEXT[headline] + f", {reduce} reduction", "M": g.M, "K": g.K,
                    "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32},
         "effective_GBps": round(comp / (ms_per_step * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(comp / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -301,7 +305,7 @@ def main():
         r.close()
         del r
         torch.cuda.empty_cache()
-        for name in [x for x in args.regimes.split(",") if x]:
+        for name in [x for x in args.regimes.split(",") if x and x != headline]:
             rr = Runner(name)
             print(f"[bench] {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N} gen={rr.gen_s:.1f}s",
                   file=sys.stderr, flush=True)

@@ -33,6 +33,7 @@ SPMM_OPT_VEC = 6
 SPMM_OPT_XCD_REMAP = 7
 SPMM_OPT_NT_STORE = 8
 SPMM_OPT_TILES = 9
+SPMM_OPT_WINDOW = 10
 
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
@@ -62,7 +63,8 @@ class _Info(ctypes.Structure):
         ("route_slices", ctypes.c_int32), ("route_xcd_remap", ctypes.c_int32),
         ("route_nt_store", ctypes.c_int32), ("route_split", ctypes.c_int32),
         ("tiles", ctypes.c_int32), ("tile_cap", ctypes.c_int32),
-        ("route_tiled", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("route_tiled", ctypes.c_int32), ("route_window", ctypes.c_int32),
+        ("win_frac", ctypes.c_double),
     ]
 
 

@@ -25,6 +25,7 @@ SOURCES = [
     "row_kernels_v1.hip",
     "row_kernels_v2.hip",
     "row_kernels_v4.hip",
+    "window_kernels.hip",
 ]
 
 COMMON = [

@@ -286,6 +286,17 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
     r.split = p->split;
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
+    // community structure with wide features: stage B's row blocks in LDS
+    r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 &&
+               (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
+    if (r.window) {
+        r.lanes = kWinCols / 4;
+        r.coarsen = 1;
+        r.slices = (int)((N + kWinCols - 1) / kWinCols);
+        r.tiled = false;
+        // measured: the slices of a row block spread over XCDs run faster
+        r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 0;
+    }
     return r;
 }
 
@@ -469,6 +480,28 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
         }
     }
 
+    // share of entries inside their row's aligned kWinRows block
+    if (nnz > 0) {
+        const int64_t wblocks = (M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
+        int64_t *d_w = nullptr;
+        if ((st = dev_alloc(&d_w, wblocks, "window scan"))) {
+            free_plan(p);
+            return nullptr;
+        }
+        e = launch_window_scan(p->rowptr, p->col, M, d_w, wblocks, nullptr);
+        std::vector<int64_t> wc((size_t)wblocks);
+        if (e == hipSuccess) e = hipMemcpy(wc.data(), d_w, sizeof(int64_t) * wblocks, hipMemcpyDeviceToHost);
+        dev_free(d_w);
+        if (e != hipSuccess) {
+            fail_hip(e, "window scan");
+            free_plan(p);
+            return nullptr;
+        }
+        int64_t inside = 0;
+        for (int64_t c : wc) inside += c;
+        p->win_frac = (double)inside / (double)nnz;
+    }
+
     // descriptors (RA-SpMM: M, mean degree, coefficient of variation)
     p->dmax = dmax;
     p->n_empty = n_empty;
@@ -527,6 +560,10 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (st) return st;
             return succeed();
         }
+        case SPMM_OPT_WINDOW:
+            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "window must be -1, 0 or 1");
+            p->opt_window = value;
+            return succeed();
         case SPMM_OPT_LANES:
             if (!(value == 0 || value == 4 || value == 8 || value == 16 || value == 32 || value == 64))
                 return fail(SPMM_E_INVALID_ARG, "lanes per row must be 0, 4, 8, 16, 32 or 64");
@@ -592,6 +629,8 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.tiles = p->tiles ? 1 : 0;
     info.tile_cap = p->tile_cap;
     info.route_tiled = p->route.tiled ? 1 : 0;
+    info.route_window = p->route.window ? 1 : 0;
+    info.win_frac = p->win_frac;
 
     *out = info;
     return succeed();
@@ -695,6 +734,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.argmax = argmax;
     a.ldo = N;
     a.N = N;
+    a.K = p->K;
     a.c_begin = 0;
     a.c_end = N;
     a.ntasks = p->M;
@@ -702,7 +742,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.mean = reduce == SPMM_MEAN;
     a.xcd_remap = r.xcd_remap;
     a.nt_store = r.nt_store;
-    hipError_t e = launch_rows(fn, a, 64 / r.lanes, r.slices, s);
+    hipError_t e = r.window ? launch_window(a, has_val, is_max, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
     if (e != hipSuccess) return fail_hip(e, "row kernel launch");
 
     if (p->split && p->n_seg > 0) {
@@ -724,6 +764,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
             pa.part_arg = p->part_arg;
             pa.ldo = kPartialWidth;
             pa.N = N;
+            pa.K = p->K;
             pa.c_begin = w0;
             pa.c_end = w1;
             pa.ntasks = p->n_seg;

@@ -203,7 +203,37 @@ __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restric
     }
 }
 
+// Entries whose column lies in the same aligned block of kWinRows rows as
+// their row (one count per scan block).
+__global__ __launch_bounds__(kBlock) void window_scan_kernel(const int *__restrict__ rowptr,
+                                                             const int *__restrict__ col, int64_t M,
+                                                             int64_t *__restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock;
+    int64_t cnt = 0;
+    for (int j = threadIdx.x; j < kRowsPerScanBlock; j += kBlock) {
+        const int64_t i = base + j;
+        if (i >= M) break;
+        const int blk = (int)(i / kWinRows);
+        for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) cnt += (col[p] / kWinRows == blk);
+    }
+    __shared__ int64_t sh[kBlock];
+    sh[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = sh[0];
+}
+
 }  // namespace
+
+hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int64_t *out, int64_t nblocks,
+                              hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(window_scan_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr, col, M, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
                              int *tiles, hipStream_t s) {

@@ -104,11 +104,14 @@ __device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
 // the tail of a long one) is one predicated batch rather than one round trip
 // per entry.  Entries are folded in stored order with one accumulator per
 // output: fused multiply-add (plain add when unweighted) or strict '>'.
-template <int F, int VEC, bool HAS_VAL, bool IS_MAX>
+// WIN: entries whose column lies in [w0, w0 + kWinRows) read B from the
+// block's LDS copy sB (kWinCols columns per row, lane quad g) instead of HBM.
+template <int F, int VEC, bool HAS_VAL, bool IS_MAX, bool WIN = false, int UB = 0>
 __device__ __forceinline__ void consume(const int *cp, const int *vp, int lo, int hi, const float *__restrict__ Bp,
                                         int64_t N, const int (&colf)[F], const bool (&ok)[F],
-                                        float (&acc)[F][VEC], int (&arg)[F][VEC]) {
-    constexpr int U = (F * VEC <= 4) ? 8 : 4;
+                                        float (&acc)[F][VEC], int (&arg)[F][VEC],
+                                        const f32x4 *sB = nullptr, int64_t w0 = 0, int g = 0) {
+    constexpr int U = UB ? UB : ((F * VEC <= 4) ? 8 : 4);
     for (int k = lo; k < hi; k += U) {
         int cidx[U];
         float w[U];
@@ -127,7 +130,20 @@ __device__ __forceinline__ void consume(const int *cp, const int *vp, int lo, in
             for (int f = 0; f < F; ++f) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) bv[u][f][e] = 0.0f;
-                if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                if constexpr (WIN) {
+                    static_assert(F == 1 && VEC == 4, "window path: one float4 per lane");
+                    const int64_t wr = (int64_t)cidx[u] - w0;
+                    if (vld[u] && ok[f]) {
+                        if (wr >= 0 && wr < kWinRows) {
+                            const f32x4 t = sB[wr * (kWinCols / 4) + g];
+                            bv[u][f][0] = t.x; bv[u][f][1] = t.y; bv[u][f][2] = t.z; bv[u][f][3] = t.w;
+                        } else {
+                            load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                        }
+                    }
+                } else {
+                    if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                }
             }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -205,11 +221,12 @@ __device__ __forceinline__ void lane_columns(const RowArgs &a, int64_t c0, int g
 
 // Rows (or pieces) task0 .. task0 + 64/G - 1 of one wave from the CSR arrays:
 // row bounds, then the wave's index chunk staged in LDS, then the gathers.
-template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES, int CH = kChunk, bool WIN = false>
 __device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int lane, int *s_col, int *s_val,
-                                         const int (&colf)[F], const bool (&ok)[F]) {
+                                         const int (&colf)[F], const bool (&ok)[F],
+                                         const f32x4 *sB = nullptr, int64_t w0 = 0) {
     constexpr int R = 64 / G;
-    constexpr int NT = kChunk / 64;    // staging loads per lane per chunk
+    constexpr int NT = CH / 64;        // staging loads per lane per chunk
     const int sub = lane / G;
     const int64_t v = task0 + sub;
     bool live = v < a.ntasks;
@@ -246,8 +263,8 @@ __device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int la
     int arg[F][VEC];
     init_acc<F, VEC, IS_MAX>(acc, arg);
 
-    for (int cb = 0; cb < total; cb += kChunk) {
-        const int cn = min(kChunk, total - cb);
+    for (int cb = 0; cb < total; cb += CH) {
+        const int cn = min(CH, total - cb);
         const int nt = (cn + 63) >> 6;
         int cr[NT];
         int vr[NT];
@@ -283,7 +300,10 @@ __device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int la
         wave_lds_sync();
         const int lo = max(off, cb) - cb;
         const int hi = min(off + deg, cb + cn) - cb;
-        consume<F, VEC, HAS_VAL, IS_MAX>(s_col, s_val, lo, hi, a.B, a.N, colf, ok, acc, arg);
+        // window blocks read most of B from LDS: shorter batches keep the
+        // 1024-thread block within 64 VGPRs (two blocks per CU)
+        consume<F, VEC, HAS_VAL, IS_MAX, WIN, WIN ? 4 : 0>(s_col, s_val, lo, hi, a.B, a.N, colf, ok, acc, arg,
+                                                          sB, w0, lane % G);
         wave_lds_sync();
     }
 
@@ -384,6 +404,57 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     init_acc<F, VEC, IS_MAX>(acc, arg);
     consume<F, VEC, HAS_VAL, IS_MAX>(cp, cp + a.tile_cap, 0, deg, a.B, a.N, colf, ok, acc, arg);
     if (live) store_out<F, VEC, IS_MAX, false>(a, orow, deg, colf, ok, acc, arg);
+}
+
+// Window kernel for graphs whose neighbours mostly fall in their own aligned
+// block of kWinRows rows (community / locality structure, RA-SpMM's
+// community regime).  A 1024-thread block owns one such block of rows and one
+// kWinCols-wide column slice: it first copies B's rows of that block (the
+// window, 64 KB) into LDS, then its 16 waves walk the block's rows four at a
+// time (16 lanes x float4 per row) exactly as the row kernel does, except
+// that entries inside the window read B from LDS.  Every B row of the window
+// is then read from HBM once per slice instead of once per referencing row,
+// and the entry order, hence every result bit, is the row kernel's.
+template <bool HAS_VAL, bool IS_MAX>
+__global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
+    constexpr int G = kWinCols / 4, VEC = 4, F = 1, R = 64 / G;   // one float4 per lane
+    constexpr int WW = kWinBlock / 64;              // waves per block
+    constexpr int Q = kWinCols / 4;                 // float4 per window row
+    __shared__ f32x4 s_B[kWinRows * Q];
+    __shared__ int s_col[WW][kWinChunk];
+    __shared__ int s_val[WW][HAS_VAL ? kWinChunk : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t gx = gridDim.x;
+    int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
+    // consecutive linear ids walk the slices of one row block, so the
+    // block's indexes stay in one L2 while its slices run
+    const int64_t nsl = gridDim.y;
+    const int64_t tile = lin / nsl;
+    const int64_t slice = lin % nsl;
+    const int64_t w0 = tile * kWinRows;
+    const int64_t c0 = slice * kWinCols;
+
+    for (int i = threadIdx.x; i < kWinRows * Q; i += kWinBlock) {
+        const int r = i / Q, q = i - (i / Q) * Q;
+        const int64_t brow = w0 + r, bcol = c0 + q * 4;
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (brow < a.K && bcol < a.N) v = *reinterpret_cast<const f32x4 *>(a.B + brow * a.N + bcol);
+        s_B[i] = v;
+    }
+    __syncthreads();
+
+    int colf[F];
+    bool ok[F];
+    lane_columns<G, VEC, F>(a, c0, lane % G, colf, ok);
+    for (int pass = 0; pass < kWinRows / (WW * R); ++pass) {
+        const int64_t task0 = w0 + (int64_t)(pass * WW + wv) * R;
+        if (task0 < a.ntasks)
+            row_task<G, VEC, F, HAS_VAL, IS_MAX, false, kWinChunk, true>(a, task0, lane, s_col[wv], s_val[wv],
+                                                                       colf, ok, s_B, w0);
+    }
 }
 
 // Lookup of one instantiated kernel; G = 64 also gets the piece-mode kernels,

@@ -20,6 +20,10 @@ constexpr int kXcds = 8;                // MI355X: 8 XCDs, 32 CUs each
 constexpr int kTileRows = 8;            // rows per row-tile record
 constexpr int kTileLdsWords = 512;      // LDS words per wave for row-tile records (2 records)
 constexpr int kTileMaxCap = 120;        // largest entries per row-tile record
+constexpr int kWinRows = 256;           // rows of a community window
+constexpr int kWinCols = 64;            // B columns staged per window block
+constexpr int kWinBlock = 1024;         // threads of a window block
+constexpr int kWinChunk = 128;          // staged entries per wave in window blocks
 
 // Arguments of the row kernel (light rows or split pieces).
 struct RowArgs {
@@ -37,6 +41,7 @@ struct RowArgs {
     int *part_arg;         // int32 partial argmax             (piece mode, max)
     int64_t ldo;           // row stride of out / argmax / part_arg, in elements
     int64_t N;             // columns of B (row stride of B)
+    int64_t K;             // rows of B
     int64_t c_begin;       // first column handled by this launch
     int64_t c_end;         // one past the last column handled
     int64_t task_base;     // first task of this launch
@@ -81,6 +86,7 @@ RowKernelFn row_kernel_v4(const RowKernelKey &k);
 RowKernelFn row_kernel(const RowKernelKey &k);
 
 hipError_t launch_combine(const CombineArgs &a, bool is_max, hipStream_t s);
+hipError_t launch_window(const RowArgs &a, bool has_val, bool is_max, hipStream_t s);
 
 // ---- plan-time kernels (plan_kernels.hip) ----
 struct RowScanOut {        // one record per scan block
@@ -105,6 +111,8 @@ hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t 
                              int *seg_begin, int *seg_end, int *light_rows, int64_t nblocks,
                              hipStream_t s);
 
+hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int64_t *out, int64_t nblocks,
+                              hipStream_t s);
 hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
                              int *tiles, hipStream_t s);
 
@@ -114,6 +122,7 @@ struct Route {
     int xcd_remap = 1, nt_store = 0;
     bool split = false;
     bool tiled = false;
+    bool window = false;
 };
 
 }  // namespace gspmm
@@ -137,8 +146,9 @@ struct spmm_plan {
     // row-tile records (low-degree graphs)
     int *tiles = nullptr;
     int tile_cap = 0, tile_words = 0;
+    double win_frac = 0;       // share of entries inside their row's kWinRows block
     // options (-1 / 0 = automatic)
-    int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1;
+    int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
     int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1;
     // last routing decision
     int64_t route_N = 0;

@@ -328,3 +328,48 @@ def test_row_tiles_match_csr_path(orc, weighted):
             check(orc, g, B, red, C1, a1, exact_rows=np.arange(g.M), what=f"tiles N={N} {red}")
         G.spmm_plan_destroy(on)
         G.spmm_plan_destroy(off)
+
+
+def _sub_csr(g, M, K):
+    """The first M rows of g, keeping only columns below K."""
+    keep_rows = g.rowptr[: M + 1]
+    cols = g.col[: keep_rows[-1]]
+    vals = None if g.val is None else g.val[: keep_rows[-1]]
+    rows = np.repeat(np.arange(M), np.diff(keep_rows))
+    m = cols < K
+    rowptr, col, order = W.csr_from_pairs(M, rows[m], cols[m])
+    val = None if vals is None else vals[m][order]
+    return W.Graph("sub", M, K, rowptr, col, val)
+
+
+@pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted"])
+def test_community_window_matches_row_kernel(orc, shape):
+    """The LDS window path (B's 256-row blocks staged per workgroup) gives the
+    row kernel's bits, with a ragged last block, N not a multiple of the
+    64-column slice, and K different from M."""
+    g = W.make_graph("community", M=5_000, seed=11)
+    if shape == "wide":
+        g = _sub_csr(g, 4_000, 5_000)
+    elif shape == "tall":
+        g = _sub_csr(g, 5_000, 4_100)
+    elif shape == "unweighted":
+        g = W.Graph("u", g.M, g.K, g.rowptr, g.col, None)
+    rng = np.random.default_rng(77)
+    for N in (128, 200, 512):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        on = make_plan(g, [(G.SPMM_OPT_WINDOW, 1)])
+        off = make_plan(g, [(G.SPMM_OPT_WINDOW, 0)])
+        assert G.spmm_plan_info(on)["win_frac"] > 0.5
+        for red in ("sum", "mean", "max"):
+            C1, a1 = gpu_run(on, g.M, Bd, red)
+            assert G.spmm_plan_info(on)["route_window"] == 1
+            C0, a0 = gpu_run(off, g.M, Bd, red)
+            assert G.spmm_plan_info(off)["route_window"] == 0
+            log(f"window {shape} N={N} {red}")
+            assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), f"window vs row kernel {shape} N={N} {red}"
+            if a1 is not None:
+                assert np.array_equal(a1, a0)
+            check(orc, g, B, red, C1, a1, exact_rows=np.arange(g.M), what=f"window {shape} N={N} {red}")
+        G.spmm_plan_destroy(on)
+        G.spmm_plan_destroy(off)
