@@ -64,7 +64,7 @@ class _Info(ctypes.Structure):
         ("route_nt_store", ctypes.c_int32), ("route_split", ctypes.c_int32),
         ("tiles", ctypes.c_int32), ("tile_cap", ctypes.c_int32),
         ("route_tiled", ctypes.c_int32), ("route_window", ctypes.c_int32),
-        ("win_frac", ctypes.c_double),
+        ("win_frac", ctypes.c_double), ("tile_overflow", ctypes.c_int64),
     ]
 
 

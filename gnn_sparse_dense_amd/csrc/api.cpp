@@ -204,32 +204,60 @@ int build_split(spmm_plan *p) {
 // sized to cover the mean tile plus four standard deviations of its entry
 // count.  Built when the mean degree is at most 16 and the degree CV at most
 // 1, and the graph is not split.
-int build_tiles(spmm_plan *p) {
+int build_tiles_as(spmm_plan *p, int cap, bool compact) {
     free_tiles(p);
-    const double mt = kTileRows * p->mean_deg;
-    const double st = std::sqrt((double)kTileRows) * p->cv_deg * p->mean_deg;
-    int cap = (int)std::ceil((mt + 4.0 * st + 4.0) / 8.0) * 8;
-    cap = std::max(8, cap);
-    const bool fits = cap <= kTileMaxCap;
-    cap = std::min(cap, kTileMaxCap);
-    const bool enabled =
-        p->opt_tiles == 1 ||
-        (p->opt_tiles == -1 && !p->split && p->mean_deg <= 16.0 && p->cv_deg <= 1.0 && fits);
-    if (!enabled || p->M == 0 || p->split) return SPMM_OK;
-    const int rs = kTileRows + cap * (p->val ? 2 : 1);
+    const int idx_words = compact ? cap / 2 : cap;
+    const int rs = (compact ? 3 : kTileRows) + idx_words + (p->val ? cap : 0);
     const int64_t ntiles = (p->M + kTileRows - 1) / kTileRows;
-    int st2 = dev_alloc(&p->tiles, ntiles * rs, "row tiles");
-    if (st2) return st2;
+    const int64_t nblocks = tile_build_blocks(p->M);
+    int64_t *d_ovf = nullptr;
+    int st = dev_alloc(&d_ovf, nblocks, "tile overflow counts");
+    if (!st) st = dev_alloc(&p->tiles, ntiles * rs, "row tiles");
+    if (st) {
+        dev_free(d_ovf);
+        return st;
+    }
+    std::vector<int64_t> ovf((size_t)nblocks);
     hipError_t e = hipMemset(p->tiles, 0, sizeof(int) * ntiles * rs);
-    if (e == hipSuccess) e = launch_tile_build(p->rowptr, p->col, p->val, p->M, cap, rs, p->tiles, nullptr);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+        e = launch_tile_build(p->rowptr, p->col, p->val, p->M, cap, rs, compact, p->tiles, d_ovf, nblocks, nullptr);
+    if (e == hipSuccess) e = hipMemcpy(ovf.data(), d_ovf, sizeof(int64_t) * nblocks, hipMemcpyDeviceToHost);
+    dev_free(d_ovf);
     if (e != hipSuccess) {
         free_tiles(p);
         return fail_hip(e, "row tile build");
     }
     p->tile_cap = cap;
     p->tile_words = rs;
+    p->tile_compact = compact;
+    p->tile_overflow = 0;
+    for (int64_t n : ovf) p->tile_overflow += n;
     return SPMM_OK;
+}
+
+// Row-tile records for low, even degrees (RA-SpMM's sparse-uniform regime):
+// a record holds 8 row bounds plus up to `cap` indexes (and values), with cap
+// sized to cover the mean tile plus four standard deviations of its entry
+// count.  Built when the mean degree is at most 16, the degree CV at most 1
+// and the graph is not split.  Compact records (16-bit offsets from a tile
+// base) are kept when at most 5% of tiles overflow them; otherwise wide ones.
+int build_tiles(spmm_plan *p) {
+    free_tiles(p);
+    const double mt = kTileRows * p->mean_deg;
+    const double sd = std::sqrt((double)kTileRows) * p->cv_deg * p->mean_deg;
+    int cap = (int)std::ceil((mt + 4.0 * sd + 4.0) / 8.0) * 8;
+    cap = std::max(8, cap);
+    const bool fits = cap <= kTileMaxCap;
+    cap = std::min(cap, kTileMaxCap);
+    const bool enabled =
+        p->opt_tiles >= 1 ||
+        (p->opt_tiles == -1 && !p->split && p->mean_deg <= 16.0 && p->cv_deg <= 1.0 && fits);
+    if (!enabled || p->M == 0 || p->split) return SPMM_OK;
+    const int64_t ntiles = (p->M + kTileRows - 1) / kTileRows;
+    int st = build_tiles_as(p, cap, p->opt_tiles != 2);
+    if (st) return st;
+    if (p->tile_compact && p->tile_overflow * 20 > ntiles) st = build_tiles_as(p, cap, false);
+    return st;
 }
 
 int pow2_ceil(int64_t x) {
@@ -286,6 +314,7 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
     r.split = p->split;
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
+    r.compact = r.tiled && p->tile_compact;
     // community structure with wide features: stage B's row blocks in LDS
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 &&
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
@@ -294,6 +323,7 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
         r.coarsen = 1;
         r.slices = (int)((N + kWinCols - 1) / kWinCols);
         r.tiled = false;
+        r.compact = false;
         // measured: the slices of a row block spread over XCDs run faster
         r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 0;
     }
@@ -552,7 +582,7 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             p->opt_split = value;
             break;
         case SPMM_OPT_TILES: {
-            if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "tiles must be -1, 0 or 1");
+            if (value < -1 || value > 2) return fail(SPMM_E_INVALID_ARG, "tiles must be -1, 0, 1 or 2");
             p->opt_tiles = value;
             const hipError_t e = hipDeviceSynchronize();
             if (e != hipSuccess) return fail_hip(e, "synchronise before rebuilding the tiles");
@@ -626,7 +656,8 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_xcd_remap = p->route.xcd_remap;
     info.route_nt_store = p->route.nt_store;
     info.route_split = p->route.split ? 1 : 0;
-    info.tiles = p->tiles ? 1 : 0;
+    info.tiles = p->tiles ? (p->tile_compact ? 2 : 1) : 0;
+    info.tile_overflow = p->tile_overflow;
     info.tile_cap = p->tile_cap;
     info.route_tiled = p->route.tiled ? 1 : 0;
     info.route_window = p->route.window ? 1 : 0;
@@ -714,7 +745,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     const bool has_val = p->val != nullptr;
 
     Route r = route_for(p, N, B, C, argmax);
-    RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled};
+    RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled, r.compact};
     RowKernelFn fn = row_kernel(key);
     if (!fn) return fail(SPMM_E_UNSUPPORTED, "no kernel for lanes=%d vec=%d coarsen=%d", r.lanes, r.vec, r.coarsen);
     if (r.slices > 65535) return fail(SPMM_E_UNSUPPORTED, "N = %lld needs too many column slices", (long long)N);
@@ -751,7 +782,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
             const int64_t Wv = (w1 - w0) / r.vec;
             const int F = Wv > 64 ? 2 : 1;
             const int slices = (int)((Wv + 64 * F - 1) / (64 * F));
-            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true, false});
+            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true, false, false});
             if (!pf) return fail(SPMM_E_UNSUPPORTED, "no piece kernel for vec=%d", r.vec);
             RowArgs pa;
             std::memset(&pa, 0, sizeof(pa));

@@ -176,30 +176,79 @@ __global__ __launch_bounds__(kBlock) void part_write_kernel(
     }
 }
 
-// One wave per row tile: header of cumulative row ends (or -1 in the last
-// word when the tile holds more than cap entries), then the tile's column ids
-// and, when weighted, their values as fp32 bit patterns.
+// One wave per row tile (record layouts in row_kernel_impl.h).  A tile with
+// more than cap entries, or (compact) a column span beyond 16 bits, gets the
+// overflow mark; each block reports how many of its tiles overflowed.
 __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restrict__ rowptr,
                                                             const int *__restrict__ col,
                                                             const float *__restrict__ val, int64_t M,
-                                                            int cap, int rs, int *__restrict__ tiles) {
+                                                            int cap, int rs, int compact,
+                                                            int *__restrict__ tiles,
+                                                            int64_t *__restrict__ overflow) {
+    __shared__ int s_ovf[kWaves];
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int wv = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
     const int64_t ntiles = (M + kTileRows - 1) / kTileRows;
-    if (t >= ntiles) return;
-    const int64_t r0 = t * kTileRows;
-    const int rb = rowptr[r0];
-    const int re = rowptr[min(r0 + kTileRows, M)];
-    const int total = re - rb;
-    int *rec = tiles + t * rs;
-    if (total > cap) {
-        if (lane < kTileRows) rec[lane] = (lane == kTileRows - 1) ? -1 : 0;
-        return;
+    int ovf = 0;
+    if (t < ntiles) {
+        const int64_t r0 = t * kTileRows;
+        const int rb = rowptr[r0];
+        const int re = rowptr[min(r0 + kTileRows, M)];
+        const int total = re - rb;
+        int *rec = tiles + t * rs;
+        ovf = total > cap;
+        int mn = INT_MAX, mx = INT_MIN;
+        if (!ovf && compact) {
+            for (int k = lane; k < total; k += 64) {
+                const int c = col[rb + k];
+                mn = min(mn, c);
+                mx = max(mx, c);
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                mn = min(mn, __shfl_xor(mn, o));
+                mx = max(mx, __shfl_xor(mx, o));
+            }
+            ovf = total > 0 && (int64_t)mx - (int64_t)mn > 65535;
+        }
+        if (ovf) {
+            if (compact) {
+                if (lane == 0) rec[0] = -1;
+            } else if (lane < kTileRows) {
+                rec[lane] = (lane == kTileRows - 1) ? -1 : 0;
+            }
+        } else {
+            const int e = rowptr[min(r0 + (lane & (kTileRows - 1)) + 1, M)] - rb;   // lanes 0..7: row ends
+            const int hdr = compact ? 3 : kTileRows;
+            const int idx_words = compact ? cap / 2 : cap;
+            if (compact) {
+                const int base = total > 0 ? mn : 0;
+                int w1 = 0, w2 = 0;
+                for (int j = 0; j < 4; ++j) {
+                    w1 |= (__shfl(e, j) & 255) << (8 * j);
+                    w2 |= (__shfl(e, 4 + j) & 255) << (8 * j);
+                }
+                if (lane == 0) {
+                    rec[0] = base;
+                    rec[1] = w1;
+                    rec[2] = w2;
+                }
+                unsigned short *rec16 = reinterpret_cast<unsigned short *>(rec + hdr);
+                for (int k = lane; k < total; k += 64) rec16[k] = (unsigned short)(col[rb + k] - base);
+            } else {
+                if (lane < kTileRows) rec[lane] = e;
+                for (int k = lane; k < total; k += 64) rec[hdr + k] = col[rb + k];
+            }
+            if (val)
+                for (int k = lane; k < total; k += 64) rec[hdr + idx_words + k] = __float_as_int(val[rb + k]);
+        }
     }
-    if (lane < kTileRows) rec[lane] = rowptr[min(r0 + lane + 1, M)] - rb;
-    for (int k = lane; k < total; k += 64) {
-        rec[kTileRows + k] = col[rb + k];
-        if (val) rec[kTileRows + cap + k] = __float_as_int(val[rb + k]);
+    if (lane == 0) s_ovf[wv] = ovf;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t n = 0;
+        for (int w = 0; w < kWaves; ++w) n += s_ovf[w];
+        overflow[blockIdx.x] = n;
     }
 }
 
@@ -235,13 +284,16 @@ hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int6
     return hipGetLastError();
 }
 
-hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
-                             int *tiles, hipStream_t s) {
+int64_t tile_build_blocks(int64_t M) {
     const int64_t ntiles = (M + kTileRows - 1) / kTileRows;
-    if (ntiles <= 0) return hipSuccess;
-    const int64_t blocks = (ntiles + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(tile_build_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, rowptr, col, val, M, cap,
-                       rs, tiles);
+    return (ntiles + kWaves - 1) / kWaves;
+}
+
+hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
+                             bool compact, int *tiles, int64_t *overflow, int64_t nblocks, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(tile_build_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr, col, val, M, cap,
+                       rs, compact ? 1 : 0, tiles, overflow);
     return hipGetLastError();
 }
 

@@ -106,11 +106,14 @@ __device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
 // output: fused multiply-add (plain add when unweighted) or strict '>'.
 // WIN: entries whose column lies in [w0, w0 + kWinRows) read B from the
 // block's LDS copy sB (kWinCols columns per row, lane quad g) instead of HBM.
-template <int F, int VEC, bool HAS_VAL, bool IS_MAX, bool WIN = false, int UB = 0>
-__device__ __forceinline__ void consume(const int *cp, const int *vp, int lo, int hi, const float *__restrict__ Bp,
+// IDX16: the index list holds 16-bit offsets from `base` (compact row tiles).
+template <int F, int VEC, bool HAS_VAL, bool IS_MAX, bool WIN = false, int UB = 0, bool IDX16 = false>
+__device__ __forceinline__ void consume(const void *cpv, const int *vp, int lo, int hi, const float *__restrict__ Bp,
                                         int64_t N, const int (&colf)[F], const bool (&ok)[F],
                                         float (&acc)[F][VEC], int (&arg)[F][VEC],
-                                        const f32x4 *sB = nullptr, int64_t w0 = 0, int g = 0) {
+                                        const f32x4 *sB = nullptr, int64_t w0 = 0, int g = 0, int base = 0) {
+    const int *cp = static_cast<const int *>(cpv);
+    const unsigned short *cp16 = static_cast<const unsigned short *>(cpv);
     constexpr int U = UB ? UB : ((F * VEC <= 4) ? 8 : 4);
     for (int k = lo; k < hi; k += U) {
         int cidx[U];
@@ -121,7 +124,7 @@ __device__ __forceinline__ void consume(const int *cp, const int *vp, int lo, in
         for (int u = 0; u < U; ++u) {
             vld[u] = k + u < hi;
             const int kk = vld[u] ? k + u : lo;
-            cidx[u] = cp[kk];
+            cidx[u] = IDX16 ? base + (int)cp16[kk] : cp[kk];
             w[u] = HAS_VAL ? __int_as_float(vp[kk]) : 1.0f;
         }
 #pragma unroll
@@ -340,19 +343,25 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
 }
 
 // Row-tile kernel for low-degree graphs.  The plan stores every kTileRows-row
-// tile as one fixed-size record: kTileRows cumulative row ends, then up to
-// tile_cap column ids, then (weighted) as many values.  A wave reads its
-// 64/G / kTileRows records with one coalesced pass and has row bounds and
-// indexes together, so its gathers start one memory latency after launch
-// instead of two (bounds, then indexes).  Tiles longer than tile_cap carry an
-// end of -1 in their last header word and go through the CSR path.
-template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX>
+// tile as one fixed-size record holding the tile's row bounds and indexes
+// (and values), so a wave reads its 64/G / kTileRows records with one
+// coalesced pass and has bounds and indexes together: its gathers start one
+// memory latency after launch instead of two (bounds, then indexes).
+//   wide record:    kTileRows int32 cumulative row ends (-1 in the last word
+//                   marks an overflow tile), tile_cap int32 column ids;
+//   compact record: int32 base column (-1 marks an overflow tile), kTileRows
+//                   uint8 cumulative row ends in two words, tile_cap uint16
+//                   offsets from the base;
+// then, when weighted, tile_cap fp32 values.  Overflow tiles (more entries
+// than tile_cap, or a column span beyond 16 bits) go through the CSR path.
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool COMPACT>
 __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     static_assert(G == 4 || G == 8, "a wave holds one or two row tiles");
     constexpr int R = 64 / G;
     constexpr int TPW = R / kTileRows;       // tiles per wave
     constexpr int SL = G * VEC * F;
     constexpr int NL = kTileLdsWords / 64;   // record loads per lane
+    constexpr int HDR = COMPACT ? 3 : kTileRows;
     __shared__ int s_rec[kWaves][kTileLdsWords];
     __shared__ int s_col[kWaves][kChunk];
     __shared__ int s_val[kWaves][HAS_VAL ? kChunk : 1];
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     bool overflow = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
-        if (t * rs < nwords) overflow = overflow || s_rec[wv][t * rs + kTileRows - 1] < 0;
+        if (t * rs < nwords) overflow = overflow || s_rec[wv][t * rs + (COMPACT ? 0 : kTileRows - 1)] < 0;
     if (overflow) {                                     // uniform: CSR path for these rows
         row_task<G, VEC, F, HAS_VAL, IS_MAX, false>(a, row0, lane, s_col[wv], s_val[wv], colf, ok);
         return;
@@ -396,13 +405,28 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     const int64_t orow = row0 + sub;
     const bool live = orow < a.ntasks;
     const int *hdr = s_rec[wv] + t * rs;
-    const int b = live ? (j ? hdr[j - 1] : 0) : 0;
-    const int deg = live ? hdr[j] - b : 0;
-    const int *cp = hdr + kTileRows + b;
+    int b = 0, e = 0, base = 0;
+    if constexpr (COMPACT) {
+        base = hdr[0];
+        e = (hdr[1 + (j >> 2)] >> (8 * (j & 3))) & 255;
+        if (j) b = (hdr[1 + ((j - 1) >> 2)] >> (8 * ((j - 1) & 3))) & 255;
+    } else {
+        e = hdr[j];
+        if (j) b = hdr[j - 1];
+    }
+    const int deg = live ? e - b : 0;
+    const int idx_words = COMPACT ? a.tile_cap / 2 : a.tile_cap;
+    const int *vp = hdr + HDR + idx_words + b;
     float acc[F][VEC];
     int arg[F][VEC];
     init_acc<F, VEC, IS_MAX>(acc, arg);
-    consume<F, VEC, HAS_VAL, IS_MAX>(cp, cp + a.tile_cap, 0, deg, a.B, a.N, colf, ok, acc, arg);
+    if constexpr (COMPACT) {
+        const unsigned short *cp16 = reinterpret_cast<const unsigned short *>(hdr + HDR) + b;
+        consume<F, VEC, HAS_VAL, IS_MAX, false, 0, true>(cp16, vp, 0, deg, a.B, a.N, colf, ok, acc, arg, nullptr,
+                                                       0, 0, base);
+    } else {
+        consume<F, VEC, HAS_VAL, IS_MAX>(hdr + HDR + b, vp, 0, deg, a.B, a.N, colf, ok, acc, arg);
+    }
     if (live) store_out<F, VEC, IS_MAX, false>(a, orow, deg, colf, ok, acc, arg);
 }
 
@@ -464,9 +488,18 @@ RowKernelFn pick_row_kernel(const RowKernelKey &k) {
     if (k.tiled) {
         if constexpr (G == 4 || G == 8) {
             if (k.pieces) return nullptr;
+            if (k.compact) {
+                if (k.is_max)
+                    return k.has_val ? tile_kernel_t<G, VEC, F, true, true, true>
+                                     : tile_kernel_t<G, VEC, F, false, true, true>;
+                return k.has_val ? tile_kernel_t<G, VEC, F, true, false, true>
+                                 : tile_kernel_t<G, VEC, F, false, false, true>;
+            }
             if (k.is_max)
-                return k.has_val ? tile_kernel_t<G, VEC, F, true, true> : tile_kernel_t<G, VEC, F, false, true>;
-            return k.has_val ? tile_kernel_t<G, VEC, F, true, false> : tile_kernel_t<G, VEC, F, false, false>;
+                return k.has_val ? tile_kernel_t<G, VEC, F, true, true, false>
+                                 : tile_kernel_t<G, VEC, F, false, true, false>;
+            return k.has_val ? tile_kernel_t<G, VEC, F, true, false, false>
+                             : tile_kernel_t<G, VEC, F, false, false, false>;
         } else {
             return nullptr;
         }

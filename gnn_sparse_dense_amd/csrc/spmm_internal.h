@@ -75,6 +75,7 @@ struct RowKernelKey {
     bool is_max;
     bool pieces;  // piece mode (split rows) instead of row mode
     bool tiled;   // row-tile records instead of CSR row bounds
+    bool compact; // compact (16-bit) row-tile records
 };
 
 typedef void (*RowKernelFn)(RowArgs);
@@ -114,7 +115,8 @@ hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t 
 hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int64_t *out, int64_t nblocks,
                               hipStream_t s);
 hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
-                             int *tiles, hipStream_t s);
+                             bool compact, int *tiles, int64_t *overflow, int64_t nblocks, hipStream_t s);
+int64_t tile_build_blocks(int64_t M);
 
 // ---- the plan ----
 struct Route {
@@ -122,6 +124,7 @@ struct Route {
     int xcd_remap = 1, nt_store = 0;
     bool split = false;
     bool tiled = false;
+    bool compact = false;
     bool window = false;
 };
 
@@ -146,6 +149,8 @@ struct spmm_plan {
     // row-tile records (low-degree graphs)
     int *tiles = nullptr;
     int tile_cap = 0, tile_words = 0;
+    bool tile_compact = false;
+    int64_t tile_overflow = 0;
     double win_frac = 0;       // share of entries inside their row's kWinRows block
     // options (-1 / 0 = automatic)
     int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;

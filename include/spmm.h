@@ -66,8 +66,9 @@ enum spmm_option {
     SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto            */
     SPMM_OPT_XCD_REMAP = 7,    /* -1 auto, 0 off, 1 on: contiguous rows per XCD  */
     SPMM_OPT_NT_STORE = 8,     /* -1 auto, 0 off, 1 on: non-temporal C stores    */
-    SPMM_OPT_TILES = 9,        /* -1 auto (low, even degrees), 0 off, 1 on: keep
-                                  8-row tile records with bounds + indexes    */
+    SPMM_OPT_TILES = 9,        /* -1 auto (low, even degrees), 0 off, 1 on, 2 on
+                                  with 32-bit records: keep 8-row tile records
+                                  holding row bounds + indexes               */
     SPMM_OPT_WINDOW = 10       /* -1 auto (community structure, N >= 128), 0 off,
                                   1 on: stage each 256-row block of B in LDS  */
 };
@@ -88,10 +89,12 @@ struct spmm_plan_info {
     int64_t route_N;
     int32_t route_lanes, route_vec, route_coarsen, route_rows_per_wave;
     int32_t route_slices, route_xcd_remap, route_nt_store, route_split;
-    int32_t tiles, tile_cap;     /* row-tile records built; entries per record   */
+    int32_t tiles, tile_cap;     /* row tiles: 0 none, 1 32-bit, 2 16-bit offset
+                                    records; entries per record               */
     int32_t route_tiled, route_window;
     double win_frac;             /* share of entries inside their row's 256-row
                                     block (community structure)               */
+    int64_t tile_overflow;       /* tiles that take the CSR path              */
 };
 
 /*

@@ -300,28 +300,34 @@ def test_regimes_full_size_sampled(orc, name):
     G.spmm_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("weighted", [False, True])
-def test_row_tiles_match_csr_path(orc, weighted):
+@pytest.mark.parametrize("weighted,mode,K", [(False, 1, 15_000), (True, 1, 15_000), (False, 2, 15_000),
+                                              (True, 1, 300_000)],
+                         ids=["compact", "compact-weighted", "wide-forced", "wide-span"])
+def test_row_tiles_match_csr_path(orc, weighted, mode, K):
     """Row-tile records (bounds + indexes in one record per 8 rows) give the same
-    bits as the CSR path, including tiles too long for a record (which take the
-    CSR path inside the tile kernel) and a ragged last tile."""
-    rng = np.random.default_rng(404 + weighted)
-    g = W.random_csr(rng, 20_003, 15_000, mean_deg=3.0, empty_frac=0.05, heavy_rows=40, heavy_deg=150,
+    bits as the CSR path: compact 16-bit records, forced 32-bit records, and a
+    graph whose column spans exceed 16 bits (the plan falls back to 32-bit
+    records); tiles too long for a record take the CSR path inside the tile
+    kernel, and the last tile is ragged."""
+    rng = np.random.default_rng(404 + weighted + K)
+    g = W.random_csr(rng, 20_003, K, mean_deg=3.0, empty_frac=0.05, heavy_rows=40, heavy_deg=150,
                      dup_frac=0.05, shuffle_rows=True, weighted=weighted)
     for N in (16, 64, 32):
         B = rng.standard_normal((g.K, N)).astype(np.float32)
         _, _, _, Bd = to_dev(g, B)
-        on = make_plan(g, [(G.SPMM_OPT_TILES, 1)])
+        on = make_plan(g, [(G.SPMM_OPT_TILES, mode)])
         off = make_plan(g, [(G.SPMM_OPT_TILES, 0)])
         info = G.spmm_plan_info(on)
-        assert info["tiles"] == 1 and info["tile_cap"] > 0
+        expect = 1 if (mode == 2 or K > 65536) else 2
+        assert info["tiles"] == expect and info["tile_cap"] > 0, info["tiles"]
+        assert info["tile_overflow"] >= 1            # the 150-entry rows overflow their tiles
         assert G.spmm_plan_info(off)["tiles"] == 0
         for red in ("sum", "mean", "max"):
             C1, a1 = gpu_run(on, g.M, Bd, red)
             assert G.spmm_plan_info(on)["route_tiled"] == 1, f"N={N}: tile kernel not routed"
             C0, a0 = gpu_run(off, g.M, Bd, red)
             assert G.spmm_plan_info(off)["route_tiled"] == 0
-            log(f"tiles N={N} {red} cap={info['tile_cap']}")
+            log(f"tiles mode={mode} K={K} N={N} {red} cap={info['tile_cap']} kind={info['tiles']}")
             assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), f"tiles vs CSR N={N} {red}"
             if a1 is not None:
                 assert np.array_equal(a1, a0)
