@@ -64,10 +64,18 @@ def byte_model(g, N, reduce):
     return comp, g.nnz * N * 4
 
 
-def read_traffic(workload: str):
+def kernel_family(info) -> str:
+    if info.get("route_window"):
+        return "window_kernel"
+    if info.get("route_tiled"):
+        return "tile_kernel"
+    return "row_kernel"
+
+
+def read_traffic(family: str, workload: str):
     """Measured HBM bytes per launch from a committed rocprofv3 counter summary,
     or None when absent or taken on different kernel sources."""
-    path = os.path.join(PROFILES, f"row_kernel_{workload}_traffic.txt")
+    path = os.path.join(PROFILES, f"{family}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -257,7 +265,8 @@ def main():
     flops = 2.0 * g.nnz * N
     value = flops / (ms_per_step * 1e-3) / 1e9
     achieved = comp / (avg_launch_ms * 1e-3) / 1e9
-    traffic = read_traffic(headline)
+    family = kernel_family(r.info)
+    traffic = read_traffic(family, headline)
 
     result = {
         "metric": METRIC,
@@ -283,8 +292,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else round(traffic),
-            "kernel": "row_kernel_t (lanes=%d vec=%d coarsen=%d)" % (
-                r.info["route_lanes"], r.info["route_vec"], r.info["route_coarsen"]),
+            "kernel": "%s_t (lanes=%d vec=%d coarsen=%d)" % (
+                family, r.info["route_lanes"], r.info["route_vec"], r.info["route_coarsen"]),
             "bytes_per_launch": comp, "avg_launch_ms": round(avg_launch_ms, 5),
         },
     }
