@@ -44,6 +44,12 @@ class Oracle:
         lib.oracle_partition.restype = ctypes.c_int
         lib.oracle_mac_gap.argtypes = [_i64, _i64, _i64]
         lib.oracle_mac_gap.restype = _i64
+        lib.oracle_coo_to_csr.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
+        lib.oracle_coo_to_csr.restype = _i64
+        lib.oracle_transpose.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_int, _p, _p, _p]
+        lib.oracle_transpose.restype = None
+        lib.oracle_max_backward.argtypes = [_p, _p, _i64, _i64, _i64, _p]
+        lib.oracle_max_backward.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -114,6 +120,40 @@ class Oracle:
 
     def mac_gap(self, dim, F, omega) -> int:
         return int(self.lib.oracle_mac_gap(dim, F, omega))
+
+    def coo_to_csr(self, row, col, val, M, K):
+        """(rowptr, col, val) of the stable row-grouping of an edge list; raises
+        ValueError naming the first bad edge."""
+        row = np.ascontiguousarray(row, dtype=np.int64)
+        col = np.ascontiguousarray(col, dtype=np.int64)
+        val = None if val is None else np.ascontiguousarray(val, dtype=np.float32)
+        E = row.size
+        rp = np.empty(M + 1, np.int64)
+        co = np.empty(E, np.int64)
+        vo = None if val is None else np.empty(E, np.float32)
+        bad = self.lib.oracle_coo_to_csr(_ptr(row), _ptr(col), _ptr(val), E, M, K, _ptr(rp), _ptr(co), _ptr(vo))
+        if bad != -1:
+            raise ValueError(f"bad edge {bad}")
+        return rp, co, vo
+
+    def transpose(self, rowptr, col, val, M, K, scale=False):
+        rowptr, col, val = self._csr(rowptr, col, val)
+        nnz = int(rowptr[M])
+        rt = np.empty(K + 1, np.int64)
+        ct = np.empty(nnz, np.int64)
+        vt = np.empty(nnz, np.float32)
+        self.lib.oracle_transpose(_ptr(rowptr), _ptr(col), _ptr(val), M, K, int(bool(scale)), _ptr(rt),
+                                  _ptr(ct), _ptr(vt))
+        return rt, ct, vt
+
+    def max_backward(self, argmax, dC, M, K):
+        argmax = np.ascontiguousarray(argmax, dtype=np.int64)
+        dC = np.ascontiguousarray(dC, dtype=np.float32)
+        N = dC.shape[1]
+        dB = np.empty((K, N), np.float32)
+        if self.lib.oracle_max_backward(_ptr(argmax), _ptr(dC), M, K, N, _ptr(dB)) != 0:
+            raise ValueError("argmax entry outside [-1, K)")
+        return dB
 
 
 _default: Optional[Oracle] = None

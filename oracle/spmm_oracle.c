@@ -38,6 +38,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #define RED_SUM 0
 #define RED_MEAN 1
@@ -226,4 +227,86 @@ int64_t oracle_mac_gap(int64_t dim, int64_t F, int64_t omega) {
     int64_t tr = dim % span;
     if (tr == 0) return 0;
     return tn - tr;
+}
+
+/*
+ * Backward pieces and graph construction (graph-spmm kernel card: API table
+ * row SparseAdj.from_edge_index; "Requirements and limits": the backward of a
+ * sum is the transposed product from a second adjacency on the reversed edge
+ * list; "Method": the argmax is what a max-pool backward needs).
+ */
+
+/*
+ * Edge list -> CSR.  Edge e is entry (row[e], col[e]) with value val[e] (or
+ * none).  Rows are grouped in ascending order and, within a row, entries keep
+ * the order of the edge list (a stable sort by row).  rowptr_out [M+1],
+ * col_out [E], val_out [E] (when val != NULL).  Returns -1 when valid, else
+ * the first edge whose row is outside [0, M) or column outside [0, K).
+ */
+int64_t oracle_coo_to_csr(const int64_t *row, const int64_t *col, const float *val,
+                          int64_t E, int64_t M, int64_t K, int64_t *rowptr_out,
+                          int64_t *col_out, float *val_out) {
+    for (int64_t e = 0; e < E; ++e)
+        if (row[e] < 0 || row[e] >= M || col[e] < 0 || col[e] >= K) return e;
+    for (int64_t i = 0; i <= M; ++i) rowptr_out[i] = 0;
+    for (int64_t e = 0; e < E; ++e) rowptr_out[row[e] + 1] += 1;
+    for (int64_t i = 0; i < M; ++i) rowptr_out[i + 1] += rowptr_out[i];
+    /* place edges in edge order: a running cursor per row keeps them stable */
+    int64_t *cursor = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    if (!cursor) return -2;
+    for (int64_t i = 0; i < M; ++i) cursor[i] = rowptr_out[i];
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t p = cursor[row[e]]++;
+        col_out[p] = col[e];
+        if (val) val_out[p] = val[e];
+    }
+    free(cursor);
+    return -1;
+}
+
+/*
+ * CSR of A [M, K] -> CSR of its transpose [K, M]: entry (i, j, a) of A becomes
+ * entry (j, i, a') of the transpose, listed in A's stored order within each
+ * transposed row (so rows i ascend).  scale = 0: a' = a (1 when unweighted);
+ * scale = 1: a' = a / deg_i in fp32, one division (the mean's backward).
+ * rowptr_t [K+1], col_t [nnz], val_t [nnz] (always written).
+ */
+void oracle_transpose(const int64_t *rowptr, const int64_t *col, const float *val,
+                      int64_t M, int64_t K, int scale, int64_t *rowptr_t,
+                      int64_t *col_t, float *val_t) {
+    for (int64_t j = 0; j <= K; ++j) rowptr_t[j] = 0;
+    for (int64_t p = 0; p < rowptr[M]; ++p) rowptr_t[col[p] + 1] += 1;
+    for (int64_t j = 0; j < K; ++j) rowptr_t[j + 1] += rowptr_t[j];
+    int64_t *cursor = (int64_t *)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1));
+    if (!cursor) return;
+    for (int64_t j = 0; j < K; ++j) cursor[j] = rowptr_t[j];
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t deg = rowptr[i + 1] - rowptr[i];
+        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+            int64_t q = cursor[col[p]]++;
+            float a = val ? val[p] : 1.0f;
+            col_t[q] = i;
+            val_t[q] = scale ? a / (float)deg : a;
+        }
+    }
+    free(cursor);
+}
+
+/*
+ * Max-pool backward for an unweighted adjacency: dB[j][k] = sum over rows i
+ * with argmax[i][k] == j of dC[i][k], summed in ascending i (fp32).  Rows with
+ * argmax -1 (empty) contribute nothing.  dB is [K, N], fully written.
+ * Returns 0, or -1 when an argmax entry is outside [-1, K).
+ */
+int oracle_max_backward(const int64_t *argmax, const float *dC, int64_t M, int64_t K,
+                        int64_t N, float *dB) {
+    for (int64_t x = 0; x < M * N; ++x)
+        if (argmax[x] < -1 || argmax[x] >= K) return -1;
+    for (int64_t x = 0; x < K * N; ++x) dB[x] = 0.0f;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < N; ++k) {
+            int64_t j = argmax[i * N + k];
+            if (j >= 0) dB[j * N + k] = dB[j * N + k] + dC[i * N + k];
+        }
+    return 0;
 }

@@ -328,8 +328,86 @@ def pin_tiny_config(orc):
     assert np.allclose(S2, S, rtol=1e-12, atol=0)
 
 
+def pin_coo_to_csr(orc):
+    rowptr, col, val = orc.coo_to_csr([2, 0, 2, 1], [1, 3, 0, 0], np.float32([1, 2, 3, 4]), 3, 4)
+    assert rowptr.tolist() == [0, 1, 2, 4] and col.tolist() == [3, 0, 1, 0] and val.tolist() == [2, 4, 1, 3]
+    try:
+        orc.coo_to_csr([0, 3], [0, 0], None, 3, 4)
+        raise AssertionError("row 3 of 3 accepted")
+    except ValueError as e:
+        assert "bad edge 1" in str(e)
+    import scipy.sparse as sp
+    rng = np.random.default_rng(41)
+    M, K, E = 300, 200, 2500
+    r = rng.integers(0, M, E)
+    c = rng.integers(0, K, E)
+    v = rng.random(E, dtype=np.float32)
+    rowptr, col, val = orc.coo_to_csr(r, c, v, M, K)
+    order = np.argsort(r, kind="stable")                  # numpy's stable sort
+    assert np.array_equal(rowptr, np.concatenate([[0], np.cumsum(np.bincount(r, minlength=M))]))
+    assert np.array_equal(col, c[order]) and np.array_equal(val, v[order])
+    B = rng.standard_normal((K, 6)).astype(np.float32)
+    ref = np.asarray(sp.coo_matrix((v.astype(np.float64), (r, c)), shape=(M, K)).tocsr() @ B.astype(np.float64))
+    S = np.asarray(sp.coo_matrix((np.abs(v.astype(np.float64)), (r, c)), shape=(M, K)).tocsr()
+                   @ np.abs(B.astype(np.float64)))
+    C = orc.spmm(rowptr, col, val, M, K, B, "sum")
+    _bound_check(C, ref, S, np.diff(rowptr), "coo product")
+
+
+def pin_transpose(orc):
+    rng = np.random.default_rng(43)
+    for weighted in (True, False):
+        g = W.random_csr(rng, 150, 120, mean_deg=5.0, empty_frac=0.1, dup_frac=0.2, shuffle_rows=True,
+                         weighted=weighted)
+        rt, ct, vt = orc.transpose(g.rowptr, g.col, g.val, g.M, g.K)
+        gt = W.Graph("t", g.K, g.M, rt, ct, vt)
+        assert np.array_equal(_dense(gt), _dense(g).T), "dense transpose"
+        for j in range(g.K):                                  # rows i ascend within each row
+            assert np.all(np.diff(ct[rt[j]:rt[j + 1]]) >= 0)
+        rtt, ctt, vtt = orc.transpose(rt, ct, vt, g.K, g.M)
+        for i in range(g.M):                                  # twice = rows sorted by column, stably
+            a, b = g.rowptr[i], g.rowptr[i + 1]
+            o = np.argsort(g.col[a:b], kind="stable")
+            assert np.array_equal(ctt[a:b], g.col[a:b][o])
+            vals = np.ones(b - a, np.float32) if g.val is None else g.val[a:b]
+            assert np.array_equal(vtt[a:b], vals[o])
+        _, _, vs = orc.transpose(g.rowptr, g.col, g.val, g.M, g.K, scale=True)
+        deg = np.diff(g.rowptr)
+        a = np.ones(g.nnz, np.float32) if g.val is None else g.val
+        expect = (a / np.repeat(deg, deg).astype(np.float32)).astype(np.float32)
+        perm = np.argsort(g.col, kind="stable")               # entry order of the transpose
+        assert np.array_equal(vs, expect[perm]), "mean-backward weights"
+        # adjoint: <A B, G> == <B, A^T G>
+        B = rng.standard_normal((g.K, 5)).astype(np.float32)
+        Gm = rng.standard_normal((g.M, 5)).astype(np.float32)
+        lhs = float(np.sum(orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, B, "sum").astype(np.float64) * Gm))
+        rhs = float(np.sum(B.astype(np.float64) * orc.spmm(rt, ct, vt, g.K, g.M, Gm, "sum")))
+        assert abs(lhs - rhs) <= 1e-4 * (1 + abs(lhs)), (lhs, rhs)
+
+
+def pin_max_backward(orc):
+    argmax = np.array([[2, -1], [0, 2], [2, 2]], np.int64)
+    dC = np.float32([[1.5, 7.0], [0.25, -1.0], [2.0, 0.5]])
+    dB = orc.max_backward(argmax, dC, 3, 4)
+    assert np.array_equal(dB, np.float32([[0.25, 0], [0, 0], [1.5 + 2.0, -1.0 + 0.5], [0, 0]]))
+    rng = np.random.default_rng(47)
+    g = W.random_csr(rng, 400, 250, mean_deg=6.0, empty_frac=0.1, dup_frac=0.1, weighted=False)
+    B = rng.integers(0, 4, size=(g.K, 7)).astype(np.float32)
+    C, arg = orc.spmm(g.rowptr, g.col, None, g.M, g.K, B, "max")
+    dC = rng.standard_normal((g.M, 7)).astype(np.float32)
+    dB = orc.max_backward(arg, dC, g.M, g.K)
+    ref = np.zeros((g.K, 7), np.float32)
+    ii, kk = np.nonzero(arg >= 0)                             # i-major order
+    np.add.at(ref, (arg[ii, kk], kk), dC[ii, kk])
+    assert np.array_equal(dB.view(np.uint32), ref.view(np.uint32)), "max backward vs np.add.at"
+    lhs = float(np.sum(dC.astype(np.float64) * np.where(arg >= 0, C, 0)))
+    rhs = float(np.sum(dB.astype(np.float64) * B))
+    assert abs(lhs - rhs) <= 1e-4 * (1 + abs(lhs))
+
+
 ALL_PINS = [
     pin_dense_bruteforce, pin_scipy_product, pin_identity, pin_ones, pin_empty_rows,
     pin_max_numpy, pin_val_null_is_ones, pin_mean_sum_relation, pin_row_subset,
     pin_partition, pin_descriptors, pin_validate, pin_mac_gap, pin_tiny_config,
+    pin_coo_to_csr, pin_transpose, pin_max_backward,
 ]

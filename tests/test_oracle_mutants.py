@@ -36,6 +36,10 @@ MUTANTS = {
     "validate_skips_last_row": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t p",
                                 "for (int64_t i = 0; i + 1 < M; ++i)\n        for (int64_t p"),
     "sumabs_signed": ("s += fabs(a * (double)B[col[p] * N + k]);", "s += a * (double)B[col[p] * N + k];"),
+    "coo_unstable": ("int64_t p = cursor[row[e]]++;", "int64_t p = rowptr_out[row[e] + 1] - 1 - (cursor[row[e]]++ - rowptr_out[row[e]]);"),
+    "transpose_scale_off": ("val_t[q] = scale ? a / (float)deg : a;", "val_t[q] = scale ? a / (float)(deg + 1) : a;"),
+    "max_backward_skips_row0": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t k = 0; k < N; ++k) {\n            int64_t j",
+                                "for (int64_t i = 1; i < M; ++i)\n        for (int64_t k = 0; k < N; ++k) {\n            int64_t j"),
 }
 
 
