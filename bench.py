@@ -223,6 +223,57 @@ def regime_result(r, reduce, steps, warmup, flush):
     }
 
 
+def time_flushed(fn, flush, steps, warmup=3):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        ts.append(s.elapsed_time(e))
+    return statistics.median(ts)
+
+
+def backward_result(r, flush, steps):
+    """Backward pieces of one regime: the transposed plan (A^T, built once), the
+    backward product dB = A^T dC of a sum, the max-pool backward where the
+    regime reduces by max, and the stable edge-list -> CSR build."""
+    import torch
+    G, g, N = r.G, r.g, r.w.N
+    dev = r.C.device
+    t0 = time.perf_counter()
+    pt = G.spmm_plan_transpose(r.plan, 0)
+    t_plan = (time.perf_counter() - t0) * 1e3
+    dC = torch.randn((g.M, N), dtype=torch.float32, device=dev)
+    dB = torch.empty((g.K, N), dtype=torch.float32, device=dev)
+    ms = time_flushed(lambda: G.spmm_run(pt, dC, dB, None, N, "sum", None), flush, steps)
+    comp_t = (g.K + 1) * 4 + g.nnz * (4 + (4 if g.val is not None else 0)) + g.M * N * 4 + g.K * N * 4
+    out = {"transpose_plan_ms": round(t_plan, 2), "sum_backward_ms": round(ms, 5),
+           "sum_backward_GBps": round(comp_t / (ms * 1e-3) / 1e9, 1)}
+    if "max" in r.w.reduces and g.val is None:
+        arg = torch.empty((g.M, N), dtype=torch.int64, device=dev)
+        G.spmm_run(r.plan, r.B, r.C, arg, N, "max", None)
+        ms = time_flushed(lambda: G.spmm_max_backward(pt, arg, dC, dB, N, None), flush, steps)
+        comp_m = (g.K + 1) * 4 + g.nnz * 4 + g.M * N * 12 + g.K * N * 4
+        out.update({"max_backward_ms": round(ms, 5), "max_backward_GBps": round(comp_m / (ms * 1e-3) / 1e9, 1)})
+    G.spmm_plan_destroy(pt)
+    rows = torch.repeat_interleave(torch.arange(g.M, device=dev), torch.diff(r.rowptr))
+    perm = torch.randperm(g.nnz, device=dev, generator=torch.Generator(device=dev).manual_seed(0))
+    er, ec = rows[perm].contiguous(), r.col[perm].contiguous()
+    ev = None if r.val is None else r.val[perm].contiguous()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    G.spmm_coo_to_csr(er, ec, ev, g.M, g.K)
+    out["edge_list_to_csr_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +285,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true", help="skip the other regimes")
     ap.add_argument("--regimes", default="road,tiny,diffusion,community,powerlaw")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -308,9 +360,11 @@ def main():
 
     if not args.headline_only:
         flush = make_flush()
-        regimes = {}
+        regimes, backward = {}, {}
         regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush)
                              for red in r.w.reduces]
+        if not args.no_backward:
+            backward[headline] = backward_result(r, flush, min(args.steps, 50))
         r.close()
         del r
         torch.cuda.empty_cache()
@@ -320,10 +374,14 @@ def main():
                   file=sys.stderr, flush=True)
             regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush)
                              for red in rr.w.reduces]
+            if not args.no_backward:
+                backward[name] = backward_result(rr, flush, min(args.steps, 50))
             rr.close()
             del rr
             torch.cuda.empty_cache()
         result["regimes"] = regimes
+        if backward:
+            result["backward"] = backward
     else:
         r.close()
 

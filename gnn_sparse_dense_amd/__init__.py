@@ -38,6 +38,7 @@ SPMM_OPT_WINDOW = 10
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
+    "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward",
 )
 
 
@@ -90,6 +91,12 @@ def _load() -> ctypes.CDLL:
     lib.spmm_plan_set_option.restype = i32
     lib.spmm_last_error.argtypes = [ctypes.c_char_p, i64]
     lib.spmm_last_error.restype = i32
+    lib.spmm_coo_to_csr.argtypes = [p, p, p, i64, i64, i64, p, p, p]
+    lib.spmm_coo_to_csr.restype = i32
+    lib.spmm_plan_transpose.argtypes = [p, i32]
+    lib.spmm_plan_transpose.restype = p
+    lib.spmm_max_backward.argtypes = [p, p, p, p, i64, p]
+    lib.spmm_max_backward.restype = i32
     return lib
 
 
@@ -182,15 +189,71 @@ def spmm_plan_set_option(plan: int, option: int, value: int) -> None:
     _check(_lib.spmm_plan_set_option(plan, int(option), int(value)))
 
 
+def spmm_coo_to_csr(row, col, val, M: int, K: int):
+    """Stable edge-list -> CSR on the device: returns (rowptr, col, val) tensors."""
+    import torch
+    E = int(row.numel())
+    dev = row.device
+    rowptr = torch.empty(M + 1, dtype=torch.int64, device=dev)
+    col_out = torch.empty(max(E, 1), dtype=torch.int64, device=dev)[:E]
+    val_out = None if val is None else torch.empty(max(E, 1), dtype=torch.float32, device=dev)[:E]
+    _check(_lib.spmm_coo_to_csr(_addr(row), _addr(col), _addr(val), E, int(M), int(K), _addr(rowptr),
+                                _addr(col_out), _addr(val_out)))
+    return rowptr, col_out, val_out
+
+
+def spmm_plan_transpose(plan: int, scale: int = 0) -> int:
+    h = _lib.spmm_plan_transpose(plan, int(scale))
+    if not h:
+        st, msg = spmm_last_error()
+        raise SpmmError(st, msg)
+    return h
+
+
+def spmm_max_backward(plan_t: int, argmax, dC, dB, N: int, stream=None) -> None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(_lib.spmm_max_backward(plan_t, _addr(argmax), _addr(dC), _addr(dB), int(N), stream))
+
+
 class SparseAdj:
     """A CSR adjacency held once on the GPU and applied many times
     (graph-spmm card, "Usage": build the CSR once, apply it per layer)."""
 
-    def __init__(self, rowptr, col, val=None, num_cols: Optional[int] = None):
-        self.M = int(rowptr.numel()) - 1
-        self.K = int(num_cols if num_cols is not None else self.M)
-        self.device = rowptr.device
-        self._plan = spmm_plan_create(rowptr, col, val, self.M, self.K)
+    def __init__(self, rowptr, col, val=None, num_cols: Optional[int] = None, _plan: Optional[int] = None):
+        if _plan is not None:                      # wraps an existing plan (a transpose)
+            self._plan = _plan
+            info = spmm_plan_info(_plan)
+            self.M, self.K = int(info["M"]), int(info["K"])
+            self.weighted = bool(info["has_val"])
+            self.device = None
+        else:
+            self.M = int(rowptr.numel()) - 1
+            self.K = int(num_cols if num_cols is not None else self.M)
+            self.device = rowptr.device
+            self.weighted = val is not None
+            self._plan = spmm_plan_create(rowptr, col, val, self.M, self.K)
+        self._transposes = {}
+
+    @classmethod
+    def from_edge_index(cls, edge_index, num_nodes: int, val=None, num_cols: Optional[int] = None):
+        """CSR from a [2, E] edge list: entry (edge_index[0][e], edge_index[1][e])
+        keeps its edge-list position within its row (graph-spmm card, API table)."""
+        K = int(num_cols if num_cols is not None else num_nodes)
+        row = edge_index[0].contiguous()
+        col = edge_index[1].contiguous()
+        rowptr, c, v = spmm_coo_to_csr(row, col, None if val is None else val.contiguous(), int(num_nodes), K)
+        return cls(rowptr, c, v, num_cols=K)
+
+    def transpose(self, scale_by_inverse_degree: bool = False) -> "SparseAdj":
+        """A^T as its own plan (cached); scaled by 1/deg for the mean's backward."""
+        key = int(bool(scale_by_inverse_degree))
+        if key not in self._transposes:
+            self._transposes[key] = SparseAdj(None, None, _plan=spmm_plan_transpose(self._plan, key))
+        return self._transposes[key]
 
     @property
     def plan(self) -> int:
@@ -215,7 +278,19 @@ class SparseAdj:
     def __matmul__(self, B):
         return self.reduce(B, "sum")
 
+    def max_backward(self, argmax, dC, out=None, stream=None):
+        """dB for a max aggregation over this (unweighted) adjacency."""
+        import torch
+        N = int(dC.shape[1])
+        if out is None:
+            out = torch.empty((self.K, N), dtype=torch.float32, device=dC.device)
+        spmm_max_backward(self.transpose().plan, argmax, dC, out, N, stream)
+        return out
+
     def close(self) -> None:
+        for t in self._transposes.values():
+            t.close()
+        self._transposes = {}
         if self._plan:
             spmm_plan_destroy(self._plan)
             self._plan = 0
@@ -225,3 +300,32 @@ class SparseAdj:
             self.close()
         except Exception:
             pass
+
+
+def aggregate(adj: SparseAdj, B, reduce: str = "sum"):
+    """Differentiable aggregation: forward and backward both run in the HIP
+    library (backward of sum / mean: the transposed product, of max: the
+    argmax scatter).  Returns C (and, for max, the argmax as a second output
+    without a gradient)."""
+    import torch
+
+    class _Aggregate(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, B_):
+            out = adj.reduce(B_.contiguous(), reduce)
+            if reduce == "max":
+                C, arg = out
+                ctx.save_for_backward(arg)
+                ctx.mark_non_differentiable(arg)
+                return C, arg
+            return out
+
+        @staticmethod
+        def backward(ctx, dC, *unused):
+            dC = dC.contiguous()
+            if reduce == "max":
+                (arg,) = ctx.saved_tensors
+                return adj.max_backward(arg, dC)
+            return adj.transpose(scale_by_inverse_degree=(reduce == "mean")).reduce(dC, "sum")
+
+    return _Aggregate.apply(B)

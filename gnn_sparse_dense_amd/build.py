@@ -26,6 +26,7 @@ SOURCES = [
     "row_kernels_v2.hip",
     "row_kernels_v4.hip",
     "window_kernels.hip",
+    "transform.hip",
 ]
 
 COMMON = [

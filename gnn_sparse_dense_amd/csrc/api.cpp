@@ -822,3 +822,83 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     }
     return succeed();
 }
+
+SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                             int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out) {
+    if (E < 0 || M < 0 || K < 0) return fail(SPMM_E_INVALID_ARG, "negative size");
+    if (E >= INT_MAX || M >= INT_MAX || K >= INT_MAX)
+        return fail(SPMM_E_UNSUPPORTED, "E, M and K must be below 2^31 - 1");
+    if (!is_device_ptr(rowptr_out)) return fail(SPMM_E_INVALID_ARG, "rowptr_out is NULL or not device memory");
+    if (E > 0) {
+        if (!is_device_ptr(row) || !is_device_ptr(col))
+            return fail(SPMM_E_INVALID_ARG, "row / col are NULL or not device memory");
+        if (!is_device_ptr(col_out)) return fail(SPMM_E_INVALID_ARG, "col_out is NULL or not device memory");
+        if (val && !is_device_ptr(val)) return fail(SPMM_E_INVALID_ARG, "val is not device memory");
+        if (val && !is_device_ptr(val_out)) return fail(SPMM_E_INVALID_ARG, "val_out is NULL or not device memory");
+    }
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(e, "synchronise before the edge-list sort");
+    int64_t bad = -1;
+    e = coo_to_csr(row, col, val, E, M, K, rowptr_out, col_out, val ? val_out : nullptr, &bad, nullptr);
+    if (e != hipSuccess) return fail_hip(e, "edge-list sort");
+    if (bad >= 0) return fail(SPMM_E_BAD_CSR, "edge %lld has a row outside [0, %lld) or a column outside [0, %lld)",
+                              (long long)bad, (long long)M, (long long)K);
+    return succeed();
+}
+
+SPMM_API spmm_plan_t spmm_plan_transpose(spmm_plan_t p, int scale) {
+    if (!p) {
+        fail(SPMM_E_INVALID_ARG, "plan is NULL");
+        return nullptr;
+    }
+    if (scale != 0 && scale != 1) {
+        fail(SPMM_E_INVALID_ARG, "scale must be 0 or 1");
+        return nullptr;
+    }
+    DeviceGuard dg(p->device);
+    int64_t *rp = nullptr, *cl = nullptr;
+    float *vl = nullptr;
+    const bool want_val = p->val != nullptr || scale == 1;
+    int st;
+    if ((st = dev_alloc(&rp, p->K + 1, "transposed rowptr")) || (st = dev_alloc(&cl, p->nnz, "transposed col")) ||
+        (want_val && (st = dev_alloc(&vl, p->nnz, "transposed val")))) {
+        dev_free(rp);
+        dev_free(cl);
+        dev_free(vl);
+        return nullptr;
+    }
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+        e = transpose_csr(p->rowptr, p->col, p->val, p->M, p->K, p->nnz, scale == 1, rp, cl, vl, nullptr);
+    spmm_plan_t t = nullptr;
+    if (e != hipSuccess) fail_hip(e, "transpose");
+    else t = spmm_plan_create(rp, cl, vl, p->K, p->M);
+    dev_free(rp);
+    dev_free(cl);
+    dev_free(vl);
+    return t;
+}
+
+SPMM_API int spmm_max_backward(spmm_plan_t pt, const int64_t *argmax, const float *dC, float *dB, int64_t N,
+                               void *stream) {
+    if (!pt) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
+    if (N <= 0) return fail(SPMM_E_INVALID_ARG, "N must be positive");
+    if (N >= INT_MAX) return fail(SPMM_E_UNSUPPORTED, "N must be below 2^31 - 1");
+    if (pt->val) return fail(SPMM_E_UNSUPPORTED, "max backward needs the transpose of an unweighted adjacency");
+    if (pt->M == 0) return succeed();
+    if (!is_device_ptr(dB)) return fail(SPMM_E_INVALID_ARG, "dB is NULL or not device memory");
+    if (pt->K > 0 && (!is_device_ptr(argmax) || !is_device_ptr(dC)))
+        return fail(SPMM_E_INVALID_ARG, "argmax / dC are NULL or not device memory");
+    DeviceGuard dg(pt->device);
+    MaxGradArgs a;
+    a.rowptr_t = pt->rowptr;
+    a.col_t = pt->col;
+    a.argmax = argmax;
+    a.dC = dC;
+    a.dB = dB;
+    a.rows = pt->M;
+    a.N = N;
+    const hipError_t e = launch_maxgrad(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "max backward launch");
+    return succeed();
+}

@@ -118,6 +118,22 @@ hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val
                              bool compact, int *tiles, int64_t *overflow, int64_t nblocks, hipStream_t s);
 int64_t tile_build_blocks(int64_t M);
 
+// ---- graph construction and backward (transform.hip) ----
+struct MaxGradArgs {
+    const int *rowptr_t;     // int32 [rows+1]: transposed (unweighted) CSR
+    const int *col_t;        // int32 [nnz]: source rows i, ascending within a row
+    const int64_t *argmax;   // int64 [M, N] from the forward max
+    const float *dC;         // fp32 [M, N]
+    float *dB;               // fp32 [rows, N]
+    int64_t rows;            // rows of the transpose (= columns K of the forward)
+    int64_t N;
+};
+hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                      int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s);
+hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
+                         bool scale, int64_t *rowptr_t, int64_t *col_t, float *val_t, hipStream_t s);
+hipError_t launch_maxgrad(const MaxGradArgs &a, hipStream_t s);
+
 // ---- the plan ----
 struct Route {
     int lanes = 64, vec = 4, coarsen = 1, slices = 1;

@@ -1,0 +1,347 @@
+// Graph construction and backward support.
+//
+//  * Edge list -> CSR (graph-spmm kernel card, API table:
+//    SparseAdj.from_edge_index sorts an unsorted [2, E] edge list into CSR):
+//    a stable LSD radix sort of the rows (hipCUB) keeps each row's entries in
+//    edge-list order, so the result and every later product are deterministic.
+//  * Transposed CSR of a plan (card, "Requirements and limits": the backward of
+//    a sum aggregation is the transposed product from a second adjacency on the
+//    reversed edge list), optionally with weights a / deg_i for the backward of
+//    a mean.
+//  * Max-pool backward (card, "Method": the argmax returned in the forward
+//    sweep is what a max-pool backward needs): dB[j][k] sums dC[i][k] over
+//    rows i with argmax[i][k] == j, walking row j of the transpose in
+//    ascending i, with no atomics.
+#include <hipcub/hipcub.hpp>
+
+#include <algorithm>
+#include <vector>
+
+#include <climits>
+
+#include "spmm_internal.h"
+
+namespace gspmm {
+
+namespace {
+
+constexpr int kEdgesPerBlock = kBlock * 4;
+
+// Range check of an edge list and the sort inputs: key = row (int32), value =
+// edge index.  One record per block: the first bad edge or INT64_MAX.
+__global__ __launch_bounds__(kBlock) void coo_prepare_kernel(const int64_t *__restrict__ row,
+                                                             const int64_t *__restrict__ col, int64_t E,
+                                                             int64_t M, int64_t K, int *__restrict__ keys,
+                                                             int *__restrict__ idx, int64_t *__restrict__ bad) {
+    int64_t first_bad = INT64_MAX;
+    for (int j = 0; j < 4; ++j) {
+        const int64_t e = (int64_t)blockIdx.x * kEdgesPerBlock + j * kBlock + threadIdx.x;
+        if (e < E) {
+            const int64_t r = row[e], c = col[e];
+            if (r < 0 || r >= M || c < 0 || c >= K) first_bad = min(first_bad, e);
+            keys[e] = (int)r;
+            idx[e] = (int)e;
+        }
+    }
+    __shared__ int64_t sh[kBlock];
+    sh[threadIdx.x] = first_bad;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] = min(sh[threadIdx.x], sh[threadIdx.x + o]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) bad[blockIdx.x] = sh[0];
+}
+
+// Sort inputs of a plan's transpose: key = column of entry p, value = p, and
+// the row id of every entry.
+__global__ __launch_bounds__(kBlock) void transpose_prepare_kernel(const int *__restrict__ rowptr,
+                                                                   const int *__restrict__ col, int64_t M,
+                                                                   int *__restrict__ keys, int *__restrict__ idx,
+                                                                   int *__restrict__ rowid) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= M) return;
+    for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+        keys[p] = col[p];
+        idx[p] = p;
+        rowid[p] = (int)i;
+    }
+}
+
+// rowptr of a CSR with sorted row keys: every boundary k (0..E) writes the
+// starts of the rows between the previous key and its own.
+__global__ __launch_bounds__(kBlock) void rowptr_from_sorted_kernel(const int *__restrict__ sorted, int64_t E,
+                                                                    int64_t M, int64_t *__restrict__ rowptr) {
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k > E) return;
+    const int64_t prev = k > 0 ? sorted[k - 1] : -1;
+    const int64_t cur = k < E ? sorted[k] : M;
+    for (int64_t r = prev + 1; r <= cur; ++r) rowptr[r] = k;
+}
+
+// Entries in sorted order: column ids from the original columns (edge list)
+// or from the row ids (transpose); values copied, or scaled by 1 / deg(row).
+__global__ __launch_bounds__(kBlock) void gather_entries_kernel(const int *__restrict__ perm, int64_t E,
+                                                                const int64_t *__restrict__ col64,
+                                                                const int *__restrict__ rowid,
+                                                                const float *__restrict__ val,
+                                                                const int *__restrict__ deg_rowptr,
+                                                                int64_t *__restrict__ col_out,
+                                                                float *__restrict__ val_out) {
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k >= E) return;
+    const int p = perm[k];
+    col_out[k] = col64 ? col64[p] : (int64_t)rowid[p];
+    if (val_out) {
+        float a = val ? val[p] : 1.0f;
+        if (deg_rowptr) {
+            const int r = rowid[p];
+            a = a / (float)(deg_rowptr[r + 1] - deg_rowptr[r]);
+        }
+        val_out[k] = a;
+    }
+}
+
+int key_bits(int64_t n) {
+    int b = 1;
+    while (b < 31 && ((int64_t)1 << b) <= n) ++b;
+    return b;
+}
+
+// Stable sort of (keys, idx) by key into (skeys, perm); temporary storage is
+// allocated here and released before returning.
+hipError_t stable_sort(const int *keys, const int *idx, int *skeys, int *perm, int64_t n, int64_t key_range,
+                       hipStream_t s) {
+    size_t tmp_bytes = 0;
+    hipError_t e = hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_bytes, keys, skeys, idx, perm, (int)n, 0,
+                                                      key_bits(key_range), s);
+    if (e != hipSuccess) return e;
+    void *tmp = nullptr;
+    e = hipMalloc(&tmp, std::max<size_t>(tmp_bytes, 1));
+    if (e != hipSuccess) return e;
+    e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, keys, skeys, idx, perm, (int)n, 0, key_bits(key_range),
+                                          s);
+    const hipError_t e2 = hipStreamSynchronize(s);
+    (void)hipFree(tmp);
+    return e != hipSuccess ? e : e2;
+}
+
+struct Scratch {
+    int *keys = nullptr, *idx = nullptr, *skeys = nullptr, *perm = nullptr, *rowid = nullptr;
+    int64_t *bad = nullptr;
+    ~Scratch() {
+        for (int *q : {keys, idx, skeys, perm, rowid})
+            if (q) (void)hipFree(q);
+        if (bad) (void)hipFree(bad);
+    }
+};
+
+template <typename T>
+hipError_t alloc(T **p, int64_t n) {
+    return hipMalloc(reinterpret_cast<void **>(p), sizeof(T) * (size_t)std::max<int64_t>(n, 1));
+}
+
+}  // namespace
+
+hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                      int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s) {
+    *first_bad = -1;
+    Scratch t;
+    const int64_t nb = (E + kEdgesPerBlock - 1) / kEdgesPerBlock;
+    hipError_t e = alloc(&t.keys, E);
+    if (e == hipSuccess) e = alloc(&t.idx, E);
+    if (e == hipSuccess) e = alloc(&t.skeys, E);
+    if (e == hipSuccess) e = alloc(&t.perm, E);
+    if (e == hipSuccess) e = alloc(&t.bad, nb);
+    if (e != hipSuccess) return e;
+    if (E > 0) {
+        hipLaunchKernelGGL(coo_prepare_kernel, dim3((unsigned)nb), dim3(kBlock), 0, s, row, col, E, M, K, t.keys,
+                           t.idx, t.bad);
+        std::vector<int64_t> bad((size_t)nb);
+        e = hipMemcpyAsync(bad.data(), t.bad, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return e;
+        const int64_t b = *std::min_element(bad.begin(), bad.end());
+        if (b != INT64_MAX) {
+            *first_bad = b;
+            return hipSuccess;
+        }
+        e = stable_sort(t.keys, t.idx, t.skeys, t.perm, E, M, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gather_entries_kernel, dim3((unsigned)((E + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           t.perm, E, col, (const int *)nullptr, val, (const int *)nullptr, col_out, val_out);
+    }
+    hipLaunchKernelGGL(rowptr_from_sorted_kernel, dim3((unsigned)((E + 1 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       s, t.skeys, E, M, rowptr_out);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
+hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
+                         bool scale, int64_t *rowptr_t, int64_t *col_t, float *val_t, hipStream_t s) {
+    Scratch t;
+    hipError_t e = alloc(&t.keys, nnz);
+    if (e == hipSuccess) e = alloc(&t.idx, nnz);
+    if (e == hipSuccess) e = alloc(&t.skeys, nnz);
+    if (e == hipSuccess) e = alloc(&t.perm, nnz);
+    if (e == hipSuccess) e = alloc(&t.rowid, nnz);
+    if (e != hipSuccess) return e;
+    if (nnz > 0) {
+        hipLaunchKernelGGL(transpose_prepare_kernel, dim3((unsigned)((M + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           rowptr, col, M, t.keys, t.idx, t.rowid);
+        e = stable_sort(t.keys, t.idx, t.skeys, t.perm, nnz, K, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gather_entries_kernel, dim3((unsigned)((nnz + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           t.perm, nnz, (const int64_t *)nullptr, t.rowid, val, scale ? rowptr : nullptr, col_t,
+                           val_t);
+    }
+    hipLaunchKernelGGL(rowptr_from_sorted_kernel, dim3((unsigned)((nnz + 1 + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, s, t.skeys, nnz, K, rowptr_t);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
+// Max-pool backward over the rows j of the transposed (unweighted) plan.  A
+// wave owns 64/G consecutive rows j, whose source rows i are contiguous in
+// col_t: they are staged kChunk at a time in LDS with coalesced loads (as in
+// the forward row kernel), then lane g of row j's group gathers dC[i][c..] and
+// argmax[i][c..] in predicated batches and adds dC where argmax == j, in
+// ascending i.  A repeated i (a duplicated edge) is counted once.
+template <int G, int VEC>
+__global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef long long l2 __attribute__((ext_vector_type(2)));
+    constexpr int R = 64 / G;
+    constexpr int U = 4;
+    constexpr int NT = kChunk / 64;
+    __shared__ int s_idx[kWaves][kChunk];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int sub = lane / G;
+    const int g = lane - sub * G;
+    const int64_t j0 = ((int64_t)blockIdx.x * kWaves + wv) * R;
+    if (j0 >= a.rows) return;                               // uniform per wave
+    const int64_t j = j0 + sub;
+    const bool live = j < a.rows;
+    const int64_t c = (int64_t)blockIdx.y * (G * VEC) + g * VEC;
+    const bool ok = c < a.N;
+    const int beg = live ? a.rowptr_t[j] : 0;
+    const int deg = live ? a.rowptr_t[j + 1] - beg : 0;
+    const int beg0 = __builtin_amdgcn_readfirstlane(beg);
+    int off = 0, total = 0;
+#pragma unroll
+    for (int s = 0; s < R; ++s) {          // rows are consecutive, so entries are too
+        const int ds = __builtin_amdgcn_readlane(deg, s * G);
+        off += (s < sub) ? ds : 0;
+        total += ds;
+    }
+    int *sidx = s_idx[wv];
+    float acc[VEC];
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+    int prev = -1;
+    for (int cb = 0; cb < total; cb += kChunk) {
+        const int cn = min(kChunk, total - cb);
+        const int nt = (cn + 63) >> 6;
+        int r[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (t < nt) r[t] = a.col_t[beg0 + cb + min(t * 64 + lane, cn - 1)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (t < nt) sidx[t * 64 + lane] = r[t];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int lo = max(off, cb) - cb;
+        const int hi = min(off + deg, cb + cn) - cb;
+        for (int k = lo; k < hi; k += U) {
+            int ii[U];
+            bool use[U];
+            float d[U][VEC];
+            int64_t am[U][VEC];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = k + u < hi;
+                ii[u] = sidx[in ? k + u : lo];
+                use[u] = in && ok && ii[u] != prev;
+                if (in) prev = ii[u];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    d[u][e] = 0.0f;
+                    am[u][e] = -1;
+                }
+                if (use[u]) {
+                    const int64_t o = (int64_t)ii[u] * a.N + c;
+                    if constexpr (VEC == 4) {
+                        const f4 dv = *reinterpret_cast<const f4 *>(a.dC + o);
+                        const l2 a0 = *reinterpret_cast<const l2 *>(a.argmax + o);
+                        const l2 a1 = *reinterpret_cast<const l2 *>(a.argmax + o + 2);
+                        d[u][0] = dv.x; d[u][1] = dv.y; d[u][2] = dv.z; d[u][3] = dv.w;
+                        am[u][0] = a0.x; am[u][1] = a0.y; am[u][2] = a1.x; am[u][3] = a1.y;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            d[u][e] = a.dC[o + e];
+                            am[u][e] = a.argmax[o + e];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (use[u] && am[u][e] == j) acc[e] = acc[e] + d[u][e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (!live || !ok) return;
+    if constexpr (VEC == 4) {
+        *reinterpret_cast<f4 *>(a.dB + j * a.N + c) = f4{acc[0], acc[1], acc[2], acc[3]};
+    } else {
+        for (int e = 0; e < VEC; ++e) a.dB[j * a.N + c + e] = acc[e];
+    }
+}
+
+hipError_t launch_maxgrad(const MaxGradArgs &a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    const bool a16 = ((uintptr_t)a.dC % 16 == 0) && ((uintptr_t)a.argmax % 16 == 0) && ((uintptr_t)a.dB % 16 == 0);
+    const int vec = (a.N % 4 == 0 && a16) ? 4 : 1;
+    const int64_t W = a.N / vec;
+    int G = 4;
+    while (G < W && G < 64) G <<= 1;
+    const int64_t per_block = (int64_t)(64 / G) * kWaves;
+    const int64_t slices = (W + G - 1) / G;
+    const int64_t blocks = (a.rows + per_block - 1) / per_block;
+    if (slices > 65535 || blocks > (int64_t)(UINT32_MAX / kBlock)) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks, (unsigned)slices);
+#define GSPMM_MAXGRAD(GG, VV) hipLaunchKernelGGL((maxgrad_kernel_t<GG, VV>), grid, dim3(kBlock), 0, s, a)
+    if (vec == 4) {
+        switch (G) {
+            case 4: GSPMM_MAXGRAD(4, 4); break;
+            case 8: GSPMM_MAXGRAD(8, 4); break;
+            case 16: GSPMM_MAXGRAD(16, 4); break;
+            case 32: GSPMM_MAXGRAD(32, 4); break;
+            default: GSPMM_MAXGRAD(64, 4); break;
+        }
+    } else {
+        switch (G) {
+            case 4: GSPMM_MAXGRAD(4, 1); break;
+            case 8: GSPMM_MAXGRAD(8, 1); break;
+            case 16: GSPMM_MAXGRAD(16, 1); break;
+            case 32: GSPMM_MAXGRAD(32, 1); break;
+            default: GSPMM_MAXGRAD(64, 1); break;
+        }
+    }
+#undef GSPMM_MAXGRAD
+    return hipGetLastError();
+}
+
+}  // namespace gspmm

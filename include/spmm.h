@@ -163,6 +163,49 @@ int spmm_plan_partition(spmm_plan_t plan, int64_t *seg_row, int64_t *seg_begin,
  * must not have runs on this plan in flight. */
 int spmm_plan_set_option(spmm_plan_t plan, int option, int64_t value);
 
+/*
+ * Edge list -> CSR (graph-spmm kernel card, API table: SparseAdj.from_edge_index
+ * sorts an unsorted [2, E] edge list into CSR).  Edge e is the entry
+ * (row[e], col[e]) with value val[e] (or no value when val == NULL).  Rows are
+ * grouped in ascending order and each row keeps its entries in edge-list
+ * order (a stable sort), so the CSR, and every product over it, is
+ * deterministic.
+ *   row, col          : device int64 [E] (may be NULL when E == 0)
+ *   val               : device fp32 [E] or NULL
+ *   rowptr_out        : device int64 [M+1], written
+ *   col_out, val_out  : device int64 [E] / fp32 [E] (val_out only with val)
+ * Synchronous; allocates and frees its own temporary device memory.  Returns
+ * BAD_CSR naming the first edge whose row is outside [0, M) or column outside
+ * [0, K); E, M and K must be below 2^31.
+ */
+int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                    int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out);
+
+/*
+ * Plan of the transpose A^T [K, M] of a plan's matrix (graph-spmm card,
+ * "Requirements and limits": the backward of a sum aggregation is the
+ * transposed product, from an adjacency on the reversed edge list).  Entry
+ * (i, j, a) of A becomes (j, i, a'); within a row of A^T, entries keep A's
+ * stored order (rows i ascending).  scale = 0: a' = a (unweighted stays
+ * unweighted); scale = 1: a' = a / deg_i in fp32 (1 / deg_i when unweighted),
+ * so that spmm_run(A^T, dC, SUM) is the backward of MEAN.  Synchronous;
+ * returns a new plan (destroy it separately) or NULL on error.
+ */
+spmm_plan_t spmm_plan_transpose(spmm_plan_t plan, int scale);
+
+/*
+ * Max-pool backward (graph-spmm card, "Method": the argmax returned by the
+ * forward max is what a max-pool backward needs).  plan_t is the transpose
+ * (scale 0) of an UNWEIGHTED adjacency A [M, K]; argmax and dC are the
+ * forward's argmax [M, N] (int64) and the output gradient [M, N] (fp32):
+ *   dB[j][k] = sum of dC[i][k] over rows i with argmax[i][k] == j,
+ * summed in ascending i with no atomics (bitwise reproducible); a duplicated
+ * (i, j) edge counts once.  dB [K, N] fp32 is fully written.  Asynchronous on
+ * `stream`, allocates nothing.  Returns UNSUPPORTED for a weighted plan_t.
+ */
+int spmm_max_backward(spmm_plan_t plan_t, const int64_t *argmax, const float *dC, float *dB, int64_t N,
+                      void *stream);
+
 /* The calling thread's last status; copies its message (NUL-terminated,
  * truncated to cap bytes) into buf when buf != NULL and cap > 0. */
 int spmm_last_error(char *buf, int64_t cap);
