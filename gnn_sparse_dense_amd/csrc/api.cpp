@@ -282,8 +282,9 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //    where neighbours carry no locality, with a B wider than 64 floats:
 //    64-column slices, so each pass over the graph touches a quarter-sized
 //    part of B that stays in the Infinity Cache longer;
-//  * XCD remap (contiguous rows per XCD, sharing B rows in one L2) except for
-//    those skewed graphs, which have no neighbour locality to keep.
+//  * XCD remap in chunks of 64 blocks (rows sharing B rows meet in one L2,
+//    all XCDs sweep one region together): measured neutral or better on
+//    every regime.
 // The thresholds come from rocprofv3-timed sweeps on the five regimes.
 Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, const void *argmax) {
     Route r;
@@ -310,7 +311,7 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     r.lanes = G;
     r.coarsen = F;
     r.slices = (int)((W + (int64_t)G * F - 1) / ((int64_t)G * F));
-    r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : (skewed ? 0 : 1);
+    r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 1;
     r.nt_store = p->opt_nt >= 0 ? p->opt_nt : 0;
     r.split = p->split;
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
@@ -324,8 +325,6 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
         r.slices = (int)((N + kWinCols - 1) / kWinCols);
         r.tiled = false;
         r.compact = false;
-        // measured: the slices of a row block spread over XCDs run faster
-        r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 0;
     }
     return r;
 }

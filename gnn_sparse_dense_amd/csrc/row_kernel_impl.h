@@ -32,13 +32,24 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
-// Block id permutation giving each XCD a contiguous range of logical blocks.
-// The hardware hands consecutive block ids to the 8 XCDs round-robin; this
-// maps the j-th block that lands on XCD x to logical block start(x) + j.
+// Block id permutation for the 8 XCDs.  The hardware hands consecutive block
+// ids to the XCDs round-robin, each XCD with its own L2.  Within every run of
+// kXcds * kXcdChunk hardware blocks, this gives XCD x the kXcdChunk
+// consecutive logical blocks x*kXcdChunk ..: rows that share B rows (banded
+// or community graphs) then meet in one L2, while all XCDs still sweep the
+// same region of B and C together (one moving window in DRAM rather than
+// eight).  A tail shorter than a full run is split into 8 contiguous ranges.
 __device__ __forceinline__ int64_t xcd_remap_block(int64_t b, int64_t nb) {
-    const int64_t per = nb / kXcds, rem = nb % kXcds;
-    const int64_t x = b % kXcds, j = b / kXcds;
-    return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+    constexpr int64_t S = (int64_t)kXcds * kXcdChunk;
+    const int64_t full = (nb / S) * S;
+    if (b >= full) {
+        const int64_t rb = b - full, rn = nb - full;
+        const int64_t per = rn / kXcds, rem = rn % kXcds;
+        const int64_t x = rb % kXcds, j = rb / kXcds;
+        return full + (x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j);
+    }
+    const int64_t base = (b / S) * S, r = b - base;
+    return base + (r % kXcds) * kXcdChunk + r / kXcds;
 }
 
 // Orders this wave's LDS writes before its later LDS reads (and reads before
