@@ -35,6 +35,7 @@ METRIC = "SpMM GFLOP/s (2·nnz·N) + effective HBM GB/s as % of MI355X peak, per
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/spmm_internal.h"]
+FAMILY_SOURCES = {"mfma_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"]}
 
 REGIME_TEXT = {
     "tiny": "tiny random graph M=K=2,000, Poisson(8) degrees, 1% empty rows, weighted, N=16",
@@ -48,9 +49,10 @@ REGIME_TEXT = {
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str = "") -> str:
+    """Hash of the sources that define a kernel family's device code."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES + FAMILY_SOURCES.get(family, []):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -65,6 +67,8 @@ def byte_model(g, N, reduce):
 
 
 def kernel_family(info) -> str:
+    if info.get("route_mfma"):
+        return "mfma_tile_kernel"
     if info.get("route_window"):
         return "window_kernel"
     if info.get("route_tiled"):
@@ -83,7 +87,7 @@ def read_traffic(family: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_hash():
+    if kv.get("kernel_source_sha") != kernel_source_hash(family):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -215,12 +219,32 @@ def regime_result(r, reduce, steps, warmup, flush):
         "frac_hbm_peak_flushed": round(comp / (med_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "gather_GBps_flushed": round(gather / (med_c * 1e-3) / 1e9, 1),
         "compulsory_MB": round(comp / 1e6, 1), "gather_MB": round(gather / 1e6, 1),
+        "path": kernel_family(r.info),
         "route": {k: r.info[k] for k in ("route_lanes", "route_vec", "route_coarsen",
                                          "route_rows_per_wave", "route_slices")},
         "split": {"T": r.info["split_T"], "L": r.info["split_L"], "n_heavy": r.info["n_heavy"],
                   "n_seg": r.info["n_seg"]},
         "plan_ms": round(r.info["plan_ms"], 2),
     }
+
+
+def tile_results(r, steps, warmup, flush):
+    """The same regime on the fp16 matrix-core tiles (looser fp16 contract),
+    for graphs the router sends to the community window kernel."""
+    t0 = time.perf_counter()
+    r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 1)
+    build_ms = (time.perf_counter() - t0) * 1e3
+    out = []
+    for red in r.w.reduces:
+        if red == "max":
+            continue
+        res = regime_result(r, red, steps, warmup, flush)
+        res["tile_build_ms"] = round(build_ms, 2)
+        res["mfma_resid_nnz"] = r.info["mfma_resid_nnz"]
+        out.append(res)
+    r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 0)
+    r.info = r.G.spmm_plan_info(r.plan)
+    return out
 
 
 def time_flushed(fn, flush, steps, warmup=3):
@@ -286,6 +310,8 @@ def main():
     ap.add_argument("--regimes", default="road,tiny,diffusion,community,powerlaw")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timings")
+    ap.add_argument("--mfma", action="store_true",
+                    help="time the JSON-line workload with the fp16 matrix-core tiles (sum/mean only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -306,6 +332,9 @@ def main():
     g, N = r.g, r.w.N
     print(f"[bench] {headline}: M={g.M} nnz={g.nnz} N={N} gen={r.gen_s:.1f}s plan={r.info['plan_ms']:.1f}ms",
           file=sys.stderr, flush=True)
+    if args.mfma:
+        assert reduce != "max", "the fp16 tiles serve sum and mean only"
+        r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 1)
 
     copy_gbps = copy_ceiling_gbps(reps=3 if args.calibrate_copy else 20)
 
@@ -331,7 +360,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 tiles + f32" if args.mfma else "f32",
         "data": "synthetic",
         "config": {"workload": REGIME_TEXT[headline] + f", {reduce} reduction", "M": g.M, "K": g.K,
                    "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32},
@@ -363,6 +392,8 @@ def main():
         regimes, backward = {}, {}
         regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush)
                              for red in r.w.reduces]
+        if r.info["route_window"] and not args.mfma:
+            regimes[headline] += tile_results(r, args.steps, min(args.warmup, 50), flush)
         if not args.no_backward:
             backward[headline] = backward_result(r, flush, min(args.steps, 50))
         r.close()
@@ -374,6 +405,8 @@ def main():
                   file=sys.stderr, flush=True)
             regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush)
                              for red in rr.w.reduces]
+            if rr.info["route_window"]:
+                regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush)
             if not args.no_backward:
                 backward[name] = backward_result(rr, flush, min(args.steps, 50))
             rr.close()

@@ -34,6 +34,7 @@ SPMM_OPT_XCD_REMAP = 7
 SPMM_OPT_NT_STORE = 8
 SPMM_OPT_TILES = 9
 SPMM_OPT_WINDOW = 10
+SPMM_OPT_MFMA = 11
 
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
@@ -66,6 +67,8 @@ class _Info(ctypes.Structure):
         ("tiles", ctypes.c_int32), ("tile_cap", ctypes.c_int32),
         ("route_tiled", ctypes.c_int32), ("route_window", ctypes.c_int32),
         ("win_frac", ctypes.c_double), ("tile_overflow", ctypes.c_int64),
+        ("mfma_resid_nnz", ctypes.c_int64),
+        ("mfma_tiles", ctypes.c_int32), ("route_mfma", ctypes.c_int32),
     ]
 
 

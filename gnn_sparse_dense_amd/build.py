@@ -27,6 +27,7 @@ SOURCES = [
     "row_kernels_v4.hip",
     "window_kernels.hip",
     "transform.hip",
+    "mfma_tile.hip",
 ]
 
 COMMON = [

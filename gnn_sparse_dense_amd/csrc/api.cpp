@@ -10,7 +10,7 @@
 #include <new>
 #include <vector>
 
-#include "spmm_internal.h"
+#include "plan.h"
 
 #define SPMM_API extern "C" __attribute__((visibility("default")))
 
@@ -94,10 +94,19 @@ void free_tiles(spmm_plan *p) {
     p->tile_cap = p->tile_words = 0;
 }
 
+void free_mfma(spmm_plan *p) {
+    dev_free(p->mfma_tiles);
+    dev_free(p->mfma_rowptr);
+    dev_free(p->mfma_col);
+    dev_free(p->mfma_val);
+    p->mfma_rnnz = 0;
+}
+
 void free_plan(spmm_plan *p) {
     if (!p) return;
     free_split(p);
     free_tiles(p);
+    free_mfma(p);
     dev_free(p->rowptr);
     dev_free(p->col);
     dev_free(p->val);
@@ -260,6 +269,47 @@ int build_tiles(spmm_plan *p) {
     return st;
 }
 
+// fp16 community tiles and the residual CSR (built when SPMM_OPT_MFMA is set).
+int build_mfma(spmm_plan *p) {
+    free_mfma(p);
+    if (p->M + 1 > INT_MAX) return fail(SPMM_E_UNSUPPORTED, "fp16 tiles need M + 1 below 2^31");
+    const int64_t ntiles = (p->M + kWinRows - 1) / kWinRows;
+    int *d_flag = nullptr;
+    int st;
+    if ((st = dev_alloc(&p->mfma_tiles, ntiles * 8 * kMfmaKSteps * 64, "fp16 community tiles")) ||
+        (st = dev_alloc(&p->mfma_rowptr, p->M + 1, "residual rowptr")) || (st = dev_alloc(&d_flag, 1, "range flag"))) {
+        free_mfma(p);
+        dev_free(d_flag);
+        return st;
+    }
+    hipError_t e = mfma_build_tiles(p->rowptr, p->col, p->val, p->M, p->mfma_tiles, ntiles, p->mfma_rowptr, d_flag,
+                                    nullptr);
+    int flag = 0, rnnz = 0;
+    if (e == hipSuccess) e = hipMemcpy(&flag, d_flag, sizeof(int), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(&rnnz, p->mfma_rowptr + p->M, sizeof(int), hipMemcpyDeviceToHost);
+    dev_free(d_flag);
+    if (e != hipSuccess) {
+        free_mfma(p);
+        return fail_hip(e, "fp16 tile build");
+    }
+    if (flag) {
+        free_mfma(p);
+        return fail(SPMM_E_UNSUPPORTED, "an in-block sum of weights is outside the fp16 range (or not finite)");
+    }
+    p->mfma_rnnz = rnnz;
+    if ((st = dev_alloc(&p->mfma_col, rnnz, "residual col")) ||
+        (p->val && (st = dev_alloc(&p->mfma_val, rnnz, "residual val")))) {
+        free_mfma(p);
+        return st;
+    }
+    e = mfma_write_residual(p->rowptr, p->col, p->val, p->M, p->mfma_rowptr, p->mfma_col, p->mfma_val, nullptr);
+    if (e != hipSuccess) {
+        free_mfma(p);
+        return fail_hip(e, "residual CSR build");
+    }
+    return SPMM_OK;
+}
+
 int pow2_ceil(int64_t x) {
     int g = 1;
     while (g < x && g < 64) g <<= 1;
@@ -282,11 +332,14 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //    where neighbours carry no locality, with a B wider than 64 floats:
 //    64-column slices, so each pass over the graph touches a quarter-sized
 //    part of B that stays in the Infinity Cache longer;
+//  * fp16 matrix-core tiles only when the caller enabled them (they follow
+//    the looser fp16 contract) and the run is a sum or mean with 16-byte
+//    aligned float4 access;
 //  * XCD remap in chunks of 64 blocks (rows sharing B rows meet in one L2,
 //    all XCDs sweep one region together): measured neutral or better on
 //    every regime.
 // The thresholds come from rocprofv3-timed sweeps on the five regimes.
-Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, const void *argmax) {
+Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const void *C, const void *argmax) {
     Route r;
     const bool a16 = aligned(B, 16) && aligned(C, 16) && (!argmax || aligned(argmax, 16));
     const bool a8 = aligned(B, 8) && aligned(C, 8) && (!argmax || aligned(argmax, 16));
@@ -319,12 +372,17 @@ Route route_for(const spmm_plan *p, int64_t N, const void *B, const void *C, con
     // community structure with wide features: stage B's row blocks in LDS
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 &&
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
-    if (r.window) {
+    // fp16 community tiles, when the caller asked for them
+    r.mfma = p->opt_mfma == 1 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
+    if (r.window || r.mfma) {
+        r.vec = 4;
         r.lanes = kWinCols / 4;
         r.coarsen = 1;
         r.slices = (int)((N + kWinCols - 1) / kWinCols);
         r.tiled = false;
         r.compact = false;
+        r.window = !r.mfma;
+        r.split = r.split && !r.mfma;
     }
     return r;
 }
@@ -615,6 +673,22 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
             return succeed();
+        case SPMM_OPT_MFMA: {
+            if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "mfma must be 0 or 1");
+            const hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail_hip(e, "synchronise before changing the fp16 tiles");
+            p->opt_mfma = 0;
+            if (value == 0) {
+                free_mfma(p);
+                return succeed();
+            }
+            if (!p->mfma_tiles) {
+                const int st = build_mfma(p);
+                if (st) return st;
+            }
+            p->opt_mfma = 1;
+            return succeed();
+        }
 
         default:
             return fail(SPMM_E_INVALID_ARG, "unknown option %d", option);
@@ -661,6 +735,9 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_tiled = p->route.tiled ? 1 : 0;
     info.route_window = p->route.window ? 1 : 0;
     info.win_frac = p->win_frac;
+    info.mfma_resid_nnz = p->mfma_tiles ? p->mfma_rnnz : 0;
+    info.mfma_tiles = p->mfma_tiles ? 1 : 0;
+    info.route_mfma = p->route.mfma ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -671,7 +748,7 @@ SPMM_API int spmm_plan_route(spmm_plan_t p, int64_t N, int reduce) {
     if (N <= 0) return fail(SPMM_E_INVALID_ARG, "N must be positive");
     if (reduce < SPMM_SUM || reduce > SPMM_MAX) return fail(SPMM_E_INVALID_ARG, "unknown reduce %d", reduce);
     static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
-    p->route = route_for(p, N, dummy, dummy, nullptr);
+    p->route = route_for(p, N, reduce, dummy, dummy, nullptr);
     p->route_N = N;
     return succeed();
 }
@@ -743,7 +820,28 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     const bool is_max = reduce == SPMM_MAX;
     const bool has_val = p->val != nullptr;
 
-    Route r = route_for(p, N, B, C, argmax);
+    Route r = route_for(p, N, reduce, B, C, argmax);
+    if (r.mfma) {
+        p->route = r;
+        p->route_N = N;
+        MfmaArgs ma;
+        ma.atiles = p->mfma_tiles;
+        ma.rowptr = p->rowptr;
+        ma.rrowptr = p->mfma_rowptr;
+        ma.rcol = p->mfma_col;
+        ma.rval = p->mfma_val;
+        ma.B = B;
+        ma.C = C;
+        ma.M = p->M;
+        ma.K = p->K;
+        ma.N = N;
+        ma.nslices = r.slices;
+        ma.mean = reduce == SPMM_MEAN;
+        ma.xcd_remap = r.xcd_remap;
+        const hipError_t e = launch_mfma(ma, has_val, s);
+        if (e != hipSuccess) return fail_hip(e, "fp16 tile kernel launch");
+        return succeed();
+    }
     RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled, r.compact};
     RowKernelFn fn = row_kernel(key);
     if (!fn) return fail(SPMM_E_UNSUPPORTED, "no kernel for lanes=%d vec=%d coarsen=%d", r.lanes, r.vec, r.coarsen);

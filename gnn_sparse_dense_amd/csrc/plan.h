@@ -1,0 +1,55 @@
+// Host-side plan of the CSR SpMM library: the device buffers a plan owns, its
+// descriptors, options and last routing decision.  Only the C ABI
+// implementation (api.cpp) uses it; kernels see their argument structs.
+#pragma once
+
+#include "spmm_internal.h"
+
+namespace gspmm {
+
+struct Route {
+    int lanes = 64, vec = 4, coarsen = 1, slices = 1;
+    int xcd_remap = 1, nt_store = 0;
+    bool split = false;
+    bool tiled = false;
+    bool compact = false;
+    bool window = false;
+    bool mfma = false;
+};
+
+}  // namespace gspmm
+
+struct spmm_plan {
+    int device = 0;
+    int64_t M = 0, K = 0, nnz = 0;
+    // descriptors
+    int64_t dmax = 0, n_empty = 0, sum_deg2 = 0;
+    double mean_deg = 0, cv_deg = 0, plan_ms = 0;
+    // narrowed CSR (device)
+    int *rowptr = nullptr;
+    int *col = nullptr;
+    float *val = nullptr;
+    // row split (device)
+    bool split = false;
+    int64_t T = 0, L = 0, n_heavy = 0, n_seg = 0, n_light = 0;
+    int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
+    float *partial = nullptr;
+    int *part_arg = nullptr;
+    // row-tile records (low-degree graphs)
+    int *tiles = nullptr;
+    int tile_cap = 0, tile_words = 0;
+    bool tile_compact = false;
+    int64_t tile_overflow = 0;
+    double win_frac = 0;       // share of entries inside their row's kWinRows block
+    // fp16 community tiles + residual CSR (built on request)
+    uint4 *mfma_tiles = nullptr;
+    int *mfma_rowptr = nullptr, *mfma_col = nullptr;
+    float *mfma_val = nullptr;
+    int64_t mfma_rnnz = 0;
+    // options (-1 / 0 = automatic)
+    int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0;
+    // last routing decision
+    int64_t route_N = 0;
+    gspmm::Route route;
+};

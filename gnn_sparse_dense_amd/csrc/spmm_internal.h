@@ -25,6 +25,8 @@ constexpr int kWinRows = 256;           // rows of a community window
 constexpr int kWinCols = 64;            // B columns staged per window block
 constexpr int kWinBlock = 1024;         // threads of a window block
 constexpr int kWinChunk = 128;          // staged entries per wave in window blocks
+constexpr int kMfmaKSteps = kWinRows / 16;   // k-steps of 16 per 256-wide community tile
+constexpr int kMfmaBtPitch = kWinRows + 8;   // fp16 per staged B^T row (16-byte skew per row)
 
 // Arguments of the row kernel (light rows or split pieces).
 struct RowArgs {
@@ -119,6 +121,30 @@ hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val
                              bool compact, int *tiles, int64_t *overflow, int64_t nblocks, hipStream_t s);
 int64_t tile_build_blocks(int64_t M);
 
+// ---- fp16 matrix-core tiles for community blocks (mfma_tile.hip) ----
+// Tile t covers rows and columns [t*kWinRows, (t+1)*kWinRows).  Its dense
+// fp16 values are stored in the operand order of v_mfma_f32_32x32x16_f16: for
+// row group rg (32 rows) and k-step ks (16 columns), 64 lanes x 8 halves,
+// lane l holding row rg*32 + l%32, columns ks*16 + 8*(l/32) .. +7.
+struct MfmaArgs {
+    const uint4 *atiles;   // [ntiles][8][kMfmaKSteps][64] x 8 fp16
+    const int *rowptr;     // int32 [M+1] of the whole matrix (mean divisor)
+    const int *rrowptr;    // int32 [M+1] residual CSR (entries outside the row's tile)
+    const int *rcol;       // int32 [rnnz]
+    const float *rval;     // fp32 [rnnz] or nullptr
+    const float *B;        // fp32 [K, N]
+    float *C;              // fp32 [M, N]
+    int64_t M, K, N;
+    int64_t nslices;       // kWinCols-wide column slices
+    int mean;
+    int xcd_remap;
+};
+hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val, int64_t M, uint4 *atiles,
+                            int64_t ntiles, int *rrowptr, int *range_flag, hipStream_t s);
+hipError_t mfma_write_residual(const int *rowptr, const int *col, const float *val, int64_t M,
+                               const int *rrowptr, int *rcol, float *rval, hipStream_t s);
+hipError_t launch_mfma(const MfmaArgs &a, bool has_val, hipStream_t s);
+
 // ---- graph construction and backward (transform.hip) ----
 struct MaxGradArgs {
     const int *rowptr_t;     // int32 [rows+1]: transposed (unweighted) CSR
@@ -135,44 +161,4 @@ hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, in
                          bool scale, int64_t *rowptr_t, int64_t *col_t, float *val_t, hipStream_t s);
 hipError_t launch_maxgrad(const MaxGradArgs &a, hipStream_t s);
 
-// ---- the plan ----
-struct Route {
-    int lanes = 64, vec = 4, coarsen = 1, slices = 1;
-    int xcd_remap = 1, nt_store = 0;
-    bool split = false;
-    bool tiled = false;
-    bool compact = false;
-    bool window = false;
-};
-
 }  // namespace gspmm
-
-struct spmm_plan {
-    int device = 0;
-    int64_t M = 0, K = 0, nnz = 0;
-    // descriptors
-    int64_t dmax = 0, n_empty = 0, sum_deg2 = 0;
-    double mean_deg = 0, cv_deg = 0, plan_ms = 0;
-    // narrowed CSR (device)
-    int *rowptr = nullptr;
-    int *col = nullptr;
-    float *val = nullptr;
-    // row split (device)
-    bool split = false;
-    int64_t T = 0, L = 0, n_heavy = 0, n_seg = 0, n_light = 0;
-    int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
-    float *partial = nullptr;
-    int *part_arg = nullptr;
-    // row-tile records (low-degree graphs)
-    int *tiles = nullptr;
-    int tile_cap = 0, tile_words = 0;
-    bool tile_compact = false;
-    int64_t tile_overflow = 0;
-    double win_frac = 0;       // share of entries inside their row's kWinRows block
-    // options (-1 / 0 = automatic)
-    int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
-    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1;
-    // last routing decision
-    int64_t route_N = 0;
-    gspmm::Route route;
-};

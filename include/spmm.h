@@ -69,9 +69,30 @@ enum spmm_option {
     SPMM_OPT_TILES = 9,        /* -1 auto (low, even degrees), 0 off, 1 on, 2 on
                                   with 32-bit records: keep 8-row tile records
                                   holding row bounds + indexes               */
-    SPMM_OPT_WINDOW = 10       /* -1 auto (community structure, N >= 128), 0 off,
+    SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
                                   1 on: stage each 256-row block of B in LDS  */
+    SPMM_OPT_MFMA = 11         /* 0 off (default), 1 on: fp16 matrix-core tiles
+                                  for community blocks, see below             */
 };
+
+/*
+ * SPMM_OPT_MFMA = 1 (RA-SpMM, "Kernel families": a dense tile path for
+ * community-structured blocks, which gains by cutting memory traffic rather
+ * than by reaching the matrix cores' peak).  Setting it builds, synchronously,
+ * one dense 256 x 256 fp16 tile per aligned 256-row block holding the entries
+ * whose column lies in the row's own block (duplicates summed in fp32 in
+ * stored order, then rounded once to fp16), and a residual CSR of all other
+ * entries in stored order; 128 KB of device memory per 256 rows plus the
+ * residual.  Later SUM and MEAN runs whose N is a multiple of 4 with 16-byte
+ * aligned B and C then compute the in-block part as fp16 x fp16 products with
+ * fp32 accumulation on the matrix cores (B rounded to fp16, so |B| must stay
+ * below 65504) and add the residual entries in fp32 in stored order.  Results
+ * are bitwise reproducible but follow the looser contract of fp16 tiles:
+ * |error| <= 2e-3 * sum_p |a_p * B[col_p][k]| + 1e-4 per element.  MAX runs,
+ * other N and unaligned pointers keep the fp32 kernels.  Setting 0 frees the
+ * tiles.  Returns UNSUPPORTED if an in-block sum of weights exceeds the fp16
+ * range.
+ */
 
 /* Descriptors of a plan and of its last routing decision. */
 struct spmm_plan_info {
@@ -95,6 +116,10 @@ struct spmm_plan_info {
     double win_frac;             /* share of entries inside their row's 256-row
                                     block (community structure)               */
     int64_t tile_overflow;       /* tiles that take the CSR path              */
+    int64_t mfma_resid_nnz;      /* entries outside their row's block (residual
+                                    CSR of the fp16 tile path; 0 when unbuilt) */
+    int32_t mfma_tiles;          /* 1 when the fp16 tiles are built           */
+    int32_t route_mfma;          /* 1 when the last run used them             */
 };
 
 /*

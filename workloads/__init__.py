@@ -12,5 +12,6 @@ from .graphs import (  # noqa: F401
     make_graph,
     make_features,
     random_csr,
+    block_csr,
     csr_from_pairs,
 )

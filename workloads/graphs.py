@@ -330,3 +330,39 @@ def random_csr(rng: np.random.Generator, M: int, K: int, mean_deg: float = 4.0,
         if zero_frac > 0:
             val[rng.random(nnz) < zero_frac] = 0.0
     return Graph(name="random", M=M, K=K, rowptr=rowptr, col=col, val=val)
+
+
+def block_csr(rng: np.random.Generator, M: int, K: int, in_deg: float = 12.0, off_deg: float = 2.0,
+              empty_frac: float = 0.05, weighted: bool = True, block: int = 256) -> Graph:
+    """Block-structured CSR: row i draws Poisson(in_deg) columns with
+    replacement (so duplicates occur) from its own aligned block of `block`
+    columns [block*(i//block), ...) clipped to K, plus Poisson(off_deg) columns
+    uniform over [0, K); each row's entries are shuffled (unsorted) and a
+    fraction of rows is forced empty."""
+    d_in = rng.poisson(in_deg, size=M).astype(np.int64)
+    d_off = rng.poisson(off_deg, size=M).astype(np.int64)
+    lo = (np.arange(M, dtype=np.int64) // block) * block
+    hi = np.minimum(lo + block, K)
+    d_in[lo >= hi] = 0                      # block entirely beyond K
+    if M and empty_frac > 0:
+        e = rng.choice(M, size=min(int(round(empty_frac * M)), M), replace=False)
+        d_in[e] = 0
+        d_off[e] = 0
+    if K == 0:
+        d_off[:] = 0
+    deg = d_in + d_off
+    rowptr = _rowptr_from_deg(deg)
+    nnz = int(rowptr[-1])
+    col = np.empty(nnz, dtype=np.int64)
+    rows = np.repeat(np.arange(M, dtype=np.int64), deg)
+    pos = np.arange(nnz, dtype=np.int64) - rowptr[rows]
+    inside = pos < d_in[rows]
+    span = (hi - lo)[rows]
+    col[inside] = lo[rows][inside] + (rng.random(int(inside.sum())) * span[inside]).astype(np.int64)
+    col[~inside] = rng.integers(0, max(K, 1), size=int((~inside).sum()), dtype=np.int64)
+    for i in range(M):                       # shuffle within each row
+        a, b = rowptr[i], rowptr[i + 1]
+        if b - a > 1:
+            col[a:b] = col[a:b][rng.permutation(b - a)]
+    val = rng.random(nnz, dtype=np.float32) if weighted else None
+    return Graph(name="block", M=M, K=K, rowptr=rowptr, col=col, val=val)
