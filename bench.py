@@ -247,6 +247,62 @@ def tile_results(r, steps, warmup, flush):
     return out
 
 
+def router_sweep(r, reduce, steps, flush):
+    """Router evidence (RA-SpMM abstract: the router's speed as a fraction of the
+    best of all variants, per configuration): the router's choice against every
+    forced (lanes, coarsening) pair and one-at-a-time toggles of its other
+    decisions, all cache-flushed medians on one plan.  The fp16 tiles follow a
+    looser contract and are listed apart, never counted as the best."""
+    G = r.G
+    auto = {G.SPMM_OPT_LANES: 0, G.SPMM_OPT_COARSEN: 0, G.SPMM_OPT_TILES: -1, G.SPMM_OPT_WINDOW: -1,
+            G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1}
+    variants = [("router", {})]
+    variants += [(f"lanes={g} coarsen={f}", {G.SPMM_OPT_LANES: g, G.SPMM_OPT_COARSEN: f})
+                 for g in (4, 8, 16, 32, 64) for f in (1, 2)]
+    variants += [("row tiles off", {G.SPMM_OPT_TILES: 0}), ("row tiles compact", {G.SPMM_OPT_TILES: 1}),
+                 ("row tiles wide", {G.SPMM_OPT_TILES: 2}), ("window on", {G.SPMM_OPT_WINDOW: 1}),
+                 ("window off", {G.SPMM_OPT_WINDOW: 0}), ("XCD remap off", {G.SPMM_OPT_XCD_REMAP: 0}),
+                 ("non-temporal C stores", {G.SPMM_OPT_NT_STORE: 1}), ("split on", {G.SPMM_OPT_SPLIT_MODE: 1}),
+                 ("split off", {G.SPMM_OPT_SPLIT_MODE: 0})]
+    rows = []
+    for label, opts in variants:
+        entry = {"variant": label}
+        try:
+            for k, v in opts.items():
+                G.spmm_plan_set_option(r.plan, k, v)
+            ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
+            info = G.spmm_plan_info(r.plan)
+            entry.update({"ms": round(ms, 5), "path": kernel_family(info),
+                          "route": [info["route_lanes"], info["route_vec"], info["route_coarsen"],
+                                    info["route_slices"], info["route_xcd_remap"], info["route_nt_store"],
+                                    info["route_split"], info["route_tiled"] * info["tiles"],
+                                    info["route_window"]]})
+        except G.SpmmError as e:
+            entry["unsupported"] = str(e)
+        finally:
+            for k in opts:
+                G.spmm_plan_set_option(r.plan, k, auto[k])
+        rows.append(entry)
+    timed = [x for x in rows if "ms" in x]
+    # variants that resolve to the router's own kernel and launch shape time the
+    # same code: the best of them is the router's figure, their spread the noise
+    key = (rows[0]["path"], tuple(rows[0]["route"]))
+    same = [x["ms"] for x in timed if (x["path"], tuple(x["route"])) == key]
+    router_ms = min(same)
+    best = min(timed, key=lambda x: x["ms"])
+    out = {"reduce": reduce, "variants": rows, "router_ms": router_ms, "best_ms": best["ms"],
+           "best_variant": best["variant"], "router_speed_vs_best": round(best["ms"] / router_ms, 4),
+           "router_route_repeats": len(same),
+           "router_route_spread": round(max(same) / min(same) - 1.0, 4)}
+    if reduce != "max" and rows[0]["path"] == "window_kernel":
+        G.spmm_plan_set_option(r.plan, G.SPMM_OPT_MFMA, 1)
+        ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
+        G.spmm_plan_set_option(r.plan, G.SPMM_OPT_MFMA, 0)
+        out["fp16_tiles_ms"] = round(ms, 5)
+    r.info = G.spmm_plan_info(r.plan)
+    return out
+
+
 def time_flushed(fn, flush, steps, warmup=3):
     import torch
     for _ in range(warmup):
@@ -312,6 +368,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timings")
     ap.add_argument("--mfma", action="store_true",
                     help="time the JSON-line workload with the fp16 matrix-core tiles (sum/mean only)")
+    ap.add_argument("--router-sweep", action="store_true",
+                    help="only the router evidence: every forced variant per regime against the router's pick")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -325,6 +383,25 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.router_sweep:
+        flush = make_flush()
+        evidence = {}
+        for name in [x for x in args.regimes.split(",") if x]:
+            rr = Runner(name)
+            print(f"[bench] router sweep {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N}", file=sys.stderr, flush=True)
+            evidence[name] = [router_sweep(rr, red, min(args.steps, 30), flush) for red in rr.w.reduces]
+            rr.close()
+            del rr
+            torch.cuda.empty_cache()
+        ratios = [x["router_speed_vs_best"] for v in evidence.values() for x in v]
+        geo = 1.0
+        for q in ratios:
+            geo *= q
+        print(json.dumps({"router_evidence": evidence,
+                          "router_speed_vs_best_geomean": round(geo ** (1.0 / len(ratios)), 4),
+                          "router_speed_vs_best_min": min(ratios)}), flush=True)
+        return
 
     headline = args.workload
     r = Runner(headline)
