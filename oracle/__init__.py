@@ -50,6 +50,8 @@ class Oracle:
         lib.oracle_transpose.restype = None
         lib.oracle_max_backward.argtypes = [_p, _p, _i64, _i64, _i64, _p]
         lib.oracle_max_backward.restype = ctypes.c_int
+        lib.oracle_features.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p]
+        lib.oracle_features.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -154,6 +156,21 @@ class Oracle:
         if self.lib.oracle_max_backward(_ptr(argmax), _ptr(dC), M, K, N, _ptr(dB)) != 0:
             raise ValueError("argmax entry outside [-1, K)")
         return dB
+
+    def features(self, rowptr, col, M, K, V=2):
+        """ParamSpMM Table 3 features (see oracle_features)."""
+        rowptr, col, _ = self._csr(rowptr, col, None)
+        ints = np.zeros(7, np.int64)
+        dbl = np.zeros(8, np.float64)
+        if self.lib.oracle_features(_ptr(rowptr), _ptr(col), M, K, V, _ptr(ints), _ptr(dbl)) != 0:
+            raise ValueError("oracle_features rejected its arguments")
+        names_i = ("n", "n_nonempty", "nnz", "dmax", "max_bandwidth", "nnz_distinct", "nnz_vectors")
+        names_d = ("delta", "mean_deg", "mean_deg_nonempty", "cv_deg", "cv_deg_nonempty", "density",
+                   "mean_bandwidth", "padding_ratio")
+        out = {k: int(v) for k, v in zip(names_i, ints)}
+        out.update({k: float(v) for k, v in zip(names_d, dbl)})
+        out["V"] = int(V)
+        return out
 
 
 _default: Optional[Oracle] = None

@@ -310,3 +310,104 @@ int oracle_max_backward(const int64_t *argmax, const float *dC, int64_t M, int64
         }
     return 0;
 }
+
+/*
+ * Sparse-matrix features of ParamSpMM section 5.1, Table 3, for the CSR
+ * matrix A [M, K] and a vectorized-blocking width V (section 3.1: V
+ * consecutive rows form one block, rows V*g .. V*g+V-1).
+ *   ints = {n, n_nonempty, nnz, dmax, max_bandwidth, nnz_distinct, nnz_vectors}
+ *   dbl  = {delta, mean_deg, mean_deg_nonempty, cv_deg, cv_deg_nonempty,
+ *           density, mean_bandwidth, padding_ratio}
+ * delta = n_nonempty / n; the "hat" quantities ignore empty rows; cv is the
+ * population standard deviation over the mean (two passes); density =
+ * nnz / (M * K) with nnz the stored entry count.  Bandwidth of a row: its
+ * largest minus its smallest column id (Table 3 footnote: the column distance
+ * between the row's first and last nonzero, columns taken in ascending
+ * order); averaged over non-empty rows.  nnz_distinct counts distinct
+ * (row, col) pairs; a nonzero vector is a column with at least one entry in a
+ * block, nnz_vectors counts them over all blocks, and the padding ratio is
+ * eq. 2, 1 - nnz_distinct / (nnz_vectors * V) (0 when there are no entries).
+ * Returns 0, or -1 for V < 1 or an allocation failure.
+ */
+static int cmp_i64(const void *a, const void *b) {
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+static int64_t count_distinct(int64_t *buf, int64_t n) {
+    if (n == 0) return 0;
+    qsort(buf, (size_t)n, sizeof(int64_t), cmp_i64);
+    int64_t d = 1;
+    for (int64_t i = 1; i < n; ++i)
+        if (buf[i] != buf[i - 1]) d += 1;
+    return d;
+}
+
+int oracle_features(const int64_t *rowptr, const int64_t *col, int64_t M, int64_t K,
+                    int64_t V, int64_t *ints, double *dbl) {
+    if (V < 1) return -1;
+    int64_t nnz = 0, dmax = 0, nonempty = 0, bwmax = 0;
+    double bwsum = 0.0;
+    int64_t longest = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t d = rowptr[i + 1] - rowptr[i];
+        nnz += d;
+        if (d > dmax) dmax = d;
+        if (d > 0) {
+            nonempty += 1;
+            int64_t lo = col[rowptr[i]], hi = col[rowptr[i]];
+            for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+                if (col[p] < lo) lo = col[p];
+                if (col[p] > hi) hi = col[p];
+            }
+            bwsum += (double)(hi - lo);
+            if (hi - lo > bwmax) bwmax = hi - lo;
+        }
+    }
+    /* degree moments, all rows and non-empty rows, two passes each */
+    double mean = M > 0 ? (double)nnz / (double)M : 0.0;
+    double mean_ne = nonempty > 0 ? (double)nnz / (double)nonempty : 0.0;
+    double var = 0.0, var_ne = 0.0;
+    for (int64_t i = 0; i < M; ++i) {
+        double d = (double)(rowptr[i + 1] - rowptr[i]);
+        var += (d - mean) * (d - mean);
+        if (d > 0) var_ne += (d - mean_ne) * (d - mean_ne);
+    }
+    var = M > 0 ? var / (double)M : 0.0;
+    var_ne = nonempty > 0 ? var_ne / (double)nonempty : 0.0;
+    /* distinct (row, col) pairs, row by row; nonzero vectors, block by block */
+    for (int64_t i = 0; i < M; ++i)
+        if (rowptr[i + 1] - rowptr[i] > longest) longest = rowptr[i + 1] - rowptr[i];
+    int64_t cap = longest * V > 0 ? longest * V : 1;
+    int64_t *buf = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    if (!buf) return -1;
+    int64_t distinct = 0, vectors = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t n = 0;
+        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p) buf[n++] = col[p];
+        distinct += count_distinct(buf, n);
+    }
+    for (int64_t g = 0; g * V < M; ++g) {
+        int64_t n = 0;
+        for (int64_t i = g * V; i < g * V + V && i < M; ++i)
+            for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p) buf[n++] = col[p];
+        vectors += count_distinct(buf, n);
+    }
+    free(buf);
+    ints[0] = M;
+    ints[1] = nonempty;
+    ints[2] = nnz;
+    ints[3] = dmax;
+    ints[4] = bwmax;
+    ints[5] = distinct;
+    ints[6] = vectors;
+    dbl[0] = M > 0 ? (double)nonempty / (double)M : 0.0;
+    dbl[1] = mean;
+    dbl[2] = mean_ne;
+    dbl[3] = mean > 0.0 ? sqrt(var) / mean : 0.0;
+    dbl[4] = mean_ne > 0.0 ? sqrt(var_ne) / mean_ne : 0.0;
+    dbl[5] = (M > 0 && K > 0) ? (double)nnz / ((double)M * (double)K) : 0.0;
+    dbl[6] = nonempty > 0 ? bwsum / (double)nonempty : 0.0;
+    dbl[7] = vectors > 0 ? 1.0 - (double)distinct / ((double)vectors * (double)V) : 0.0;
+    return 0;
+}

@@ -405,9 +405,58 @@ def pin_max_backward(orc):
     assert abs(lhs - rhs) <= 1e-4 * (1 + abs(lhs))
 
 
+def _read_features_golden():
+    kv = {}
+    for line in open(os.path.join(GOLDEN, "features_hand.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, *v = line.split()
+        kv[k] = v
+    return kv
+
+
+def pin_features(orc):
+    kv = _read_features_golden()
+    rp = np.array(kv["rowptr"], np.int64)
+    col = np.array(kv["col"], np.int64)
+    M, K = int(kv["M"][0]), int(kv["K"][0])
+    for V in (1, 2, 3):
+        f = orc.features(rp, col, M, K, V)
+        for key in ("n_nonempty", "nnz", "dmax", "max_bandwidth", "nnz_distinct"):
+            assert f[key] == int(kv[key][0]), (key, f[key])
+        for key in ("delta", "mean_deg", "mean_deg_nonempty", "cv_deg", "cv_deg_nonempty", "density",
+                    "mean_bandwidth"):
+            assert abs(f[key] - float(kv[key][0])) <= 1e-12, (key, f[key])
+        assert f["nnz_vectors"] == int(kv[f"vectors_V{V}"][0]), (V, f["nnz_vectors"])
+        assert abs(f["padding_ratio"] - float(kv[f"padding_V{V}"][0])) <= 1e-12, (V, f["padding_ratio"])
+    # numpy brute force on irregular graphs (duplicates, unsorted rows, empty rows)
+    rng = np.random.default_rng(53)
+    for V in (1, 2, 4):
+        g = W.random_csr(rng, 333, 97, mean_deg=6.0, empty_frac=0.2, dup_frac=0.3, shuffle_rows=True)
+        f = orc.features(g.rowptr, g.col, g.M, g.K, V)
+        deg = g.degrees()
+        rows = np.repeat(np.arange(g.M), deg)
+        ne = deg > 0
+        pairs = np.unique(rows * g.K + g.col).size
+        vecs = np.unique((rows // V) * g.K + g.col).size
+        assert f["nnz_distinct"] == pairs and f["nnz_vectors"] == vecs
+        assert abs(f["padding_ratio"] - (1 - pairs / (vecs * V))) <= 1e-12
+        assert abs(f["cv_deg_nonempty"] - np.std(deg[ne]) / np.mean(deg[ne])) <= 1e-12
+        assert abs(f["cv_deg"] - np.std(deg) / np.mean(deg)) <= 1e-12
+        starts = g.rowptr[:-1][ne]
+        bw = np.maximum.reduceat(g.col, starts) - np.minimum.reduceat(g.col, starts)
+        assert f["max_bandwidth"] == bw.max() and abs(f["mean_bandwidth"] - bw.mean()) <= 1e-9
+        assert 0.0 <= f["padding_ratio"] <= 1.0 - 1.0 / V + 1e-15
+    # closed cases: identical row pairs share every column (no padding), disjoint
+    # row pairs share none (the largest padding of V = 2)
+    same = np.array([0, 3, 6, 8, 10], np.int64)
+    assert orc.features(same, np.array([1, 4, 6, 1, 4, 6, 2, 9, 2, 9]), 4, 10, 2)["padding_ratio"] == 0.0
+    assert orc.features(same, np.array([1, 4, 6, 0, 5, 7, 2, 9, 3, 8]), 4, 10, 2)["padding_ratio"] == 0.5
+
+
 ALL_PINS = [
     pin_dense_bruteforce, pin_scipy_product, pin_identity, pin_ones, pin_empty_rows,
     pin_max_numpy, pin_val_null_is_ones, pin_mean_sum_relation, pin_row_subset,
     pin_partition, pin_descriptors, pin_validate, pin_mac_gap, pin_tiny_config,
-    pin_coo_to_csr, pin_transpose, pin_max_backward,
+    pin_coo_to_csr, pin_transpose, pin_max_backward, pin_features,
 ]

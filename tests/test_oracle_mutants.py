@@ -40,6 +40,13 @@ MUTANTS = {
     "transpose_scale_off": ("val_t[q] = scale ? a / (float)deg : a;", "val_t[q] = scale ? a / (float)(deg + 1) : a;"),
     "max_backward_skips_row0": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t k = 0; k < N; ++k) {\n            int64_t j",
                                 "for (int64_t i = 1; i < M; ++i)\n        for (int64_t k = 0; k < N; ++k) {\n            int64_t j"),
+    "features_bandwidth_stored_order": ("                if (col[p] < lo) lo = col[p];\n", ""),
+    "features_cv_all_rows": ("if (d > 0) var_ne += (d - mean_ne) * (d - mean_ne);",
+                             "var_ne += (d - mean_ne) * (d - mean_ne);"),
+    "features_padding_counts_duplicates": ("1.0 - (double)distinct / ((double)vectors * (double)V)",
+                                           "1.0 - (double)nnz / ((double)vectors * (double)V)"),
+    "features_block_skips_first_row": ("for (int64_t i = g * V; i < g * V + V && i < M; ++i)",
+                                       "for (int64_t i = g * V + 1; i < g * V + V && i < M; ++i)"),
 }
 
 
