@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SpMM GFLOP/s (2·nnz·N) + effective HBM GB/s as % of MI355X peak, per regime"
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/spmm_internal.h"]
+KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/kernels.h"]
 FAMILY_SOURCES = {"mfma_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"]}
 
 REGIME_TEXT = {
@@ -228,7 +228,7 @@ def regime_result(r, reduce, steps, warmup, flush):
     }
 
 
-def tile_results(r, steps, warmup, flush):
+def tile_results(r, steps, warmup, flush, fp32_results=()):
     """The same regime on the fp16 matrix-core tiles (looser fp16 contract),
     for graphs the router sends to the community window kernel."""
     t0 = time.perf_counter()
@@ -240,10 +240,46 @@ def tile_results(r, steps, warmup, flush):
             continue
         res = regime_result(r, red, steps, warmup, flush)
         res["tile_build_ms"] = round(build_ms, 2)
+        fp32 = [x for x in fp32_results if x["reduce"] == red]
+        if fp32:
+            saving = fp32[0]["ms_flushed_median"] - res["ms_flushed_median"]
+            res["break_even_runs"] = round(build_ms / saving, 1) if saving > 0 else None
         res["mfma_resid_nnz"] = r.info["mfma_resid_nnz"]
         out.append(res)
     r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 0)
     r.info = r.G.spmm_plan_info(r.plan)
+    return out
+
+
+def reuse_result(r, reduce, steps, flush):
+    """First call against steady state (RA-SpMM, "When does RA-SpMM help?": a
+    structure built once pays off after build / saving runs).  For each
+    optional structure the router uses on this graph: its build time, the
+    flushed per-run time with and without it, and the break-even run count."""
+    G = r.G
+    t_with = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
+    out = {"reduce": reduce, "plan_create_ms": round(r.info["plan_ms"], 3), "run_ms": round(t_with, 5),
+           "first_call_ms": round(r.info["plan_ms"] + t_with, 3)}
+
+    def structure(opt, off, auto):
+        G.spmm_plan_set_option(r.plan, opt, off)
+        t_off = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
+        t0 = time.perf_counter()
+        G.spmm_plan_set_option(r.plan, opt, auto)
+        build = (time.perf_counter() - t0) * 1e3
+        saving = t_off - t_with
+        return {"build_ms": round(build, 3), "ms_without": round(t_off, 5), "ms_with": round(t_with, 5),
+                "break_even_runs": round(build / saving, 1) if saving > 0 else None}
+
+    info = G.spmm_plan_info(r.plan)
+    if info["route_tiled"]:
+        out["row_tiles"] = structure(G.SPMM_OPT_TILES, 0, -1)
+    if info["route_split"]:
+        out["row_split"] = structure(G.SPMM_OPT_SPLIT_MODE, 0, -1)
+    t0 = time.perf_counter()
+    G.spmm_plan_features(r.plan, 2)
+    out["features_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+    r.info = G.spmm_plan_info(r.plan)
     return out
 
 
@@ -466,11 +502,12 @@ def main():
 
     if not args.headline_only:
         flush = make_flush()
-        regimes, backward = {}, {}
+        regimes, backward, reuse = {}, {}, {}
         regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush)
                              for red in r.w.reduces]
         if r.info["route_window"] and not args.mfma:
-            regimes[headline] += tile_results(r, args.steps, min(args.warmup, 50), flush)
+            regimes[headline] += tile_results(r, args.steps, min(args.warmup, 50), flush, regimes[headline])
+        reuse[headline] = reuse_result(r, r.w.reduces[0], min(args.steps, 50), flush)
         if not args.no_backward:
             backward[headline] = backward_result(r, flush, min(args.steps, 50))
         r.close()
@@ -483,13 +520,15 @@ def main():
             regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush)
                              for red in rr.w.reduces]
             if rr.info["route_window"]:
-                regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush)
+                regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush, regimes[name])
+            reuse[name] = reuse_result(rr, rr.w.reduces[0], min(args.steps, 50), flush)
             if not args.no_backward:
                 backward[name] = backward_result(rr, flush, min(args.steps, 50))
             rr.close()
             del rr
             torch.cuda.empty_cache()
         result["regimes"] = regimes
+        result["reuse"] = reuse
         if backward:
             result["backward"] = backward
     else:

@@ -39,7 +39,7 @@ SPMM_OPT_MFMA = 11
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
-    "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward",
+    "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward", "spmm_plan_features",
 )
 
 
@@ -72,6 +72,18 @@ class _Info(ctypes.Structure):
     ]
 
 
+class _Features(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64), ("n_nonempty", ctypes.c_int64), ("nnz", ctypes.c_int64),
+        ("dmax", ctypes.c_int64),
+        ("delta", ctypes.c_double), ("mean_deg", ctypes.c_double), ("mean_deg_nonempty", ctypes.c_double),
+        ("cv_deg", ctypes.c_double), ("cv_deg_nonempty", ctypes.c_double), ("density", ctypes.c_double),
+        ("mean_bandwidth", ctypes.c_double), ("max_bandwidth", ctypes.c_int64),
+        ("V", ctypes.c_int64), ("nnz_distinct", ctypes.c_int64), ("nnz_vectors", ctypes.c_int64),
+        ("padding_ratio", ctypes.c_double), ("split_ratio", ctypes.c_double), ("win_frac", ctypes.c_double),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -92,6 +104,8 @@ def _load() -> ctypes.CDLL:
     lib.spmm_plan_partition.restype = i32
     lib.spmm_plan_set_option.argtypes = [p, i32, i64]
     lib.spmm_plan_set_option.restype = i32
+    lib.spmm_plan_features.argtypes = [p, i64, ctypes.POINTER(_Features)]
+    lib.spmm_plan_features.restype = i32
     lib.spmm_last_error.argtypes = [ctypes.c_char_p, i64]
     lib.spmm_last_error.restype = i32
     lib.spmm_coo_to_csr.argtypes = [p, p, p, i64, i64, i64, p, p, p]
@@ -186,6 +200,13 @@ def spmm_plan_partition(plan: int):
     _check(_lib.spmm_plan_partition(plan, sr.ctypes.data, sb.ctypes.data, se.ctypes.data, ns,
                                     light.ctypes.data, nl, counts.ctypes.data))
     return dict(n_heavy=int(counts[0]), seg_row=sr, seg_begin=sb, seg_end=se, light=light)
+
+
+def spmm_plan_features(plan: int, V: int = 2) -> dict:
+    """ParamSpMM Table 3 features of the plan's pattern (synchronous)."""
+    f = _Features()
+    _check(_lib.spmm_plan_features(plan, int(V), ctypes.byref(f)))
+    return {name: getattr(f, name) for name, _ in _Features._fields_}
 
 
 def spmm_plan_set_option(plan: int, option: int, value: int) -> None:

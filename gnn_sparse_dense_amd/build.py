@@ -28,6 +28,7 @@ SOURCES = [
     "window_kernels.hip",
     "transform.hip",
     "mfma_tile.hip",
+    "features.hip",
 ]
 
 COMMON = [

@@ -920,6 +920,49 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     return succeed();
 }
 
+SPMM_API int spmm_plan_features(spmm_plan_t p, int64_t V, struct spmm_features *out) {
+    if (!p || !out) return fail(SPMM_E_INVALID_ARG, "plan or output is NULL");
+    if (V < 1 || V > 64) return fail(SPMM_E_INVALID_ARG, "V must be in [1, 64]");
+    DeviceGuard dg(p->device);
+    struct spmm_features f;
+    std::memset(&f, 0, sizeof(f));
+    f.n = p->M;
+    f.nnz = p->nnz;
+    f.dmax = p->dmax;
+    f.V = V;
+    f.n_nonempty = p->M - p->n_empty;
+    f.delta = p->M > 0 ? (double)f.n_nonempty / (double)p->M : 0.0;
+    f.mean_deg = p->mean_deg;
+    f.cv_deg = p->cv_deg;
+    if (f.n_nonempty > 0) {
+        // empty rows add nothing to the degree sums: the same exact fold as the plan's CV
+        const int64_t n = f.n_nonempty;
+        f.mean_deg_nonempty = (double)p->nnz / (double)n;
+        const __int128 num = (__int128)n * (__int128)p->sum_deg2 - (__int128)p->nnz * (__int128)p->nnz;
+        const double var = (double)num / ((double)n * (double)n);
+        f.cv_deg_nonempty = f.mean_deg_nonempty > 0 ? std::sqrt(std::max(var, 0.0)) / f.mean_deg_nonempty : 0.0;
+    }
+    f.density = (p->M > 0 && p->K > 0) ? (double)p->nnz / ((double)p->M * (double)p->K) : 0.0;
+    f.split_ratio = p->M > 0 ? (double)(p->split ? p->n_light + p->n_seg : p->M) / (double)p->M : 1.0;
+    f.win_frac = p->win_frac;
+    hipError_t e = hipDeviceSynchronize();
+    int64_t bw_sum = 0, bw_max = 0, rows = 0, distinct = 0, vectors = 0;
+    if (e == hipSuccess)
+        e = pattern_features(p->rowptr, p->col, p->M, p->K, p->nnz, V, &bw_sum, &bw_max, &rows, &distinct, &vectors);
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        return fail(SPMM_E_OOM, "feature pass: device allocation failed");
+    }
+    if (e != hipSuccess) return fail_hip(e, "feature pass");
+    f.mean_bandwidth = rows > 0 ? (double)bw_sum / (double)rows : 0.0;
+    f.max_bandwidth = bw_max;
+    f.nnz_distinct = distinct;
+    f.nnz_vectors = vectors;
+    f.padding_ratio = vectors > 0 ? 1.0 - (double)distinct / ((double)vectors * (double)V) : 0.0;
+    *out = f;
+    return succeed();
+}
+
 SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
                              int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out) {
     if (E < 0 || M < 0 || K < 0) return fail(SPMM_E_INVALID_ARG, "negative size");

@@ -231,6 +231,43 @@ spmm_plan_t spmm_plan_transpose(spmm_plan_t plan, int scale);
 int spmm_max_backward(spmm_plan_t plan_t, const int64_t *argmax, const float *dC, float *dB, int64_t N,
                       void *stream);
 
+/*
+ * Sparse-matrix features of ParamSpMM section 5.1, Table 3 (size, degree
+ * distribution and data-locality features), for analysing a graph and
+ * choosing a layout; V is the width of ParamSpMM's vectorized blocking
+ * (section 3.1: blocks of V consecutive rows, rows V*g .. V*g+V-1).
+ *   n, n_nonempty, nnz, dmax : rows, rows with entries, stored entries,
+ *                              largest row degree
+ *   delta                    : n_nonempty / n
+ *   mean_deg, cv_deg         : nnz / n and the degree's population
+ *                              coefficient of variation over all rows
+ *   mean_deg_nonempty, cv_deg_nonempty : the same over non-empty rows
+ *   density                  : nnz / (n * K)
+ *   mean_bandwidth, max_bandwidth : a row's bandwidth is its largest minus
+ *                              its smallest column id (Table 3 footnote);
+ *                              mean over non-empty rows, and the maximum
+ *   nnz_distinct             : distinct (row, col) pairs
+ *   nnz_vectors              : nonzero vectors of V-row blocking: columns
+ *                              with at least one entry in a block, summed
+ *                              over blocks
+ *   padding_ratio            : eq. 2, 1 - nnz_distinct / (nnz_vectors * V)
+ *                              (0 when the matrix has no entries)
+ *   split_ratio, win_frac    : as in spmm_plan_info
+ * 1 <= V <= 64.  Synchronous: sorts a temporary copy of the pattern on the
+ * GPU (16 bytes per entry of device memory, freed before returning).
+ * Returns OK, INVALID_ARG, OOM or HIP.
+ */
+struct spmm_features {
+    int64_t n, n_nonempty, nnz, dmax;
+    double delta, mean_deg, mean_deg_nonempty, cv_deg, cv_deg_nonempty, density;
+    double mean_bandwidth;
+    int64_t max_bandwidth;
+    int64_t V, nnz_distinct, nnz_vectors;
+    double padding_ratio;
+    double split_ratio, win_frac;
+};
+int spmm_plan_features(spmm_plan_t plan, int64_t V, struct spmm_features *out);
+
 /* The calling thread's last status; copies its message (NUL-terminated,
  * truncated to cap bytes) into buf when buf != NULL and cap > 0. */
 int spmm_last_error(char *buf, int64_t cap);

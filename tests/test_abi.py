@@ -42,20 +42,22 @@ def test_header_compiles_as_c():
     assert r.returncode == 0, r.stderr
 
 
-def test_header_struct_layout_matches_binding():
+@pytest.mark.parametrize("struct,cls", [("spmm_plan_info", "_Info"), ("spmm_features", "_Features")])
+def test_header_struct_layout_matches_binding(struct, cls, tmp_path):
     import gnn_sparse_dense_amd as G
+    py = getattr(G, cls)
+    fields = [name for name, _ in py._fields_]
+    body = "".join(f'printf("%zu\\n", offsetof(struct {struct}, {f}));' for f in fields)
     src = ('#include <stdio.h>\n#include <stddef.h>\n#include "spmm.h"\n'
-           'int main(void){printf("%zu %zu %zu\\n", sizeof(struct spmm_plan_info),'
-           ' offsetof(struct spmm_plan_info, plan_ms), offsetof(struct spmm_plan_info, route_split));return 0;}\n')
-    tmp = os.path.join(ROOT, "_work")
-    os.makedirs(tmp, exist_ok=True)
-    c = os.path.join(tmp, "layout_probe.c")
-    exe = os.path.join(tmp, "layout_probe")
-    open(c, "w").write(src)
-    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
-    size, off_ms, off_split = map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split())
-    assert size == ctypes.sizeof(G._Info)
-    assert off_ms == G._Info.plan_ms.offset and off_split == G._Info.route_split.offset
+           f'int main(void){{printf("%zu\\n", sizeof(struct {struct}));{body}return 0;}}\n')
+    c = tmp_path / "layout_probe.c"
+    exe = tmp_path / "layout_probe"
+    c.write_text(src)
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()))
+    assert vals[0] == ctypes.sizeof(py), (struct, vals[0], ctypes.sizeof(py))
+    for f, off in zip(fields, vals[1:]):
+        assert off == getattr(py, f).offset, (struct, f)
 
 
 def _err():
