@@ -35,6 +35,7 @@ SPMM_OPT_NT_STORE = 8
 SPMM_OPT_TILES = 9
 SPMM_OPT_WINDOW = 10
 SPMM_OPT_MFMA = 11
+SPMM_OPT_VBLOCK = 12
 
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
@@ -69,6 +70,8 @@ class _Info(ctypes.Structure):
         ("win_frac", ctypes.c_double), ("tile_overflow", ctypes.c_int64),
         ("mfma_resid_nnz", ctypes.c_int64),
         ("mfma_tiles", ctypes.c_int32), ("route_mfma", ctypes.c_int32),
+        ("pair_vectors", ctypes.c_int64), ("pair_padding", ctypes.c_double),
+        ("pairs_built", ctypes.c_int32), ("route_pairs", ctypes.c_int32),
     ]
 
 

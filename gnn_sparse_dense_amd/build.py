@@ -29,6 +29,7 @@ SOURCES = [
     "transform.hip",
     "mfma_tile.hip",
     "features.hip",
+    "pair_kernel.hip",
 ]
 
 COMMON = [

@@ -102,11 +102,20 @@ void free_mfma(spmm_plan *p) {
     p->mfma_rnnz = 0;
 }
 
+void free_pairs(spmm_plan *p) {
+    dev_free(p->pair_prow);
+    dev_free(p->pair_col);
+    dev_free(p->pair_val);
+    p->pair_nvec = 0;
+    p->pair_unsorted = false;
+}
+
 void free_plan(spmm_plan *p) {
     if (!p) return;
     free_split(p);
     free_tiles(p);
     free_mfma(p);
+    free_pairs(p);
     dev_free(p->rowptr);
     dev_free(p->col);
     dev_free(p->val);
@@ -310,6 +319,35 @@ int build_mfma(spmm_plan *p) {
     return SPMM_OK;
 }
 
+// V = 2 panels (built when SPMM_OPT_VBLOCK is set).
+int build_pairs(spmm_plan *p) {
+    free_pairs(p);
+    if (p->K >= (int64_t(1) << 30)) return fail(SPMM_E_UNSUPPORTED, "V = 2 panels need K below 2^30");
+    const int64_t npanels = (p->M + 1) / 2;
+    int st = dev_alloc(&p->pair_prow, npanels + 1, "panel rowptr");
+    if (st) return st;
+    PairOutput out;
+    const hipError_t e = pair_build(p->rowptr, p->col, p->val, p->M, p->K, p->nnz, p->pair_prow, &out);
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        free_pairs(p);
+        return fail(SPMM_E_OOM, "V = 2 panel build: device allocation failed");
+    }
+    if (e != hipSuccess) {
+        free_pairs(p);
+        return fail_hip(e, "V = 2 panel build");
+    }
+    p->pair_col = out.pcol;
+    p->pair_val = out.pval;
+    p->pair_nvec = out.nvec;
+    p->pair_unsorted = out.unsorted != 0;
+    return SPMM_OK;
+}
+
+double pair_padding(const spmm_plan *p) {
+    return p->pair_nvec > 0 ? 1.0 - (double)p->nnz / (2.0 * (double)p->pair_nvec) : 0.0;
+}
+
 int pow2_ceil(int64_t x) {
     int g = 1;
     while (g < x && g < 64) g <<= 1;
@@ -374,6 +412,19 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
     // fp16 community tiles, when the caller asked for them
     r.mfma = p->opt_mfma == 1 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
+    // V = 2 panels, when built: by padding share (ParamSpMM's PR for V), or forced
+    r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock > 0 &&
+              (reduce != SPMM_MAX || !p->pair_unsorted) &&
+              (p->opt_vblock == 2 || (!p->split && pair_padding(p) <= kPairMaxPadding));
+    if (r.pairs) {
+        r.vec = vec == 4 ? 4 : 1;
+        const int64_t Wp = (N + r.vec - 1) / r.vec;
+        r.lanes = p->opt_lanes ? p->opt_lanes : std::min(64, std::max(4, pow2_ceil(Wp)));
+        r.coarsen = 1;
+        r.slices = (int)((Wp + r.lanes - 1) / r.lanes);
+        r.tiled = r.compact = r.window = r.split = false;
+        return r;
+    }
     if (r.window || r.mfma) {
         r.vec = 4;
         r.lanes = kWinCols / 4;
@@ -673,6 +724,22 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
             return succeed();
+        case SPMM_OPT_VBLOCK: {
+            if (value < 0 || value > 2) return fail(SPMM_E_INVALID_ARG, "vblock must be 0, 1 or 2");
+            const hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail_hip(e, "synchronise before changing the V = 2 panels");
+            p->opt_vblock = 0;
+            if (value == 0) {
+                free_pairs(p);
+                return succeed();
+            }
+            if (!p->pair_prow) {
+                const int st = build_pairs(p);
+                if (st) return st;
+            }
+            p->opt_vblock = (int)value;
+            return succeed();
+        }
         case SPMM_OPT_MFMA: {
             if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "mfma must be 0 or 1");
             const hipError_t e = hipDeviceSynchronize();
@@ -738,6 +805,10 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.mfma_resid_nnz = p->mfma_tiles ? p->mfma_rnnz : 0;
     info.mfma_tiles = p->mfma_tiles ? 1 : 0;
     info.route_mfma = p->route.mfma ? 1 : 0;
+    info.pair_vectors = p->pair_prow ? p->pair_nvec : 0;
+    info.pair_padding = p->pair_prow ? pair_padding(p) : 0.0;
+    info.pairs_built = p->pair_prow ? (p->pair_unsorted ? 2 : 1) : 0;
+    info.route_pairs = p->route.pairs ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -840,6 +911,30 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
         ma.xcd_remap = r.xcd_remap;
         const hipError_t e = launch_mfma(ma, has_val, s);
         if (e != hipSuccess) return fail_hip(e, "fp16 tile kernel launch");
+        return succeed();
+    }
+    if (r.pairs) {
+        PairKernelFn pf = pair_kernel(r.lanes, r.vec, has_val, is_max);
+        if (!pf) return fail(SPMM_E_UNSUPPORTED, "no panel kernel for lanes=%d vec=%d", r.lanes, r.vec);
+        if (r.slices > 65535) return fail(SPMM_E_UNSUPPORTED, "N = %lld needs too many column slices", (long long)N);
+        p->route = r;
+        p->route_N = N;
+        PairArgs pa;
+        std::memset(&pa, 0, sizeof(pa));
+        pa.prow = p->pair_prow;
+        pa.pcol = p->pair_col;
+        pa.pval = p->pair_val;
+        pa.rowptr = p->rowptr;
+        pa.B = B;
+        pa.C = C;
+        pa.argmax = argmax;
+        pa.M = p->M;
+        pa.N = N;
+        pa.npanels = (p->M + 1) / 2;
+        pa.mean = reduce == SPMM_MEAN;
+        pa.xcd_remap = r.xcd_remap;
+        const hipError_t e = launch_pairs(pf, pa, r.lanes, r.slices, s);
+        if (e != hipSuccess) return fail_hip(e, "panel kernel launch");
         return succeed();
     }
     RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled, r.compact};

@@ -15,7 +15,12 @@ struct Route {
     bool compact = false;
     bool window = false;
     bool mfma = false;
+    bool pairs = false;
 };
+
+// V = 2 panels are used by default only up to this padding share of vector
+// slots (1 - nnz / (2 * vectors)).
+constexpr double kPairMaxPadding = 0.3;
 
 }  // namespace gspmm
 
@@ -46,9 +51,15 @@ struct spmm_plan {
     int *mfma_rowptr = nullptr, *mfma_col = nullptr;
     float *mfma_val = nullptr;
     int64_t mfma_rnnz = 0;
+    // V = 2 panels (built on request)
+    int *pair_prow = nullptr;
+    unsigned *pair_col = nullptr;
+    float *pair_val = nullptr;
+    int64_t pair_nvec = 0;
+    bool pair_unsorted = false;
     // options (-1 / 0 = automatic)
     int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
-    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = 0;
     // last routing decision
     int64_t route_N = 0;
     gspmm::Route route;

@@ -59,6 +59,18 @@ hipError_t mfma_write_residual(const int *rowptr, const int *col, const float *v
                                const int *rrowptr, int *rcol, float *rval, hipStream_t s);
 hipError_t launch_mfma(const MfmaArgs &a, bool has_val, hipStream_t s);
 
+// ---- V = 2 vectorized blocking (pair_kernel.hip) ----
+struct PairOutput {
+    unsigned *pcol;   // device, allocated by pair_build
+    float *pval;      // device, allocated when weighted
+    int nvec;         // nonzero vectors
+    int unsorted;     // some row is not stored with ascending columns
+};
+hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
+                      int *prow, PairOutput *out);
+PairKernelFn pair_kernel(int lanes, int vec, bool has_val, bool is_max);
+hipError_t launch_pairs(PairKernelFn fn, PairArgs a, int lanes, int slices, hipStream_t s);
+
 // ---- pattern features (features.hip) ----
 struct FeatureRecord {   // one per block, folded on the host in block order
     int64_t a, b, c;

@@ -71,9 +71,28 @@ enum spmm_option {
                                   holding row bounds + indexes               */
     SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
                                   1 on: stage each 256-row block of B in LDS  */
-    SPMM_OPT_MFMA = 11         /* 0 off (default), 1 on: fp16 matrix-core tiles
+    SPMM_OPT_MFMA = 11,        /* 0 off (default), 1 on: fp16 matrix-core tiles
                                   for community blocks, see below             */
+    SPMM_OPT_VBLOCK = 12       /* vectorized blocking V = 2, see below: 0 off
+                                  (default), 1 build, use when padding <= 0.3,
+                                  2 build, always use                          */
 };
+
+/*
+ * SPMM_OPT_VBLOCK (ParamSpMM section 3.1 vectorized blocking and section 4.2
+ * PCSR, with V = 2): setting 1 or 2 builds, synchronously, a panel copy of
+ * the matrix in which rows 2g and 2g+1 share one list of nonzero vectors (a
+ * column present in either row; a column stored k and m times in the two rows
+ * gives max(k, m) vectors), so each gather of a B row serves both rows.
+ * Vectors run in ascending column order: rows stored with ascending columns
+ * keep their stored order and give the same bits as without panels; other
+ * rows are summed in ascending column order (same fp32 contract, different
+ * rounding order), and MAX uses panels only when every row is stored with
+ * ascending columns (tie order).  Needs K < 2^30; memory 4 bytes per vector
+ * (+ 8 when weighted) + 4 per panel.  With 1, runs use the panels only when
+ * the padding share 1 - nnz / (2 * vectors) is at most 0.3; with 2, always.
+ * 0 frees them.  Split plans keep their own path unless the value is 2.
+ */
 
 /*
  * SPMM_OPT_MFMA = 1 (RA-SpMM, "Kernel families": a dense tile path for
@@ -120,6 +139,11 @@ struct spmm_plan_info {
                                     CSR of the fp16 tile path; 0 when unbuilt) */
     int32_t mfma_tiles;          /* 1 when the fp16 tiles are built           */
     int32_t route_mfma;          /* 1 when the last run used them             */
+    int64_t pair_vectors;        /* nonzero vectors of the V = 2 panels (0 when
+                                    unbuilt)                                  */
+    double pair_padding;         /* 1 - nnz / (2 * pair_vectors)              */
+    int32_t pairs_built;         /* 1 built, 2 built and some row unsorted     */
+    int32_t route_pairs;         /* 1 when the last run used the panels       */
 };
 
 /*

@@ -13,5 +13,6 @@ from .graphs import (  # noqa: F401
     make_features,
     random_csr,
     block_csr,
+    knn_line,
     csr_from_pairs,
 )

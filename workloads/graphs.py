@@ -366,3 +366,17 @@ def block_csr(rng: np.random.Generator, M: int, K: int, in_deg: float = 12.0, of
             col[a:b] = col[a:b][rng.permutation(b - a)]
     val = rng.random(nnz, dtype=np.float32) if weighted else None
     return Graph(name="block", M=M, K=K, rowptr=rowptr, col=col, val=val)
+
+
+def knn_line(M: int, k: int = 10) -> Graph:
+    """k-nearest-neighbour graph of M points on a line: row i holds the k/2
+    nearest points on each side (i - k/2 .. i + k/2 without i, clipped to
+    [0, M)), ascending, unweighted.  Adjacent rows share all but a few
+    neighbours: the locality that vectorized blocking exploits."""
+    h = k // 2
+    i = np.arange(M, dtype=np.int64)
+    offs = np.concatenate([np.arange(-h, 0), np.arange(1, h + 1)]).astype(np.int64)
+    cand = i[:, None] + offs[None, :]
+    keep = (cand >= 0) & (cand < M)
+    deg = keep.sum(axis=1).astype(np.int64)
+    return Graph(name="knn", M=M, K=M, rowptr=_rowptr_from_deg(deg), col=cand[keep], val=None)
