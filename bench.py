@@ -277,10 +277,45 @@ def reuse_result(r, reduce, steps, flush):
     if info["route_split"]:
         out["row_split"] = structure(G.SPMM_OPT_SPLIT_MODE, 0, -1)
     t0 = time.perf_counter()
-    G.spmm_plan_features(r.plan, 2)
+    feat = G.spmm_plan_features(r.plan, 2)
     out["features_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+    out["padding_ratio_V2"] = round(feat["padding_ratio"], 4)
+    out["mean_row_bandwidth"] = round(feat["mean_bandwidth"], 1)
     r.info = G.spmm_plan_info(r.plan)
     return out
+
+
+def vblock_result(steps, flush):
+    """Vectorized blocking V = 2 (ParamSpMM section 3.1) where it is meant to
+    pay: a k-nearest-neighbour graph of points on a line (M = K = 1,000,000,
+    k = 10, unweighted, B [1M, 64]), row kernels against two-row panels."""
+    import torch
+    import gnn_sparse_dense_amd as G
+    import workloads as W
+    g = W.knn_line(1_000_000, 10)
+    N = 64
+    dev = torch.device("cuda:0")
+    rp, cl = torch.from_numpy(g.rowptr).to(dev), torch.from_numpy(g.col).to(dev)
+    B = torch.from_numpy(W.make_features("road", g.K, N)).to(dev)
+    C = torch.empty((g.M, N), dtype=torch.float32, device=dev)
+    plan = G.spmm_plan_create(rp, cl, None, g.M, g.K)
+
+    def run():
+        G.spmm_run(plan, B, C, None, N, "sum", None)
+    t_rows = time_flushed(run, flush, steps)
+    t0 = time.perf_counter()
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_VBLOCK, 1)
+    build = (time.perf_counter() - t0) * 1e3
+    t_pan = time_flushed(run, flush, steps)
+    info = G.spmm_plan_info(plan)
+    G.spmm_plan_destroy(plan)
+    comp, _ = byte_model(g, N, "sum")
+    return {"workload": "kNN line M=K=1,000,000, k=10, unweighted, N=64, sum", "nnz": g.nnz,
+            "padding_ratio": round(info["pair_padding"], 4), "routed_to_panels": info["route_pairs"],
+            "ms_rows": round(t_rows, 5), "ms_panels": round(t_pan, 5), "speedup": round(t_rows / t_pan, 3),
+            "effective_GBps_panels": round(comp / (t_pan * 1e-3) / 1e9, 1),
+            "build_ms": round(build, 2),
+            "break_even_runs": round(build / (t_rows - t_pan), 1) if t_rows > t_pan else None}
 
 
 def router_sweep(r, reduce, steps, flush):
@@ -529,6 +564,7 @@ def main():
             torch.cuda.empty_cache()
         result["regimes"] = regimes
         result["reuse"] = reuse
+        result["vblock"] = vblock_result(min(args.steps, 50), flush)
         if backward:
             result["backward"] = backward
     else:
