@@ -52,6 +52,10 @@ class Oracle:
         lib.oracle_max_backward.restype = ctypes.c_int
         lib.oracle_features.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p]
         lib.oracle_features.restype = ctypes.c_int
+        lib.oracle_rcm.argtypes = [_p, _p, _i64, _p]
+        lib.oracle_rcm.restype = ctypes.c_int
+        lib.oracle_permute.argtypes = [_p, _p, _p, _i64, _p, _p, _p, _p]
+        lib.oracle_permute.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -171,6 +175,27 @@ class Oracle:
         out.update({k: float(v) for k, v in zip(names_d, dbl)})
         out["V"] = int(V)
         return out
+
+    def rcm(self, rowptr, col, M):
+        """Reverse Cuthill-McKee permutation (perm[i] = node at position i)."""
+        rowptr, col, _ = self._csr(rowptr, col, None)
+        perm = np.empty(M, np.int64)
+        if self.lib.oracle_rcm(_ptr(rowptr), _ptr(col), M, _ptr(perm)) != 0:
+            raise MemoryError("oracle_rcm")
+        return perm
+
+    def permute(self, rowptr, col, val, M, perm):
+        """CSR of P A P^T (see oracle_permute)."""
+        rowptr, col, val = self._csr(rowptr, col, val)
+        perm = np.ascontiguousarray(perm, dtype=np.int64)
+        nnz = int(rowptr[M])
+        rp = np.empty(M + 1, np.int64)
+        cp = np.empty(nnz, np.int64)
+        vp = None if val is None else np.empty(nnz, np.float32)
+        if self.lib.oracle_permute(_ptr(rowptr), _ptr(col), _ptr(val), M, _ptr(perm), _ptr(rp), _ptr(cp),
+                                   _ptr(vp)) != 0:
+            raise ValueError("perm is not a permutation of [0, M)")
+        return rp, cp, vp
 
 
 _default: Optional[Oracle] = None

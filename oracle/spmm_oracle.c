@@ -411,3 +411,146 @@ int oracle_features(const int64_t *rowptr, const int64_t *col, int64_t M, int64_
     dbl[7] = vectors > 0 ? 1.0 - (double)distinct / ((double)vectors * (double)V) : 0.0;
     return 0;
 }
+
+/*
+ * Locality reordering.  Reverse Cuthill-McKee (Cuthill and McKee, 1969; the
+ * reversal by George, 1971) of a square CSR matrix A [M, M], on the symmetric
+ * pattern of A + A^T: the neighbours of a node are the distinct other nodes
+ * it shares an entry with in either direction, its degree their count.
+ * Cuthill-McKee order: take nodes in ascending (degree, id) order; each one
+ * not yet placed starts a component; placing proceeds breadth-first, each
+ * placed node appending its unplaced neighbours in ascending (degree, id)
+ * order.  perm[i] = the node at position i of the reversed order.
+ * Returns 0, or -1 on an allocation failure.
+ */
+static const int64_t *g_deg;
+static int cmp_deg_id(const void *a, const void *b) {
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    if (g_deg[x] != g_deg[y]) return (g_deg[x] > g_deg[y]) - (g_deg[x] < g_deg[y]);
+    return (x > y) - (x < y);
+}
+
+int oracle_rcm(const int64_t *rowptr, const int64_t *col, int64_t M, int64_t *perm) {
+    int64_t nnz = M > 0 ? rowptr[M] : 0;
+    int64_t *cnt = (int64_t *)calloc((size_t)M + 1, sizeof(int64_t));
+    int64_t *adj = (int64_t *)malloc(sizeof(int64_t) * (size_t)(2 * nnz + 1));
+    int64_t *deg = (int64_t *)calloc((size_t)M + 1, sizeof(int64_t));
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M + 1));
+    int64_t *queue = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M + 1));
+    int64_t *start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M + 2));
+    char *placed = (char *)calloc((size_t)M + 1, 1);
+    if (!cnt || !adj || !deg || !order || !queue || !start || !placed) {
+        free(cnt); free(adj); free(deg); free(order); free(queue); free(start); free(placed);
+        return -1;
+    }
+    /* symmetric adjacency lists: both directions of every off-diagonal entry */
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p)
+            if (col[p] != i) {
+                cnt[i] += 1;
+                cnt[col[p]] += 1;
+            }
+    start[0] = 0;
+    for (int64_t i = 0; i < M; ++i) start[i + 1] = start[i] + cnt[i];
+    for (int64_t i = 0; i < M; ++i) cnt[i] = start[i];
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p)
+            if (col[p] != i) {
+                adj[cnt[i]++] = col[p];
+                adj[cnt[col[p]]++] = i;
+            }
+    /* distinct neighbours, ascending, compacted in place; degree = their count */
+    int64_t w = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t n = start[i + 1] - start[i];
+        int64_t *l = adj + start[i];
+        qsort(l, (size_t)n, sizeof(int64_t), cmp_i64);
+        int64_t b = w;
+        for (int64_t q = 0; q < n; ++q)
+            if (q == 0 || l[q] != l[q - 1]) adj[w++] = l[q];
+        start[i] = b;
+        deg[i] = w - b;
+    }
+    start[M] = w;
+    for (int64_t i = 0; i < M; ++i) order[i] = i;
+    g_deg = deg;
+    qsort(order, (size_t)M, sizeof(int64_t), cmp_deg_id);
+    int64_t head = 0, tail = 0;
+    for (int64_t s = 0; s < M; ++s) {
+        int64_t root = order[s];
+        if (placed[root]) continue;
+        placed[root] = 1;
+        queue[tail++] = root;
+        while (head < tail) {
+            int64_t u = queue[head++];
+            int64_t first = tail;
+            for (int64_t q = start[u]; q < start[u] + deg[u]; ++q) {
+                int64_t v = adj[q];
+                if (!placed[v]) {
+                    placed[v] = 1;
+                    queue[tail++] = v;
+                }
+            }
+            qsort(queue + first, (size_t)(tail - first), sizeof(int64_t), cmp_deg_id);
+        }
+    }
+    for (int64_t i = 0; i < M; ++i) perm[i] = queue[M - 1 - i];
+    free(cnt); free(adj); free(deg); free(order); free(queue); free(start); free(placed);
+    return 0;
+}
+
+/*
+ * P A P^T for a square CSR matrix and a permutation perm (perm[i] = the old
+ * node placed at i): new row i is old row perm[i] with every column c renamed
+ * to its new position inv[c]; each new row lists its entries by ascending new
+ * column, equal columns in stored order.  rowptr_p [M+1], col_p [nnz],
+ * val_p [nnz] (when val != NULL).  Returns 0, or -1 when perm is not a
+ * permutation of [0, M) or on an allocation failure.
+ */
+typedef struct {
+    int64_t c, p;
+} cp_pair;
+static int cmp_cp(const void *a, const void *b) {
+    const cp_pair *x = (const cp_pair *)a, *y = (const cp_pair *)b;
+    if (x->c != y->c) return (x->c > y->c) - (x->c < y->c);
+    return (x->p > y->p) - (x->p < y->p);
+}
+
+int oracle_permute(const int64_t *rowptr, const int64_t *col, const float *val, int64_t M,
+                   const int64_t *perm, int64_t *rowptr_p, int64_t *col_p, float *val_p) {
+    int64_t *inv = (int64_t *)malloc(sizeof(int64_t) * (size_t)(M + 1));
+    if (!inv) return -1;
+    for (int64_t i = 0; i < M; ++i) inv[i] = -1;
+    for (int64_t i = 0; i < M; ++i) {
+        if (perm[i] < 0 || perm[i] >= M || inv[perm[i]] != -1) {
+            free(inv);
+            return -1;
+        }
+        inv[perm[i]] = i;
+    }
+    int64_t longest = 1;
+    for (int64_t i = 0; i < M; ++i)
+        if (rowptr[i + 1] - rowptr[i] > longest) longest = rowptr[i + 1] - rowptr[i];
+    cp_pair *buf = (cp_pair *)malloc(sizeof(cp_pair) * (size_t)longest);
+    if (!buf) {
+        free(inv);
+        return -1;
+    }
+    rowptr_p[0] = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t o = perm[i], n = rowptr[o + 1] - rowptr[o];
+        for (int64_t q = 0; q < n; ++q) {
+            buf[q].c = inv[col[rowptr[o] + q]];
+            buf[q].p = rowptr[o] + q;
+        }
+        qsort(buf, (size_t)n, sizeof(cp_pair), cmp_cp);
+        for (int64_t q = 0; q < n; ++q) {
+            col_p[rowptr_p[i] + q] = buf[q].c;
+            if (val) val_p[rowptr_p[i] + q] = val[buf[q].p];
+        }
+        rowptr_p[i + 1] = rowptr_p[i] + n;
+    }
+    free(buf);
+    free(inv);
+    return 0;
+}

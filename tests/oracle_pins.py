@@ -454,9 +454,80 @@ def pin_features(orc):
     assert orc.features(same, np.array([1, 4, 6, 0, 5, 7, 2, 9, 3, 8]), 4, 10, 2)["padding_ratio"] == 0.5
 
 
+def _read_rcm_golden():
+    kv = {}
+    for line in open(os.path.join(GOLDEN, "rcm_hand.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            kv[k] = np.array(v, np.int64)
+    return kv
+
+
+def _check_cuthill_mckee(rowptr, col, M, perm):
+    """Verifies the defining properties of the (unreversed) Cuthill-McKee order
+    q = perm[::-1] on the symmetric pattern, independently of how it was built."""
+    assert np.array_equal(np.sort(perm), np.arange(M)), "not a permutation"
+    rows = np.repeat(np.arange(M), np.diff(rowptr))
+    off = rows != col
+    a, b = rows[off], col[off]
+    und = np.unique(np.concatenate([a * M + b, b * M + a])) if off.any() else np.zeros(0, np.int64)
+    nbr = [[] for _ in range(M)]
+    for k in und.tolist():
+        nbr[k // M].append(k % M)
+    deg = np.array([len(x) for x in nbr])
+    q = perm[::-1]
+    pos = np.empty(M, np.int64)
+    pos[q] = np.arange(M)
+    key = deg * (M + 1) + np.arange(M)                 # (degree, id) rank
+    parent = np.full(M, -1)
+    for t, v in enumerate(q.tolist()):
+        earlier = [pos[u] for u in nbr[v] if pos[u] < t]
+        if earlier:
+            parent[v] = min(earlier)
+        else:                                          # a component start: the smallest
+            rest = q[t:]                               # unplaced node in (degree, id) order
+            assert key[v] == key[rest].min(), f"start {v} is not the smallest remaining"
+    par = parent[q]
+    for t in range(1, M):
+        if par[t] >= 0 and par[t - 1] >= 0:
+            assert par[t] >= par[t - 1], "parents out of order"
+            if par[t] == par[t - 1]:
+                assert key[q[t]] > key[q[t - 1]], "siblings not in (degree, id) order"
+
+
+def pin_rcm(orc):
+    kv = _read_rcm_golden()
+    M = kv["rowptr"].size - 1
+    perm = orc.rcm(kv["rowptr"], kv["col"], M)
+    assert np.array_equal(perm, kv["perm"]), f"hand RCM: {perm}"
+    rp, cp, vp = orc.permute(kv["rowptr"], kv["col"], np.arange(1, 10, dtype=np.float32), M, kv["perm"])
+    assert np.array_equal(rp, kv["rowptr_p"]) and np.array_equal(cp, kv["col_p"])
+    assert np.array_equal(vp, kv["val_p"].astype(np.float32))
+    # a shuffled path: Cuthill-McKee from an end recovers bandwidth 1
+    rng = np.random.default_rng(61)
+    n = 300
+    lab = rng.permutation(n)
+    g = W.csr_from_pairs(n, lab[:-1], lab[1:])
+    p = orc.rcm(g[0], g[1], n)
+    rq, cq, _ = orc.permute(g[0], g[1], None, n, p)
+    assert np.abs(np.repeat(np.arange(n), np.diff(rq)) - cq).max() == 1
+    # defining properties on irregular graphs (several components, duplicates, self loops)
+    for seed in (62, 63):
+        r = np.random.default_rng(seed)
+        gr = W.random_csr(r, 400, 400, mean_deg=2.0, empty_frac=0.2, dup_frac=0.2, shuffle_rows=True)
+        pr = orc.rcm(gr.rowptr, gr.col, gr.M)
+        _check_cuthill_mckee(gr.rowptr, gr.col, gr.M, pr)
+        # P A P^T against dense indexing; rows ascending by new column
+        rq, cq, vq = orc.permute(gr.rowptr, gr.col, gr.val, gr.M, pr)
+        gq = W.Graph("p", gr.M, gr.M, rq, cq, vq)
+        assert np.array_equal(_dense(gq), _dense(gr)[np.ix_(pr, pr)])
+        for i in range(gr.M):
+            assert np.all(np.diff(cq[rq[i]:rq[i + 1]]) >= 0)
+
+
 ALL_PINS = [
     pin_dense_bruteforce, pin_scipy_product, pin_identity, pin_ones, pin_empty_rows,
     pin_max_numpy, pin_val_null_is_ones, pin_mean_sum_relation, pin_row_subset,
     pin_partition, pin_descriptors, pin_validate, pin_mac_gap, pin_tiny_config,
-    pin_coo_to_csr, pin_transpose, pin_max_backward, pin_features,
+    pin_coo_to_csr, pin_transpose, pin_max_backward, pin_features, pin_rcm,
 ]

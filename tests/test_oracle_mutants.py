@@ -33,8 +33,8 @@ MUTANTS = {
     "sample_variance": ("var = (M > 0) ? var / (double)M : 0.0;",
                         "var = (M > 1) ? var / (double)(M - 1) : 0.0;"),
     "gap_as_printed": ("if (tr == 0) return 0;", ""),
-    "validate_skips_last_row": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t p",
-                                "for (int64_t i = 0; i + 1 < M; ++i)\n        for (int64_t p"),
+    "validate_skips_last_row": ("for (int64_t i = 0; i < M; ++i)\n        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p)\n            if (col[p] < 0",
+                                "for (int64_t i = 0; i + 1 < M; ++i)\n        for (int64_t p = rowptr[i]; p < rowptr[i + 1]; ++p)\n            if (col[p] < 0"),
     "sumabs_signed": ("s += fabs(a * (double)B[col[p] * N + k]);", "s += a * (double)B[col[p] * N + k];"),
     "coo_unstable": ("int64_t p = cursor[row[e]]++;", "int64_t p = rowptr_out[row[e] + 1] - 1 - (cursor[row[e]]++ - rowptr_out[row[e]]);"),
     "transpose_scale_off": ("val_t[q] = scale ? a / (float)deg : a;", "val_t[q] = scale ? a / (float)(deg + 1) : a;"),
@@ -47,6 +47,14 @@ MUTANTS = {
                                            "1.0 - (double)nnz / ((double)vectors * (double)V)"),
     "features_block_skips_first_row": ("for (int64_t i = g * V; i < g * V + V && i < M; ++i)",
                                        "for (int64_t i = g * V + 1; i < g * V + V && i < M; ++i)"),
+    "rcm_not_reversed": ("for (int64_t i = 0; i < M; ++i) perm[i] = queue[M - 1 - i];",
+                         "for (int64_t i = 0; i < M; ++i) perm[i] = queue[i];"),
+    "rcm_children_unsorted": ("            qsort(queue + first, (size_t)(tail - first), sizeof(int64_t), cmp_deg_id);\n", ""),
+    "rcm_largest_degree_first": ("if (g_deg[x] != g_deg[y]) return (g_deg[x] > g_deg[y]) - (g_deg[x] < g_deg[y]);",
+                                 "if (g_deg[x] != g_deg[y]) return (g_deg[x] < g_deg[y]) - (g_deg[x] > g_deg[y]);"),
+    "rcm_degree_counts_duplicates": ("        deg[i] = w - b;", "        deg[i] = n;"),
+    "permute_columns_not_renamed": ("buf[q].c = inv[col[rowptr[o] + q]];", "buf[q].c = col[rowptr[o] + q];"),
+    "permute_rows_unsorted": ("        qsort(buf, (size_t)n, sizeof(cp_pair), cmp_cp);\n", ""),
 }
 
 
