@@ -37,10 +37,13 @@ SPMM_OPT_WINDOW = 10
 SPMM_OPT_MFMA = 11
 SPMM_OPT_VBLOCK = 12
 
+SPMM_REORDER_RCM = 1
+
 EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
     "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward", "spmm_plan_features",
+    "spmm_plan_reorder", "spmm_plan_permute",
 )
 
 
@@ -115,6 +118,10 @@ def _load() -> ctypes.CDLL:
     lib.spmm_coo_to_csr.restype = i32
     lib.spmm_plan_transpose.argtypes = [p, i32]
     lib.spmm_plan_transpose.restype = p
+    lib.spmm_plan_reorder.argtypes = [p, i32, p]
+    lib.spmm_plan_reorder.restype = i32
+    lib.spmm_plan_permute.argtypes = [p, p]
+    lib.spmm_plan_permute.restype = p
     lib.spmm_max_backward.argtypes = [p, p, p, p, i64, p]
     lib.spmm_max_backward.restype = i32
     return lib
@@ -231,6 +238,25 @@ def spmm_coo_to_csr(row, col, val, M: int, K: int):
 
 def spmm_plan_transpose(plan: int, scale: int = 0) -> int:
     h = _lib.spmm_plan_transpose(plan, int(scale))
+    if not h:
+        st, msg = spmm_last_error()
+        raise SpmmError(st, msg)
+    return h
+
+
+def spmm_plan_reorder(plan: int, method: int = 1):
+    """Reverse Cuthill-McKee permutation of a square plan as a device int64
+    tensor: perm[i] = the node placed at position i (synchronous)."""
+    import torch
+    M = spmm_plan_info(plan)["M"]
+    perm = torch.empty(M, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
+    _check(_lib.spmm_plan_reorder(plan, int(method), _addr(perm) if M else None))
+    return perm
+
+
+def spmm_plan_permute(plan: int, perm) -> int:
+    """Plan of P A P^T for a device int64 permutation (synchronous)."""
+    h = _lib.spmm_plan_permute(plan, _addr(perm) if perm is not None and perm.numel() else None)
     if not h:
         st, msg = spmm_last_error()
         raise SpmmError(st, msg)

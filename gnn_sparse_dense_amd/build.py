@@ -30,6 +30,7 @@ SOURCES = [
     "mfma_tile.hip",
     "features.hip",
     "pair_kernel.hip",
+    "reorder.hip",
 ]
 
 COMMON = [

@@ -1058,6 +1058,62 @@ SPMM_API int spmm_plan_features(spmm_plan_t p, int64_t V, struct spmm_features *
     return succeed();
 }
 
+SPMM_API int spmm_plan_reorder(spmm_plan_t p, int method, int64_t *perm) {
+    if (!p) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
+    if (method != SPMM_REORDER_RCM) return fail(SPMM_E_INVALID_ARG, "unknown reordering method %d", method);
+    if (p->M != p->K) return fail(SPMM_E_INVALID_ARG, "reordering needs a square matrix (M = %lld, K = %lld)",
+                                  (long long)p->M, (long long)p->K);
+    if (p->M == 0) return succeed();
+    if (!is_device_ptr(perm)) return fail(SPMM_E_INVALID_ARG, "perm is NULL or not device memory");
+    DeviceGuard dg(p->device);
+    hipError_t e = hipDeviceSynchronize();
+    int64_t levels = 0;
+    if (e == hipSuccess) e = rcm_order(p->rowptr, p->col, p->M, p->nnz, perm, &levels);
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        return fail(SPMM_E_OOM, "reordering: device allocation failed");
+    }
+    if (e != hipSuccess) return fail_hip(e, "reordering");
+    return succeed();
+}
+
+SPMM_API spmm_plan_t spmm_plan_permute(spmm_plan_t p, const int64_t *perm) {
+    if (!p) {
+        fail(SPMM_E_INVALID_ARG, "plan is NULL");
+        return nullptr;
+    }
+    if (p->M != p->K) {
+        fail(SPMM_E_INVALID_ARG, "permuting needs a square matrix");
+        return nullptr;
+    }
+    if (p->M > 0 && !is_device_ptr(perm)) {
+        fail(SPMM_E_INVALID_ARG, "perm is NULL or not device memory");
+        return nullptr;
+    }
+    DeviceGuard dg(p->device);
+    int64_t *rp = nullptr, *cl = nullptr;
+    float *vl = nullptr;
+    if (dev_alloc(&rp, p->M + 1, "permuted rowptr") || dev_alloc(&cl, p->nnz, "permuted col") ||
+        (p->val && dev_alloc(&vl, p->nnz, "permuted val"))) {
+        dev_free(rp);
+        dev_free(cl);
+        dev_free(vl);
+        return nullptr;
+    }
+    bool bad = false;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && p->M > 0) e = permute_csr(p->rowptr, p->col, p->val, p->M, p->nnz, perm, rp, cl, vl, &bad);
+    else if (e == hipSuccess) e = hipMemset(rp, 0, sizeof(int64_t));
+    spmm_plan_t t = nullptr;
+    if (e != hipSuccess) fail_hip(e, "permute");
+    else if (bad) fail(SPMM_E_INVALID_ARG, "perm is not a permutation of [0, %lld)", (long long)p->M);
+    else t = spmm_plan_create(rp, cl, vl, p->M, p->K);
+    dev_free(rp);
+    dev_free(cl);
+    dev_free(vl);
+    return t;
+}
+
 SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
                              int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out) {
     if (E < 0 || M < 0 || K < 0) return fail(SPMM_E_INVALID_ARG, "negative size");

@@ -292,6 +292,36 @@ struct spmm_features {
 };
 int spmm_plan_features(spmm_plan_t plan, int64_t V, struct spmm_features *out);
 
+/* Reordering methods for spmm_plan_reorder. */
+enum spmm_reorder_method { SPMM_REORDER_RCM = 1 };
+
+/*
+ * Locality reordering (ParamSpMM section 4.4: a reordering that puts nodes
+ * with shared neighbours close together complements the kernels and is
+ * amortised over the reuses of the graph).  SPMM_REORDER_RCM: reverse
+ * Cuthill-McKee (Cuthill and McKee 1969; reversal by George 1971) on the
+ * symmetric pattern of A + A^T (distinct neighbours, self loops ignored):
+ * nodes taken in ascending (degree, id) order start components, each placed
+ * breadth first with every node appending its unplaced neighbours in
+ * ascending (degree, id) order; the order is then reversed.  Deterministic.
+ *   perm : device int64 [M], written: perm[i] = the node placed at position i.
+ * Needs a square plan (M == K).  Synchronous; allocates and frees temporary
+ * device memory (about 40 bytes per entry).  Returns OK, INVALID_ARG
+ * (non-square plan, unknown method, bad pointer), OOM or HIP.
+ */
+int spmm_plan_reorder(spmm_plan_t plan, int method, int64_t *perm);
+
+/*
+ * Plan of P A P^T for a square plan and a permutation perm (device int64
+ * [M], perm[i] = the old node placed at position i): new row i is old row
+ * perm[i] with every column c renamed to its new position; each new row lists
+ * its entries by ascending new column, equal columns in stored order.  Use it
+ * with B' = P B (row i of B' = row perm[i] of B); then C' = P C.
+ * Synchronous; returns a new plan (destroy it separately) or NULL: INVALID_ARG
+ * when perm is not a permutation of [0, M) or the plan is not square.
+ */
+spmm_plan_t spmm_plan_permute(spmm_plan_t plan, const int64_t *perm);
+
 /* The calling thread's last status; copies its message (NUL-terminated,
  * truncated to cap bytes) into buf when buf != NULL and cap > 0. */
 int spmm_last_error(char *buf, int64_t cap);

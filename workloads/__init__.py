@@ -14,5 +14,6 @@ from .graphs import (  # noqa: F401
     random_csr,
     block_csr,
     knn_line,
+    relabel,
     csr_from_pairs,
 )

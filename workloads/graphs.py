@@ -380,3 +380,20 @@ def knn_line(M: int, k: int = 10) -> Graph:
     keep = (cand >= 0) & (cand < M)
     deg = keep.sum(axis=1).astype(np.int64)
     return Graph(name="knn", M=M, K=M, rowptr=_rowptr_from_deg(deg), col=cand[keep], val=None)
+
+
+def relabel(g: Graph, seed: int) -> Graph:
+    """The same graph under uniformly random node ids (square graphs): node u
+    becomes pi[u] for a seeded permutation pi; every row keeps its entries in
+    their stored order.  Hides the locality of the original numbering."""
+    assert g.M == g.K
+    rng = np.random.default_rng(seed)
+    pi = rng.permutation(g.M).astype(np.int64)
+    inv = np.empty_like(pi)
+    inv[pi] = np.arange(g.M)
+    deg = g.degrees()[inv]                      # new row r is old row inv[r]
+    rowptr = _rowptr_from_deg(deg)
+    src = _concat_ranges(g.rowptr[:-1][inv], deg)
+    col = pi[g.col[src]]
+    val = None if g.val is None else g.val[src]
+    return Graph(name=g.name + "-relabelled", M=g.M, K=g.K, rowptr=rowptr, col=col, val=val)
