@@ -318,6 +318,39 @@ def vblock_result(steps, flush):
             "break_even_runs": round(build / (t_rows - t_pan), 1) if t_rows > t_pan else None}
 
 
+def reorder_result(steps, flush):
+    """Locality reordering (reverse Cuthill-McKee, then P A P^T) on the road
+    graph under random node ids: the kernels' time before and after, the
+    one-time cost, and the runs that repay it."""
+    import torch
+    import gnn_sparse_dense_amd as G
+    import workloads as W
+    g = W.relabel(W.make_graph("road"), 74)
+    N = 64
+    dev = torch.device("cuda:0")
+    rp, cl = torch.from_numpy(g.rowptr).to(dev), torch.from_numpy(g.col).to(dev)
+    B = torch.from_numpy(W.make_features("road", g.K, N)).to(dev)
+    C = torch.empty((g.M, N), dtype=torch.float32, device=dev)
+    plan = G.spmm_plan_create(rp, cl, None, g.M, g.K)
+    t_before = time_flushed(lambda: G.spmm_run(plan, B, C, None, N, "sum", None), flush, steps)
+    t0 = time.perf_counter()
+    perm = G.spmm_plan_reorder(plan)
+    torch.cuda.synchronize()
+    t_rcm = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    pp = G.spmm_plan_permute(plan, perm)
+    t_perm = (time.perf_counter() - t0) * 1e3
+    Bp = B[perm].contiguous()
+    t_after = time_flushed(lambda: G.spmm_run(pp, Bp, C, None, N, "sum", None), flush, steps)
+    G.spmm_plan_destroy(pp)
+    G.spmm_plan_destroy(plan)
+    once = t_rcm + t_perm
+    return {"workload": "road-like graph under random node ids (M=K=1,000,000, N=64, sum)",
+            "ms_before": round(t_before, 5), "ms_after": round(t_after, 5),
+            "speedup": round(t_before / t_after, 3), "rcm_ms": round(t_rcm, 1), "permute_ms": round(t_perm, 1),
+            "break_even_runs": round(once / (t_before - t_after)) if t_before > t_after else None}
+
+
 def router_sweep(r, reduce, steps, flush):
     """Router evidence (RA-SpMM abstract: the router's speed as a fraction of the
     best of all variants, per configuration): the router's choice against every
@@ -565,6 +598,7 @@ def main():
         result["regimes"] = regimes
         result["reuse"] = reuse
         result["vblock"] = vblock_result(min(args.steps, 50), flush)
+        result["reorder"] = reorder_result(min(args.steps, 50), flush)
         if backward:
             result["backward"] = backward
     else:
