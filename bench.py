@@ -359,7 +359,8 @@ def router_sweep(r, reduce, steps, flush):
     looser contract and are listed apart, never counted as the best."""
     G = r.G
     auto = {G.SPMM_OPT_LANES: 0, G.SPMM_OPT_COARSEN: 0, G.SPMM_OPT_TILES: -1, G.SPMM_OPT_WINDOW: -1,
-            G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1}
+            G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1,
+            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: 0}
     variants = [("router", {})]
     variants += [(f"lanes={g} coarsen={f}", {G.SPMM_OPT_LANES: g, G.SPMM_OPT_COARSEN: f})
                  for g in (4, 8, 16, 32, 64) for f in (1, 2)]
@@ -367,7 +368,8 @@ def router_sweep(r, reduce, steps, flush):
                  ("row tiles wide", {G.SPMM_OPT_TILES: 2}), ("window on", {G.SPMM_OPT_WINDOW: 1}),
                  ("window off", {G.SPMM_OPT_WINDOW: 0}), ("XCD remap off", {G.SPMM_OPT_XCD_REMAP: 0}),
                  ("non-temporal C stores", {G.SPMM_OPT_NT_STORE: 1}), ("split on", {G.SPMM_OPT_SPLIT_MODE: 1}),
-                 ("split off", {G.SPMM_OPT_SPLIT_MODE: 0})]
+                 ("split off", {G.SPMM_OPT_SPLIT_MODE: 0}), ("merge-path balancing", {G.SPMM_OPT_BALANCE: 1}),
+                 ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2})]
     rows = []
     for label, opts in variants:
         entry = {"variant": label}
@@ -376,7 +378,8 @@ def router_sweep(r, reduce, steps, flush):
                 G.spmm_plan_set_option(r.plan, k, v)
             ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
             info = G.spmm_plan_info(r.plan)
-            entry.update({"ms": round(ms, 5), "path": kernel_family(info),
+            entry.update({"ms": round(ms, 5), "path": kernel_family(info) + ("+merge" if info["route_merge"] else "")
+                          + ("+panels" if info["route_pairs"] else ""),
                           "route": [info["route_lanes"], info["route_vec"], info["route_coarsen"],
                                     info["route_slices"], info["route_xcd_remap"], info["route_nt_store"],
                                     info["route_split"], info["route_tiled"] * info["tiles"],

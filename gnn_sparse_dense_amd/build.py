@@ -31,6 +31,7 @@ SOURCES = [
     "features.hip",
     "pair_kernel.hip",
     "reorder.hip",
+    "merge_kernel.hip",
 ]
 
 COMMON = [

@@ -110,8 +110,18 @@ void free_pairs(spmm_plan *p) {
     p->pair_unsorted = false;
 }
 
+void free_merge(spmm_plan *p) {
+    dev_free(p->merge_seg_row);
+    dev_free(p->merge_seg_entry);
+    dev_free(p->merge_carry_row);
+    dev_free(p->merge_carry_arg);
+    dev_free(p->merge_carry);
+    p->merge_nseg = 0;
+}
+
 void free_plan(spmm_plan *p) {
     if (!p) return;
+    free_merge(p);
     free_split(p);
     free_tiles(p);
     free_mfma(p);
@@ -344,6 +354,29 @@ int build_pairs(spmm_plan *p) {
     return SPMM_OK;
 }
 
+// Merge-path segments (built when SPMM_OPT_BALANCE is 1).
+int build_merge(spmm_plan *p) {
+    free_merge(p);
+    if (p->M + p->nnz >= INT_MAX) return fail(SPMM_E_UNSUPPORTED, "merge path needs M + nnz below 2^31");
+    const int64_t nseg = (p->M + p->nnz + kMergeItems - 1) / kMergeItems;
+    int st;
+    if ((st = dev_alloc(&p->merge_seg_row, nseg + 1, "merge rows")) ||
+        (st = dev_alloc(&p->merge_seg_entry, nseg + 1, "merge entries")) ||
+        (st = dev_alloc(&p->merge_carry_row, nseg, "merge carry rows")) ||
+        (st = dev_alloc(&p->merge_carry, nseg * kPartialWidth, "merge carries")) ||
+        (st = dev_alloc(&p->merge_carry_arg, nseg * kPartialWidth, "merge carry argmax"))) {
+        free_merge(p);
+        return st;
+    }
+    const hipError_t e = merge_build(p->rowptr, p->M, p->nnz, nseg, p->merge_seg_row, p->merge_seg_entry);
+    if (e != hipSuccess) {
+        free_merge(p);
+        return fail_hip(e, "merge path build");
+    }
+    p->merge_nseg = nseg;
+    return SPMM_OK;
+}
+
 double pair_padding(const spmm_plan *p) {
     return p->pair_nvec > 0 ? 1.0 - (double)p->nnz / (2.0 * (double)p->pair_nvec) : 0.0;
 }
@@ -412,6 +445,20 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
     // fp16 community tiles, when the caller asked for them
     r.mfma = p->opt_mfma == 1 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
+    // merge-path balancing, when the caller chose it
+    r.merge = !r.mfma && p->opt_balance == 1 && p->merge_seg_row != nullptr;
+    if (r.merge) {
+        const bool al4 = N % 4 == 0 && a16, al2 = N % 2 == 0 && a8;
+        // skewed graphs: 64-column slices (each pass over the graph touches a
+        // quarter of a 256-byte B row), as for the row kernels
+        r.vec = p->cv_deg > 1.0 ? 1 : (N >= 256 && al4) ? 4 : (N >= 128 && al2) ? 2 : 1;
+        r.lanes = 64;
+        r.coarsen = 1;
+        const int64_t w = std::min<int64_t>(N, kPartialWidth);
+        r.slices = (int)((w + 64 * r.vec - 1) / (64 * r.vec));
+        r.tiled = r.compact = r.window = r.split = r.pairs = false;
+        return r;
+    }
     // V = 2 panels, when built: by padding share (ParamSpMM's PR for V), or forced
     r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock > 0 &&
               (reduce != SPMM_MAX || !p->pair_unsorted) &&
@@ -724,6 +771,22 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
             return succeed();
+        case SPMM_OPT_BALANCE: {
+            if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "balance must be 0 or 1");
+            const hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail_hip(e, "synchronise before changing the balancing");
+            p->opt_balance = 0;
+            if (value == 0) {
+                free_merge(p);
+                return succeed();
+            }
+            if (!p->merge_seg_row) {
+                const int st = build_merge(p);
+                if (st) return st;
+            }
+            p->opt_balance = 1;
+            return succeed();
+        }
         case SPMM_OPT_VBLOCK: {
             if (value < 0 || value > 2) return fail(SPMM_E_INVALID_ARG, "vblock must be 0, 1 or 2");
             const hipError_t e = hipDeviceSynchronize();
@@ -809,6 +872,8 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.pair_padding = p->pair_prow ? pair_padding(p) : 0.0;
     info.pairs_built = p->pair_prow ? (p->pair_unsorted ? 2 : 1) : 0;
     info.route_pairs = p->route.pairs ? 1 : 0;
+    info.merge_segments = p->merge_seg_row ? p->merge_nseg : 0;
+    info.route_merge = p->route.merge ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -911,6 +976,36 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
         ma.xcd_remap = r.xcd_remap;
         const hipError_t e = launch_mfma(ma, has_val, s);
         if (e != hipSuccess) return fail_hip(e, "fp16 tile kernel launch");
+        return succeed();
+    }
+    if (r.merge) {
+        MergeKernelFn mf = merge_kernel(r.vec, has_val, is_max);
+        if (!mf) return fail(SPMM_E_UNSUPPORTED, "no merge kernel for vec=%d", r.vec);
+        p->route = r;
+        p->route_N = N;
+        MergeArgs ma;
+        std::memset(&ma, 0, sizeof(ma));
+        ma.rowptr = p->rowptr;
+        ma.col = p->col;
+        ma.val = p->val;
+        ma.seg_row = p->merge_seg_row;
+        ma.seg_entry = p->merge_seg_entry;
+        ma.B = B;
+        ma.C = C;
+        ma.argmax = argmax;
+        ma.carry = p->merge_carry;
+        ma.carry_arg = p->merge_carry_arg;
+        ma.carry_row = p->merge_carry_row;
+        ma.M = p->M;
+        ma.N = N;
+        ma.nseg = p->merge_nseg;
+        ma.mean = reduce == SPMM_MEAN;
+        for (int64_t w0 = 0; w0 < N; w0 += kPartialWidth) {
+            ma.c_begin = w0;
+            ma.c_end = std::min<int64_t>(N, w0 + kPartialWidth);
+            const hipError_t e = launch_merge(mf, ma, r.vec, is_max, s);
+            if (e != hipSuccess) return fail_hip(e, "merge kernel launch");
+        }
         return succeed();
     }
     if (r.pairs) {

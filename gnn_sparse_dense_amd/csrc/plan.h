@@ -16,6 +16,7 @@ struct Route {
     bool window = false;
     bool mfma = false;
     bool pairs = false;
+    bool merge = false;
 };
 
 // V = 2 panels are used by default only up to this padding share of vector
@@ -57,9 +58,13 @@ struct spmm_plan {
     float *pair_val = nullptr;
     int64_t pair_nvec = 0;
     bool pair_unsorted = false;
+    // merge-path segments (built on request)
+    int *merge_seg_row = nullptr, *merge_seg_entry = nullptr, *merge_carry_row = nullptr, *merge_carry_arg = nullptr;
+    float *merge_carry = nullptr;
+    int64_t merge_nseg = 0;
     // options (-1 / 0 = automatic)
     int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
-    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = 0;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = 0, opt_balance = 0;
     // last routing decision
     int64_t route_N = 0;
     gspmm::Route route;

@@ -71,6 +71,11 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
 PairKernelFn pair_kernel(int lanes, int vec, bool has_val, bool is_max);
 hipError_t launch_pairs(PairKernelFn fn, PairArgs a, int lanes, int slices, hipStream_t s);
 
+// ---- merge-path balancing (merge_kernel.hip) ----
+hipError_t merge_build(const int *rowptr, int64_t M, int64_t nnz, int64_t nseg, int *seg_row, int *seg_entry);
+MergeKernelFn merge_kernel(int vec, bool has_val, bool is_max);
+hipError_t launch_merge(MergeKernelFn fn, const MergeArgs &a, int vec, bool is_max, hipStream_t s);
+
 // ---- locality reordering (reorder.hip) ----
 hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, int64_t *perm, int64_t *levels);
 hipError_t permute_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t nnz,

@@ -73,10 +73,25 @@ enum spmm_option {
                                   1 on: stage each 256-row block of B in LDS  */
     SPMM_OPT_MFMA = 11,        /* 0 off (default), 1 on: fp16 matrix-core tiles
                                   for community blocks, see below             */
-    SPMM_OPT_VBLOCK = 12       /* vectorized blocking V = 2, see below: 0 off
+    SPMM_OPT_VBLOCK = 12,      /* vectorized blocking V = 2, see below: 0 off
                                   (default), 1 build, use when padding <= 0.3,
                                   2 build, always use                          */
+    SPMM_OPT_BALANCE = 13      /* load balance: 0 row split of heavy rows
+                                  (default), 1 merge path, see below          */
 };
+
+/*
+ * SPMM_OPT_BALANCE = 1 (merge-based balancing, RA-SpMM related work: the work
+ * is partitioned along a virtual merge path over the CSR stream): setting it
+ * builds, synchronously, the start coordinates of segments of 512 items (row
+ * ends plus entries) of the merge of rowptr[1..M] with the entry indices,
+ * and carry buffers of 2 KB per segment.  Later runs give every wave one
+ * segment; rows that end inside a segment they started in are summed in
+ * stored order (the same bits as the row kernels), rows spread over several
+ * segments are summed piece by piece, pieces folded in order (same fp32
+ * contract, deterministic); max ties still go to the first entry.  Setting 0
+ * frees the segments and returns to the row split.
+ */
 
 /*
  * SPMM_OPT_VBLOCK (ParamSpMM section 3.1 vectorized blocking and section 4.2
@@ -144,6 +159,9 @@ struct spmm_plan_info {
     double pair_padding;         /* 1 - nnz / (2 * pair_vectors)              */
     int32_t pairs_built;         /* 1 built, 2 built and some row unsorted     */
     int32_t route_pairs;         /* 1 when the last run used the panels       */
+    int64_t merge_segments;      /* merge-path segments (0 when unbuilt)      */
+    int32_t route_merge;         /* 1 when the last run used them             */
+    int32_t reserved;
 };
 
 /*
