@@ -229,23 +229,27 @@ def regime_result(r, reduce, steps, warmup, flush):
 
 
 def tile_results(r, steps, warmup, flush, fp32_results=()):
-    """The same regime on the fp16 matrix-core tiles (looser fp16 contract),
-    for graphs the router sends to the community window kernel."""
-    t0 = time.perf_counter()
-    r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 1)
-    build_ms = (time.perf_counter() - t0) * 1e3
+    """The same regime on the matrix-core community tiles, for graphs the
+    router sends to the community window kernel: fp16 tiles (their own looser
+    contract) and split fp16 tiles (the fp32 contract), each with its build
+    time and the runs that repay it against the fp32 route."""
     out = []
-    for red in r.w.reduces:
-        if red == "max":
-            continue
-        res = regime_result(r, red, steps, warmup, flush)
-        res["tile_build_ms"] = round(build_ms, 2)
-        fp32 = [x for x in fp32_results if x["reduce"] == red]
-        if fp32:
-            saving = fp32[0]["ms_flushed_median"] - res["ms_flushed_median"]
-            res["break_even_runs"] = round(build_ms / saving, 1) if saving > 0 else None
-        res["mfma_resid_nnz"] = r.info["mfma_resid_nnz"]
-        out.append(res)
+    for mode, contract in ((1, "fp16 tiles: 2e-3 * sum|a*b| + 1e-4"), (2, "split fp16 tiles: fp32 tolerance")):
+        t0 = time.perf_counter()
+        r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, mode)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        for red in r.w.reduces:
+            if red == "max":
+                continue
+            res = regime_result(r, red, steps, warmup, flush)
+            res["contract"] = contract
+            res["tile_build_ms"] = round(build_ms, 2)
+            fp32 = [x for x in fp32_results if x["reduce"] == red]
+            if fp32:
+                saving = fp32[0]["ms_flushed_median"] - res["ms_flushed_median"]
+                res["break_even_runs"] = round(build_ms / saving, 1) if saving > 0 else None
+            res["mfma_resid_nnz"] = r.info["mfma_resid_nnz"]
+            out.append(res)
     r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 0)
     r.info = r.G.spmm_plan_info(r.plan)
     return out

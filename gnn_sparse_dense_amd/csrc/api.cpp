@@ -96,6 +96,8 @@ void free_tiles(spmm_plan *p) {
 
 void free_mfma(spmm_plan *p) {
     dev_free(p->mfma_tiles);
+    dev_free(p->mfma_tiles_lo);
+    dev_free(p->mfma_tile_exp);
     dev_free(p->mfma_rowptr);
     dev_free(p->mfma_col);
     dev_free(p->mfma_val);
@@ -289,19 +291,22 @@ int build_tiles(spmm_plan *p) {
 }
 
 // fp16 community tiles and the residual CSR (built when SPMM_OPT_MFMA is set).
-int build_mfma(spmm_plan *p) {
+int build_mfma(spmm_plan *p, bool split) {
     free_mfma(p);
     if (p->M + 1 > INT_MAX) return fail(SPMM_E_UNSUPPORTED, "fp16 tiles need M + 1 below 2^31");
     const int64_t ntiles = (p->M + kWinRows - 1) / kWinRows;
     int *d_flag = nullptr;
     int st;
     if ((st = dev_alloc(&p->mfma_tiles, ntiles * 8 * kMfmaKSteps * 64, "fp16 community tiles")) ||
+        (split && (st = dev_alloc(&p->mfma_tiles_lo, ntiles * 8 * kMfmaKSteps * 64, "fp16 low halves"))) ||
+        (split && (st = dev_alloc(&p->mfma_tile_exp, ntiles, "tile exponents"))) ||
         (st = dev_alloc(&p->mfma_rowptr, p->M + 1, "residual rowptr")) || (st = dev_alloc(&d_flag, 1, "range flag"))) {
         free_mfma(p);
         dev_free(d_flag);
         return st;
     }
-    hipError_t e = mfma_build_tiles(p->rowptr, p->col, p->val, p->M, p->mfma_tiles, ntiles, p->mfma_rowptr, d_flag,
+    hipError_t e = mfma_build_tiles(p->rowptr, p->col, p->val, p->M, p->mfma_tiles, p->mfma_tiles_lo,
+                                    p->mfma_tile_exp, ntiles, p->mfma_rowptr, d_flag,
                                     nullptr);
     int flag = 0, rnnz = 0;
     if (e == hipSuccess) e = hipMemcpy(&flag, d_flag, sizeof(int), hipMemcpyDeviceToHost);
@@ -313,7 +318,8 @@ int build_mfma(spmm_plan *p) {
     }
     if (flag) {
         free_mfma(p);
-        return fail(SPMM_E_UNSUPPORTED, "an in-block sum of weights is outside the fp16 range (or not finite)");
+        return fail(SPMM_E_UNSUPPORTED, split ? "an in-block sum of weights is not finite"
+                                               : "an in-block sum of weights is outside the fp16 range (or not finite)");
     }
     p->mfma_rnnz = rnnz;
     if ((st = dev_alloc(&p->mfma_col, rnnz, "residual col")) ||
@@ -444,7 +450,7 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 &&
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
     // fp16 community tiles, when the caller asked for them
-    r.mfma = p->opt_mfma == 1 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
+    r.mfma = p->opt_mfma > 0 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
     // merge-path balancing, when the caller chose it
     r.merge = !r.mfma && p->opt_balance == 1 && p->merge_seg_row != nullptr;
     if (r.merge) {
@@ -804,7 +810,7 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             return succeed();
         }
         case SPMM_OPT_MFMA: {
-            if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "mfma must be 0 or 1");
+            if (value < 0 || value > 2) return fail(SPMM_E_INVALID_ARG, "mfma must be 0, 1 or 2");
             const hipError_t e = hipDeviceSynchronize();
             if (e != hipSuccess) return fail_hip(e, "synchronise before changing the fp16 tiles");
             p->opt_mfma = 0;
@@ -812,11 +818,11 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
                 free_mfma(p);
                 return succeed();
             }
-            if (!p->mfma_tiles) {
-                const int st = build_mfma(p);
+            if (!p->mfma_tiles || (p->mfma_tiles_lo != nullptr) != (value == 2)) {
+                const int st = build_mfma(p, value == 2);
                 if (st) return st;
             }
-            p->opt_mfma = 1;
+            p->opt_mfma = (int)value;
             return succeed();
         }
 
@@ -866,7 +872,7 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_window = p->route.window ? 1 : 0;
     info.win_frac = p->win_frac;
     info.mfma_resid_nnz = p->mfma_tiles ? p->mfma_rnnz : 0;
-    info.mfma_tiles = p->mfma_tiles ? 1 : 0;
+    info.mfma_tiles = p->mfma_tiles ? (p->mfma_tiles_lo ? 2 : 1) : 0;
     info.route_mfma = p->route.mfma ? 1 : 0;
     info.pair_vectors = p->pair_prow ? p->pair_nvec : 0;
     info.pair_padding = p->pair_prow ? pair_padding(p) : 0.0;
@@ -962,6 +968,8 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
         p->route_N = N;
         MfmaArgs ma;
         ma.atiles = p->mfma_tiles;
+        ma.atiles_lo = p->mfma_tiles_lo;
+        ma.tile_exp = p->mfma_tile_exp;
         ma.rowptr = p->rowptr;
         ma.rrowptr = p->mfma_rowptr;
         ma.rcol = p->mfma_col;

@@ -98,6 +98,9 @@ struct MfmaArgs {
     int64_t nslices;       // kWinCols-wide column slices
     int mean;
     int xcd_remap;
+    // split tiles (fp32-level accuracy): A = (hi + lo) * 2^-tile_exp
+    const uint4 *atiles_lo;  // same layout as atiles, or nullptr
+    const int *tile_exp;     // int32 [ntiles]
 };
 
 // Arguments of the V = 2 panel kernel (pair_kernel.hip).

@@ -40,11 +40,17 @@ int64_t wave_grid(int64_t M) { return std::max<int64_t>(1, std::min<int64_t>((M 
 // One wave per row.  Lane l owns tile columns 4l .. 4l+3 and adds the row's
 // in-block weights to them in stored order; the sums are rounded to fp16 and
 // stored at their operand positions.  Also counts the row's residual entries.
+// mode 0: fp16 tiles; mode 1: only the largest |sum| of every tile (split
+// tiles, first pass); mode 2: split tiles, sums scaled by 2^tile_exp[t] and
+// stored as an fp16 high half (atiles) plus an fp16 low half (atiles_lo).
 __global__ __launch_bounds__(kBlock) void mfma_tile_build_kernel(const int *__restrict__ rowptr,
                                                                  const int *__restrict__ col,
                                                                  const float *__restrict__ val, int64_t M,
                                                                  uint4 *__restrict__ atiles, int *__restrict__ rcount,
-                                                                 int *__restrict__ range_flag) {
+                                                                 int *__restrict__ range_flag, int mode,
+                                                                 unsigned *__restrict__ tile_max,
+                                                                 const int *__restrict__ tile_exp,
+                                                                 uint4 *__restrict__ atiles_lo) {
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * kWaves;
     for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < M; row += stride) {
@@ -75,20 +81,51 @@ __global__ __launch_bounds__(kBlock) void mfma_tile_build_kernel(const int *__re
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) nres += __shfl_xor(nres, o);
+        const int64_t tile = row / kWinRows;
+        if (mode == 1) {
+            float m = fmaxf(fmaxf(fabsf(s0), fabsf(s1)), fmaxf(fabsf(s2), fabsf(s3)));
+            if (!(m <= 3.0e38f)) *range_flag = 1;   // not finite
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            if (lane == 0 && m > 0.0f) atomicMax(tile_max + tile, __float_as_uint(m));   // non-negative: int order
+            continue;
+        }
 
         const int r = (int)(row - w0);
         const int k = 4 * lane;
         const int rg = r >> 5, ks = k >> 4, hh = (k >> 3) & 1, j = k & 7;
         const int lf = (r & 31) + 32 * hh;
-        const int64_t tile = row / kWinRows;
-        _Float16 *dst = reinterpret_cast<_Float16 *>(atiles + tile * kTileUnits + (rg * kMfmaKSteps + ks) * 64 + lf) + j;
-        const f16x4 h = {(_Float16)s0, (_Float16)s1, (_Float16)s2, (_Float16)s3};
-        *reinterpret_cast<f16x4 *>(dst) = h;
-        // fp32 values at or above 65520 round to infinity in fp16 (NaN fails the test too)
-        const bool bad = !(fabsf(s0) < 65520.0f) || !(fabsf(s1) < 65520.0f) || !(fabsf(s2) < 65520.0f) ||
-                         !(fabsf(s3) < 65520.0f);
-        if (bad) *range_flag = 1;   // every writer stores the same value
+        const int64_t unit = tile * kTileUnits + (rg * kMfmaKSteps + ks) * 64 + lf;
+        _Float16 *dst = reinterpret_cast<_Float16 *>(atiles + unit) + j;
+        if (mode == 2) {
+            const int ex = tile_exp[tile];
+            const float x0 = ldexpf(s0, ex), x1 = ldexpf(s1, ex), x2 = ldexpf(s2, ex), x3 = ldexpf(s3, ex);
+            const f16x4 h = {(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
+            const f16x4 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1]), (_Float16)(x2 - (float)h[2]),
+                             (_Float16)(x3 - (float)h[3])};
+            *reinterpret_cast<f16x4 *>(dst) = h;
+            *reinterpret_cast<f16x4 *>(reinterpret_cast<_Float16 *>(atiles_lo + unit) + j) = l;
+        } else {
+            const f16x4 h = {(_Float16)s0, (_Float16)s1, (_Float16)s2, (_Float16)s3};
+            *reinterpret_cast<f16x4 *>(dst) = h;
+            // fp32 values at or above 65520 round to infinity in fp16 (NaN fails the test too)
+            const bool bad = !(fabsf(s0) < 65520.0f) || !(fabsf(s1) < 65520.0f) || !(fabsf(s2) < 65520.0f) ||
+                             !(fabsf(s3) < 65520.0f);
+            if (bad) *range_flag = 1;   // every writer stores the same value
+        }
         if (lane == 0) rcount[row] = nres;
+    }
+}
+
+// Split tiles: the power of two that brings a tile's largest |sum| just
+// below 2^15, so the low halves stay normal fp16 numbers.
+__global__ void tile_exp_kernel(const unsigned *__restrict__ tile_max, int64_t ntiles, int *__restrict__ tile_exp) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < ntiles; t += stride) {
+        const float m = __uint_as_float(tile_max[t]);
+        int e = 0;
+        if (m > 0.0f) (void)frexpf(m, &e);   // m < 2^e
+        tile_exp[t] = m > 0.0f ? 15 - e : 0;
     }
 }
 
@@ -196,14 +233,30 @@ __device__ __forceinline__ void residual_rows(const MfmaArgs &a, int64_t task0, 
     }
 }
 
-template <bool HAS_VAL>
-__global__ __launch_bounds__(kWinBlock) void mfma_tile_kernel_t(MfmaArgs a, int64_t block_base, int64_t nblocks) {
+// LDS of one workgroup: B^T (fp16; high and low halves for split tiles) while
+// the products run, then the fp32 C tile and the residual walk's staging.
+constexpr int kBtBytes = kWinCols * kMfmaBtPitch * 2;
+constexpr int kTileBytes = kWinRows * kWinCols * 4;
+constexpr int kStageBytes = (kWinBlock / 64) * kWinChunk * 4;
+constexpr int kMfmaLds = kTileBytes + 2 * kStageBytes;
+static_assert(2 * kBtBytes <= kMfmaLds, "both B^T halves fit");
+
+// Two workgroups (32 waves) per CU: at most 64 VGPRs.
+template <bool HAS_VAL, bool SPLIT>
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void mfma_tile_kernel_t(
+    MfmaArgs a, int64_t block_base, int64_t nblocks) {
     constexpr int WW = kWinBlock / 64;   // 16 waves: 8 row groups x 2 column groups of 32
     constexpr int R = 64 / (kWinCols / 4);
-    __shared__ __align__(16) float s_tile[kWinRows * kWinCols];   // fp16 B^T, then the fp32 C tile
-    __shared__ int s_col[WW][kWinChunk];
-    __shared__ int s_val[WW][HAS_VAL ? kWinChunk : 1];
-    static_assert(kWinCols * kMfmaBtPitch * 2 <= (int)sizeof(float) * kWinRows * kWinCols, "B^T fits the C tile");
+    constexpr int AH = SPLIT ? 2 : 4;    // k-steps of A in flight
+    __shared__ __align__(16) unsigned char smem[kMfmaLds];
+    // per-wave maxima of the B slice: in the staging area, idle until the residual walk
+    float *s_red = reinterpret_cast<float *>(smem + kMfmaLds) - WW;
+    static_assert(2 * kBtBytes + (int)sizeof(float) * WW <= kMfmaLds, "scratch clear of B^T");
+    float *s_tile = reinterpret_cast<float *>(smem);
+    int *s_col = reinterpret_cast<int *>(smem + kTileBytes);
+    int *s_val = reinterpret_cast<int *>(smem + kTileBytes + kStageBytes);
+    _Float16 *sbt = reinterpret_cast<_Float16 *>(smem);
+    _Float16 *sbt_lo = reinterpret_cast<_Float16 *>(smem + kBtBytes);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int64_t lin = blockIdx.x;
@@ -214,12 +267,17 @@ __global__ __launch_bounds__(kWinBlock) void mfma_tile_kernel_t(MfmaArgs a, int6
     const int64_t w0 = tile * kWinRows, c0 = slice * kWinCols;
     const int rg = wv & 7, cg = wv >> 3;
 
-    const uint4 *ap = a.atiles + tile * kTileUnits + (int64_t)rg * kMfmaKSteps * 64 + lane;
-    uint4 ar[4];
+    const int64_t aoff = tile * kTileUnits + (int64_t)rg * kMfmaKSteps * 64 + lane;
+    const uint4 *ap = a.atiles + aoff;
+    const uint4 *apl = SPLIT ? a.atiles_lo + aoff : nullptr;
+    uint4 ar[AH], arl[AH];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ar[s] = ap[s * 64];
+    for (int s = 0; s < AH; ++s) {
+        ar[s] = ap[s * 64];
+        if constexpr (SPLIT) arl[s] = apl[s * 64];
+    }
 
-    _Float16 *sbt = reinterpret_cast<_Float16 *>(s_tile);
+    int bexp = 0;
     {
         // thread (q, o): rows 4o .. 4o+3 of column quad q, stored as 4 columns of B^T
         const int q = tid & 15, o = tid >> 4;
@@ -231,28 +289,67 @@ __global__ __launch_bounds__(kWinBlock) void mfma_tile_kernel_t(MfmaArgs a, int6
             v[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             if (br < a.K && cc < a.N) v[r] = *reinterpret_cast<const f32x4 *>(a.B + br * a.N + cc);
         }
+        if constexpr (SPLIT) {
+            // the slice's largest |b| sets a power of two that keeps the low halves normal
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v[r].x), fabsf(v[r].y)), fmaxf(fabsf(v[r].z), fabsf(v[r].w))));
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            if (lane == 0) s_red[wv] = m;
+            __syncthreads();
+            m = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WW; ++w) m = fmaxf(m, s_red[w]);
+            int e = 0;
+            if (m > 0.0f && m <= 3.0e38f) (void)frexpf(m, &e);
+            bexp = (m > 0.0f && m <= 3.0e38f) ? 15 - e : 0;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const f16x4 h = {(_Float16)v[0][e], (_Float16)v[1][e], (_Float16)v[2][e], (_Float16)v[3][e]};
-            *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
+            if constexpr (SPLIT) {
+                f16x4 h, l;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = ldexpf(v[r][e], bexp);
+                    h[r] = (_Float16)x;
+                    l[r] = (_Float16)(x - (float)h[r]);
+                }
+                *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
+                *reinterpret_cast<f16x4 *>(sbt_lo + (4 * q + e) * kMfmaBtPitch + 4 * o) = l;
+            } else {
+                const f16x4 h = {(_Float16)v[0][e], (_Float16)v[1][e], (_Float16)v[2][e], (_Float16)v[3][e]};
+                *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
+            }
         }
     }
     __syncthreads();
 
     f32x16 acc = {};
-    const _Float16 *bp = sbt + (cg * 32 + (lane & 31)) * kMfmaBtPitch + 8 * (lane >> 5);
+    const int boff = (cg * 32 + (lane & 31)) * kMfmaBtPitch + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < kMfmaKSteps; ++ks) {
-        const uint4 au = ar[ks & 3];
-        if (ks + 4 < kMfmaKSteps) ar[ks & 3] = ap[(ks + 4) * 64];
+        const uint4 au = ar[ks % AH];
+        if (ks + AH < kMfmaKSteps) ar[ks % AH] = ap[(ks + AH) * 64];
         const f16x8 av = __builtin_bit_cast(f16x8, au);
-        const f16x8 bv = *reinterpret_cast<const f16x8 *>(bp + ks * 16);
+        const f16x8 bv = *reinterpret_cast<const f16x8 *>(sbt + boff + ks * 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
+        if constexpr (SPLIT) {
+            const uint4 aul = arl[ks % AH];
+            if (ks + AH < kMfmaKSteps) arl[ks % AH] = apl[(ks + AH) * 64];
+            const f16x8 avl = __builtin_bit_cast(f16x8, aul);
+            const f16x8 bvl = *reinterpret_cast<const f16x8 *>(sbt_lo + boff + ks * 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bvl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(avl, bv, acc, 0, 0, 0);
+        }
     }
+    const int unscale = SPLIT ? -(a.tile_exp[tile] + bexp) : 0;
     __syncthreads();   // all waves are done with B^T
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-        s_tile[(rg * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kWinCols + cg * 32 + (lane & 31)] = acc[r];
+        s_tile[(rg * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kWinCols + cg * 32 + (lane & 31)] =
+            SPLIT ? ldexpf(acc[r], unscale) : acc[r];
     __syncthreads();
 
     const int g = lane % (kWinCols / 4);
@@ -262,26 +359,45 @@ __global__ __launch_bounds__(kWinBlock) void mfma_tile_kernel_t(MfmaArgs a, int6
     ok[0] = c0 + 4 * g < a.N;
     for (int pass = 0; pass < kWinRows / (WW * R); ++pass) {
         const int64_t task0 = w0 + (int64_t)(pass * WW + wv) * R;
-        if (task0 < a.M) residual_rows<HAS_VAL>(a, task0, lane, s_col[wv], s_val[wv], colf, ok, s_tile, w0);
+        if (task0 < a.M)
+            residual_rows<HAS_VAL>(a, task0, lane, s_col + wv * kWinChunk, s_val + wv * kWinChunk, colf, ok, s_tile,
+                                   w0);
     }
 }
 
 }  // namespace
 
 hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val, int64_t M, uint4 *atiles,
-                            int64_t ntiles, int *rrowptr, int *range_flag, hipStream_t s) {
+                            uint4 *atiles_lo, int *tile_exp, int64_t ntiles, int *rrowptr, int *range_flag,
+                            hipStream_t s) {
     hipError_t e = hipSuccess;
-    if (ntiles > 0 && (e = hipMemsetAsync(atiles, 0, (size_t)ntiles * kTileUnits * sizeof(uint4), s)) != hipSuccess)
-        return e;
+    const size_t tile_bytes = (size_t)ntiles * kTileUnits * sizeof(uint4);
+    if (ntiles > 0 && (e = hipMemsetAsync(atiles, 0, tile_bytes, s)) != hipSuccess) return e;
+    if (ntiles > 0 && atiles_lo && (e = hipMemsetAsync(atiles_lo, 0, tile_bytes, s)) != hipSuccess) return e;
     if ((e = hipMemsetAsync(range_flag, 0, sizeof(int), s)) != hipSuccess) return e;
     int *cnt = nullptr;
+    unsigned *tmax = nullptr;
     void *tmp = nullptr;
     size_t tmp_bytes = 0;
     if ((e = hipMalloc(&cnt, sizeof(int) * (size_t)(M + 1))) != hipSuccess) return e;
     e = hipMemsetAsync(cnt + M, 0, sizeof(int), s);
+    if (e == hipSuccess && atiles_lo && ntiles > 0) {
+        e = hipMalloc(&tmax, sizeof(unsigned) * (size_t)ntiles);
+        if (e == hipSuccess) e = hipMemsetAsync(tmax, 0, sizeof(unsigned) * (size_t)ntiles, s);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(mfma_tile_build_kernel, dim3((unsigned)wave_grid(M)), dim3(kBlock), 0, s, rowptr, col,
+                               val, M, atiles, cnt, range_flag, 1, tmax, nullptr, nullptr);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) {
+            const int64_t g = std::max<int64_t>(1, std::min<int64_t>((ntiles + kBlock - 1) / kBlock, 1 << 16));
+            hipLaunchKernelGGL(tile_exp_kernel, dim3((unsigned)g), dim3(kBlock), 0, s, tmax, ntiles, tile_exp);
+            e = hipGetLastError();
+        }
+    }
     if (e == hipSuccess && M > 0) {
         hipLaunchKernelGGL(mfma_tile_build_kernel, dim3((unsigned)wave_grid(M)), dim3(kBlock), 0, s, rowptr, col, val,
-                           M, atiles, cnt, range_flag);
+                           M, atiles, cnt, range_flag, atiles_lo ? 2 : 0, nullptr, tile_exp, atiles_lo);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_bytes, cnt, rrowptr, (int)(M + 1), s);
@@ -289,6 +405,7 @@ hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val,
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(tmp, tmp_bytes, cnt, rrowptr, (int)(M + 1), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (tmp) (void)hipFree(tmp);
+    if (tmax) (void)hipFree(tmax);
     (void)hipFree(cnt);
     return e;
 }
@@ -309,10 +426,10 @@ hipError_t launch_mfma(const MfmaArgs &a, bool has_val, hipStream_t s) {
     const int64_t max_blocks = (int64_t)(UINT32_MAX / kWinBlock);
     for (int64_t base = 0; base < nb; base += max_blocks) {
         const int64_t n = std::min(nb - base, max_blocks);
-        if (has_val)
-            hipLaunchKernelGGL(mfma_tile_kernel_t<true>, dim3((unsigned)n), dim3(kWinBlock), 0, s, a, base, base + n);
-        else
-            hipLaunchKernelGGL(mfma_tile_kernel_t<false>, dim3((unsigned)n), dim3(kWinBlock), 0, s, a, base, base + n);
+        void (*kern)(MfmaArgs, int64_t, int64_t) =
+            a.atiles_lo ? (has_val ? mfma_tile_kernel_t<true, true> : mfma_tile_kernel_t<false, true>)
+                        : (has_val ? mfma_tile_kernel_t<true, false> : mfma_tile_kernel_t<false, false>);
+        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(kWinBlock), 0, s, a, base, base + n);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -49,6 +49,8 @@ struct spmm_plan {
     double win_frac = 0;       // share of entries inside their row's kWinRows block
     // fp16 community tiles + residual CSR (built on request)
     uint4 *mfma_tiles = nullptr;
+    uint4 *mfma_tiles_lo = nullptr;   // split tiles only
+    int *mfma_tile_exp = nullptr;     // split tiles only
     int *mfma_rowptr = nullptr, *mfma_col = nullptr;
     float *mfma_val = nullptr;
     int64_t mfma_rnnz = 0;

@@ -54,7 +54,8 @@ int64_t tile_build_blocks(int64_t M);
 
 // ---- fp16 matrix-core tiles for community blocks (mfma_tile.hip) ----
 hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val, int64_t M, uint4 *atiles,
-                            int64_t ntiles, int *rrowptr, int *range_flag, hipStream_t s);
+                            uint4 *atiles_lo, int *tile_exp, int64_t ntiles, int *rrowptr, int *range_flag,
+                            hipStream_t s);
 hipError_t mfma_write_residual(const int *rowptr, const int *col, const float *val, int64_t M,
                                const int *rrowptr, int *rcol, float *rval, hipStream_t s);
 hipError_t launch_mfma(const MfmaArgs &a, bool has_val, hipStream_t s);

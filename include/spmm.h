@@ -71,8 +71,9 @@ enum spmm_option {
                                   holding row bounds + indexes               */
     SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
                                   1 on: stage each 256-row block of B in LDS  */
-    SPMM_OPT_MFMA = 11,        /* 0 off (default), 1 on: fp16 matrix-core tiles
-                                  for community blocks, see below             */
+    SPMM_OPT_MFMA = 11,        /* matrix-core tiles for community blocks, see
+                                  below: 0 off (default), 1 fp16 tiles, 2 split
+                                  fp16 tiles (fp32 tolerance)                 */
     SPMM_OPT_VBLOCK = 12,      /* vectorized blocking V = 2, see below: 0 off
                                   (default), 1 build, use when padding <= 0.3,
                                   2 build, always use                          */
@@ -126,6 +127,16 @@ enum spmm_option {
  * other N and unaligned pointers keep the fp32 kernels.  Setting 0 frees the
  * tiles.  Returns UNSUPPORTED if an in-block sum of weights exceeds the fp16
  * range.
+ * SPMM_OPT_MFMA = 2 builds split tiles instead: each tile is scaled by a power
+ * of two (from its largest in-block sum) and stored as an fp16 high half plus
+ * an fp16 low half (twice the memory); in the kernel each B slice is scaled
+ * by a power of two (from its largest |b|) and split the same way, and three
+ * products hi*hi + hi*lo + lo*hi per step leave about 2^-22 relative error
+ * per term, so sum and mean meet the fp32 contract, |error| <= 1e-5 *
+ * sum_p |a_p * B[col_p][k]| + 1e-6 (not bit-identical to the fp32 kernels).
+ * Limit: a weight (feature) more than 2^18 below the largest in-block weight
+ * sum of its tile (largest |b| of its 256-row x 64-column block of B) keeps
+ * only an absolute accuracy of 2^-39 times that largest value.
  */
 
 /* Descriptors of a plan and of its last routing decision. */
@@ -152,7 +163,7 @@ struct spmm_plan_info {
     int64_t tile_overflow;       /* tiles that take the CSR path              */
     int64_t mfma_resid_nnz;      /* entries outside their row's block (residual
                                     CSR of the fp16 tile path; 0 when unbuilt) */
-    int32_t mfma_tiles;          /* 1 when the fp16 tiles are built           */
+    int32_t mfma_tiles;          /* 1 fp16 tiles built, 2 split tiles built    */
     int32_t route_mfma;          /* 1 when the last run used them             */
     int64_t pair_vectors;        /* nonzero vectors of the V = 2 panels (0 when
                                     unbuilt)                                  */

@@ -149,7 +149,7 @@ def test_tile_fallbacks_and_option(orc):
     assert G.spmm_plan_info(plan)["route_mfma"] == 0
     check(orc, g, B, "sum", C, None, what="tiles off")
     with pytest.raises(G.SpmmError) as ei:
-        G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 2)
+        G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 3)
     assert ei.value.status == G.SPMM_E_INVALID_ARG
     G.spmm_plan_destroy(plan)
 
@@ -177,4 +177,73 @@ def test_tile_full_community_sampled(orc):
     rows = np.unique(np.concatenate([np.linspace(0, g.M - 1, 400).astype(np.int64),
                                      np.arange(g.M - 40, g.M), np.arange(0, 300)]))
     check_tiles(orc, g, B, "sum", C[rows], rows=rows, what="full community (sampled rows)")
+    G.spmm_plan_destroy(plan)
+
+
+# ---- split tiles (SPMM_OPT_MFMA = 2): the fp32 contract ----
+
+def split_plan(g):
+    plan = make_plan(g)
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 2)
+    assert G.spmm_plan_info(plan)["mfma_tiles"] == 2
+    return plan
+
+
+SPLIT_CASES = [
+    ("community", dict(M=6000), 512),
+    ("community", dict(M=6000), 68),
+    ("block", dict(M=1500, K=700), 64),
+    ("block_unweighted", dict(M=1000, K=1000), 128),
+]
+
+
+@pytest.mark.parametrize("name,kw,N", SPLIT_CASES, ids=[f"{c[0]}-{c[2]}" for c in SPLIT_CASES])
+@pytest.mark.parametrize("reduce", ["sum", "mean"])
+def test_split_tiles_fp32_contract(orc, name, kw, N, reduce):
+    g = _graph(name, kw, seed=N + 1)
+    rng = np.random.default_rng(300 + N)
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    plan = split_plan(g)
+    _, _, _, Bd = to_dev(g, B)
+    C, _ = gpu_run(plan, g.M, Bd, reduce)
+    assert G.spmm_plan_info(plan)["route_mfma"] == 1
+    check(orc, g, B, reduce, C, None, what=f"split {name} N={N} {reduce}")
+    C2, _ = gpu_run(plan, g.M, Bd, reduce)
+    assert np.array_equal(C.view(np.uint32), C2.view(np.uint32)), "runs differ"
+    G.spmm_plan_destroy(plan)
+
+
+def test_split_tiles_wide_range(orc):
+    rng = np.random.default_rng(31)
+    g = W.block_csr(rng, 2048, 2048, in_deg=20.0, off_deg=3.0)
+    rows = np.repeat(np.arange(g.M), g.degrees())
+    scale = np.float32(10.0) ** ((rows // 256) % 7 - 3).astype(np.float32)   # 1e-3 .. 1e3 by block
+    g.val = (g.val * scale).astype(np.float32)
+    B = rng.standard_normal((g.K, 64)).astype(np.float32)
+    B[:, :32] *= np.float32(1e4)
+    B[rng.random(B.shape) < 0.05] *= np.float32(1e-6)
+    plan = split_plan(g)
+    _, _, _, Bd = to_dev(g, B)
+    for red in ("sum", "mean"):
+        C, _ = gpu_run(plan, g.M, Bd, red)
+        check(orc, g, B, red, C, None, what=f"split wide range {red}")
+    # mode changes rebuild or free the tiles
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 1)
+    assert G.spmm_plan_info(plan)["mfma_tiles"] == 1
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 2)
+    assert G.spmm_plan_info(plan)["mfma_tiles"] == 2
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_MFMA, 0)
+    assert G.spmm_plan_info(plan)["mfma_tiles"] == 0
+    G.spmm_plan_destroy(plan)
+
+
+def test_split_tiles_full_community_sampled(orc):
+    w = W.make("community")
+    g, B = w.graph, w.B
+    plan = split_plan(g)
+    _, _, _, Bd = to_dev(g, B)
+    C, _ = gpu_run(plan, g.M, Bd, "sum")
+    rows = np.unique(np.concatenate([np.linspace(0, g.M - 1, 400).astype(np.int64),
+                                     np.arange(g.M - 40, g.M), np.arange(0, 300)]))
+    check(orc, g, B, "sum", C[rows], None, rows=rows, what="split full community (sampled rows)")
     G.spmm_plan_destroy(plan)
