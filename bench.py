@@ -35,7 +35,8 @@ METRIC = "SpMM GFLOP/s (2·nnz·N) + effective HBM GB/s as % of MI355X peak, per
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/kernels.h"]
-FAMILY_SOURCES = {"mfma_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"]}
+FAMILY_SOURCES = {"mfma_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"],
+                  "mfma_split_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"]}
 
 REGIME_TEXT = {
     "tiny": "tiny random graph M=K=2,000, Poisson(8) degrees, 1% empty rows, weighted, N=16",
@@ -68,7 +69,7 @@ def byte_model(g, N, reduce):
 
 def kernel_family(info) -> str:
     if info.get("route_mfma"):
-        return "mfma_tile_kernel"
+        return "mfma_split_tile_kernel" if info.get("mfma_tiles") == 2 else "mfma_tile_kernel"
     if info.get("route_window"):
         return "window_kernel"
     if info.get("route_tiled"):
@@ -477,8 +478,8 @@ def main():
     ap.add_argument("--regimes", default="road,tiny,diffusion,community,powerlaw")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timings")
-    ap.add_argument("--mfma", action="store_true",
-                    help="time the JSON-line workload with the fp16 matrix-core tiles (sum/mean only)")
+    ap.add_argument("--mfma", type=int, nargs="?", const=1, default=0, choices=(0, 1, 2),
+                    help="time the JSON-line workload on the matrix-core tiles: 1 fp16, 2 split fp16 (sum/mean)")
     ap.add_argument("--router-sweep", action="store_true",
                     help="only the router evidence: every forced variant per regime against the router's pick")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -522,7 +523,7 @@ def main():
           file=sys.stderr, flush=True)
     if args.mfma:
         assert reduce != "max", "the fp16 tiles serve sum and mean only"
-        r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, 1)
+        r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, args.mfma)
 
     copy_gbps = copy_ceiling_gbps(reps=3 if args.calibrate_copy else 20)
 
@@ -548,7 +549,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 tiles + f32" if args.mfma else "f32",
+        "dtype": {0: "f32", 1: "f16 tiles + f32", 2: "split f16 tiles + f32"}[args.mfma],
         "data": "synthetic",
         "config": {"workload": REGIME_TEXT[headline] + f", {reduce} reduction", "M": g.M, "K": g.K,
                    "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32},
