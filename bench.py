@@ -35,8 +35,8 @@ METRIC = "SpMM GFLOP/s (2·nnz·N) + effective HBM GB/s as % of MI355X peak, per
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/kernels.h"]
-FAMILY_SOURCES = {"mfma_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"],
-                  "mfma_split_tile_kernel": ["gnn_sparse_dense_amd/csrc/mfma_tile.hip"]}
+MFMA_SOURCES = ["gnn_sparse_dense_amd/csrc/mfma_tile.hip", "gnn_sparse_dense_amd/csrc/mfma_args.h"]
+FAMILY_SOURCES = {"mfma_tile_kernel": MFMA_SOURCES, "mfma_split_tile_kernel": MFMA_SOURCES}
 
 REGIME_TEXT = {
     "tiny": "tiny random graph M=K=2,000, Poisson(8) degrees, 1% empty rows, weighted, N=16",

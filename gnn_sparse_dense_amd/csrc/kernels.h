@@ -23,9 +23,6 @@ constexpr int kWinRows = 256;           // rows of a community window
 constexpr int kWinCols = 64;            // B columns staged per window block
 constexpr int kWinBlock = 1024;         // threads of a window block
 constexpr int kWinChunk = 128;          // staged entries per wave in window blocks
-constexpr int kMergeItems = 512;        // merge-path items (entries + row ends) per wave
-constexpr int kMfmaKSteps = kWinRows / 16;   // k-steps of 16 per 256-wide community tile
-constexpr int kMfmaBtPitch = kWinRows + 8;   // fp16 per staged B^T row (16-byte skew per row)
 
 // Arguments of the row kernel (light rows or split pieces).
 struct RowArgs {
@@ -81,62 +78,5 @@ struct RowKernelKey {
 };
 
 typedef void (*RowKernelFn)(RowArgs);
-
-// Tile t covers rows and columns [t*kWinRows, (t+1)*kWinRows).  Its dense
-// fp16 values are stored in the operand order of v_mfma_f32_32x32x16_f16: for
-// row group rg (32 rows) and k-step ks (16 columns), 64 lanes x 8 halves,
-// lane l holding row rg*32 + l%32, columns ks*16 + 8*(l/32) .. +7.
-struct MfmaArgs {
-    const uint4 *atiles;   // [ntiles][8][kMfmaKSteps][64] x 8 fp16
-    const int *rowptr;     // int32 [M+1] of the whole matrix (mean divisor)
-    const int *rrowptr;    // int32 [M+1] residual CSR (entries outside the row's tile)
-    const int *rcol;       // int32 [rnnz]
-    const float *rval;     // fp32 [rnnz] or nullptr
-    const float *B;        // fp32 [K, N]
-    float *C;              // fp32 [M, N]
-    int64_t M, K, N;
-    int64_t nslices;       // kWinCols-wide column slices
-    int mean;
-    int xcd_remap;
-    // split tiles (fp32-level accuracy): A = (hi + lo) * 2^-tile_exp
-    const uint4 *atiles_lo;  // same layout as atiles, or nullptr
-    const int *tile_exp;     // int32 [ntiles]
-};
-
-// Arguments of the V = 2 panel kernel (pair_kernel.hip).
-struct PairArgs {
-    const int *prow;          // int32 [npanels+1]: vector range of each panel of rows 2g, 2g+1
-    const unsigned *pcol;     // uint32 [nvec]: column | row-2g absent << 30 | row-2g+1 absent << 31
-    const float *pval;        // fp32 [nvec][2] or nullptr
-    const int *rowptr;        // int32 [M+1] (row degrees)
-    const float *B;           // fp32 [K, N]
-    float *C;                 // fp32 [M, N]
-    int64_t *argmax;          // int64 [M, N] or nullptr
-    int64_t M, N;
-    int64_t npanels;          // panels: tasks end here
-    int64_t task_base;        // first panel of this launch
-    int mean;
-    int xcd_remap;
-};
-typedef void (*PairKernelFn)(PairArgs);
-
-// Arguments of the merge-path kernel and its fix-up (merge_kernel.hip).
-struct MergeArgs {
-    const int *rowptr;        // int32 [M+1]
-    const int *col;           // int32 [nnz]
-    const float *val;         // fp32 [nnz] or nullptr
-    const int *seg_row;       // int32 [nseg+1]: row ends consumed before segment w
-    const int *seg_entry;     // int32 [nseg+1]: entries consumed before segment w
-    const float *B;           // fp32 [K, N]
-    float *C;                 // fp32 [M, N]
-    int64_t *argmax;          // int64 [M, N] or nullptr
-    float *carry;             // fp32 [nseg, kPartialWidth]: open row's partial per segment
-    int *carry_arg;           // int32 [nseg, kPartialWidth] (max)
-    int *carry_row;           // int32 [nseg]: the open row, or -1
-    int64_t M, N, nseg;
-    int64_t c_begin, c_end;   // columns of this pass (at most kPartialWidth)
-    int mean;
-};
-typedef void (*MergeKernelFn)(MergeArgs);
 
 }  // namespace gspmm

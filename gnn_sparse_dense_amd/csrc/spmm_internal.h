@@ -10,6 +10,9 @@
 #include <string>
 
 #include "kernels.h"
+#include "merge_args.h"
+#include "mfma_args.h"
+#include "pair_args.h"
 #include "spmm.h"
 
 namespace gspmm {
