@@ -197,6 +197,19 @@ def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
     return t, len(times)
 
 
+def host_cpu() -> str:
+    """The host's CPU model name and hardware thread count."""
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} hardware threads"
+
+
 def percentile(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
@@ -573,7 +586,7 @@ def main():
         result["cpu_baseline"] = {
             "value": round(flops / t_cpu / 1e9, 3), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {headline} graph and B, {reduce}, median of {reps} single-threaded "
-                      f"oracle runs ({t_cpu * 1e3:.1f} ms each)",
+                      f"oracle runs ({t_cpu * 1e3:.1f} ms each) on {host_cpu()}",
         }
 
     if not args.headline_only:
