@@ -202,7 +202,9 @@ spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const fl
  *   N      : feature width, N >= 1.
  * Asynchronous: it validates its arguments, picks a kernel from the plan's
  * descriptors and N, enqueues the kernels and returns without waiting.  It
- * allocates nothing.  B must not overlap C or argmax.  Runs on one plan must
+ * allocates nothing and enqueues kernels only (no memset or copy), so a call
+ * can be captured in a HIP graph on a stream in thread-local capture mode
+ * and replayed while the plan, B and C stay alive.  B must not overlap C or argmax.  Runs on one plan must
  * be ordered on one stream (the plan's split buffer is shared); use one plan
  * per stream for concurrency.  Kernel faults surface at the caller's next
  * synchronisation, as usual in HIP.
