@@ -320,6 +320,17 @@ class SparseAdj:
     def set_option(self, option: int, value: int) -> None:
         spmm_plan_set_option(self._plan, option, value)
 
+    def features(self, V: int = 2) -> dict:
+        """ParamSpMM Table 3 features of the adjacency (synchronous)."""
+        return spmm_plan_features(self._plan, V)
+
+    def reordered(self):
+        """(P A P^T as a new SparseAdj, perm) with the reverse Cuthill-McKee order:
+        perm[i] = the node placed at position i; use B[perm] as its features and
+        C_new[inv] (inv[perm] = arange) to return to the original numbering."""
+        perm = spmm_plan_reorder(self._plan)
+        return SparseAdj(None, None, _plan=spmm_plan_permute(self._plan, perm)), perm
+
     def reduce(self, B, reduce: str = "sum", out=None, argmax=None, stream=None):
         import torch
         N = int(B.shape[1])

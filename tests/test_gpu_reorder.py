@@ -125,3 +125,23 @@ def test_reorder_errors(orc):
     empty = W.Graph("e", 5, 5, np.zeros(6, np.int64), np.zeros(0, np.int64), None)
     plan, perm, ref = rcm_and_check(orc, empty, "no entries")
     G.spmm_plan_destroy(plan)
+
+
+def test_sparse_adj_reordered_roundtrip(orc):
+    g = W.relabel(W.make_graph("road", M=20_000), 77)
+    rowptr, col, val, _ = to_dev(g)
+    adj = G.SparseAdj(rowptr, col, val, num_cols=g.K)
+    radj, perm = adj.reordered()
+    rng = np.random.default_rng(78)
+    B = torch.from_numpy(rng.standard_normal((g.K, 32)).astype(np.float32)).to(DEV)
+    C = adj.reduce(B, "sum")
+    Cp = radj.reduce(B[perm].contiguous(), "sum")
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(g.M, device=DEV)
+    got = Cp[inv].cpu().numpy()
+    check(orc, g, B.cpu().numpy(), "sum", got, None, what="reordered round trip")
+    f = radj.features(2)
+    assert f["n"] == g.M and f["nnz"] == g.nnz
+    assert f["mean_bandwidth"] < adj.features(2)["mean_bandwidth"] / 10
+    radj.close()
+    adj.close()
