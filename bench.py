@@ -269,6 +269,34 @@ def tile_results(r, steps, warmup, flush, fp32_results=()):
     return out
 
 
+def graph_replay_result(r, reduce, reps=100, rounds=20):
+    """Launch-bound products captured in one HIP graph (reps products per graph)
+    and replayed: microseconds per product, against eager back-to-back launches."""
+    import torch
+    G = r.G
+    N = r.w.N
+    arg = torch.empty((r.g.M, N), dtype=torch.int64, device=r.C.device) if reduce == "max" else None
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side, capture_error_mode="thread_local"):
+        for _ in range(reps):
+            G.spmm_run(r.plan, r.B, r.C, arg, N, reduce, None)
+    graph.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(rounds):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        graph.replay()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e) * 1e3 / reps)
+    eager, _ = r.time_steps(reduce, reps, 5)
+    del graph
+    return {"reduce": reduce, "us_per_product_graph": round(statistics.median(times), 2),
+            "us_per_product_eager_events": round(statistics.median(eager) * 1e3, 2), "products_per_graph": reps}
+
+
 def reuse_result(r, reduce, steps, flush):
     """First call against steady state (RA-SpMM, "When does RA-SpMM help?": a
     structure built once pays off after build / saving runs).  For each
@@ -611,6 +639,8 @@ def main():
             if rr.info["route_window"]:
                 regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush, regimes[name])
             reuse[name] = reuse_result(rr, rr.w.reduces[0], min(args.steps, 50), flush)
+            if name == "tiny":
+                reuse[name]["graph_replay"] = graph_replay_result(rr, rr.w.reduces[0])
             if not args.no_backward:
                 backward[name] = backward_result(rr, flush, min(args.steps, 50))
             rr.close()
