@@ -149,6 +149,28 @@ def test_degenerate_shapes(orc):
     G.spmm_plan_destroy(plan)
 
 
+def test_size_limits(orc):
+    # rowptr[M] at the int32 limit is refused from rowptr alone: col is never read
+    rp = torch.tensor([0, 2**31 - 1], dtype=torch.int64, device=DEV)
+    cl = torch.zeros(1, dtype=torch.int64, device=DEV)
+    with pytest.raises(G.SpmmError) as ei:
+        G.spmm_plan_create(rp, cl, None, 1, 4)
+    assert ei.value.status == G.SPMM_E_UNSUPPORTED and "nnz" in str(ei.value)
+    # very wide feature rows: hundreds of column slices with a ragged last one
+    rng = np.random.default_rng(12)
+    g = W.random_csr(rng, 40, 30, mean_deg=6.0, empty_frac=0.1, heavy_rows=1, heavy_deg=25,
+                     dup_frac=0.1)
+    plan = make_plan(g)
+    for N in (20_001, 65_540):
+        log(f"wide N={N}")
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        for red in ("sum", "mean", "max"):
+            C, arg = gpu_run(plan, g.M, Bd, red)
+            check(orc, g, B, red, C, arg, exact_rows=None, what=f"wide N={N} {red}")
+    G.spmm_plan_destroy(plan)
+
+
 @pytest.mark.parametrize("T,L", [(64, 64), (100, 37), (0, 1000), (513, 512)])
 def test_row_split(orc, T, L):
     rng = np.random.default_rng(T * 7 + L)
