@@ -71,7 +71,7 @@ def kernel_family(info) -> str:
     if info.get("route_mfma"):
         return "mfma_split_tile_kernel" if info.get("mfma_tiles") == 2 else "mfma_tile_kernel"
     if info.get("route_window"):
-        return "window_kernel"
+        return "window_sorted_kernel" if info.get("route_window") == 2 else "window_kernel"
     if info.get("route_tiled"):
         return "tile_kernel"
     return "row_kernel"
@@ -448,7 +448,7 @@ def router_sweep(r, reduce, steps, flush):
            "best_variant": best["variant"], "router_speed_vs_best": round(best["ms"] / router_ms, 4),
            "router_route_repeats": len(same),
            "router_route_spread": round(max(same) / min(same) - 1.0, 4)}
-    if reduce != "max" and rows[0]["path"] == "window_kernel":
+    if reduce != "max" and rows[0]["path"].startswith("window"):
         G.spmm_plan_set_option(r.plan, G.SPMM_OPT_MFMA, 1)
         ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
         G.spmm_plan_set_option(r.plan, G.SPMM_OPT_MFMA, 0)

@@ -486,6 +486,7 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         r.tiled = false;
         r.compact = false;
         r.window = !r.mfma;
+        r.window_sorted = r.window && p->rows_sorted;
         r.split = r.split && !r.mfma;
     }
     return r;
@@ -675,22 +676,26 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
     if (nnz > 0) {
         const int64_t wblocks = (M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
         int64_t *d_w = nullptr;
-        if ((st = dev_alloc(&d_w, wblocks, "window scan"))) {
+        if ((st = dev_alloc(&d_w, 2 * wblocks, "window scan"))) {
             free_plan(p);
             return nullptr;
         }
         e = launch_window_scan(p->rowptr, p->col, M, d_w, wblocks, nullptr);
-        std::vector<int64_t> wc((size_t)wblocks);
-        if (e == hipSuccess) e = hipMemcpy(wc.data(), d_w, sizeof(int64_t) * wblocks, hipMemcpyDeviceToHost);
+        std::vector<int64_t> wc((size_t)(2 * wblocks));
+        if (e == hipSuccess) e = hipMemcpy(wc.data(), d_w, sizeof(int64_t) * 2 * wblocks, hipMemcpyDeviceToHost);
         dev_free(d_w);
         if (e != hipSuccess) {
             fail_hip(e, "window scan");
             free_plan(p);
             return nullptr;
         }
-        int64_t inside = 0;
-        for (int64_t c : wc) inside += c;
+        int64_t inside = 0, unsorted = 0;
+        for (int64_t b = 0; b < wblocks; ++b) {
+            inside += wc[2 * b];
+            unsorted += wc[2 * b + 1];
+        }
         p->win_frac = (double)inside / (double)nnz;
+        p->rows_sorted = unsorted == 0;
     }
 
     // descriptors (RA-SpMM: M, mean degree, coefficient of variation)
@@ -869,7 +874,7 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.tile_overflow = p->tile_overflow;
     info.tile_cap = p->tile_cap;
     info.route_tiled = p->route.tiled ? 1 : 0;
-    info.route_window = p->route.window ? 1 : 0;
+    info.route_window = p->route.window ? (p->route.window_sorted ? 2 : 1) : 0;
     info.win_frac = p->win_frac;
     info.mfma_resid_nnz = p->mfma_tiles ? p->mfma_rnnz : 0;
     info.mfma_tiles = p->mfma_tiles ? (p->mfma_tiles_lo ? 2 : 1) : 0;
@@ -1068,7 +1073,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.mean = reduce == SPMM_MEAN;
     a.xcd_remap = r.xcd_remap;
     a.nt_store = r.nt_store;
-    hipError_t e = r.window ? launch_window(a, has_val, is_max, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
+    hipError_t e = r.window ? launch_window(a, has_val, is_max, r.window_sorted, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
     if (e != hipSuccess) return fail_hip(e, "row kernel launch");
 
     if (p->split && p->n_seg > 0) {

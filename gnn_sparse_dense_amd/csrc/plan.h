@@ -14,6 +14,7 @@ struct Route {
     bool tiled = false;
     bool compact = false;
     bool window = false;
+    bool window_sorted = false;   // the window kernel for rows in column order
     bool mfma = false;
     bool pairs = false;
     bool merge = false;
@@ -47,6 +48,7 @@ struct spmm_plan {
     bool tile_compact = false;
     int64_t tile_overflow = 0;
     double win_frac = 0;       // share of entries inside their row's kWinRows block
+    bool rows_sorted = false;  // every row's columns are non-decreasing
     // fp16 community tiles + residual CSR (built on request)
     uint4 *mfma_tiles = nullptr;
     uint4 *mfma_tiles_lo = nullptr;   // split tiles only

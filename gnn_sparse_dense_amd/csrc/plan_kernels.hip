@@ -252,27 +252,43 @@ __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restric
     }
 }
 
-// Entries whose column lies in the same aligned block of kWinRows rows as
-// their row (one count per scan block).
+// Per scan block: out[2b] = entries whose column lies in the same aligned
+// block of kWinRows rows as their row, out[2b+1] = rows whose columns are not
+// in non-decreasing order.
 __global__ __launch_bounds__(kBlock) void window_scan_kernel(const int *__restrict__ rowptr,
                                                              const int *__restrict__ col, int64_t M,
                                                              int64_t *__restrict__ out) {
     const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock;
-    int64_t cnt = 0;
+    int64_t cnt = 0, unsorted = 0;
     for (int j = threadIdx.x; j < kRowsPerScanBlock; j += kBlock) {
         const int64_t i = base + j;
         if (i >= M) break;
         const int blk = (int)(i / kWinRows);
-        for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) cnt += (col[p] / kWinRows == blk);
+        int prev = INT_MIN;
+        bool up = true;
+        for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+            const int c = col[p];
+            cnt += (c / kWinRows == blk);
+            up = up && c >= prev;
+            prev = c;
+        }
+        unsorted += up ? 0 : 1;
     }
-    __shared__ int64_t sh[kBlock];
-    sh[threadIdx.x] = cnt;
+    __shared__ int64_t sh[2][kBlock];
+    sh[0][threadIdx.x] = cnt;
+    sh[1][threadIdx.x] = unsorted;
     __syncthreads();
     for (int o = kBlock / 2; o > 0; o >>= 1) {
-        if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        if (threadIdx.x < o) {
+            sh[0][threadIdx.x] += sh[0][threadIdx.x + o];
+            sh[1][threadIdx.x] += sh[1][threadIdx.x + o];
+        }
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = sh[0];
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = sh[0][0];
+        out[2 * blockIdx.x + 1] = sh[1][0];
+    }
 }
 
 }  // namespace

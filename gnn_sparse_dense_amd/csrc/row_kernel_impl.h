@@ -20,6 +20,7 @@
 // results (plus int32 partial argmax) for the ordered combine.
 #pragma once
 
+#include <climits>
 #include <cmath>
 
 #include "spmm_internal.h"
@@ -441,37 +442,33 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     if (live) store_out<F, VEC, IS_MAX, false>(a, orow, deg, colf, ok, acc, arg);
 }
 
-// Window kernel for graphs whose neighbours mostly fall in their own aligned
+// Window kernels for graphs whose neighbours mostly fall in their own aligned
 // block of kWinRows rows (community / locality structure, RA-SpMM's
 // community regime).  A 1024-thread block owns one such block of rows and one
 // kWinCols-wide column slice: it first copies B's rows of that block (the
 // window, 64 KB) into LDS, then its 16 waves walk the block's rows four at a
-// time (16 lanes x float4 per row) exactly as the row kernel does, except
-// that entries inside the window read B from LDS.  Every B row of the window
-// is then read from HBM once per slice instead of once per referencing row,
-// and the entry order, hence every result bit, is the row kernel's.
-template <bool HAS_VAL, bool IS_MAX>
-__global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
-    constexpr int G = kWinCols / 4, VEC = 4, F = 1, R = 64 / G;   // one float4 per lane
-    constexpr int WW = kWinBlock / 64;              // waves per block
-    constexpr int Q = kWinCols / 4;                 // float4 per window row
-    __shared__ f32x4 s_B[kWinRows * Q];
-    __shared__ int s_col[WW][kWinChunk];
-    __shared__ int s_val[WW][HAS_VAL ? kWinChunk : 1];
+// time (16 lanes x float4 per row), reading entries inside the window from
+// LDS.  Every B row of the window is then read from HBM once per slice
+// instead of once per referencing row.  Both kernels fold each row's entries
+// in stored order with one accumulator, so every result bit is the row
+// kernel's.
 
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+// Block -> (first row of the window, first column of the slice).  Consecutive
+// linear ids walk the slices of one row block, so the block's indexes stay in
+// one L2 while its slices run.
+__device__ __forceinline__ void window_coords(const RowArgs &a, int64_t *w0, int64_t *c0) {
     const int64_t gx = gridDim.x;
     int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
     if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
-    // consecutive linear ids walk the slices of one row block, so the
-    // block's indexes stay in one L2 while its slices run
     const int64_t nsl = gridDim.y;
-    const int64_t tile = lin / nsl;
-    const int64_t slice = lin % nsl;
-    const int64_t w0 = tile * kWinRows;
-    const int64_t c0 = slice * kWinCols;
+    *w0 = (lin / nsl) * kWinRows;
+    *c0 = (lin % nsl) * kWinCols;
+}
 
+// The window: B rows w0 .. w0 + kWinRows - 1, columns c0 .. c0 + kWinCols - 1,
+// zero past the edges of B.
+__device__ __forceinline__ void load_window(const RowArgs &a, f32x4 *s_B, int64_t w0, int64_t c0) {
+    constexpr int Q = kWinCols / 4;                 // float4 per window row
     for (int i = threadIdx.x; i < kWinRows * Q; i += kWinBlock) {
         const int r = i / Q, q = i - (i / Q) * Q;
         const int64_t brow = w0 + r, bcol = c0 + q * 4;
@@ -480,6 +477,22 @@ __global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
         s_B[i] = v;
     }
     __syncthreads();
+}
+
+// Any column order: each entry picks LDS or HBM by its own column.
+template <bool HAS_VAL, bool IS_MAX>
+__global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
+    constexpr int G = kWinCols / 4, VEC = 4, F = 1, R = 64 / G;   // one float4 per lane
+    constexpr int WW = kWinBlock / 64;              // waves per block
+    __shared__ f32x4 s_B[kWinRows * (kWinCols / 4)];
+    __shared__ int s_col[WW][kWinChunk];
+    __shared__ int s_val[WW][HAS_VAL ? kWinChunk : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    int64_t w0, c0;
+    window_coords(a, &w0, &c0);
+    load_window(a, s_B, w0, c0);
 
     int colf[F];
     bool ok[F];
@@ -489,6 +502,182 @@ __global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
         if (task0 < a.ntasks)
             row_task<G, VEC, F, HAS_VAL, IS_MAX, false, kWinChunk, true>(a, task0, lane, s_col[wv], s_val[wv],
                                                                        colf, ok, s_B, w0);
+    }
+}
+
+// Staged entry of the sorted-row window kernel: column, and the value's bits
+// beside it when the graph is weighted, so one LDS read returns both.
+template <bool HAS_VAL> struct WinEntry { typedef int type; };
+template <> struct WinEntry<true> { typedef i32x2 type; };
+__device__ __forceinline__ int ent_col(int e) { return e; }
+__device__ __forceinline__ int ent_col(i32x2 e) { return e.x; }
+__device__ __forceinline__ float ent_val(int) { return 1.0f; }
+__device__ __forceinline__ float ent_val(i32x2 e) { return __int_as_float(e.y); }
+
+// Folds one B vector (entry column c, weight w) into the accumulators.
+template <bool HAS_VAL, bool IS_MAX>
+__device__ __forceinline__ void win_fold(float (&acc)[1][4], int (&arg)[1][4], const f32x4 &b, float w, int c) {
+    const float b4[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (IS_MAX) {
+            const float t = HAS_VAL ? w * b4[e] : b4[e];
+            if (arg[0][e] < 0 || t > acc[0][e]) {
+                acc[0][e] = t;
+                arg[0][e] = c;
+            }
+        } else {
+            acc[0][e] = HAS_VAL ? __builtin_fmaf(w, b4[e], acc[0][e]) : acc[0][e] + b4[e];
+        }
+    }
+}
+
+// Staged entries [lo, hi) of one row, all outside the window: predicated
+// batches of U gathers from HBM, as in the row kernel.
+template <bool HAS_VAL, bool IS_MAX, int U, typename E>
+__device__ __forceinline__ void win_hbm_run(const E *se, int lo, int hi, const RowArgs &a, int colf, bool ok,
+                                            float (&acc)[1][4], int (&arg)[1][4]) {
+    for (int k = lo; k < hi; k += U) {
+        E ent[U];
+        f32x4 b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            ent[u] = se[k + u < hi ? k + u : lo];
+            b[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + (int64_t)ent_col(ent[u]) * a.N + colf);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k + u < hi) win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]), ent_col(ent[u]));
+    }
+}
+
+// Staged entries [lo, hi) of one row, all inside the window: B from LDS.
+// Lanes past the end of the batch re-read entry lo (inside the window too),
+// so every LDS address stays in the window.
+template <bool HAS_VAL, bool IS_MAX, int U, typename E>
+__device__ __forceinline__ void win_lds_run(const E *se, int lo, int hi, const f32x4 *sB, int wlo, int g,
+                                            float (&acc)[1][4], int (&arg)[1][4]) {
+    for (int k = lo; k < hi; k += U) {
+        E ent[U];
+        f32x4 b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ent[u] = se[k + u < hi ? k + u : lo];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(max(ent_col(ent[u]) - wlo, 0), kWinRows - 1);   // in range for sorted rows
+            b[u] = sB[r * (kWinCols / 4) + g];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k + u < hi) win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]), ent_col(ent[u]));
+    }
+}
+
+// Rows with non-decreasing columns (checked when the plan is built).  Within
+// any stretch of such a row the entries fall in three runs: columns below
+// the window, inside it, above it.  Folding the runs one after the other
+// keeps the stored order, while the HBM gathers of the outer runs no longer
+// hold up the LDS batches of the inner run, and the inner run needs no
+// per-entry choice between LDS and HBM.  Run lengths come from two wave
+// ballots per 16 staged entries.
+template <bool HAS_VAL, bool IS_MAX>
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void window_sorted_kernel_t(RowArgs a) {
+    constexpr int G = kWinCols / 4, R = 64 / G;     // 16 lanes x float4 per row, 4 rows per wave
+    constexpr int WW = kWinBlock / 64;
+    constexpr int NT = kWinChunk / 64;
+    typedef typename WinEntry<HAS_VAL>::type E;
+    __shared__ f32x4 s_B[kWinRows * (kWinCols / 4)];
+    __shared__ E s_e[WW][kWinChunk];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int sub = lane / G, g = lane % G;
+    int64_t w0, c0;
+    window_coords(a, &w0, &c0);
+    load_window(a, s_B, w0, c0);
+    const int wlo = (int)w0, whi = wlo + kWinRows;
+    const int colf = (int)(c0 + g * 4);
+    const bool ok = c0 + g * 4 < a.c_end;
+    E *se = s_e[wv];
+
+    for (int pass = 0; pass < kWinRows / (WW * R); ++pass) {
+        const int64_t task0 = w0 + (int64_t)(pass * WW + wv) * R;
+        if (task0 >= a.ntasks) continue;            // uniform per wave
+        const int64_t v = task0 + sub;
+        bool live = v < a.ntasks;
+        int beg = 0, end = 0;
+        if (live) {
+            beg = a.rowptr[v];
+            end = a.rowptr[v + 1];
+        }
+        int deg = end - beg;
+        if (deg > a.skip_above) {                   // split row: its pieces produce the output
+            deg = 0;
+            live = false;
+        }
+        const int beg0 = __builtin_amdgcn_readfirstlane(beg);
+        int off = 0, total = 0;
+        bool contiguous = true;
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+            const int ds = __builtin_amdgcn_readlane(deg, s * G);
+            const int bs = __builtin_amdgcn_readlane(beg, s * G);
+            off += (s < sub) ? ds : 0;
+            contiguous = contiguous && (ds == 0 || bs == beg0 + total);
+            total += ds;
+        }
+
+        float acc[1][4];
+        int arg[1][4];
+        init_acc<1, 4, IS_MAX>(acc, arg);
+        for (int cb = 0; cb < total; cb += kWinChunk) {
+            const int cn = min(kWinChunk, total - cb);
+            E er[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t * 64 < cn) {
+                    const int q = cb + min(t * 64 + lane, cn - 1);
+                    int p;
+                    if (contiguous) {
+                        p = beg0 + q;
+                    } else {
+                        p = 0;
+                        int o = 0;
+#pragma unroll
+                        for (int s = 0; s < R; ++s) {
+                            const int ds = __builtin_amdgcn_readlane(deg, s * G);
+                            const int bs = __builtin_amdgcn_readlane(beg, s * G);
+                            p = (q >= o && q < o + ds) ? bs + (q - o) : p;
+                            o += ds;
+                        }
+                    }
+                    if constexpr (HAS_VAL) er[t] = i32x2{a.col[p], __float_as_int(a.val[p])};
+                    else er[t] = a.col[p];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t * 64 < cn) se[t * 64 + lane] = er[t];
+            wave_lds_sync();
+            const int lo = max(off, cb) - cb;
+            const int hi = max(lo, min(off + deg, cb + cn) - cb);
+            int nlo = 0, nin = 0;
+            for (int q0 = lo; q0 < hi; q0 += G) {
+                const int c = q0 + g < hi ? ent_col(se[q0 + g]) : INT_MAX;
+                const uint64_t blo = __ballot(c < wlo), bin = __ballot(c >= wlo && c < whi);
+                nlo += __popcll((blo >> (sub * G)) & ((1ull << G) - 1));
+                nin += __popcll((bin >> (sub * G)) & ((1ull << G) - 1));
+            }
+            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo, lo + nlo, a, colf, ok, acc, arg);
+            win_lds_run<HAS_VAL, IS_MAX, 4>(se, lo + nlo, lo + nlo + nin, s_B, wlo, g, acc, arg);
+            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo + nlo + nin, hi, a, colf, ok, acc, arg);
+            wave_lds_sync();
+        }
+        const int colv[1] = {colf};
+        const bool okv[1] = {ok};
+        if (live) store_out<1, 4, IS_MAX, false>(a, v, deg, colv, okv, acc, arg);
     }
 }
 

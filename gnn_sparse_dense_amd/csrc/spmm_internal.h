@@ -24,7 +24,7 @@ RowKernelFn row_kernel_v4(const RowKernelKey &k);
 RowKernelFn row_kernel(const RowKernelKey &k);
 
 hipError_t launch_combine(const CombineArgs &a, bool is_max, hipStream_t s);
-hipError_t launch_window(const RowArgs &a, bool has_val, bool is_max, hipStream_t s);
+hipError_t launch_window(const RowArgs &a, bool has_val, bool is_max, bool sorted, hipStream_t s);
 
 // ---- plan-time kernels (plan_kernels.hip) ----
 struct RowScanOut {        // one record per scan block

@@ -157,7 +157,10 @@ struct spmm_plan_info {
     int32_t route_slices, route_xcd_remap, route_nt_store, route_split;
     int32_t tiles, tile_cap;     /* row tiles: 0 none, 1 32-bit, 2 16-bit offset
                                     records; entries per record               */
-    int32_t route_tiled, route_window;
+    int32_t route_tiled;
+    int32_t route_window;        /* 0 off; 1 window kernel, any column order;
+                                    2 window kernel for rows whose columns are
+                                    non-decreasing (checked at plan creation) */
     double win_frac;             /* share of entries inside their row's 256-row
                                     block (community structure)               */
     int64_t tile_overflow;       /* tiles that take the CSR path              */

@@ -370,11 +370,35 @@ def _sub_csr(g, M, K):
     return W.Graph("sub", M, K, rowptr, col, val)
 
 
-@pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted"])
-def test_community_window_matches_row_kernel(orc, shape):
-    """The LDS window path (B's 256-row blocks staged per workgroup) gives the
-    row kernel's bits, with a ragged last block, N not a multiple of the
-    64-column slice, and K different from M."""
+def _permute_within_rows(g, rng):
+    """The same matrix with each row's entries (and values) in random order."""
+    col = g.col.copy()
+    val = None if g.val is None else g.val.copy()
+    for i in range(g.M):
+        a, b = g.rowptr[i], g.rowptr[i + 1]
+        if b - a > 1:
+            p = a + rng.permutation(b - a)
+            col[a:b] = g.col[p]
+            if val is not None:
+                val[a:b] = g.val[p]
+    return W.Graph(g.name, g.M, g.K, g.rowptr, col, val)
+
+
+def _sort_within_rows(g):
+    """The same matrix with each row's entries in column order (stable)."""
+    rows = np.repeat(np.arange(g.M), np.diff(g.rowptr))
+    order = np.lexsort((g.col, rows))
+    return W.Graph(g.name, g.M, g.K, g.rowptr, g.col[order], None if g.val is None else g.val[order])
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+@pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted", "duplicates"])
+def test_community_window_matches_row_kernel(orc, shape, order):
+    """Both LDS window kernels (B's 256-row blocks staged per workgroup) give
+    the row kernel's bits, with a ragged last block, N not a multiple of the
+    64-column slice, K different from M, and repeated columns: rows in
+    column order take the three-run kernel (route 2), others the per-entry
+    kernel (route 1)."""
     g = W.make_graph("community", M=5_000, seed=11)
     if shape == "wide":
         g = _sub_csr(g, 4_000, 5_000)
@@ -382,7 +406,11 @@ def test_community_window_matches_row_kernel(orc, shape):
         g = _sub_csr(g, 5_000, 4_100)
     elif shape == "unweighted":
         g = W.Graph("u", g.M, g.K, g.rowptr, g.col, None)
+    elif shape == "duplicates":
+        g = W.block_csr(np.random.default_rng(5), 3_000, 3_000, in_deg=40.0, off_deg=3.0)
     rng = np.random.default_rng(77)
+    g = _sort_within_rows(g) if order == "sorted" else _permute_within_rows(g, rng)
+    want_route = 2 if order == "sorted" else 1
     for N in (128, 200, 512):
         B = rng.standard_normal((g.K, N)).astype(np.float32)
         _, _, _, Bd = to_dev(g, B)
@@ -391,7 +419,7 @@ def test_community_window_matches_row_kernel(orc, shape):
         assert G.spmm_plan_info(on)["win_frac"] > 0.5
         for red in ("sum", "mean", "max"):
             C1, a1 = gpu_run(on, g.M, Bd, red)
-            assert G.spmm_plan_info(on)["route_window"] == 1
+            assert G.spmm_plan_info(on)["route_window"] == want_route
             C0, a0 = gpu_run(off, g.M, Bd, red)
             assert G.spmm_plan_info(off)["route_window"] == 0
             log(f"window {shape} N={N} {red}")
