@@ -505,14 +505,23 @@ __global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
     }
 }
 
-// Staged entry of the sorted-row window kernel: column, and the value's bits
-// beside it when the graph is weighted, so one LDS read returns both.
+// Staged entry of the sorted-row window kernel: a key, and the value's bits
+// beside it when the graph is weighted, so one LDS read returns both.  The
+// key of an entry outside the window is its column; inside the window it is
+// the bitwise complement of the window row's byte offset (a negative
+// number), worked out once per entry at staging time, where one instruction
+// serves 64 entries, rather than in the fold loop, where it serves four.
+constexpr int kWinRowBytes = kWinCols * 4;
 template <bool HAS_VAL> struct WinEntry { typedef int type; };
 template <> struct WinEntry<true> { typedef i32x2 type; };
-__device__ __forceinline__ int ent_col(int e) { return e; }
-__device__ __forceinline__ int ent_col(i32x2 e) { return e.x; }
+__device__ __forceinline__ int ent_key(int e) { return e; }
+__device__ __forceinline__ int ent_key(i32x2 e) { return e.x; }
 __device__ __forceinline__ float ent_val(int) { return 1.0f; }
 __device__ __forceinline__ float ent_val(i32x2 e) { return __int_as_float(e.y); }
+__device__ __forceinline__ int win_key(int c, int wlo) {
+    const int r = c - wlo;
+    return (unsigned)r < (unsigned)kWinRows ? ~(r * kWinRowBytes) : c;
+}
 
 // Folds one B vector (entry column c, weight w) into the accumulators.
 template <bool HAS_VAL, bool IS_MAX>
@@ -532,8 +541,8 @@ __device__ __forceinline__ void win_fold(float (&acc)[1][4], int (&arg)[1][4], c
     }
 }
 
-// Staged entries [lo, hi) of one row, all outside the window: predicated
-// batches of U gathers from HBM, as in the row kernel.
+// Staged entries [lo, hi) of one row, all outside the window (keys are
+// columns): predicated batches of U gathers from HBM, as in the row kernel.
 template <bool HAS_VAL, bool IS_MAX, int U, typename E>
 __device__ __forceinline__ void win_hbm_run(const E *se, int lo, int hi, const RowArgs &a, int colf, bool ok,
                                             float (&acc)[1][4], int (&arg)[1][4]) {
@@ -544,33 +553,52 @@ __device__ __forceinline__ void win_hbm_run(const E *se, int lo, int hi, const R
         for (int u = 0; u < U; ++u) {
             ent[u] = se[k + u < hi ? k + u : lo];
             b[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + (int64_t)ent_col(ent[u]) * a.N + colf);
+            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + (int64_t)ent_key(ent[u]) * a.N + colf);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (k + u < hi) win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]), ent_col(ent[u]));
+            if (k + u < hi) win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]), ent_key(ent[u]));
     }
 }
 
-// Staged entries [lo, hi) of one row, all inside the window: B from LDS.
-// Lanes past the end of the batch re-read entry lo (inside the window too),
-// so every LDS address stays in the window.
-template <bool HAS_VAL, bool IS_MAX, int U, typename E>
-__device__ __forceinline__ void win_lds_run(const E *se, int lo, int hi, const f32x4 *sB, int wlo, int g,
+// B vector of an inside-window key for the lane whose float4 sits at byte
+// g16 of each window row: g16 + ~key = (g16 - 1) - key.
+__device__ __forceinline__ f32x4 win_vec(const f32x4 *sB, int g16m1, int key) {
+    return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const char *>(sB) + (g16m1 - key));
+}
+
+// Staged entries [lo, hi) of one row, all inside the window: B from LDS, in
+// full batches of four, then one predicated batch for the last one to three
+// (lanes past the end re-read entry lo, inside the window too).
+template <bool HAS_VAL, bool IS_MAX, typename E>
+__device__ __forceinline__ void win_lds_run(const E *se, int lo, int hi, const f32x4 *sB, int g16m1, int wlo,
                                             float (&acc)[1][4], int (&arg)[1][4]) {
-    for (int k = lo; k < hi; k += U) {
+    constexpr int U = 4;
+    int k = lo;
+    for (; k + U <= hi; k += U) {
         E ent[U];
         f32x4 b[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) ent[u] = se[k + u < hi ? k + u : lo];
+        for (int u = 0; u < U; ++u) ent[u] = se[k + u];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = min(max(ent_col(ent[u]) - wlo, 0), kWinRows - 1);   // in range for sorted rows
-            b[u] = sB[r * (kWinCols / 4) + g];
-        }
+        for (int u = 0; u < U; ++u) b[u] = win_vec(sB, g16m1, ent_key(ent[u]));
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (k + u < hi) win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]), ent_col(ent[u]));
+            win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]),
+                                      IS_MAX ? wlo + (~ent_key(ent[u])) / kWinRowBytes : 0);
+    }
+    if (k < hi) {
+        E ent[U - 1];
+        f32x4 b[U - 1];
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) ent[u] = se[k + u < hi ? k + u : lo];
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) b[u] = win_vec(sB, g16m1, ent_key(ent[u]));
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u)
+            if (k + u < hi)
+                win_fold<HAS_VAL, IS_MAX>(acc, arg, b[u], ent_val(ent[u]),
+                                          IS_MAX ? wlo + (~ent_key(ent[u])) / kWinRowBytes : 0);
     }
 }
 
@@ -597,7 +625,8 @@ void window_sorted_kernel_t(RowArgs a) {
     int64_t w0, c0;
     window_coords(a, &w0, &c0);
     load_window(a, s_B, w0, c0);
-    const int wlo = (int)w0, whi = wlo + kWinRows;
+    const int wlo = (int)w0;
+    const int g16m1 = g * 16 - 1;
     const int colf = (int)(c0 + g * 4);
     const bool ok = c0 + g * 4 < a.c_end;
     E *se = s_e[wv];
@@ -653,8 +682,8 @@ void window_sorted_kernel_t(RowArgs a) {
                             o += ds;
                         }
                     }
-                    if constexpr (HAS_VAL) er[t] = i32x2{a.col[p], __float_as_int(a.val[p])};
-                    else er[t] = a.col[p];
+                    if constexpr (HAS_VAL) er[t] = i32x2{win_key(a.col[p], wlo), __float_as_int(a.val[p])};
+                    else er[t] = win_key(a.col[p], wlo);
                 }
             }
 #pragma unroll
@@ -665,13 +694,13 @@ void window_sorted_kernel_t(RowArgs a) {
             const int hi = max(lo, min(off + deg, cb + cn) - cb);
             int nlo = 0, nin = 0;
             for (int q0 = lo; q0 < hi; q0 += G) {
-                const int c = q0 + g < hi ? ent_col(se[q0 + g]) : INT_MAX;
-                const uint64_t blo = __ballot(c < wlo), bin = __ballot(c >= wlo && c < whi);
+                const int key = q0 + g < hi ? ent_key(se[q0 + g]) : INT_MAX;
+                const uint64_t blo = __ballot(key >= 0 && key < wlo), bin = __ballot(key < 0);
                 nlo += __popcll((blo >> (sub * G)) & ((1ull << G) - 1));
                 nin += __popcll((bin >> (sub * G)) & ((1ull << G) - 1));
             }
             win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo, lo + nlo, a, colf, ok, acc, arg);
-            win_lds_run<HAS_VAL, IS_MAX, 4>(se, lo + nlo, lo + nlo + nin, s_B, wlo, g, acc, arg);
+            win_lds_run<HAS_VAL, IS_MAX>(se, lo + nlo, lo + nlo + nin, s_B, g16m1, wlo, acc, arg);
             win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo + nlo + nin, hi, a, colf, ok, acc, arg);
             wave_lds_sync();
         }
