@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_t(MergeArgs a) {
             wgt[u] = HAS_VAL ? __int_as_float(s_val[wv][kk]) : 1.0f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) bv[u][e] = 0.0f;
-            if (vld[u] && ok) load_vec<VEC>(a.B + (int64_t)cidx[u] * a.N + colf, bv[u]);
+            if (vld[u] && ok) load_vec<VEC>(a.B + elem_off(cidx[u], a.N, colf), bv[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

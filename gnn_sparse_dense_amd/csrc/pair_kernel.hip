@@ -123,7 +123,7 @@ __device__ __forceinline__ void consume_pair(const unsigned *cp, const float *vp
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) bv[u][e] = 0.0f;
-            if (vld[u] && ok) load_vec<VEC>(Bp + (int64_t)(cw[u] & kColMask) * N + colf, bv[u]);
+            if (vld[u] && ok) load_vec<VEC>(Bp + elem_off(cw[u] & kColMask, N, colf), bv[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

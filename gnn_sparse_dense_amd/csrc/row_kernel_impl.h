@@ -53,6 +53,13 @@ __device__ __forceinline__ int64_t xcd_remap_block(int64_t b, int64_t nb) {
     return base + (r % kXcds) * kXcdChunk + r / kXcds;
 }
 
+// Element offset of row r, column c of a row-major matrix with n columns,
+// for 0 <= r, c, n < 2^31: one 32 x 32 -> 64-bit multiply-add rather than a
+// full 64-bit product (three quarter-rate multiplies per gather).
+__device__ __forceinline__ int64_t elem_off(int r, int64_t n, int c) {
+    return (int64_t)((uint64_t)(uint32_t)r * (uint32_t)n + (uint32_t)c);
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and reads before
 // the next overwrite).  A wave's LDS operations execute in program order, so
 // only compiler reordering has to be prevented.
@@ -153,11 +160,11 @@ __device__ __forceinline__ void consume(const void *cpv, const int *vp, int lo, 
                             const f32x4 t = sB[wr * (kWinCols / 4) + g];
                             bv[u][f][0] = t.x; bv[u][f][1] = t.y; bv[u][f][2] = t.z; bv[u][f][3] = t.w;
                         } else {
-                            load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                            load_vec<VEC>(Bp + elem_off(cidx[u], N, colf[f]), bv[u][f]);
                         }
                     }
                 } else {
-                    if (vld[u] && ok[f]) load_vec<VEC>(Bp + (int64_t)cidx[u] * N + colf[f], bv[u][f]);
+                    if (vld[u] && ok[f]) load_vec<VEC>(Bp + elem_off(cidx[u], N, colf[f]), bv[u][f]);
                 }
             }
 #pragma unroll
@@ -553,7 +560,7 @@ __device__ __forceinline__ void win_hbm_run(const E *se, int lo, int hi, const R
         for (int u = 0; u < U; ++u) {
             ent[u] = se[k + u < hi ? k + u : lo];
             b[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + (int64_t)ent_key(ent[u]) * a.N + colf);
+            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + elem_off(ent_key(ent[u]), a.N, colf));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
