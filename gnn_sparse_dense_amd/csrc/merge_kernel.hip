@@ -59,9 +59,10 @@ __device__ __forceinline__ void merge_emit(const MergeArgs &a, int64_t row, int 
             res[e] = (complete && deg == 0) ? 0.0f : acc[e];
             ar[e] = (complete && deg == 0) ? -1 : arg[e];
         } else {
-            res[e] = (complete && a.mean && deg > 0) ? acc[e] / (float)deg : acc[e];
+            res[e] = acc[e];
         }
     }
+    if constexpr (!IS_MAX) mean_divide<VEC>(a.mean != 0, complete ? deg : 0, res);
     store_vec<VEC>(a.C + row * a.N + colf, res, false);
     if constexpr (IS_MAX)
         if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar);
@@ -204,8 +205,9 @@ __global__ __launch_bounds__(kPartialWidth) void merge_fixup_kernel(MergeArgs a)
         *cp = total;
         if (a.argmax) a.argmax[(int64_t)r * a.N + c] = targ;
     } else {
-        total = total + tail;
-        *cp = (a.mean && deg > 0) ? total / (float)deg : total;
+        float res[1] = {total + tail};
+        mean_divide<1>(a.mean != 0, deg, res);
+        *cp = res[0];
     }
 }
 

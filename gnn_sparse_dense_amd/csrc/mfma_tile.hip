@@ -228,7 +228,8 @@ __device__ __forceinline__ void residual_rows(const MfmaArgs &a, int64_t task0, 
         const int dfull = a.mean ? a.rowptr[v + 1] - a.rowptr[v] : 0;
         float res[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) res[e] = dfull > 0 ? acc[0][e] / (float)dfull : acc[0][e];
+        for (int e = 0; e < 4; ++e) res[e] = acc[0][e];
+        mean_divide<4>(a.mean != 0, dfull, res);
         store_vec<4>(a.C + v * a.N + colf[0], res, false);
     }
 }

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
     __shared__ float s_val[kWaves][HAS_VAL ? 2 * kChunk : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int64_t gx = gridDim.x;
     int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
     if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
@@ -246,9 +246,10 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
                 res[e] = d > 0 ? acc[h][e] : 0.0f;
                 ar[e] = d > 0 ? arg[h][e] : -1;
             } else {
-                res[e] = (a.mean && d > 0) ? acc[h][e] / (float)d : acc[h][e];
+                res[e] = acc[h][e];
             }
         }
+        if constexpr (!IS_MAX) mean_divide<VEC>(a.mean != 0, d, res);
         store_vec<VEC>(a.C + row * a.N + colf, res, false);
         if constexpr (IS_MAX)
             if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar);

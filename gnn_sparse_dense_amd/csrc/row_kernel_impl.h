@@ -199,6 +199,19 @@ __device__ __forceinline__ void init_acc(float (&acc)[F][VEC], int (&arg)[F][VEC
         }
 }
 
+// The mean's division by the row degree (one IEEE fp32 division per output;
+// empty rows keep their 0).  The mean flag is uniform, and the branch on it
+// must stay a branch: the compiler would otherwise run the division sequence
+// (about 15 instructions per element) for every sum as well and select.
+template <int VEC>
+__device__ __forceinline__ void mean_divide(bool mean, int deg, float (&res)[VEC]) {
+    if (mean) {
+        asm volatile("" ::: "memory");   // nothing to hoist out of this branch
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) res[e] = deg > 0 ? res[e] / (float)deg : res[e];
+    }
+}
+
 // Epilogue of one output row (or piece): mean division, empty-row values,
 // argmax as int64 column ids (int32 in piece mode).
 template <int F, int VEC, bool IS_MAX, bool PIECES>
@@ -217,12 +230,11 @@ __device__ __forceinline__ void store_out(const RowArgs &a, int64_t orow, int de
             if constexpr (IS_MAX) {
                 res[e] = deg > 0 ? acc[f][e] : 0.0f;
                 ar[e] = deg > 0 ? arg[f][e] : -1;
-            } else if constexpr (PIECES) {
-                res[e] = acc[f][e];
             } else {
-                res[e] = (a.mean && deg > 0) ? acc[f][e] / (float)deg : acc[f][e];
+                res[e] = acc[f][e];
             }
         }
+        if constexpr (!IS_MAX && !PIECES) mean_divide<VEC>(a.mean != 0, deg, res);
         store_vec<VEC>(orow_p + cc, res, a.nt_store != 0);
         if constexpr (IS_MAX) {
             if constexpr (PIECES) store_arg32<VEC>(a.part_arg + orow * a.ldo + cc, ar);
@@ -332,13 +344,34 @@ __device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int la
     if (live) store_out<F, VEC, IS_MAX, PIECES>(a, v, deg, colf, ok, acc, arg);
 }
 
+// lin -> (lin mod d, lin div d) for a linear block id: nothing to divide for
+// d = 1, a 32-bit division while the grid has fewer than 2^32 blocks (a
+// 64-bit one costs about 80 scalar instructions per wave).
+__device__ __forceinline__ void split_block_id(int64_t lin, int64_t d, int64_t *rem, int64_t *quo) {
+    if (d == 1) {
+        *rem = 0;
+        *quo = lin;
+    } else if ((int64_t)gridDim.x * gridDim.y <= (int64_t)UINT32_MAX) {
+        const uint32_t l = (uint32_t)lin, q = l / (uint32_t)d;
+        *quo = q;
+        *rem = l - q * (uint32_t)d;
+    } else {
+        *quo = lin / d;
+        *rem = lin - *quo * d;
+    }
+}
+
 // Block -> (first wave task, column slice), optionally XCD-aware.
 __device__ __forceinline__ void block_coords(const RowArgs &a, int64_t *bx, int64_t *by) {
     const int64_t gx = gridDim.x;
     int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
     if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
-    *bx = lin % gx;
-    *by = lin / gx;
+    if (gridDim.y == 1) {            // one column slice: lin is the task group
+        *bx = lin;
+        *by = 0;
+        return;
+    }
+    split_block_id(lin, gx, bx, by);
 }
 
 template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool PIECES>
@@ -350,7 +383,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
     __shared__ int s_val[kWaves][HAS_VAL ? kChunk : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     int64_t bx, by;
     block_coords(a, &bx, &by);
     const int64_t task0 = a.task_base + (bx * kWaves + wv) * R;
@@ -386,7 +419,7 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     __shared__ int s_val[kWaves][HAS_VAL ? kChunk : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int sub = lane / G;
     int64_t bx, by;
     block_coords(a, &bx, &by);
@@ -467,9 +500,10 @@ __device__ __forceinline__ void window_coords(const RowArgs &a, int64_t *w0, int
     const int64_t gx = gridDim.x;
     int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
     if (a.xcd_remap) lin = xcd_remap_block(lin, gx * (int64_t)gridDim.y);
-    const int64_t nsl = gridDim.y;
-    *w0 = (lin / nsl) * kWinRows;
-    *c0 = (lin % nsl) * kWinCols;
+    int64_t tile, slice;
+    split_block_id(lin, gridDim.y, &slice, &tile);
+    *w0 = tile * kWinRows;
+    *c0 = slice * kWinCols;
 }
 
 // The window: B rows w0 .. w0 + kWinRows - 1, columns c0 .. c0 + kWinCols - 1,
@@ -496,7 +530,7 @@ __global__ __launch_bounds__(kWinBlock) void window_kernel_t(RowArgs a) {
     __shared__ int s_val[WW][HAS_VAL ? kWinChunk : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     int64_t w0, c0;
     window_coords(a, &w0, &c0);
     load_window(a, s_B, w0, c0);
@@ -627,7 +661,7 @@ void window_sorted_kernel_t(RowArgs a) {
     __shared__ E s_e[WW][kWinChunk];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int sub = lane / G, g = lane % G;
     int64_t w0, c0;
     window_coords(a, &w0, &c0);
