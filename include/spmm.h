@@ -70,7 +70,9 @@ enum spmm_option {
                                   with 32-bit records: keep 8-row tile records
                                   holding row bounds + indexes               */
     SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
-                                  1 on: stage each 256-row block of B in LDS  */
+                                  1 on: stage each 256-row block of B in LDS
+                                  (a faster kernel when every row's columns
+                                  are non-decreasing, bit-identical either way) */
     SPMM_OPT_MFMA = 11,        /* matrix-core tiles for community blocks, see
                                   below: 0 off (default), 1 fp16 tiles, 2 split
                                   fp16 tiles (fp32 tolerance)                 */
