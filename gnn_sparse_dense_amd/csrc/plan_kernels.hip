@@ -254,25 +254,52 @@ __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restric
 
 // Per scan block: out[2b] = entries whose column lies in the same aligned
 // block of kWinRows rows as their row, out[2b+1] = rows whose columns are not
-// in non-decreasing order.
+// in non-decreasing order.  A thread takes each short row; rows longer than
+// kScanLong entries are walked by the whole block afterwards (one thread per
+// row would leave a hub of 50,000 entries to a single thread).
+constexpr int kScanLong = 64;
+
 __global__ __launch_bounds__(kBlock) void window_scan_kernel(const int *__restrict__ rowptr,
                                                              const int *__restrict__ col, int64_t M,
                                                              int64_t *__restrict__ out) {
+    __shared__ int s_long[kRowsPerScanBlock];
+    __shared__ int s_nlong;
+    if (threadIdx.x == 0) s_nlong = 0;
+    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRowsPerScanBlock;
     int64_t cnt = 0, unsorted = 0;
     for (int j = threadIdx.x; j < kRowsPerScanBlock; j += kBlock) {
         const int64_t i = base + j;
         if (i >= M) break;
+        const int pb = rowptr[i], pe = rowptr[i + 1];
+        if (pe - pb > kScanLong) {
+            s_long[atomicAdd(&s_nlong, 1)] = j;
+            continue;
+        }
         const int blk = (int)(i / kWinRows);
         int prev = INT_MIN;
         bool up = true;
-        for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) {
+        for (int p = pb; p < pe; ++p) {
             const int c = col[p];
             cnt += (c / kWinRows == blk);
             up = up && c >= prev;
             prev = c;
         }
         unsorted += up ? 0 : 1;
+    }
+    __syncthreads();
+    const int nlong = s_nlong;
+    for (int t = 0; t < nlong; ++t) {              // counts are order-free: any list order
+        const int64_t i = base + s_long[t];
+        const int blk = (int)(i / kWinRows);
+        const int pb = rowptr[i], pe = rowptr[i + 1];
+        bool up = true;
+        for (int p = pb + threadIdx.x; p < pe; p += kBlock) {
+            const int c = col[p];
+            cnt += (c / kWinRows == blk);
+            if (p > pb) up = up && c >= col[p - 1];
+        }
+        if (__syncthreads_or(up ? 0 : 1) && threadIdx.x == 0) ++unsorted;
     }
     __shared__ int64_t sh[2][kBlock];
     sh[0][threadIdx.x] = cnt;

@@ -55,16 +55,41 @@ __global__ __launch_bounds__(kBlock) void coo_prepare_kernel(const int64_t *__re
 
 // Sort inputs of a plan's transpose: key = column of entry p, value = p, and
 // the row id of every entry.
+// A thread takes each short row of its block's kBlock rows; rows longer than
+// kPrepLong entries are written by the whole block afterwards.
+constexpr int kPrepLong = 64;
+
 __global__ __launch_bounds__(kBlock) void transpose_prepare_kernel(const int *__restrict__ rowptr,
                                                                    const int *__restrict__ col, int64_t M,
                                                                    int *__restrict__ keys, int *__restrict__ idx,
                                                                    int *__restrict__ rowid) {
+    __shared__ int s_long[kBlock];
+    __shared__ int s_nlong;
+    if (threadIdx.x == 0) s_nlong = 0;
+    __syncthreads();
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= M) return;
-    for (int p = rowptr[i]; p < rowptr[i + 1]; ++p) {
-        keys[p] = col[p];
-        idx[p] = p;
-        rowid[p] = (int)i;
+    if (i < M) {
+        const int pb = rowptr[i], pe = rowptr[i + 1];
+        if (pe - pb > kPrepLong) {
+            s_long[atomicAdd(&s_nlong, 1)] = (int)i;
+        } else {
+            for (int p = pb; p < pe; ++p) {
+                keys[p] = col[p];
+                idx[p] = p;
+                rowid[p] = (int)i;
+            }
+        }
+    }
+    __syncthreads();
+    const int nlong = s_nlong;
+    for (int t = 0; t < nlong; ++t) {
+        const int r = s_long[t];
+        const int pe = rowptr[r + 1];
+        for (int p = rowptr[r] + threadIdx.x; p < pe; p += kBlock) {
+            keys[p] = col[p];
+            idx[p] = p;
+            rowid[p] = r;
+        }
     }
 }
 
