@@ -121,8 +121,33 @@ void free_merge(spmm_plan *p) {
     p->merge_nseg = 0;
 }
 
+void free_window_runs(spmm_plan *p) {
+    dev_free(p->win_lo);
+    dev_free(p->win_in);
+    p->win_lo = p->win_in = nullptr;
+}
+
+// Per-row run lengths (entries below / inside the row's window) for the
+// sorted-row window kernel; only for plans whose rows are all sorted.
+int build_window_runs(spmm_plan *p) {
+    if (!p->rows_sorted || p->win_lo || p->M == 0) return SPMM_OK;
+    int st;
+    if ((st = dev_alloc(&p->win_lo, p->M, "window runs")) || (st = dev_alloc(&p->win_in, p->M, "window runs"))) {
+        free_window_runs(p);
+        return st;
+    }
+    hipError_t e = launch_window_runs(p->rowptr, p->col, p->M, p->win_lo, p->win_in, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_window_runs(p);
+        return fail_hip(e, "window runs");
+    }
+    return SPMM_OK;
+}
+
 void free_plan(spmm_plan *p) {
     if (!p) return;
+    free_window_runs(p);
     free_merge(p);
     free_split(p);
     free_tiles(p);
@@ -486,7 +511,7 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         r.tiled = false;
         r.compact = false;
         r.window = !r.mfma;
-        r.window_sorted = r.window && p->rows_sorted;
+        r.window_sorted = r.window && p->rows_sorted && p->win_lo != nullptr;
         r.split = r.split && !r.mfma;
     }
     return r;
@@ -696,6 +721,10 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
         }
         p->win_frac = (double)inside / (double)nnz;
         p->rows_sorted = unsorted == 0;
+        if (p->win_frac >= 0.5 && (st = build_window_runs(p))) {
+            free_plan(p);
+            return nullptr;
+        }
     }
 
     // descriptors (RA-SpMM: M, mean degree, coefficient of variation)
@@ -758,6 +787,11 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
         }
         case SPMM_OPT_WINDOW:
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "window must be -1, 0 or 1");
+            if (value == 1) {
+                DeviceGuard dg(p->device);
+                const int st = build_window_runs(p);
+                if (st) return st;
+            }
             p->opt_window = value;
             return succeed();
         case SPMM_OPT_LANES:
@@ -1073,6 +1107,8 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.mean = reduce == SPMM_MEAN;
     a.xcd_remap = r.xcd_remap;
     a.nt_store = r.nt_store;
+    a.win_lo = p->win_lo;
+    a.win_in = p->win_in;
     hipError_t e = r.window ? launch_window(a, has_val, is_max, r.window_sorted, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
     if (e != hipSuccess) return fail_hip(e, "row kernel launch");
 

@@ -49,6 +49,8 @@ struct RowArgs {
     int mean;              // divide by the row degree (row mode)
     int xcd_remap;         // give each XCD a contiguous range of tasks
     int nt_store;          // non-temporal output stores
+    const int *win_lo;     // int32 [M]: entries of row i below its window (sorted-row window kernel)
+    const int *win_in;     // int32 [M]: entries of row i inside its window
 };
 
 // Arguments of the ordered combine of split pieces.

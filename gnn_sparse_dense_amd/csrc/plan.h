@@ -49,6 +49,7 @@ struct spmm_plan {
     int64_t tile_overflow = 0;
     double win_frac = 0;       // share of entries inside their row's kWinRows block
     bool rows_sorted = false;  // every row's columns are non-decreasing
+    int *win_lo = nullptr, *win_in = nullptr;   // per-row run lengths (sorted rows)
     // fp16 community tiles + residual CSR (built on request)
     uint4 *mfma_tiles = nullptr;
     uint4 *mfma_tiles_lo = nullptr;   // split tiles only

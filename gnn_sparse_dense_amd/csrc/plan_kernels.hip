@@ -318,7 +318,41 @@ __global__ __launch_bounds__(kBlock) void window_scan_kernel(const int *__restri
     }
 }
 
+// Rows with non-decreasing columns: entries below row i's aligned window of
+// kWinRows rows and entries inside it, by two binary searches per row.
+__global__ __launch_bounds__(kBlock) void window_runs_kernel(const int *__restrict__ rowptr,
+                                                             const int *__restrict__ col, int64_t M,
+                                                             int *__restrict__ win_lo, int *__restrict__ win_in) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= M) return;
+    const int64_t w0 = (i / kWinRows) * kWinRows;
+    const int pb = rowptr[i], pe = rowptr[i + 1];
+    int lo = pb, hi = pe;
+    while (lo < hi) {                                 // first column >= w0
+        const int m = lo + ((hi - lo) >> 1);
+        if (col[m] < w0) lo = m + 1;
+        else hi = m;
+    }
+    const int first_in = lo;
+    hi = pe;
+    while (lo < hi) {                                 // first column >= w0 + kWinRows
+        const int m = lo + ((hi - lo) >> 1);
+        if (col[m] < w0 + kWinRows) lo = m + 1;
+        else hi = m;
+    }
+    win_lo[i] = first_in - pb;
+    win_in[i] = lo - first_in;
+}
+
 }  // namespace
+
+hipError_t launch_window_runs(const int *rowptr, const int *col, int64_t M, int *win_lo, int *win_in,
+                              hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(window_runs_kernel, dim3((unsigned)((M + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, rowptr,
+                       col, M, win_lo, win_in);
+    return hipGetLastError();
+}
 
 hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int64_t *out, int64_t nblocks,
                               hipStream_t s) {

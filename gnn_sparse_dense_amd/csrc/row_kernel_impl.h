@@ -648,8 +648,8 @@ __device__ __forceinline__ void win_lds_run(const E *se, int lo, int hi, const f
 // the window, inside it, above it.  Folding the runs one after the other
 // keeps the stored order, while the HBM gathers of the outer runs no longer
 // hold up the LDS batches of the inner run, and the inner run needs no
-// per-entry choice between LDS and HBM.  Run lengths come from two wave
-// ballots per 16 staged entries.
+// per-entry choice between LDS and HBM.  Run lengths per row come from the
+// plan (win_lo, win_in), read beside the row bounds.
 template <bool HAS_VAL, bool IS_MAX>
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void window_sorted_kernel_t(RowArgs a) {
@@ -677,10 +677,12 @@ void window_sorted_kernel_t(RowArgs a) {
         if (task0 >= a.ntasks) continue;            // uniform per wave
         const int64_t v = task0 + sub;
         bool live = v < a.ntasks;
-        int beg = 0, end = 0;
+        int beg = 0, end = 0, rlo = 0, rin = 0;
         if (live) {
             beg = a.rowptr[v];
             end = a.rowptr[v + 1];
+            rlo = a.win_lo[v];
+            rin = a.win_in[v];
         }
         int deg = end - beg;
         if (deg > a.skip_above) {                   // split row: its pieces produce the output
@@ -731,18 +733,14 @@ void window_sorted_kernel_t(RowArgs a) {
             for (int t = 0; t < NT; ++t)
                 if (t * 64 < cn) se[t * 64 + lane] = er[t];
             wave_lds_sync();
+            // the row's stretch of this chunk and its run boundaries, in chunk positions
             const int lo = max(off, cb) - cb;
             const int hi = max(lo, min(off + deg, cb + cn) - cb);
-            int nlo = 0, nin = 0;
-            for (int q0 = lo; q0 < hi; q0 += G) {
-                const int key = q0 + g < hi ? ent_key(se[q0 + g]) : INT_MAX;
-                const uint64_t blo = __ballot(key >= 0 && key < wlo), bin = __ballot(key < 0);
-                nlo += __popcll((blo >> (sub * G)) & ((1ull << G) - 1));
-                nin += __popcll((bin >> (sub * G)) & ((1ull << G) - 1));
-            }
-            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo, lo + nlo, a, colf, ok, acc, arg);
-            win_lds_run<HAS_VAL, IS_MAX>(se, lo + nlo, lo + nlo + nin, s_B, g16m1, wlo, acc, arg);
-            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo + nlo + nin, hi, a, colf, ok, acc, arg);
+            const int q1 = min(max(off + rlo - cb, lo), hi);
+            const int q2 = min(max(off + rlo + rin - cb, lo), hi);
+            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, lo, q1, a, colf, ok, acc, arg);
+            win_lds_run<HAS_VAL, IS_MAX>(se, q1, q2, s_B, g16m1, wlo, acc, arg);
+            win_hbm_run<HAS_VAL, IS_MAX, 2>(se, q2, hi, a, colf, ok, acc, arg);
             wave_lds_sync();
         }
         const int colv[1] = {colf};

@@ -391,6 +391,29 @@ def _sort_within_rows(g):
     return W.Graph(g.name, g.M, g.K, g.rowptr, g.col[order], None if g.val is None else g.val[order])
 
 
+def test_window_forced_on_scattered_graph(orc):
+    """The window forced on for a graph with few in-window entries: the sorted-row
+    kernel's per-row run lengths are built by the option call, and the result is
+    the row kernel's, bit for bit."""
+    rng = np.random.default_rng(21)
+    g = _sort_within_rows(W.random_csr(rng, 3_000, 2_000, mean_deg=9.0, empty_frac=0.05, dup_frac=0.05))
+    B = rng.standard_normal((g.K, 136)).astype(np.float32)
+    _, _, _, Bd = to_dev(g, B)
+    on = make_plan(g, [(G.SPMM_OPT_WINDOW, 1)])
+    off = make_plan(g, [(G.SPMM_OPT_WINDOW, 0)])
+    assert G.spmm_plan_info(on)["win_frac"] < 0.5
+    for red in ("sum", "mean", "max"):
+        C1, a1 = gpu_run(on, g.M, Bd, red)
+        assert G.spmm_plan_info(on)["route_window"] == 2
+        C0, a0 = gpu_run(off, g.M, Bd, red)
+        assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), red
+        if a1 is not None:
+            assert np.array_equal(a1, a0)
+        check(orc, g, B, red, C1, a1, exact_rows=np.arange(g.M), what=f"forced window {red}")
+    G.spmm_plan_destroy(on)
+    G.spmm_plan_destroy(off)
+
+
 @pytest.mark.parametrize("order", ["sorted", "shuffled"])
 @pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted", "duplicates"])
 def test_community_window_matches_row_kernel(orc, shape, order):
