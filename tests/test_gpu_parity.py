@@ -415,13 +415,13 @@ def test_window_forced_on_scattered_graph(orc):
 
 
 @pytest.mark.parametrize("order", ["sorted", "shuffled"])
-@pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted", "duplicates"])
+@pytest.mark.parametrize("shape", ["square", "wide", "tall", "unweighted", "duplicates", "long rows"])
 def test_community_window_matches_row_kernel(orc, shape, order):
     """Both LDS window kernels (B's 256-row blocks staged per workgroup) give
     the row kernel's bits, with a ragged last block, N not a multiple of the
-    64-column slice, K different from M, and repeated columns: rows in
-    column order take the three-run kernel (route 2), others the per-entry
-    kernel (route 1)."""
+    64-column slice, K different from M, repeated columns and rows longer
+    than a staging chunk: rows in column order take the three-run kernel
+    (route 2), others the per-entry kernel (route 1)."""
     g = W.make_graph("community", M=5_000, seed=11)
     if shape == "wide":
         g = _sub_csr(g, 4_000, 5_000)
@@ -431,6 +431,8 @@ def test_community_window_matches_row_kernel(orc, shape, order):
         g = W.Graph("u", g.M, g.K, g.rowptr, g.col, None)
     elif shape == "duplicates":
         g = W.block_csr(np.random.default_rng(5), 3_000, 3_000, in_deg=40.0, off_deg=3.0)
+    elif shape == "long rows":      # rows of ~240 entries: runs cross the 128-entry staging chunks
+        g = W.block_csr(np.random.default_rng(6), 1_500, 1_600, in_deg=180.0, off_deg=60.0)
     rng = np.random.default_rng(77)
     g = _sort_within_rows(g) if order == "sorted" else _permute_within_rows(g, rng)
     want_route = 2 if order == "sorted" else 1
