@@ -530,7 +530,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(rows would shard with a per-layer halo exchange of B; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
