@@ -197,6 +197,41 @@ def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
     return t, len(times)
 
 
+def oracle_regime_timing(w, reduce, budget_elems=1.5e9, reps_small=3):
+    """The single-threaded CPU oracle on one regime, bounded to about
+    budget_elems multiply-adds (about 1.5 s): the whole graph when it fits
+    (median of reps_small runs), else one contiguous block of rows from the
+    middle of the graph, its time scaled to the whole graph by entry count."""
+    import numpy as np
+
+    import oracle
+    g = w.graph
+    orc = oracle.default()
+    N = w.N
+    total = g.nnz * N
+    if total <= budget_elems:
+        rows, reps, frac = None, reps_small, 1.0
+        what = f"the whole graph, median of {reps_small} runs"
+    else:
+        want = budget_elems / N                         # entries to cover
+        deg = np.diff(g.rowptr)
+        mid = g.M // 2
+        cum = np.cumsum(deg[mid:])
+        m = int(np.searchsorted(cum, want)) + 1
+        rows = np.arange(mid, min(g.M, mid + m), dtype=np.int64)
+        covered = int(g.rowptr[rows[-1] + 1] - g.rowptr[rows[0]])
+        reps, frac = 1, covered / g.nnz
+        what = f"rows {rows[0]}..{rows[-1]} ({covered} of {g.nnz} entries), one run, scaled by entry count"
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce, rows=rows)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times) / frac
+    return {"oracle_ms": round(t * 1e3, 2), "oracle_gflops": round(2.0 * total / t / 1e9, 3),
+            "oracle_sample": what}
+
+
 def host_cpu() -> str:
     """The host's CPU model name and hardware thread count."""
     model = "unknown CPU"
@@ -215,7 +250,7 @@ def percentile(xs, q):
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
 
-def regime_result(r, reduce, steps, warmup, flush):
+def regime_result(r, reduce, steps, warmup, flush, cpu=False):
     g, N = r.g, r.w.N
     warm, _ = r.time_steps(reduce, steps, warmup)
     cold, _ = r.time_steps(reduce, steps, 2, flush=flush)
@@ -223,7 +258,7 @@ def regime_result(r, reduce, steps, warmup, flush):
     comp, gather = byte_model(g, N, reduce)
     med_c = statistics.median(cold)
     med_w = statistics.median(warm)
-    return {
+    res = {
         "reduce": reduce, "M": g.M, "nnz": g.nnz, "N": N,
         "ms_flushed_median": round(med_c, 5), "ms_flushed_min": round(min(cold), 5),
         "ms_flushed_p90": round(percentile(cold, 0.9), 5),
@@ -240,6 +275,11 @@ def regime_result(r, reduce, steps, warmup, flush):
                   "n_seg": r.info["n_seg"]},
         "plan_ms": round(r.info["plan_ms"], 2),
     }
+    if cpu:
+        o = oracle_regime_timing(r.w, reduce)
+        o["gpu_speedup_vs_oracle"] = round(o["oracle_ms"] / med_c, 1)
+        res.update(o)
+    return res
 
 
 def tile_results(r, steps, warmup, flush, fp32_results=()):
@@ -621,7 +661,7 @@ def main():
     if not args.headline_only:
         flush = make_flush()
         regimes, backward, reuse = {}, {}, {}
-        regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush)
+        regimes[headline] = [regime_result(r, red, args.steps, min(args.warmup, 50), flush, cpu=not args.no_cpu)
                              for red in r.w.reduces]
         if r.info["route_window"] and not args.mfma:
             regimes[headline] += tile_results(r, args.steps, min(args.warmup, 50), flush, regimes[headline])
@@ -635,7 +675,7 @@ def main():
             rr = Runner(name)
             print(f"[bench] {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N} gen={rr.gen_s:.1f}s",
                   file=sys.stderr, flush=True)
-            regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush)
+            regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush, cpu=not args.no_cpu)
                              for red in rr.w.reduces]
             if rr.info["route_window"]:
                 regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush, regimes[name])
