@@ -37,6 +37,7 @@ SPMM_OPT_WINDOW = 10
 SPMM_OPT_MFMA = 11
 SPMM_OPT_VBLOCK = 12
 SPMM_OPT_BALANCE = 13
+SPMM_OPT_PIECE_ORDER = 14
 
 SPMM_REORDER_RCM = 1
 
@@ -76,7 +77,7 @@ class _Info(ctypes.Structure):
         ("mfma_tiles", ctypes.c_int32), ("route_mfma", ctypes.c_int32),
         ("pair_vectors", ctypes.c_int64), ("pair_padding", ctypes.c_double),
         ("pairs_built", ctypes.c_int32), ("route_pairs", ctypes.c_int32),
-        ("merge_segments", ctypes.c_int64), ("route_merge", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("merge_segments", ctypes.c_int64), ("route_merge", ctypes.c_int32), ("piece_order", ctypes.c_int32),
     ]
 
 

@@ -84,6 +84,7 @@ void free_split(spmm_plan *p) {
     dev_free(p->seg_end);
     dev_free(p->partial);
     dev_free(p->part_arg);
+    dev_free(p->seg_order);
     p->split = false;
     p->n_heavy = p->n_seg = 0;
     p->n_light = p->M;
@@ -251,6 +252,24 @@ int build_split(spmm_plan *p) {
         return fail_hip(e, "row split write");
     }
     p->split = true;
+    // run the pieces of all heavy rows in the order of their first column:
+    // pieces in flight together then gather from nearby B rows (same bits)
+    if (p->opt_piece_order) {
+        if ((st = dev_alloc(&p->seg_order, p->n_seg, "piece order"))) {
+            free_split(p);
+            return st;
+        }
+        e = build_piece_order(p->col, p->seg_begin, p->n_seg, p->seg_order);
+        if (e == hipErrorOutOfMemory) {
+            (void)hipGetLastError();
+            free_split(p);
+            return fail(SPMM_E_OOM, "piece order: device allocation failed");
+        }
+        if (e != hipSuccess) {
+            free_split(p);
+            return fail_hip(e, "piece order");
+        }
+    }
     return SPMM_OK;
 }
 
@@ -812,6 +831,10 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "XCD remap must be -1, 0 or 1");
             p->opt_xcd = (int)value;
             return succeed();
+        case SPMM_OPT_PIECE_ORDER:
+            if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "piece order must be 0 or 1");
+            p->opt_piece_order = (int)value;
+            break;
         case SPMM_OPT_NT_STORE:
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
@@ -919,6 +942,7 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.route_pairs = p->route.pairs ? 1 : 0;
     info.merge_segments = p->merge_seg_row ? p->merge_nseg : 0;
     info.route_merge = p->route.merge ? 1 : 0;
+    info.piece_order = p->seg_order != nullptr ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -1137,6 +1161,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
             pa.ntasks = p->n_seg;
             pa.xcd_remap = 0;
             pa.nt_store = 0;
+            pa.task_perm = p->seg_order;
             e = launch_rows(pf, pa, 1, slices, s);
             if (e != hipSuccess) return fail_hip(e, "piece kernel launch");
             CombineArgs ca;

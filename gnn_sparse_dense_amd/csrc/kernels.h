@@ -51,6 +51,7 @@ struct RowArgs {
     int nt_store;          // non-temporal output stores
     const int *win_lo;     // int32 [M]: entries of row i below its window (sorted-row window kernel)
     const int *win_in;     // int32 [M]: entries of row i inside its window
+    const int *task_perm;  // piece mode, or nullptr: task t computes piece task_perm[t]
 };
 
 // Arguments of the ordered combine of split pieces.

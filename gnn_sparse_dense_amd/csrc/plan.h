@@ -40,6 +40,7 @@ struct spmm_plan {
     bool split = false;
     int64_t T = 0, L = 0, n_heavy = 0, n_seg = 0, n_light = 0;
     int *heavy_rows = nullptr, *seg_first = nullptr, *seg_begin = nullptr, *seg_end = nullptr;
+    int *seg_order = nullptr;     // pieces in the order they run (column of their first entry)
     float *partial = nullptr;
     int *part_arg = nullptr;
     // row-tile records (low-degree graphs)
@@ -69,7 +70,7 @@ struct spmm_plan {
     int64_t merge_nseg = 0;
     // options (-1 / 0 = automatic)
     int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
-    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = 0, opt_balance = 0;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = 0, opt_balance = 0, opt_piece_order = 1;
     // last routing decision
     int64_t route_N = 0;
     gspmm::Route route;

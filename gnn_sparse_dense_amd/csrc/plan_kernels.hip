@@ -8,6 +8,8 @@
 // block order, so every result is exact and independent of scheduling.
 #include <climits>
 
+#include <hipcub/hipcub.hpp>
+
 #include "spmm_internal.h"
 
 namespace gspmm {
@@ -408,6 +410,50 @@ hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t 
     hipLaunchKernelGGL(part_write_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr32, M, T,
                        L, offsets, heavy_rows, seg_first, seg_begin, seg_end, light_rows);
     return hipGetLastError();
+}
+
+// Piece keys (column of the first entry, piece id): unique, so the radix sort
+// gives the order with ties by piece id.  Every piece holds at least one entry.
+__global__ __launch_bounds__(kBlock) void piece_keys_kernel(const int *__restrict__ col,
+                                                            const int *__restrict__ seg_begin, int64_t n_seg,
+                                                            uint64_t *__restrict__ keys) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n_seg; p += stride)
+        keys[p] = ((uint64_t)(uint32_t)col[seg_begin[p]] << 32) | (uint64_t)(uint32_t)p;
+}
+
+__global__ __launch_bounds__(kBlock) void piece_ids_kernel(const uint64_t *__restrict__ keys, int64_t n_seg,
+                                                           int *__restrict__ order) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x; p < n_seg; p += stride)
+        order[p] = (int)(uint32_t)keys[p];
+}
+
+hipError_t build_piece_order(const int *col, const int *seg_begin, int64_t n_seg, int *order) {
+    if (n_seg <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n_seg + kBlock - 1) / kBlock, 4096);
+    uint64_t *ka = nullptr, *kb = nullptr;
+    void *tmp = nullptr;
+    size_t tmp_bytes = 0;
+    hipError_t e = hipMalloc(&ka, sizeof(uint64_t) * n_seg);
+    if (e == hipSuccess) e = hipMalloc(&kb, sizeof(uint64_t) * n_seg);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(piece_keys_kernel, dim3(grid), dim3(kBlock), 0, nullptr, col, seg_begin, n_seg, ka);
+        e = hipGetLastError();
+    }
+    hipcub::DoubleBuffer<uint64_t> keys(ka, kb);
+    if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, (int)n_seg);
+    if (e == hipSuccess) e = hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1);
+    if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(tmp, tmp_bytes, keys, (int)n_seg);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(piece_ids_kernel, dim3(grid), dim3(kBlock), 0, nullptr, keys.Current(), n_seg, order);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (tmp) (void)hipFree(tmp);
+    if (ka) (void)hipFree(ka);
+    if (kb) (void)hipFree(kb);
+    return e;
 }
 
 }  // namespace gspmm

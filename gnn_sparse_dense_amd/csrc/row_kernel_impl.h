@@ -262,8 +262,10 @@ __device__ __forceinline__ void row_task(const RowArgs &a, int64_t task0, int la
     constexpr int R = 64 / G;
     constexpr int NT = CH / 64;        // staging loads per lane per chunk
     const int sub = lane / G;
-    const int64_t v = task0 + sub;
+    int64_t v = task0 + sub;
     bool live = v < a.ntasks;
+    if constexpr (PIECES)
+        if (live && a.task_perm) v = a.task_perm[v];   // the piece this task computes
     int beg = 0, end = 0;
     if (live) {
         if constexpr (PIECES) {

@@ -49,6 +49,10 @@ hipError_t launch_part_write(const int *rowptr32, int64_t M, int64_t T, int64_t 
                              int *seg_begin, int *seg_end, int *light_rows, int64_t nblocks,
                              hipStream_t s);
 
+// Order in which the pieces run: ascending column of each piece's first
+// entry, ties by piece id (synchronous; allocates its own sort buffers).
+hipError_t build_piece_order(const int *col, const int *seg_begin, int64_t n_seg, int *order);
+
 hipError_t launch_window_runs(const int *rowptr, const int *col, int64_t M, int *win_lo, int *win_in,
                               hipStream_t s);
 hipError_t launch_window_scan(const int *rowptr, const int *col, int64_t M, int64_t *out, int64_t nblocks,

@@ -79,8 +79,12 @@ enum spmm_option {
     SPMM_OPT_VBLOCK = 12,      /* vectorized blocking V = 2, see below: 0 off
                                   (default), 1 build, use when padding <= 0.3,
                                   2 build, always use                          */
-    SPMM_OPT_BALANCE = 13      /* load balance: 0 row split of heavy rows
+    SPMM_OPT_BALANCE = 13,     /* load balance: 0 row split of heavy rows
                                   (default), 1 merge path, see below          */
+    SPMM_OPT_PIECE_ORDER = 14  /* 1 (default): the row split's pieces run in
+                                  ascending order of their first entry's
+                                  column; 0: in partition order.  Same
+                                  partition, same bits; rebuilds the split    */
 };
 
 /*
@@ -177,7 +181,8 @@ struct spmm_plan_info {
     int32_t route_pairs;         /* 1 when the last run used the panels       */
     int64_t merge_segments;      /* merge-path segments (0 when unbuilt)      */
     int32_t route_merge;         /* 1 when the last run used them             */
-    int32_t reserved;
+    int32_t piece_order;         /* 1 when split pieces run in the order of
+                                    their first column (SPMM_OPT_PIECE_ORDER) */
 };
 
 /*

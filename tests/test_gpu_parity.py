@@ -194,6 +194,42 @@ def test_row_split(orc, T, L):
     G.spmm_plan_destroy(plan)
 
 
+@pytest.mark.parametrize("shuffled", [False, True], ids=["sorted-rows", "shuffled-rows"])
+def test_piece_order_same_bits(orc, shuffled):
+    """The split's pieces run in the order of their first entry's column by
+    default: the partition it reports is unchanged, and every output bit
+    equals that of the pieces run in partition order (sum, mean, max and
+    argmax, column passes of 256 and a ragged tail)."""
+    rng = np.random.default_rng(9090 + shuffled)
+    g = W.random_csr(rng, 6000, 50_000, mean_deg=5.0, empty_frac=0.05, heavy_rows=60, heavy_deg=4000,
+                     dup_frac=0.02, shuffle_rows=shuffled)
+    opts = [(G.SPMM_OPT_SPLIT_T, 256), (G.SPMM_OPT_SPLIT_L, 200), (G.SPMM_OPT_SPLIT_MODE, 1)]
+    on = make_plan(g, opts)
+    off = make_plan(g, opts + [(G.SPMM_OPT_PIECE_ORDER, 0)])
+    assert G.spmm_plan_info(on)["piece_order"] == 1
+    assert G.spmm_plan_info(off)["piece_order"] == 0
+    p_on, p_off = G.spmm_plan_partition(on), G.spmm_plan_partition(off)
+    ref = orc.partition(g.rowptr, g.M, 256, 200)
+    for k in ("seg_row", "seg_begin", "seg_end", "light"):
+        assert np.array_equal(p_on[k], ref[k]) and np.array_equal(p_off[k], ref[k]), k
+    for N in (64, 300):
+        B = rng.standard_normal((g.K, N)).astype(np.float32)
+        _, _, _, Bd = to_dev(g, B)
+        for red in ("sum", "mean", "max"):
+            C1, a1 = gpu_run(on, g.M, Bd, red)
+            C0, a0 = gpu_run(off, g.M, Bd, red)
+            log(f"piece order shuffled={shuffled} N={N} {red}")
+            assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), f"N={N} {red}"
+            if red == "max":
+                assert np.array_equal(a1, a0)
+            check(orc, g, B, red, C1, a1, exact_rows=ref["light"], what=f"piece order N={N} {red}")
+    # switching the option rebuilds the split in place
+    G.spmm_plan_set_option(off, G.SPMM_OPT_PIECE_ORDER, 1)
+    assert G.spmm_plan_info(off)["piece_order"] == 1
+    G.spmm_plan_destroy(on)
+    G.spmm_plan_destroy(off)
+
+
 def test_determinism_bitwise(orc):
     w = _workload("powerlaw", M=200_000)
     g = w.graph
