@@ -449,6 +449,8 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //  * low mean degree (< 8, RA-SpMM's sparse-uniform regime): half the lanes
 //    and F = 2, doubling the rows per wave so more rows' gathers are in
 //    flight per wave;
+//  * small graphs (fewer than two waves per CU at 16 rows per wave): 8 rows
+//    per wave, so that twice as many waves share the launch-bound latency;
 //  * skewed degrees (CV > 1, RA-SpMM's sparse-skewed / extreme-skew regime),
 //    where neighbours carry no locality, with a B wider than 64 floats:
 //    64-column slices, so each pass over the graph touches a quarter-sized
@@ -478,6 +480,8 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     } else if (p->mean_deg < 8.0 && G >= 16 && W <= G) {
         G /= 2;
         F = 2;
+    } else if (G == 4 && F == 1 && p->M * G < (int64_t)p->num_cus * 2 * 64) {
+        G = 8;   // small graph: 8 rows per wave, so that more waves fill the CUs
     }
     if (p->opt_lanes) G = p->opt_lanes;
     if (p->opt_coarsen) F = p->opt_coarsen;
@@ -630,6 +634,9 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
         return nullptr;
     }
     (void)hipGetDevice(&p->device);
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) == hipSuccess && cus > 0)
+        p->num_cus = cus;
     p->M = M;
     p->K = K;
     p->nnz = nnz;

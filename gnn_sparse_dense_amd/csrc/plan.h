@@ -28,6 +28,7 @@ constexpr double kPairMaxPadding = 0.3;
 
 struct spmm_plan {
     int device = 0;
+    int num_cus = 256;            // compute units of the plan's device
     int64_t M = 0, K = 0, nnz = 0;
     // descriptors
     int64_t dmax = 0, n_empty = 0, sum_deg2 = 0;
