@@ -172,29 +172,34 @@ struct DeviceGuard {
     }
 };
 
-// Default split parameters.  ParamSpMM's split granularity (section 5.1,
+// Default split parameters.  ParamSpMM's split granularity SG (section 5.1,
 // eq. 3) is the mean non-empty row length rounded up to a multiple of the
-// wave width; with wave64 and GNN-typical degrees that is 64, which would cut
-// thousands of ordinary rows.  The threshold and piece length are therefore
-// max(that granularity, 512): rows above 512 entries take more than ~20x the
-// work of a typical row and are the ones that stall a wave-per-row schedule.
-void auto_split_params(const spmm_plan *p, int64_t *T, int64_t *L) {
+// wave width; with wave64 and GNN-typical degrees that is 64.  Threshold T =
+// max(2 SG, 128): rows a few times longer than the mean leave the light-row
+// waves, where they hold up the other rows of their wave.  Piece length L =
+// max(SG, 512): pieces stay long enough that the partial rows are a small
+// share of the traffic.  (Power-law: T = L = 512 3.84 ms, T = 128 / L = 512
+// 3.77 ms, with the pieces in first-column order.)  The split itself is
+// switched on only for graphs with hubs, rows longer than H = max(SG, 512)
+// (and a degree CV above 1): a low-degree graph with a few rows of a hundred
+// or so entries keeps its row tiles, which the split would turn off.
+void auto_split_params(const spmm_plan *p, int64_t *T, int64_t *L, int64_t *H) {
     const int64_t nonempty = p->M - p->n_empty;
     const double dhat = nonempty > 0 ? (double)p->nnz / (double)nonempty : 0.0;
     const int64_t sg = (int64_t)std::ceil(dhat / 64.0) * 64;
-    const int64_t base = std::max<int64_t>(sg, 512);
-    *T = p->opt_T >= 0 ? p->opt_T : base;
-    *L = p->opt_L > 0 ? p->opt_L : base;
+    *T = p->opt_T >= 0 ? p->opt_T : std::max<int64_t>(2 * sg, 128);
+    *L = p->opt_L > 0 ? p->opt_L : std::max<int64_t>(sg, 512);
+    *H = p->opt_T >= 0 ? p->opt_T : std::max<int64_t>(sg, 512);
 }
 
 int build_split(spmm_plan *p) {
     free_split(p);
-    int64_t T, L;
-    auto_split_params(p, &T, &L);
+    int64_t T, L, H;
+    auto_split_params(p, &T, &L, &H);
     p->T = T;
     p->L = L;
     const bool enabled =
-        p->opt_split == 1 || (p->opt_split == -1 && p->dmax > T && p->cv_deg > 1.0);
+        p->opt_split == 1 || (p->opt_split == -1 && p->dmax > H && p->cv_deg > 1.0);
     if (!enabled || p->M == 0) return SPMM_OK;
 
     const int64_t nblocks = (p->M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
