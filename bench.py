@@ -583,6 +583,9 @@ def main():
                     help="time the JSON-line workload on the matrix-core tiles: 1 fp16, 2 split fp16 (sum/mean)")
     ap.add_argument("--router-sweep", action="store_true",
                     help="only the router evidence: every forced variant per regime against the router's pick")
+    ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
+                    help="set a plan option on the JSON-line workload's plan, e.g. PIECE_ORDER=0 "
+                         "(SPMM_OPT_<NAME>; repeatable)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -625,6 +628,15 @@ def main():
     if args.mfma:
         assert reduce != "max", "the fp16 tiles serve sum and mean only"
         r.G.spmm_plan_set_option(r.plan, r.G.SPMM_OPT_MFMA, args.mfma)
+    for opt in args.option:
+        name, _, value = opt.partition("=")
+        r.G.spmm_plan_set_option(r.plan, getattr(r.G, "SPMM_OPT_" + name.strip().upper()), int(value))
+        print(f"[bench] option SPMM_OPT_{name.strip().upper()} = {int(value)}", file=sys.stderr, flush=True)
+    if args.option:
+        r.info = r.G.spmm_plan_info(r.plan)
+        result_options = {o.partition("=")[0].strip().upper(): int(o.partition("=")[2]) for o in args.option}
+    else:
+        result_options = None
 
     copy_gbps = copy_ceiling_gbps(reps=3 if args.calibrate_copy else 20)
 
@@ -659,7 +671,8 @@ def main():
         "dtype": {0: "f32", 1: "f16 tiles + f32", 2: "split f16 tiles + f32"}[args.mfma],
         "data": "synthetic",
         "config": {"workload": REGIME_TEXT[headline] + f", {reduce} reduction", "M": g.M, "K": g.K,
-                   "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32},
+                   "nnz": g.nnz, "N": N, "reduce": reduce, "index_bits": 32,
+                   **({"options": result_options} if result_options else {})},
         "effective_GBps": round(comp / (ms_per_step * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(comp / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "gather_GBps": round(gather / (ms_per_step * 1e-3) / 1e9, 1),
