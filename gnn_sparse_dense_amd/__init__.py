@@ -158,6 +158,26 @@ def _addr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check_matrix(name, t, dtype, rows, cols):
+    """A tensor passed by address must be what the library will read or write:
+    the C ABI sees only the pointer, so a strided view or a wrong dtype would
+    be read as packed row-major data without any error."""
+    if t is None or isinstance(t, int):
+        return
+    if str(t.dtype).split(".")[-1] != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if t.dim() != 2 or (rows is not None and t.shape[0] != rows) or t.shape[1] != cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected ({rows if rows is not None else 'any'}, {cols})")
+
+
+def _check_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not isinstance(t, int) and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
 def spmm_plan_create(rowptr, col, val, M: int, K: int) -> int:
     """Plan handle for the CSR (rowptr int64 [M+1], col int64 [nnz], val fp32 or None)."""
     for name, t, dt in (("rowptr", rowptr, "int64"), ("col", col, "int64"), ("val", val, "float32")):
@@ -175,6 +195,10 @@ def spmm_run(plan: int, B, C, argmax, N: int, reduce, stream=None) -> None:
     """Enqueue C = reduce(A . B) (argmax for 'max' only) on `stream`
     (an int handle, a torch stream, or None for torch's current stream)."""
     red = REDUCE[reduce] if isinstance(reduce, str) else int(reduce)
+    _check_matrix("B", B, "float32", None, int(N))
+    _check_matrix("C", C, "float32", None, int(N))
+    _check_matrix("argmax", argmax, "int64", None if isinstance(C, int) or C is None else C.shape[0], int(N))
+    _check_gpu(B=B, C=C, argmax=argmax)
     if stream is None:
         import torch
         stream = torch.cuda.current_stream().cuda_stream
@@ -334,7 +358,11 @@ class SparseAdj:
 
     def reduce(self, B, reduce: str = "sum", out=None, argmax=None, stream=None):
         import torch
+        if B.dim() != 2 or B.shape[0] != self.K:
+            raise ValueError(f"B has shape {tuple(B.shape)}, expected ({self.K}, N)")
         N = int(B.shape[1])
+        if out is not None and tuple(out.shape) != (self.M, N):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected ({self.M}, {N})")
         if out is None:
             out = torch.empty((self.M, N), dtype=torch.float32, device=B.device)
         if reduce == "max" and argmax is None:
@@ -349,6 +377,10 @@ class SparseAdj:
         """dB for a max aggregation over this (unweighted) adjacency."""
         import torch
         N = int(dC.shape[1])
+        _check_matrix("dC", dC, "float32", self.M, N)
+        _check_matrix("argmax", argmax, "int64", self.M, N)
+        _check_matrix("out", out, "float32", self.K, N)
+        _check_gpu(dC=dC, argmax=argmax, out=out)
         if out is None:
             out = torch.empty((self.K, N), dtype=torch.float32, device=dC.device)
         spmm_max_backward(self.transpose().plan, argmax, dC, out, N, stream)

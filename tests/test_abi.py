@@ -92,6 +92,29 @@ def test_argument_errors_without_gpu():
     assert _err()[0] == G.SPMM_OK
 
 
+def test_binding_rejects_strided_or_mistyped_tensors():
+    """The C ABI sees only pointers, so the binding refuses tensors whose
+    memory is not the packed row-major matrix the library reads or writes
+    (checked before any HIP call)."""
+    import torch
+
+    import gnn_sparse_dense_amd as G
+    C = torch.zeros((4, 8), dtype=torch.float32)
+    strided = torch.zeros((8, 6), dtype=torch.float32).t()          # [6, 8], column-major
+    with pytest.raises(ValueError, match="contiguous"):
+        G.spmm_run(0, strided, C, None, 8, "sum")
+    with pytest.raises(TypeError, match="float32"):
+        G.spmm_run(0, torch.zeros((6, 8), dtype=torch.float64), C, None, 8, "sum")
+    with pytest.raises(ValueError, match="shape"):
+        G.spmm_run(0, torch.zeros((6, 7), dtype=torch.float32), C, None, 8, "sum")
+    with pytest.raises(TypeError, match="int64"):
+        G.spmm_run(0, torch.zeros((6, 8)), C, torch.zeros((4, 8), dtype=torch.int32), 8, "max")
+    with pytest.raises(ValueError, match="shape"):
+        G.spmm_run(0, torch.zeros((6, 8)), C, torch.zeros((5, 8), dtype=torch.int64), 8, "max")
+    with pytest.raises(ValueError, match="GPU"):
+        G.spmm_run(0, torch.zeros((6, 8)), C, None, 8, "sum")
+
+
 def test_last_error_truncates():
     import gnn_sparse_dense_amd as G
     lib = G.lib()

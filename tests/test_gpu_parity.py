@@ -287,8 +287,10 @@ def test_descriptors_and_errors(orc):
     plan = make_plan(g)
     Bh = torch.zeros((g.K, 8), dtype=torch.float32)
     C = torch.empty((g.M, 8), dtype=torch.float32, device=DEV)
-    with pytest.raises(G.SpmmError) as ei:
+    with pytest.raises(ValueError):                      # the binding refuses a host tensor
         G.spmm_run(plan, Bh, C, None, 8, "sum")
+    with pytest.raises(G.SpmmError) as ei:               # and so does the library, given its address
+        G.spmm_run(plan, Bh.data_ptr(), C, None, 8, "sum")
     assert ei.value.status == G.SPMM_E_INVALID_ARG
     with pytest.raises(G.SpmmError):
         G.spmm_run(plan, C, C, None, 8, "sum")           # B overlaps C
