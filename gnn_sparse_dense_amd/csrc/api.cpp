@@ -183,12 +183,19 @@ struct DeviceGuard {
 // switched on only for graphs with hubs, rows longer than H = max(SG, 512)
 // (and a degree CV above 1): a low-degree graph with a few rows of a hundred
 // or so entries keeps its row tiles, which the split would turn off.
+//
+// Rows of more than kMaxWholeRow entries are split in every mode, and no
+// piece is longer: a wave then walks at most 64 x 2^24 entries, so its 32-bit
+// entry counters never come near 2^31 (and no single wave is left with a row
+// of hundreds of millions of entries).
+constexpr int64_t kMaxWholeRow = int64_t(1) << 24;
+
 void auto_split_params(const spmm_plan *p, int64_t *T, int64_t *L, int64_t *H) {
     const int64_t nonempty = p->M - p->n_empty;
     const double dhat = nonempty > 0 ? (double)p->nnz / (double)nonempty : 0.0;
     const int64_t sg = (int64_t)std::ceil(dhat / 64.0) * 64;
-    *T = p->opt_T >= 0 ? p->opt_T : std::max<int64_t>(2 * sg, 128);
-    *L = p->opt_L > 0 ? p->opt_L : std::max<int64_t>(sg, 512);
+    *T = std::min(p->opt_T >= 0 ? p->opt_T : std::max<int64_t>(2 * sg, 128), kMaxWholeRow);
+    *L = std::min(p->opt_L > 0 ? p->opt_L : std::max<int64_t>(sg, 512), kMaxWholeRow);
     *H = p->opt_T >= 0 ? p->opt_T : std::max<int64_t>(sg, 512);
 }
 
@@ -196,10 +203,12 @@ int build_split(spmm_plan *p) {
     free_split(p);
     int64_t T, L, H;
     auto_split_params(p, &T, &L, &H);
+    const bool chosen =
+        p->opt_split == 1 || (p->opt_split == -1 && p->dmax > H && p->cv_deg > 1.0);
+    const bool enabled = chosen || p->dmax > kMaxWholeRow;
+    if (enabled && !chosen) T = kMaxWholeRow;      // only the over-long rows
     p->T = T;
     p->L = L;
-    const bool enabled =
-        p->opt_split == 1 || (p->opt_split == -1 && p->dmax > H && p->cv_deg > 1.0);
     if (!enabled || p->M == 0) return SPMM_OK;
 
     const int64_t nblocks = (p->M + kRowsPerScanBlock - 1) / kRowsPerScanBlock;
@@ -500,7 +509,10 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
     r.compact = r.tiled && p->tile_compact;
     // community structure with wide features: stage B's row blocks in LDS
-    r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 &&
+    // (one dispatch: at most 2^32 / kWinBlock row blocks, about 10^9 rows;
+    // larger graphs take the row kernels)
+    const bool win_grid = (p->M + kWinRows - 1) / kWinRows <= (int64_t)(UINT32_MAX / kWinBlock);
+    r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 && win_grid &&
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
     // fp16 community tiles, when the caller asked for them
     r.mfma = p->opt_mfma > 0 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;

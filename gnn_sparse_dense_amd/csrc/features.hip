@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlock) void bandwidth_kernel(const int *__restrict
         const int beg = rowptr[row], end = rowptr[row + 1];
         if (beg == end) continue;   // wave-uniform
         int lo = INT_MAX, hi = INT_MIN;
-        for (int p = beg + lane; p < end; p += 64) {
+        for (int64_t p = (int64_t)beg + lane; p < end; p += 64) {
             const int c = col[p];
             lo = min(lo, c);
             hi = max(hi, c);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kBlock) void block_keys_kernel(const int *__restric
     for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < M; row += stride) {
         const uint64_t base = (uint64_t)(row / V) * (uint64_t)K;
         const uint64_t sub = (uint64_t)(row % V);
-        for (int p = rowptr[row] + lane; p < rowptr[row + 1]; p += 64)
+        for (int64_t p = (int64_t)rowptr[row] + lane; p < rowptr[row + 1]; p += 64)
             keys[p] = (base + (uint64_t)col[p]) * (uint64_t)V + sub;
     }
 }

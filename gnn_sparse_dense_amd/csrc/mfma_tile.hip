@@ -58,15 +58,15 @@ __global__ __launch_bounds__(kBlock) void mfma_tile_build_kernel(const int *__re
         const int beg = rowptr[row], end = rowptr[row + 1];
         float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
         int nres = 0;
-        for (int cb = beg; cb < end; cb += 64) {
-            const int p = cb + lane;
+        for (int64_t cb = beg; cb < end; cb += 64) {
+            const int64_t p = cb + lane;
             const bool has = p < end;
             const int c = has ? col[p] : 0;
             const float w = has ? (val ? val[p] : 1.0f) : 0.0f;
             const int64_t wr = (int64_t)c - w0;
             const bool inw = has && wr >= 0 && wr < kWinRows;
             nres += (has && !inw) ? 1 : 0;
-            const int n = min(64, end - cb);
+            const int n = (int)min((int64_t)64, end - cb);
             for (int j = 0; j < n; ++j) {
                 const int wj = __shfl(inw ? (int)wr : -1, j);
                 const float aj = __shfl(w, j);
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(kBlock) void mfma_residual_kernel(const int *__rest
         const int64_t w0 = (row / kWinRows) * kWinRows;
         const int beg = rowptr[row], end = rowptr[row + 1];
         int out = rrowptr[row];
-        for (int cb = beg; cb < end; cb += 64) {
-            const int p = cb + lane;
+        for (int64_t cb = beg; cb < end; cb += 64) {
+            const int64_t p = cb + lane;
             const bool has = p < end;
             const int c = has ? col[p] : 0;
             const int64_t wr = (int64_t)c - w0;
@@ -197,7 +197,8 @@ __device__ __forceinline__ void residual_rows(const MfmaArgs &a, int64_t task0, 
         for (int e = 0; e < 4; ++e) arg[0][e] = -1;
     }
 
-    for (int cb = 0; cb < total; cb += CH) {
+    for (int64_t cb64 = 0; cb64 < total; cb64 += CH) {   // 64-bit: total may lie within CH of 2^31
+        const int cb = (int)cb64;
         const int cn = min(CH, total - cb);
         const int nt = (cn + 63) >> 6;
         int cr[NT];

@@ -40,9 +40,9 @@ __global__ __launch_bounds__(kBlock) void pair_keys_kernel(const int *__restrict
     for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < M; row += stride) {
         const uint64_t base = (uint64_t)(row >> 1) * (uint64_t)K;
         const uint64_t half = (uint64_t)(row & 1);
-        for (int p = rowptr[row] + lane; p < rowptr[row + 1]; p += 64) {
+        for (int64_t p = (int64_t)rowptr[row] + lane; p < rowptr[row + 1]; p += 64) {
             keys[p] = ((base + (uint64_t)col[p]) << 1) | half;
-            pos[p] = p;
+            pos[p] = (int)p;
         }
     }
 }
@@ -198,7 +198,8 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
             arg[h][e] = -1;
         }
 
-    for (int cb = 0; cb < total; cb += kChunk) {
+    for (int64_t cb64 = 0; cb64 < total; cb64 += kChunk) {   // 64-bit: total may lie within kChunk of 2^31
+        const int cb = (int)cb64;
         const int cn = min(kChunk, total - cb);
         const int nt = (cn + 63) >> 6;
         unsigned cr[NT];

@@ -186,11 +186,13 @@ __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restric
                                                             const float *__restrict__ val, int64_t M,
                                                             int cap, int rs, int compact,
                                                             int *__restrict__ tiles,
-                                                            int64_t *__restrict__ overflow) {
+                                                            int64_t *__restrict__ overflow,
+                                                            int64_t block_base) {
     __shared__ int s_ovf[kWaves];
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * kWaves + wv;
+    const int64_t blk = block_base + blockIdx.x;
+    const int64_t t = blk * kWaves + wv;
     const int64_t ntiles = (M + kTileRows - 1) / kTileRows;
     int ovf = 0;
     if (t < ntiles) {
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kBlock) void tile_build_kernel(const int *__restric
     if (threadIdx.x == 0) {
         int64_t n = 0;
         for (int w = 0; w < kWaves; ++w) n += s_ovf[w];
-        overflow[blockIdx.x] = n;
+        overflow[blk] = n;
     }
 }
 
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kBlock) void window_scan_kernel(const int *__restri
         const int blk = (int)(i / kWinRows);
         const int pb = rowptr[i], pe = rowptr[i + 1];
         bool up = true;
-        for (int p = pb + threadIdx.x; p < pe; p += kBlock) {
+        for (int64_t p = (int64_t)pb + threadIdx.x; p < pe; p += kBlock) {
             const int c = col[p];
             cnt += (c / kWinRows == blk);
             if (p > pb) up = up && c >= col[p - 1];
@@ -370,10 +372,17 @@ int64_t tile_build_blocks(int64_t M) {
 
 hipError_t launch_tile_build(const int *rowptr, const int *col, const float *val, int64_t M, int cap, int rs,
                              bool compact, int *tiles, int64_t *overflow, int64_t nblocks, hipStream_t s) {
-    if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(tile_build_kernel, dim3((unsigned)nblocks), dim3(kBlock), 0, s, rowptr, col, val, M, cap,
-                       rs, compact ? 1 : 0, tiles, overflow);
-    return hipGetLastError();
+    // one wave per tile: above 2^26 tiles one grid would pass the 2^32
+    // work-item limit of a dispatch, so the blocks go out in several
+    const int64_t max_blocks = (int64_t)(UINT32_MAX / kBlock);
+    for (int64_t b0 = 0; b0 < nblocks; b0 += max_blocks) {
+        const int64_t n = std::min(nblocks - b0, max_blocks);
+        hipLaunchKernelGGL(tile_build_kernel, dim3((unsigned)n), dim3(kBlock), 0, s, rowptr, col, val, M, cap,
+                           rs, compact ? 1 : 0, tiles, overflow, b0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_rowscan(const int64_t *rowptr, int64_t M, int *rowptr32, RowScanOut *out,

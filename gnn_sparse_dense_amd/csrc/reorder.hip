@@ -40,7 +40,7 @@ __global__ void sym_keys_kernel(const int *__restrict__ rowptr, const int *__res
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * kWaves;
     for (int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); i < M; i += stride)
-        for (int p = rowptr[i] + lane; p < rowptr[i + 1]; p += 64) {
+        for (int64_t p = (int64_t)rowptr[i] + lane; p < rowptr[i + 1]; p += 64) {
             const int64_t j = col[p];
             const bool self = j == i;
             keys[2 * (int64_t)p] = self ? ~0ull : (uint64_t)i * (uint64_t)M + (uint64_t)j;
@@ -124,7 +124,7 @@ __global__ void expand_kernel(const int *__restrict__ srow, const int *__restric
     for (int64_t f = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); f < nf; f += stride) {
         const int u = frontier[f];
         const int pu = (int)(base + f);
-        for (int q = srow[u] + lane; q < srow[u + 1]; q += 64) {
+        for (int64_t q = (int64_t)srow[u] + lane; q < srow[u + 1]; q += 64) {
             const int v = scol[q];
             if (pos[v] >= 0) continue;
             atomicMin(&parent[v], pu);
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_levels_kernel(const int *__
             const int lane = tid & 63, wv = tid >> 6;
             for (int64_t f = wv; f < nf; f += kSmallBlock / 64) {
                 const int u = frontier[f];
-                for (int q = srow[u] + lane; q < srow[u + 1]; q += 64) {
+                for (int64_t q = (int64_t)srow[u] + lane; q < srow[u + 1]; q += 64) {
                     const int v = scol[q];
                     if (pos[v] >= 0) continue;
                     atomicMin(&parent[v], (int)(base + f));
@@ -485,9 +485,9 @@ __global__ void perm_keys_kernel(const int *__restrict__ rowptr, const int *__re
     const int64_t stride = (int64_t)gridDim.x * kWaves;
     for (int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); i < M; i += stride) {
         const uint64_t r = (uint64_t)inv[i] * (uint64_t)M;
-        for (int p = rowptr[i] + lane; p < rowptr[i + 1]; p += 64) {
+        for (int64_t p = (int64_t)rowptr[i] + lane; p < rowptr[i + 1]; p += 64) {
             keys[p] = r + (uint64_t)inv[col[p]];
-            idx[p] = p;
+            idx[p] = (int)p;
         }
     }
 }

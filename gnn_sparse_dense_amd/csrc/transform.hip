@@ -85,9 +85,9 @@ __global__ __launch_bounds__(kBlock) void transpose_prepare_kernel(const int *__
     for (int t = 0; t < nlong; ++t) {
         const int r = s_long[t];
         const int pe = rowptr[r + 1];
-        for (int p = rowptr[r] + threadIdx.x; p < pe; p += kBlock) {
+        for (int64_t p = (int64_t)rowptr[r] + threadIdx.x; p < pe; p += kBlock) {
             keys[p] = col[p];
-            idx[p] = p;
+            idx[p] = (int)p;
             rowid[p] = r;
         }
     }
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
     float acc[VEC];
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
     int prev = -1;
-    for (int cb = 0; cb < total; cb += kChunk) {
+    for (int64_t cb64 = 0; cb64 < total; cb64 += kChunk) {   // 64-bit: total may lie within kChunk of 2^31
+        const int cb = (int)cb64;
         const int cn = min(kChunk, total - cb);
         const int nt = (cn + 63) >> 6;
         int r[NT];

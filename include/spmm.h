@@ -60,7 +60,9 @@ enum spmm_status {
 enum spmm_option {
     SPMM_OPT_SPLIT_T = 1,      /* rows with more than T entries are split; -1 auto */
     SPMM_OPT_SPLIT_L = 2,      /* piece length of split rows; -1 auto             */
-    SPMM_OPT_SPLIT_MODE = 3,   /* -1 auto (split only skewed graphs), 0 off, 1 on */
+    SPMM_OPT_SPLIT_MODE = 3,   /* -1 auto (split only skewed graphs), 0 off, 1 on.
+                                  In every mode rows of more than 2^24 entries
+                                  are split, and T and L are capped at 2^24   */
     SPMM_OPT_LANES = 4,        /* lanes per row G in {4,8,16,32,64}; 0 auto       */
     SPMM_OPT_COARSEN = 5,      /* vectors per lane F in {1,2}; 0 auto             */
     SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto            */

@@ -16,4 +16,8 @@ from .graphs import (  # noqa: F401
     knn_line,
     relabel,
     csr_from_pairs,
+    hashed_cols,
+    small_int_features,
+    alternating_rowptr,
+    limit_degrees,
 )

@@ -397,3 +397,48 @@ def relabel(g: Graph, seed: int) -> Graph:
     col = pi[g.col[src]]
     val = None if g.val is None else g.val[src]
     return Graph(name=g.name + "-relabelled", M=g.M, K=g.K, rowptr=rowptr, col=col, val=val)
+
+
+# --- Graphs at the library's index limits -------------------------------------
+#
+# Too large to build on the host, these are given by formulas on integer
+# arrays: a test evaluates them on the device (torch tensors) to build the
+# graph and on the host (numpy arrays) to rebuild any row it samples.  Only
+# the integer operators *, +, % and // are used, which both libraries apply
+# elementwise with the same int64 results (no product exceeds 2^63).
+
+HASH_MUL = 2654435761        # Knuth's multiplicative hashing constant, 2^32 / golden ratio
+
+
+def hashed_cols(p, K: int):
+    """Column of the entry at position p (0 <= p < 2^31): (p * 2654435761 + 7)
+    mod K, spread over [0, K) with no order within a row."""
+    return (p * HASH_MUL + 7) % K
+
+
+def small_int_features(j):
+    """Feature of B row j, an integer in [-1000, 1000] (exact in fp32):
+    (j * 40503) mod 2001 - 1000."""
+    return (j * 40503) % 2001 - 1000
+
+
+def alternating_rowptr(i):
+    """rowptr of the graph whose odd rows hold one entry and even rows none:
+    rowptr[i] = i // 2."""
+    return i // 2
+
+
+def limit_degrees(M: int, nnz: int, n_heavy: int, giant: int) -> np.ndarray:
+    """Degrees of M rows summing to exactly nnz: light row i holds
+    (i * 7919) mod 701 entries, row M - 1 holds `giant` entries, and n_heavy
+    rows spread evenly over [0, M - 1) share the remainder (the first of them
+    takes what does not divide evenly)."""
+    deg = (np.arange(M, dtype=np.int64) * 7919) % 701
+    heavy = np.linspace(0, M - 2, n_heavy).astype(np.int64)
+    deg[heavy] = 0
+    deg[M - 1] = giant
+    rest = nnz - int(deg.sum())
+    assert rest > 0, "light rows and the giant row already exceed nnz"
+    deg[heavy] = rest // n_heavy
+    deg[heavy[0]] += rest - (rest // n_heavy) * n_heavy
+    return deg
