@@ -95,6 +95,45 @@ def test_ragged_widths(orc, N):
     G.spmm_plan_destroy(plan)
 
 
+@pytest.mark.parametrize("route", ["rows", "tiles", "split", "window"])
+def test_max_with_infinite_products(orc, route):
+    """Finite inputs whose products overflow to -inf: weights 1e30 times B
+    entries of -1e30 in half of B's columns.  Some rows hold only such
+    entries (their max is -inf and their argmax the first entry), some start
+    with them and continue with finite products, the rest are ordinary.  The
+    max kernels start from -inf and take strictly larger values, then give
+    an all -inf output its first entry: the oracle's stored-order rule."""
+    rng = np.random.default_rng(71)
+    g = W.random_csr(rng, 3000, 2048, mean_deg=9.0, empty_frac=0.05, dup_frac=0.1,
+                     shuffle_rows=route != "window", weighted=True, heavy_rows=6 if route == "split" else 0,
+                     heavy_deg=700)
+    deg = g.degrees()
+    all_inf = rng.choice(np.flatnonzero(deg > 0), size=300, replace=False)
+    all_inf = np.union1d(all_inf, np.flatnonzero(deg == 700)[:3])   # split rows: every piece all -inf
+    lead_inf = rng.choice(np.setdiff1d(np.flatnonzero(deg > 2), all_inf), size=300, replace=False)
+    for i in all_inf:
+        g.val[g.rowptr[i]:g.rowptr[i + 1]] = 1e30
+    for i in lead_inf:
+        g.val[g.rowptr[i]:g.rowptr[i] + 2] = 1e30
+    N = 128 if route == "window" else 24
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    B[:, ::2] = -1e30
+    opts = {"rows": [(G.SPMM_OPT_TILES, 0)], "tiles": [(G.SPMM_OPT_TILES, 1)],
+            "split": [(G.SPMM_OPT_SPLIT_T, 64), (G.SPMM_OPT_SPLIT_L, 50), (G.SPMM_OPT_SPLIT_MODE, 1)],
+            "window": [(G.SPMM_OPT_WINDOW, 1)]}[route]
+    plan = make_plan(g, opts)
+    _, _, _, Bd = to_dev(g, B)
+    C, arg = gpu_run(plan, g.M, Bd, "max")
+    info = G.spmm_plan_info(plan)
+    routed = {"rows": info["route_tiled"] == 0 and info["route_window"] == 0,
+              "tiles": info["route_tiled"] == 1, "split": info["n_heavy"] > 0,
+              "window": info["route_window"] > 0}[route]
+    assert routed, f"{route} not taken: {info}"
+    assert np.isneginf(C[all_inf][:, ::2]).all()
+    check(orc, g, B, "max", C, arg, what=f"-inf products, {route}")
+    G.spmm_plan_destroy(plan)
+
+
 def test_ties_and_signed_zeros(orc):
     rng = np.random.default_rng(7)
     for weighted in (False, True):
