@@ -472,9 +472,9 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //  * fp16 matrix-core tiles only when the caller enabled them (they follow
 //    the looser fp16 contract) and the run is a sum or mean with 16-byte
 //    aligned float4 access;
-//  * XCD remap in chunks of 64 blocks (rows sharing B rows meet in one L2,
+//  * XCD remap in chunks of 256 blocks (rows sharing B rows meet in one L2,
 //    all XCDs sweep one region together): measured neutral or better on
-//    every regime.
+//    every regime, and better than chunks of 64 or 1024.
 // The thresholds come from rocprofv3-timed sweeps on the five regimes.
 Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const void *C, const void *argmax) {
     Route r;

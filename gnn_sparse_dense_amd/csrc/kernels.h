@@ -15,7 +15,7 @@ constexpr int kChunk = 256;             // col/val entries a wave stages in LDS 
 constexpr int kPartialWidth = 256;      // columns per pass of the split path
 constexpr int kRowsPerScanBlock = 1024; // rows per block of the plan-time scans
 constexpr int kXcds = 8;                // MI355X: 8 XCDs, 32 CUs each
-constexpr int kXcdChunk = 64;           // consecutive blocks one XCD takes at a time
+constexpr int kXcdChunk = 256;           // consecutive blocks one XCD takes at a time
 constexpr int kTileRows = 8;            // rows per row-tile record
 constexpr int kTileLdsWords = 512;      // LDS words per wave for row-tile records (2 records)
 constexpr int kTileMaxCap = 120;        // largest entries per row-tile record
