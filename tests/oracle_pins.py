@@ -525,9 +525,47 @@ def pin_rcm(orc):
             assert np.all(np.diff(cq[rq[i]:rq[i + 1]]) >= 0)
 
 
+def _read_fused_golden():
+    B, entries, expect = {}, [], []
+    with open(os.path.join(GOLDEN, "fused_rounding_hand.txt")) as f:
+        for line in f:
+            t = line.split("#")[0].split()
+            if not t:
+                continue
+            if t[0] == "B":
+                B[int(t[1])] = float.fromhex(t[2])
+            elif t[0] == "entry":
+                entries.append((int(t[1]), int(t[2]), float.fromhex(t[3])))
+            elif t[0] == "expect":
+                expect.append((t[1], t[2] == "fused", int(t[3]), float.fromhex(t[4])))
+    return B, entries, expect
+
+
+def pin_fused_rounding(orc):
+    """Plain and fused sums on a row where one rounding of the multiply-add
+    and two roundings give different bits (hand-worked golden), in both entry
+    orders (stored order rules)."""
+    Bd, entries, expect = _read_fused_golden()
+    K = len(Bd)
+    M = max(r for r, _, _ in entries) + 1
+    B = np.array([[Bd[k]] for k in range(K)], np.float32)
+    rowptr = np.zeros(M + 1, np.int64)
+    for r, _, _ in entries:
+        rowptr[r + 1] += 1
+    rowptr = np.cumsum(rowptr)
+    col = np.array([c for _, c, _ in entries], np.int64)
+    val = np.array([a for _, _, a in entries], np.float32)
+    for red, fused, row, want in expect:
+        C = orc.spmm(rowptr, col, val, M, K, B, red, fused=fused)
+        got = np.float32(C[row, 0])
+        assert got.view(np.uint32) == np.float32(want).view(np.uint32), \
+            f"{red} fused={fused} row {row}: {float(got).hex()} != {want.hex()}"
+
+
 ALL_PINS = [
     pin_dense_bruteforce, pin_scipy_product, pin_identity, pin_ones, pin_empty_rows,
     pin_max_numpy, pin_val_null_is_ones, pin_mean_sum_relation, pin_row_subset,
     pin_partition, pin_descriptors, pin_validate, pin_mac_gap, pin_tiny_config,
     pin_coo_to_csr, pin_transpose, pin_max_backward, pin_features, pin_rcm,
+    pin_fused_rounding,
 ]

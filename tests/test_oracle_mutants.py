@@ -54,6 +54,8 @@ MUTANTS = {
                                  "if (g_deg[x] != g_deg[y]) return (g_deg[x] < g_deg[y]) - (g_deg[x] > g_deg[y]);"),
     "rcm_degree_counts_duplicates": ("        deg[i] = w - b;", "        deg[i] = n;"),
     "permute_columns_not_renamed": ("buf[q].c = inv[col[rowptr[o] + q]];", "buf[q].c = col[rowptr[o] + q];"),
+    "fused_is_unfused": ("acc = fmaf(val[p], b, acc);", "acc = acc + val[p] * b;"),
+    "unfused_is_fused": ("acc = acc + product(val, p, b);", "acc = fmaf(val ? val[p] : 1.0f, b, acc);"),
     "permute_rows_unsorted": ("        qsort(buf, (size_t)n, sizeof(cp_pair), cmp_cp);\n", ""),
 }
 
