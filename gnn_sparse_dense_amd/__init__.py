@@ -38,6 +38,7 @@ SPMM_OPT_MFMA = 11
 SPMM_OPT_VBLOCK = 12
 SPMM_OPT_BALANCE = 13
 SPMM_OPT_PIECE_ORDER = 14
+SPMM_OPT_MEM_LIMIT = 15
 
 SPMM_REORDER_RCM = 1
 
@@ -45,7 +46,7 @@ EXPORTED = (
     "spmm_plan_create", "spmm_run", "spmm_plan_destroy", "spmm_plan_info",
     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
     "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward", "spmm_plan_features",
-    "spmm_plan_reorder", "spmm_plan_permute",
+    "spmm_plan_reorder", "spmm_plan_permute", "spmm_set_mem_limit", "spmm_mem_stats",
 )
 
 
@@ -78,6 +79,14 @@ class _Info(ctypes.Structure):
         ("pair_vectors", ctypes.c_int64), ("pair_padding", ctypes.c_double),
         ("pairs_built", ctypes.c_int32), ("route_pairs", ctypes.c_int32),
         ("merge_segments", ctypes.c_int64), ("route_merge", ctypes.c_int32), ("piece_order", ctypes.c_int32),
+        ("generation", ctypes.c_int64), ("device_bytes", ctypes.c_int64), ("mem_limit", ctypes.c_int64),
+    ]
+
+
+class _MemStats(ctypes.Structure):
+    _fields_ = [
+        ("in_use", ctypes.c_int64), ("last_call_peak", ctypes.c_int64),
+        ("last_call_allocs", ctypes.c_int64), ("thread_limit", ctypes.c_int64),
     ]
 
 
@@ -127,6 +136,10 @@ def _load() -> ctypes.CDLL:
     lib.spmm_plan_permute.restype = p
     lib.spmm_max_backward.argtypes = [p, p, p, p, i64, p]
     lib.spmm_max_backward.restype = i32
+    lib.spmm_set_mem_limit.argtypes = [i64]
+    lib.spmm_set_mem_limit.restype = i32
+    lib.spmm_mem_stats.argtypes = [ctypes.POINTER(_MemStats)]
+    lib.spmm_mem_stats.restype = i32
     return lib
 
 
@@ -178,16 +191,54 @@ def _check_gpu(**tensors):
             raise ValueError(f"{name} must be a GPU tensor")
 
 
+# (M, K) of each live plan handle, so that row counts are checked on the host
+# before an address reaches the library (the C ABI cannot see a tensor's size).
+_plan_dims: dict = {}
+
+
+def _dims(plan: int):
+    d = _plan_dims.get(plan)
+    if d is None:
+        info = spmm_plan_info(plan)
+        d = (int(info["M"]), int(info["K"]))
+        _plan_dims[plan] = d
+    return d
+
+
+def _check_rows(name, t, rows):
+    if t is None or isinstance(t, int):
+        return
+    if t.shape[0] != rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, expected {rows}")
+
+
+def _check_vector(name, t, dtype, min_len=None, exact_len=None):
+    if t is None or isinstance(t, int):
+        return
+    if str(t.dtype).split(".")[-1] != dtype or not t.is_contiguous() or t.dim() != 1:
+        raise TypeError(f"{name} must be a contiguous 1-D {dtype} tensor")
+    if exact_len is not None and t.numel() != exact_len:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {exact_len}")
+    if min_len is not None and t.numel() < min_len:
+        raise ValueError(f"{name} has {t.numel()} elements, fewer than the {min_len} the CSR holds")
+
+
 def spmm_plan_create(rowptr, col, val, M: int, K: int) -> int:
     """Plan handle for the CSR (rowptr int64 [M+1], col int64 [nnz], val fp32 or None)."""
-    for name, t, dt in (("rowptr", rowptr, "int64"), ("col", col, "int64"), ("val", val, "float32")):
-        if t is not None and not isinstance(t, int):
-            if str(t.dtype).split(".")[-1] != dt or not t.is_contiguous():
-                raise TypeError(f"{name} must be a contiguous {dt} tensor")
-    h = _lib.spmm_plan_create(_addr(rowptr), _addr(col), _addr(val), int(M), int(K))
+    M, K = int(M), int(K)
+    _check_vector("rowptr", rowptr, "int64", exact_len=M + 1 if M >= 0 else None)
+    _check_vector("col", col, "int64")
+    _check_vector("val", val, "float32")
+    if rowptr is not None and not isinstance(rowptr, int) and M >= 0:
+        nnz = int(rowptr[M].item())        # the library reads the same entry
+        if nnz >= 0:
+            _check_vector("col", col, "int64", min_len=nnz)
+            _check_vector("val", val, "float32", min_len=nnz)
+    h = _lib.spmm_plan_create(_addr(rowptr), _addr(col), _addr(val), M, K)
     if not h:
         st, msg = spmm_last_error()
         raise SpmmError(st, msg)
+    _plan_dims[h] = (M, K)
     return h
 
 
@@ -198,6 +249,10 @@ def spmm_run(plan: int, B, C, argmax, N: int, reduce, stream=None) -> None:
     _check_matrix("B", B, "float32", None, int(N))
     _check_matrix("C", C, "float32", None, int(N))
     _check_matrix("argmax", argmax, "int64", None if isinstance(C, int) or C is None else C.shape[0], int(N))
+    M, K = _dims(plan)
+    _check_rows("B", B, K)
+    _check_rows("C", C, M)
+    _check_rows("argmax", argmax, M)
     _check_gpu(B=B, C=C, argmax=argmax)
     if stream is None:
         import torch
@@ -208,6 +263,7 @@ def spmm_run(plan: int, B, C, argmax, N: int, reduce, stream=None) -> None:
 
 
 def spmm_plan_destroy(plan: int) -> None:
+    _plan_dims.pop(plan, None)
     _check(_lib.spmm_plan_destroy(plan))
 
 
@@ -246,6 +302,18 @@ def spmm_plan_features(plan: int, V: int = 2) -> dict:
     return {name: getattr(f, name) for name, _ in _Features._fields_}
 
 
+def spmm_set_mem_limit(nbytes: int) -> None:
+    """Limit (bytes, 0 = none) on the device memory one library call of the
+    calling thread may allocate."""
+    _check(_lib.spmm_set_mem_limit(int(nbytes)))
+
+
+def spmm_mem_stats() -> dict:
+    m = _MemStats()
+    _check(_lib.spmm_mem_stats(ctypes.byref(m)))
+    return {name: getattr(m, name) for name, _ in _MemStats._fields_}
+
+
 def spmm_plan_set_option(plan: int, option: int, value: int) -> None:
     _check(_lib.spmm_plan_set_option(plan, int(option), int(value)))
 
@@ -254,6 +322,10 @@ def spmm_coo_to_csr(row, col, val, M: int, K: int):
     """Stable edge-list -> CSR on the device: returns (rowptr, col, val) tensors."""
     import torch
     E = int(row.numel())
+    _check_vector("row", row, "int64", exact_len=E)
+    _check_vector("col", col, "int64", exact_len=E)
+    _check_vector("val", val, "float32", exact_len=E)
+    _check_gpu(row=row, col=col, val=val)
     dev = row.device
     rowptr = torch.empty(M + 1, dtype=torch.int64, device=dev)
     col_out = torch.empty(max(E, 1), dtype=torch.int64, device=dev)[:E]
@@ -283,6 +355,8 @@ def spmm_plan_reorder(plan: int, method: int = 1):
 
 def spmm_plan_permute(plan: int, perm) -> int:
     """Plan of P A P^T for a device int64 permutation (synchronous)."""
+    M, _ = _dims(plan)
+    _check_vector("perm", perm, "int64", exact_len=M)
     h = _lib.spmm_plan_permute(plan, _addr(perm) if perm is not None and perm.numel() else None)
     if not h:
         st, msg = spmm_last_error()
@@ -291,6 +365,16 @@ def spmm_plan_permute(plan: int, perm) -> int:
 
 
 def spmm_max_backward(plan_t: int, argmax, dC, dB, N: int, stream=None) -> None:
+    """dB [K, N] of a max aggregation; plan_t is the transpose [K, M] of the
+    forward adjacency, argmax and dC are [M, N]."""
+    _check_matrix("argmax", argmax, "int64", None, int(N))
+    _check_matrix("dC", dC, "float32", None, int(N))
+    _check_matrix("dB", dB, "float32", None, int(N))
+    Mt, Kt = _dims(plan_t)
+    _check_rows("argmax", argmax, Kt)
+    _check_rows("dC", dC, Kt)
+    _check_rows("dB", dB, Mt)
+    _check_gpu(argmax=argmax, dC=dC, dB=dB)
     if stream is None:
         import torch
         stream = torch.cuda.current_stream().cuda_stream

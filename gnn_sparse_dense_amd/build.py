@@ -20,6 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = [
     "api.cpp",
+    "alloc.cpp",
     "plan_kernels.hip",
     "combine.hip",
     "row_kernels_v1.hip",

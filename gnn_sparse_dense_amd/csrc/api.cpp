@@ -10,6 +10,7 @@
 #include <new>
 #include <vector>
 
+#include "alloc.h"
 #include "plan.h"
 
 #define SPMM_API extern "C" __attribute__((visibility("default")))
@@ -40,8 +41,11 @@ int succeed() {
     return SPMM_OK;
 }
 
+int fail_oom(const char *context);
+
 int fail_hip(hipError_t e, const char *what) {
     (void)hipGetLastError();
+    if (e == hipErrorOutOfMemory) return fail_oom(what);
     return fail(SPMM_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -57,23 +61,27 @@ bool is_device_ptr(const void *p) {
     return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
 }
 
+// A failed device allocation as a status: OOM names the buffer and, when the
+// memory limit refused it, the limit.
+int fail_oom(const char *context) {
+    const OomInfo o = last_oom();
+    if (o.simulated)
+        return fail(SPMM_E_OOM, "%s: device allocation of %s (%lld bytes) exceeds the memory limit of %lld bytes",
+                    context, o.what, (long long)o.bytes, (long long)o.limit);
+    return fail(SPMM_E_OOM, "%s: device allocation of %s (%lld bytes) failed", context, o.what, (long long)o.bytes);
+}
+
 template <typename T>
 int dev_alloc(T **p, int64_t count, const char *what) {
     *p = nullptr;
     if (count <= 0) return SPMM_OK;
-    const hipError_t e = hipMalloc(reinterpret_cast<void **>(p), (size_t)count * sizeof(T));
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        *p = nullptr;
-        return fail(SPMM_E_OOM, "device allocation of %s (%lld bytes) failed: %s", what,
-                    (long long)(count * (int64_t)sizeof(T)), hipGetErrorString(e));
-    }
+    if (dmalloc(p, (size_t)count * sizeof(T), what) != hipSuccess) return fail_oom("out of device memory");
     return SPMM_OK;
 }
 
 template <typename T>
 void dev_free(T *&p) {
-    if (p) (void)hipFree(p);
+    dfree(p);
     p = nullptr;
 }
 
@@ -159,6 +167,38 @@ void free_plan(spmm_plan *p) {
     dev_free(p->val);
     delete p;
 }
+
+// Every device buffer a plan may own (null when not built).
+std::vector<const void *> plan_buffers(const spmm_plan *p) {
+    return {p->rowptr, p->col, p->val, p->heavy_rows, p->seg_first, p->seg_begin, p->seg_end, p->seg_order,
+            p->partial, p->part_arg, p->tiles, p->win_lo, p->win_in, p->mfma_tiles, p->mfma_tiles_lo,
+            p->mfma_tile_exp, p->mfma_rowptr, p->mfma_col, p->mfma_val, p->pair_prow, p->pair_col, p->pair_val,
+            p->merge_seg_row, p->merge_seg_entry, p->merge_carry_row, p->merge_carry_arg, p->merge_carry};
+}
+
+// Device bytes a plan holds.
+int64_t plan_bytes(const spmm_plan *p) {
+    int64_t b = 0;
+    for (const void *q : plan_buffers(p)) b += dbytes(q);
+    return b;
+}
+
+// Budget of one call on plan p (or on no plan).
+struct PlanScope {
+    CallScope scope;
+    explicit PlanScope(const spmm_plan *p) : scope(p ? plan_bytes(p) : 0, p ? p->mem_limit : 0) {}
+};
+
+// Bumps the plan's generation when a call changed the set of its device
+// buffers: kernels captured before then hold addresses that may be freed.
+struct GenerationGuard {
+    spmm_plan *p;
+    std::vector<const void *> before;
+    explicit GenerationGuard(spmm_plan *plan) : p(plan), before(plan_buffers(plan)) {}
+    ~GenerationGuard() {
+        if (plan_buffers(p) != before) ++p->generation;
+    }
+};
 
 // Restores the caller's current device on scope exit.
 struct DeviceGuard {
@@ -274,11 +314,6 @@ int build_split(spmm_plan *p) {
             return st;
         }
         e = build_piece_order(p->col, p->seg_begin, p->n_seg, p->seg_order);
-        if (e == hipErrorOutOfMemory) {
-            (void)hipGetLastError();
-            free_split(p);
-            return fail(SPMM_E_OOM, "piece order: device allocation failed");
-        }
         if (e != hipSuccess) {
             free_split(p);
             return fail_hip(e, "piece order");
@@ -402,11 +437,6 @@ int build_pairs(spmm_plan *p) {
     if (st) return st;
     PairOutput out;
     const hipError_t e = pair_build(p->rowptr, p->col, p->val, p->M, p->K, p->nnz, p->pair_prow, &out);
-    if (e == hipErrorOutOfMemory) {
-        (void)hipGetLastError();
-        free_pairs(p);
-        return fail(SPMM_E_OOM, "V = 2 panel build: device allocation failed");
-    }
     if (e != hipSuccess) {
         free_pairs(p);
         return fail_hip(e, "V = 2 panel build");
@@ -587,9 +617,25 @@ SPMM_API int spmm_last_error(char *buf, int64_t cap) {
     return t_status;
 }
 
+SPMM_API int spmm_set_mem_limit(int64_t bytes) {
+    if (bytes < 0) return fail(SPMM_E_INVALID_ARG, "memory limit must be >= 0 (0: none)");
+    set_thread_limit(bytes);
+    return succeed();
+}
+
+SPMM_API int spmm_mem_stats(struct spmm_mem_stats *out) {
+    if (!out) return fail(SPMM_E_INVALID_ARG, "output is NULL");
+    out->in_use = dbytes_in_use();
+    out->last_call_peak = last_call_peak();
+    out->last_call_allocs = last_call_allocs();
+    out->thread_limit = thread_limit();
+    return succeed();
+}
+
 SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const float *val,
                                       int64_t M, int64_t K) {
     const auto t0 = std::chrono::steady_clock::now();
+    PlanScope budget(nullptr);
     if (M < 0 || K < 0) {
         fail(SPMM_E_INVALID_ARG, "negative size (M=%lld, K=%lld)", (long long)M, (long long)K);
         return nullptr;
@@ -806,6 +852,10 @@ SPMM_API int spmm_plan_destroy(spmm_plan_t plan) {
 SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
     if (!p) return fail(SPMM_E_INVALID_ARG, "plan is NULL");
     DeviceGuard dg(p->device);
+    PlanScope budget(p);
+    GenerationGuard gen(p);
+    const int64_t prev_T = p->opt_T, prev_L = p->opt_L, prev_split = p->opt_split;
+    const int prev_order = p->opt_piece_order;
     switch (option) {
         case SPMM_OPT_SPLIT_T:
             if (value < -1) return fail(SPMM_E_INVALID_ARG, "split threshold must be >= -1");
@@ -828,15 +878,24 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (st) return st;
             return succeed();
         }
-        case SPMM_OPT_WINDOW:
+        case SPMM_OPT_WINDOW: {
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "window must be -1, 0 or 1");
-            if (value == 1) {
-                DeviceGuard dg(p->device);
+            const hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail_hip(e, "synchronise before changing the window runs");
+            // the per-row runs serve only the window kernel: off frees them,
+            // on (or automatic with community structure) builds them
+            p->opt_window = 0;
+            if (value == 0) {
+                free_window_runs(p);
+                return succeed();
+            }
+            if (value == 1 || p->win_frac >= 0.5) {
                 const int st = build_window_runs(p);
                 if (st) return st;
             }
             p->opt_window = value;
             return succeed();
+        }
         case SPMM_OPT_LANES:
             if (!(value == 0 || value == 4 || value == 8 || value == 16 || value == 32 || value == 64))
                 return fail(SPMM_E_INVALID_ARG, "lanes per row must be 0, 4, 8, 16, 32 or 64");
@@ -859,6 +918,10 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "piece order must be 0 or 1");
             p->opt_piece_order = (int)value;
             break;
+        case SPMM_OPT_MEM_LIMIT:
+            if (value < 0) return fail(SPMM_E_INVALID_ARG, "memory limit must be >= 0 (0: none)");
+            p->mem_limit = value;
+            return succeed();
         case SPMM_OPT_NT_STORE:
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
@@ -919,7 +982,22 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
     if (e != hipSuccess) return fail_hip(e, "synchronise before rebuilding the split");
     int st = build_split(p);
     if (!st) st = build_tiles(p);
-    if (st) return st;
+    if (st) {
+        // keep the plan usable: back to the previous split parameters (the
+        // memory they held was just freed), keeping the first error
+        const int keep = t_status;
+        char msg[sizeof(t_msg)];
+        std::memcpy(msg, t_msg, sizeof(msg));
+        p->opt_T = prev_T;
+        p->opt_L = prev_L;
+        p->opt_split = prev_split;
+        p->opt_piece_order = prev_order;
+        BudgetPause restore_what_the_plan_held;
+        if (build_split(p) == SPMM_OK) (void)build_tiles(p);
+        t_status = keep;
+        std::memcpy(t_msg, msg, sizeof(msg));
+        return st;
+    }
     return succeed();
 }
 
@@ -967,6 +1045,9 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.merge_segments = p->merge_seg_row ? p->merge_nseg : 0;
     info.route_merge = p->route.merge ? 1 : 0;
     info.piece_order = p->seg_order != nullptr ? 1 : 0;
+    info.generation = p->generation;
+    info.device_bytes = plan_bytes(p);
+    info.mem_limit = p->mem_limit;
 
     *out = info;
     return succeed();
@@ -1212,6 +1293,7 @@ SPMM_API int spmm_plan_features(spmm_plan_t p, int64_t V, struct spmm_features *
     if (!p || !out) return fail(SPMM_E_INVALID_ARG, "plan or output is NULL");
     if (V < 1 || V > 64) return fail(SPMM_E_INVALID_ARG, "V must be in [1, 64]");
     DeviceGuard dg(p->device);
+    PlanScope budget(p);
     struct spmm_features f;
     std::memset(&f, 0, sizeof(f));
     f.n = p->M;
@@ -1237,10 +1319,6 @@ SPMM_API int spmm_plan_features(spmm_plan_t p, int64_t V, struct spmm_features *
     int64_t bw_sum = 0, bw_max = 0, rows = 0, distinct = 0, vectors = 0;
     if (e == hipSuccess)
         e = pattern_features(p->rowptr, p->col, p->M, p->K, p->nnz, V, &bw_sum, &bw_max, &rows, &distinct, &vectors);
-    if (e == hipErrorOutOfMemory) {
-        (void)hipGetLastError();
-        return fail(SPMM_E_OOM, "feature pass: device allocation failed");
-    }
     if (e != hipSuccess) return fail_hip(e, "feature pass");
     f.mean_bandwidth = rows > 0 ? (double)bw_sum / (double)rows : 0.0;
     f.max_bandwidth = bw_max;
@@ -1259,13 +1337,10 @@ SPMM_API int spmm_plan_reorder(spmm_plan_t p, int method, int64_t *perm) {
     if (p->M == 0) return succeed();
     if (!is_device_ptr(perm)) return fail(SPMM_E_INVALID_ARG, "perm is NULL or not device memory");
     DeviceGuard dg(p->device);
+    PlanScope budget(p);
     hipError_t e = hipDeviceSynchronize();
     int64_t levels = 0;
     if (e == hipSuccess) e = rcm_order(p->rowptr, p->col, p->M, p->nnz, perm, &levels);
-    if (e == hipErrorOutOfMemory) {
-        (void)hipGetLastError();
-        return fail(SPMM_E_OOM, "reordering: device allocation failed");
-    }
     if (e != hipSuccess) return fail_hip(e, "reordering");
     return succeed();
 }
@@ -1284,6 +1359,7 @@ SPMM_API spmm_plan_t spmm_plan_permute(spmm_plan_t p, const int64_t *perm) {
         return nullptr;
     }
     DeviceGuard dg(p->device);
+    PlanScope budget(p);
     int64_t *rp = nullptr, *cl = nullptr;
     float *vl = nullptr;
     if (dev_alloc(&rp, p->M + 1, "permuted rowptr") || dev_alloc(&cl, p->nnz, "permuted col") ||
@@ -1307,8 +1383,9 @@ SPMM_API spmm_plan_t spmm_plan_permute(spmm_plan_t p, const int64_t *perm) {
     return t;
 }
 
-SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
-                             int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out) {
+// Argument checks shared by the edge-list entry points.
+static int check_coo_args(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                   const int64_t *rowptr_out, const int64_t *col_out, const float *val_out) {
     if (E < 0 || M < 0 || K < 0) return fail(SPMM_E_INVALID_ARG, "negative size");
     if (E >= INT_MAX || M >= INT_MAX || K >= INT_MAX)
         return fail(SPMM_E_UNSUPPORTED, "E, M and K must be below 2^31 - 1");
@@ -1320,8 +1397,15 @@ SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float
         if (val && !is_device_ptr(val)) return fail(SPMM_E_INVALID_ARG, "val is not device memory");
         if (val && !is_device_ptr(val_out)) return fail(SPMM_E_INVALID_ARG, "val_out is NULL or not device memory");
     }
+    return SPMM_OK;
+}
+
+SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                             int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out) {
+    if (const int st = check_coo_args(row, col, val, E, M, K, rowptr_out, col_out, val_out)) return st;
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail_hip(e, "synchronise before the edge-list sort");
+    PlanScope budget(nullptr);
     int64_t bad = -1;
     e = coo_to_csr(row, col, val, E, M, K, rowptr_out, col_out, val ? val_out : nullptr, &bad, nullptr);
     if (e != hipSuccess) return fail_hip(e, "edge-list sort");
@@ -1340,6 +1424,7 @@ SPMM_API spmm_plan_t spmm_plan_transpose(spmm_plan_t p, int scale) {
         return nullptr;
     }
     DeviceGuard dg(p->device);
+    PlanScope budget(p);
     int64_t *rp = nullptr, *cl = nullptr;
     float *vl = nullptr;
     const bool want_val = p->val != nullptr || scale == 1;

@@ -3,7 +3,8 @@
 // A row longer than the split threshold is cut into fixed-length pieces that
 // run as independent tasks of the row kernel (ParamSpMM section 3.2: workload
 // balancing splits a heavy row's entries across warps; graph-spmm card,
-// "Requirements and limits": power-law hubs need a segmented schedule).  The
+// "Requirements and limits": the card leaves the hubs of power-law graphs
+// unbalanced under one warp per row).  The
 // pages combine pieces with atomic adds; here each piece writes its own
 // partial row and this kernel folds them in piece order, so the result does
 // not depend on scheduling: sum = ((P0 + P1) + P2) + ..., max keeps the

@@ -14,6 +14,7 @@
 #include <climits>
 #include <vector>
 
+#include "alloc.h"
 #include "spmm_internal.h"
 
 namespace gspmm {
@@ -133,7 +134,7 @@ hipError_t pattern_features(const int *rowptr, const int *col, int64_t M, int64_
     *bw_sum = *bw_max = *nonempty = *distinct = *vectors = 0;
     if (M == 0) return hipSuccess;
     FeatureRecord *rec = nullptr;
-    hipError_t e = hipMalloc(&rec, sizeof(FeatureRecord) * kFeatBlocks);
+    hipError_t e = dmalloc(&rec, sizeof(FeatureRecord) * kFeatBlocks, "feature records");
     if (e != hipSuccess) return e;
     std::vector<FeatureRecord> h(kFeatBlocks);
     const int64_t gb = feature_grid(M, kWaves);
@@ -149,8 +150,8 @@ hipError_t pattern_features(const int *rowptr, const int *col, int64_t M, int64_
     uint64_t *ka = nullptr, *kb = nullptr;
     void *tmp = nullptr;
     if (e == hipSuccess && nnz > 0) {
-        e = hipMalloc(&ka, sizeof(uint64_t) * nnz);
-        if (e == hipSuccess) e = hipMalloc(&kb, sizeof(uint64_t) * nnz);
+        e = dmalloc(&ka, sizeof(uint64_t) * nnz, "feature sort keys");
+        if (e == hipSuccess) e = dmalloc(&kb, sizeof(uint64_t) * nnz, "feature sort keys (alternate)");
         if (e == hipSuccess) {
             hipLaunchKernelGGL(block_keys_kernel, dim3((unsigned)gb), dim3(kBlock), 0, nullptr, rowptr, col, M, K,
                                V, ka);
@@ -164,7 +165,7 @@ hipError_t pattern_features(const int *rowptr, const int *col, int64_t M, int64_
         hipcub::DoubleBuffer<uint64_t> keys(ka, kb);
         size_t tmp_bytes = 0;
         if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, (int)nnz, 0, end_bit);
-        if (e == hipSuccess) e = hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1);
+        if (e == hipSuccess) e = dmalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1, "feature sort storage");
         if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(tmp, tmp_bytes, keys, (int)nnz, 0, end_bit);
         const int64_t gd = feature_grid(nnz, kBlock);
         if (e == hipSuccess) {
@@ -179,10 +180,10 @@ hipError_t pattern_features(const int *rowptr, const int *col, int64_t M, int64_
                 *vectors += h[b].b;
             }
     }
-    if (tmp) (void)hipFree(tmp);
-    if (ka) (void)hipFree(ka);
-    if (kb) (void)hipFree(kb);
-    (void)hipFree(rec);
+    if (tmp) dfree(tmp);
+    if (ka) dfree(ka);
+    if (kb) dfree(kb);
+    dfree(rec);
     return e;
 }
 

@@ -21,6 +21,7 @@
 // No atomics: results are bitwise reproducible.
 #include <hipcub/hipcub.hpp>
 
+#include "alloc.h"
 #include "row_kernel_impl.h"
 
 namespace gspmm {
@@ -381,10 +382,10 @@ hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val,
     unsigned *tmax = nullptr;
     void *tmp = nullptr;
     size_t tmp_bytes = 0;
-    if ((e = hipMalloc(&cnt, sizeof(int) * (size_t)(M + 1))) != hipSuccess) return e;
+    if ((e = dmalloc(&cnt, sizeof(int) * (size_t)(M + 1), "tile entry counts")) != hipSuccess) return e;
     e = hipMemsetAsync(cnt + M, 0, sizeof(int), s);
     if (e == hipSuccess && atiles_lo && ntiles > 0) {
-        e = hipMalloc(&tmax, sizeof(unsigned) * (size_t)ntiles);
+        e = dmalloc(&tmax, sizeof(unsigned) * (size_t)ntiles, "tile maxima");
         if (e == hipSuccess) e = hipMemsetAsync(tmax, 0, sizeof(unsigned) * (size_t)ntiles, s);
         if (e == hipSuccess) {
             hipLaunchKernelGGL(mfma_tile_build_kernel, dim3((unsigned)wave_grid(M)), dim3(kBlock), 0, s, rowptr, col,
@@ -403,12 +404,12 @@ hipError_t mfma_build_tiles(const int *rowptr, const int *col, const float *val,
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_bytes, cnt, rrowptr, (int)(M + 1), s);
-    if (e == hipSuccess) e = hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1);
+    if (e == hipSuccess) e = dmalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1, "residual scan storage");
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(tmp, tmp_bytes, cnt, rrowptr, (int)(M + 1), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (tmp) (void)hipFree(tmp);
-    if (tmax) (void)hipFree(tmax);
-    (void)hipFree(cnt);
+    if (tmp) dfree(tmp);
+    if (tmax) dfree(tmax);
+    dfree(cnt);
     return e;
 }
 

@@ -21,6 +21,7 @@
 // no arithmetic and no rounding.
 #include <hipcub/hipcub.hpp>
 
+#include "alloc.h"
 #include "row_kernel_impl.h"
 
 namespace gspmm {
@@ -290,15 +291,15 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
     int *pa = nullptr, *pb = nullptr, *cnt = nullptr, *flag = nullptr;
     void *tmp = nullptr;
     size_t tmp_bytes = 0;
-    hipError_t e = hipMalloc(&cnt, sizeof(int) * (size_t)(npanels + 1));
-    if (e == hipSuccess) e = hipMalloc(&flag, sizeof(int));
+    hipError_t e = dmalloc(&cnt, sizeof(int) * (size_t)(npanels + 1), "panel counts");
+    if (e == hipSuccess) e = dmalloc(&flag, sizeof(int), "panel flag");
     if (e == hipSuccess) e = hipMemset(flag, 0, sizeof(int));
     if (e == hipSuccess) e = hipMemset(cnt + npanels, 0, sizeof(int));
     const int64_t n = std::max<int64_t>(nnz, 1);
-    if (e == hipSuccess) e = hipMalloc(&ka, sizeof(uint64_t) * n);
-    if (e == hipSuccess) e = hipMalloc(&kb, sizeof(uint64_t) * n);
-    if (e == hipSuccess) e = hipMalloc(&pa, sizeof(int) * n);
-    if (e == hipSuccess) e = hipMalloc(&pb, sizeof(int) * n);
+    if (e == hipSuccess) e = dmalloc(&ka, sizeof(uint64_t) * n, "panel sort keys");
+    if (e == hipSuccess) e = dmalloc(&kb, sizeof(uint64_t) * n, "panel sort keys (alternate)");
+    if (e == hipSuccess) e = dmalloc(&pa, sizeof(int) * n, "panel sort positions");
+    if (e == hipSuccess) e = dmalloc(&pb, sizeof(int) * n, "panel sort positions (alternate)");
     hipcub::DoubleBuffer<uint64_t> keys(ka, kb);
     hipcub::DoubleBuffer<int> pos(pa, pb);
     if (e == hipSuccess && nnz > 0) {
@@ -309,7 +310,7 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
         int end_bit = 1;
         while (end_bit < 64 && (kmax >> end_bit) != 0) ++end_bit;
         if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_bytes, keys, pos, (int)nnz, 0, end_bit);
-        if (e == hipSuccess) e = hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1);
+        if (e == hipSuccess) e = dmalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1, "panel sort storage");
         if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, keys, pos, (int)nnz, 0, end_bit);
     }
     if (e == hipSuccess && npanels > 0) {
@@ -321,14 +322,14 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
     size_t scan_bytes = 0;
     void *scan_tmp = nullptr;
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(nullptr, scan_bytes, cnt, prow, (int)(npanels + 1));
-    if (e == hipSuccess) e = hipMalloc(&scan_tmp, scan_bytes > 0 ? scan_bytes : 1);
+    if (e == hipSuccess) e = dmalloc(&scan_tmp, scan_bytes > 0 ? scan_bytes : 1, "panel scan storage");
     if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(scan_tmp, scan_bytes, cnt, prow, (int)(npanels + 1));
     int nvec = 0, unsorted = 0;
     if (e == hipSuccess) e = hipMemcpy(&nvec, prow + npanels, sizeof(int), hipMemcpyDeviceToHost);
     if (e == hipSuccess) e = hipMemcpy(&unsorted, flag, sizeof(int), hipMemcpyDeviceToHost);
     if (e == hipSuccess && nvec > 0) {
-        e = hipMalloc(&out->pcol, sizeof(unsigned) * (size_t)nvec);
-        if (e == hipSuccess && val) e = hipMalloc(&out->pval, sizeof(float) * 2 * (size_t)nvec);
+        e = dmalloc(&out->pcol, sizeof(unsigned) * (size_t)nvec, "panel columns");
+        if (e == hipSuccess && val) e = dmalloc(&out->pval, sizeof(float) * 2 * (size_t)nvec, "panel values");
         if (e == hipSuccess) {
             hipLaunchKernelGGL(pair_walk_kernel<true>, dim3((unsigned)walk_grid(npanels)), dim3(kBlock), 0, nullptr,
                                rowptr, col, val, M, K, keys.Current(), pos.Current(), nullptr, nullptr, prow,
@@ -337,8 +338,8 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
         }
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
-            if (out->pcol) (void)hipFree(out->pcol);
-            if (out->pval) (void)hipFree(out->pval);
+            if (out->pcol) dfree(out->pcol);
+            if (out->pval) dfree(out->pval);
             out->pcol = nullptr;
             out->pval = nullptr;
         }
@@ -346,7 +347,7 @@ hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64
     out->nvec = nvec;
     out->unsorted = unsorted;
     for (void *q : {(void *)ka, (void *)kb, (void *)pa, (void *)pb, (void *)cnt, (void *)flag, tmp, scan_tmp})
-        if (q) (void)hipFree(q);
+        if (q) dfree(q);
     return e;
 }
 

@@ -10,6 +10,7 @@
 
 #include <hipcub/hipcub.hpp>
 
+#include "alloc.h"
 #include "spmm_internal.h"
 
 namespace gspmm {
@@ -444,24 +445,24 @@ hipError_t build_piece_order(const int *col, const int *seg_begin, int64_t n_seg
     uint64_t *ka = nullptr, *kb = nullptr;
     void *tmp = nullptr;
     size_t tmp_bytes = 0;
-    hipError_t e = hipMalloc(&ka, sizeof(uint64_t) * n_seg);
-    if (e == hipSuccess) e = hipMalloc(&kb, sizeof(uint64_t) * n_seg);
+    hipError_t e = dmalloc(&ka, sizeof(uint64_t) * n_seg, "piece order keys");
+    if (e == hipSuccess) e = dmalloc(&kb, sizeof(uint64_t) * n_seg, "piece order keys (alternate)");
     if (e == hipSuccess) {
         hipLaunchKernelGGL(piece_keys_kernel, dim3(grid), dim3(kBlock), 0, nullptr, col, seg_begin, n_seg, ka);
         e = hipGetLastError();
     }
     hipcub::DoubleBuffer<uint64_t> keys(ka, kb);
     if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, (int)n_seg);
-    if (e == hipSuccess) e = hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1);
+    if (e == hipSuccess) e = dmalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 1, "piece order sort storage");
     if (e == hipSuccess) e = hipcub::DeviceRadixSort::SortKeys(tmp, tmp_bytes, keys, (int)n_seg);
     if (e == hipSuccess) {
         hipLaunchKernelGGL(piece_ids_kernel, dim3(grid), dim3(kBlock), 0, nullptr, keys.Current(), n_seg, order);
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (tmp) (void)hipFree(tmp);
-    if (ka) (void)hipFree(ka);
-    if (kb) (void)hipFree(kb);
+    if (tmp) dfree(tmp);
+    if (ka) dfree(ka);
+    if (kb) dfree(kb);
     return e;
 }
 

@@ -23,6 +23,7 @@
 #include <climits>
 #include <vector>
 
+#include "alloc.h"
 #include "spmm_internal.h"
 
 namespace gspmm {
@@ -289,12 +290,12 @@ struct Scratch {
     template <typename T>
     hipError_t get(T **p, size_t count) {
         *p = nullptr;
-        hipError_t e = hipMalloc(reinterpret_cast<void **>(p), std::max<size_t>(count, 1) * sizeof(T));
+        hipError_t e = dmalloc(reinterpret_cast<void **>(p), std::max<size_t>(count, 1) * sizeof(T), "reordering scratch");
         if (e == hipSuccess) ptrs.push_back(*p);
         return e;
     }
     ~Scratch() {
-        for (void *q : ptrs) (void)hipFree(q);
+        for (void *q : ptrs) dfree(q);
     }
 };
 

@@ -1,9 +1,10 @@
 // Row kernel of the CSR SpMM: G lanes per output row, 64/G rows per wave64.
 //
 // Mapping (ParamSpMM section 2, Algorithm 1: a worker owns a segment of one C
-// row and walks that row's entries; graph-spmm card, "Method": lanes hold
-// strided slices of the feature columns, each output reduces privately in a
-// register, nothing is shared between waves, so no atomics):
+// row and walks that row's entries; graph-spmm card, "Method": every feature
+// column of a row belongs to one lane, which keeps that output's running value
+// in its own register, and waves never exchange partial results, so there are
+// no atomic updates):
 //   * lane g of a row's group owns columns c0 + (f*G + g)*VEC .. +VEC-1 for
 //     f < F (F = coarsening factor, ParamSpMM section 3.3 / GE-SpMM section
 //     III-C "coarse-grained warp merging"), so for each entry the group's B

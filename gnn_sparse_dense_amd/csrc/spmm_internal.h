@@ -109,6 +109,20 @@ struct MaxGradArgs {
     int64_t rows;            // rows of the transpose (= columns K of the forward)
     int64_t N;
 };
+// Device and host workspace of an edge-list sort (coo_check_blocks(E)
+// records for the range check, hipCUB storage of coo_sort_storage_bytes).
+struct CooWorkspace {
+    int *keys = nullptr, *idx = nullptr, *skeys = nullptr, *perm = nullptr;   // int32 [E] each
+    int64_t *bad = nullptr;          // device [coo_check_blocks(E)]
+    int64_t *bad_host = nullptr;     // host [coo_check_blocks(E)]
+    void *sort = nullptr;
+    size_t sort_bytes = 0;
+};
+int64_t coo_check_blocks(int64_t E);
+hipError_t coo_sort_storage_bytes(int64_t E, int64_t M, size_t *bytes);
+hipError_t coo_to_csr_in(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                         int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad,
+                         const CooWorkspace &w, hipStream_t s);
 hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
                       int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s);
 hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,

@@ -4,12 +4,12 @@
 //    SparseAdj.from_edge_index sorts an unsorted [2, E] edge list into CSR):
 //    a stable LSD radix sort of the rows (hipCUB) keeps each row's entries in
 //    edge-list order, so the result and every later product are deterministic.
-//  * Transposed CSR of a plan (card, "Requirements and limits": the backward of
-//    a sum aggregation is the transposed product from a second adjacency on the
-//    reversed edge list), optionally with weights a / deg_i for the backward of
+//  * Transposed CSR of a plan (card, "Requirements and limits": the card is
+//    forward only and points to the reversed-edge adjacency A^T for the
+//    gradient of a sum), optionally with weights a / deg_i for the backward of
 //    a mean.
-//  * Max-pool backward (card, "Method": the argmax returned in the forward
-//    sweep is what a max-pool backward needs): dB[j][k] sums dC[i][k] over
+//  * Max-pool backward (card, "Method": the forward max reports its winning
+//    neighbour, and that index routes the gradient back): dB[j][k] sums dC[i][k] over
 //    rows i with argmax[i][k] == j, walking row j of the transpose in
 //    ascending i, with no atomics.
 #include <hipcub/hipcub.hpp>
@@ -19,6 +19,7 @@
 
 #include <climits>
 
+#include "alloc.h"
 #include "spmm_internal.h"
 
 namespace gspmm {
@@ -133,89 +134,107 @@ int key_bits(int64_t n) {
     return b;
 }
 
-// Stable sort of (keys, idx) by key into (skeys, perm); temporary storage is
-// allocated here and released before returning.
+// Bytes of hipCUB storage that stable_sort needs for n keys in [0, key_range).
+hipError_t sort_storage_bytes(int64_t n, int64_t key_range, size_t *bytes) {
+    *bytes = 0;
+    return hipcub::DeviceRadixSort::SortPairs(nullptr, *bytes, (const int *)nullptr, (int *)nullptr,
+                                              (const int *)nullptr, (int *)nullptr, (int)n, 0, key_bits(key_range),
+                                              (hipStream_t) nullptr);
+}
+
+// Stable sort of (keys, idx) by key into (skeys, perm) with the caller's
+// hipCUB storage; returns once the sort has finished on stream s.
 hipError_t stable_sort(const int *keys, const int *idx, int *skeys, int *perm, int64_t n, int64_t key_range,
-                       hipStream_t s) {
-    size_t tmp_bytes = 0;
-    hipError_t e = hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_bytes, keys, skeys, idx, perm, (int)n, 0,
-                                                      key_bits(key_range), s);
-    if (e != hipSuccess) return e;
-    void *tmp = nullptr;
-    e = hipMalloc(&tmp, std::max<size_t>(tmp_bytes, 1));
-    if (e != hipSuccess) return e;
-    e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, keys, skeys, idx, perm, (int)n, 0, key_bits(key_range),
-                                          s);
+                       void *tmp, size_t tmp_bytes, hipStream_t s) {
+    const hipError_t e = hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, keys, skeys, idx, perm, (int)n, 0,
+                                                            key_bits(key_range), s);
     const hipError_t e2 = hipStreamSynchronize(s);
-    (void)hipFree(tmp);
     return e != hipSuccess ? e : e2;
 }
 
+// Device buffers of a transpose, freed on scope exit.
 struct Scratch {
     int *keys = nullptr, *idx = nullptr, *skeys = nullptr, *perm = nullptr, *rowid = nullptr;
-    int64_t *bad = nullptr;
+    void *sort = nullptr;
     ~Scratch() {
-        for (int *q : {keys, idx, skeys, perm, rowid})
-            if (q) (void)hipFree(q);
-        if (bad) (void)hipFree(bad);
+        for (void *q : {(void *)keys, (void *)idx, (void *)skeys, (void *)perm, (void *)rowid, sort}) dfree(q);
     }
 };
 
-template <typename T>
-hipError_t alloc(T **p, int64_t n) {
-    return hipMalloc(reinterpret_cast<void **>(p), sizeof(T) * (size_t)std::max<int64_t>(n, 1));
-}
-
 }  // namespace
 
-hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
-                      int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s) {
+int64_t coo_check_blocks(int64_t E) { return (E + kEdgesPerBlock - 1) / kEdgesPerBlock; }
+
+// Edge list -> CSR in the caller's workspace: check the ranges (the host
+// reads one record per block), stable-sort the rows, gather the entries, and
+// write rowptr.  Synchronous on stream s.
+hipError_t coo_to_csr_in(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                         int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad,
+                         const CooWorkspace &w, hipStream_t s) {
     *first_bad = -1;
-    Scratch t;
-    const int64_t nb = (E + kEdgesPerBlock - 1) / kEdgesPerBlock;
-    hipError_t e = alloc(&t.keys, E);
-    if (e == hipSuccess) e = alloc(&t.idx, E);
-    if (e == hipSuccess) e = alloc(&t.skeys, E);
-    if (e == hipSuccess) e = alloc(&t.perm, E);
-    if (e == hipSuccess) e = alloc(&t.bad, nb);
-    if (e != hipSuccess) return e;
+    hipError_t e;
     if (E > 0) {
-        hipLaunchKernelGGL(coo_prepare_kernel, dim3((unsigned)nb), dim3(kBlock), 0, s, row, col, E, M, K, t.keys,
-                           t.idx, t.bad);
-        std::vector<int64_t> bad((size_t)nb);
-        e = hipMemcpyAsync(bad.data(), t.bad, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, s);
+        const int64_t nb = coo_check_blocks(E);
+        hipLaunchKernelGGL(coo_prepare_kernel, dim3((unsigned)nb), dim3(kBlock), 0, s, row, col, E, M, K, w.keys,
+                           w.idx, w.bad);
+        e = hipMemcpyAsync(w.bad_host, w.bad, sizeof(int64_t) * nb, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return e;
-        const int64_t b = *std::min_element(bad.begin(), bad.end());
+        const int64_t b = *std::min_element(w.bad_host, w.bad_host + nb);
         if (b != INT64_MAX) {
             *first_bad = b;
             return hipSuccess;
         }
-        e = stable_sort(t.keys, t.idx, t.skeys, t.perm, E, M, s);
+        e = stable_sort(w.keys, w.idx, w.skeys, w.perm, E, M, w.sort, w.sort_bytes, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(gather_entries_kernel, dim3((unsigned)((E + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
-                           t.perm, E, col, (const int *)nullptr, val, (const int *)nullptr, col_out, val_out);
+                           w.perm, E, col, (const int *)nullptr, val, (const int *)nullptr, col_out, val_out);
     }
     hipLaunchKernelGGL(rowptr_from_sorted_kernel, dim3((unsigned)((E + 1 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       s, t.skeys, E, M, rowptr_out);
+                       s, w.skeys, E, M, rowptr_out);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
+hipError_t coo_sort_storage_bytes(int64_t E, int64_t M, size_t *bytes) { return sort_storage_bytes(E, M, bytes); }
+
+hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
+                      int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s) {
+    *first_bad = -1;
+    CooWorkspace w;
+    const int64_t nb = coo_check_blocks(E);
+    std::vector<int64_t> bad_host((size_t)std::max<int64_t>(nb, 1));
+    w.bad_host = bad_host.data();
+    hipError_t e = E > 0 ? coo_sort_storage_bytes(E, M, &w.sort_bytes) : hipSuccess;
+    if (e == hipSuccess) e = dmalloc_n(&w.keys, E, "edge keys");
+    if (e == hipSuccess) e = dmalloc_n(&w.idx, E, "edge positions");
+    if (e == hipSuccess) e = dmalloc_n(&w.skeys, E, "sorted edge keys");
+    if (e == hipSuccess) e = dmalloc_n(&w.perm, E, "sorted edge positions");
+    if (e == hipSuccess) e = dmalloc_n(&w.bad, nb, "edge range records");
+    if (e == hipSuccess) e = dmalloc(&w.sort, std::max<size_t>(w.sort_bytes, 1), "edge sort storage");
+    if (e == hipSuccess)
+        e = coo_to_csr_in(row, col, val, E, M, K, rowptr_out, col_out, val_out, first_bad, w, s);
+    for (void *q : {(void *)w.keys, (void *)w.idx, (void *)w.skeys, (void *)w.perm, (void *)w.bad, w.sort}) dfree(q);
     return e;
 }
 
 hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
                          bool scale, int64_t *rowptr_t, int64_t *col_t, float *val_t, hipStream_t s) {
     Scratch t;
-    hipError_t e = alloc(&t.keys, nnz);
-    if (e == hipSuccess) e = alloc(&t.idx, nnz);
-    if (e == hipSuccess) e = alloc(&t.skeys, nnz);
-    if (e == hipSuccess) e = alloc(&t.perm, nnz);
-    if (e == hipSuccess) e = alloc(&t.rowid, nnz);
+    size_t sort_bytes = 0;
+    hipError_t e = nnz > 0 ? sort_storage_bytes(nnz, K, &sort_bytes) : hipSuccess;
+    if (e == hipSuccess) e = dmalloc_n(&t.keys, nnz, "transpose keys");
+    if (e == hipSuccess) e = dmalloc_n(&t.idx, nnz, "transpose positions");
+    if (e == hipSuccess) e = dmalloc_n(&t.skeys, nnz, "sorted transpose keys");
+    if (e == hipSuccess) e = dmalloc_n(&t.perm, nnz, "sorted transpose positions");
+    if (e == hipSuccess) e = dmalloc_n(&t.rowid, nnz, "transpose row ids");
+    if (e == hipSuccess) e = dmalloc(&t.sort, std::max<size_t>(sort_bytes, 1), "transpose sort storage");
     if (e != hipSuccess) return e;
     if (nnz > 0) {
         hipLaunchKernelGGL(transpose_prepare_kernel, dim3((unsigned)((M + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
                            rowptr, col, M, t.keys, t.idx, t.rowid);
-        e = stable_sort(t.keys, t.idx, t.skeys, t.perm, nnz, K, s);
+        e = stable_sort(t.keys, t.idx, t.skeys, t.perm, nnz, K, t.sort, sort_bytes, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(gather_entries_kernel, dim3((unsigned)((nnz + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
                            t.perm, nnz, (const int64_t *)nullptr, t.rowid, val, scale ? rowptr : nullptr, col_t,

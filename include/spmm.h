@@ -25,6 +25,10 @@
  *   MEAN : SUM / (number of stored entries), one IEEE fp32 division; 0 if empty.
  *   MAX  : largest t_p (strict '>', so the first of equal values wins) and the
  *          column id col_p of that entry; (0, -1) if the row is empty.
+ * NaN products are outside the MAX contract: a row walked whole keeps the
+ * stored-order rule exactly (a NaN first entry stays the maximum, later NaNs
+ * never win), but for a row cut into pieces (row split, merge path) a NaN
+ * that opens a later piece can hide that piece's larger values.
  * Duplicated (row, col) entries each count; columns need not be sorted.
  * Results are bitwise reproducible from run to run: no atomics are used.
  *
@@ -74,7 +78,10 @@ enum spmm_option {
     SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
                                   1 on: stage each 256-row block of B in LDS
                                   (a faster kernel when every row's columns
-                                  are non-decreasing, bit-identical either way) */
+                                  are non-decreasing, bit-identical either way;
+                                  that kernel's per-row runs, 8 bytes per row,
+                                  are built by -1 with community structure
+                                  and by 1, and freed by 0)                   */
     SPMM_OPT_MFMA = 11,        /* matrix-core tiles for community blocks, see
                                   below: 0 off (default), 1 fp16 tiles, 2 split
                                   fp16 tiles (fp32 tolerance)                 */
@@ -83,11 +90,46 @@ enum spmm_option {
                                   2 build, always use                          */
     SPMM_OPT_BALANCE = 13,     /* load balance: 0 row split of heavy rows
                                   (default), 1 merge path, see below          */
-    SPMM_OPT_PIECE_ORDER = 14  /* 1 (default): the row split's pieces run in
+    SPMM_OPT_PIECE_ORDER = 14, /* 1 (default): the row split's pieces run in
                                   ascending order of their first entry's
                                   column; 0: in partition order.  Same
                                   partition, same bits; rebuilds the split    */
+    SPMM_OPT_MEM_LIMIT = 15    /* bytes of device memory the plan may hold,
+                                  counting the temporaries of a call on it;
+                                  0 (default): no limit.  See "Device memory"
+                                  below                                       */
 };
+
+/*
+ * Device memory.  The pages do not discuss memory limits; the library keeps
+ * every device allocation it makes on a ledger so that callers can bound it:
+ *  - SPMM_OPT_MEM_LIMIT caps what one plan holds: its own buffers plus the
+ *    temporaries (and, for spmm_plan_transpose / spmm_plan_permute, the new
+ *    plan's buffers) of any call made on it.  It is checked when a call
+ *    allocates, not when the option is set.
+ *  - spmm_set_mem_limit caps, for the calling thread, what one call may
+ *    allocate (held at once, counted from zero at the start of the call); it
+ *    covers the calls that are not made on a plan too (spmm_plan_create,
+ *    spmm_coo_to_csr).
+ * An allocation that would pass either limit is not made: the call returns
+ * SPMM_E_OOM naming the buffer, the bytes asked and the limit, exactly as when
+ * the device itself is out of memory.  A failed call frees every buffer it
+ * allocated.  A failed spmm_plan_set_option leaves the plan usable: a failed
+ * optional structure (tiles, panels, merge segments, fp16 tiles, window runs)
+ * is simply absent, and a failed split rebuild puts the previous split
+ * parameters back.  spmm_run never allocates.
+ */
+int spmm_set_mem_limit(int64_t bytes);   /* 0 = no limit; INVALID_ARG if < 0 */
+
+struct spmm_mem_stats {
+    int64_t in_use;            /* device bytes the library holds now, all
+                                  plans and threads of the process           */
+    int64_t last_call_peak;    /* the calling thread's last allocating call:
+                                  most bytes it held at once                 */
+    int64_t last_call_allocs;  /* ... and the number of allocations it made  */
+    int64_t thread_limit;      /* the calling thread's spmm_set_mem_limit    */
+};
+int spmm_mem_stats(struct spmm_mem_stats *out);
 
 /*
  * SPMM_OPT_BALANCE = 1 (merge-based balancing, RA-SpMM related work: the work
@@ -185,6 +227,11 @@ struct spmm_plan_info {
     int32_t route_merge;         /* 1 when the last run used them             */
     int32_t piece_order;         /* 1 when split pieces run in the order of
                                     their first column (SPMM_OPT_PIECE_ORDER) */
+    int64_t generation;          /* bumped by every spmm_plan_set_option call
+                                    that freed or replaced a device buffer of
+                                    the plan (see spmm_run on graph capture) */
+    int64_t device_bytes;        /* device memory the plan holds             */
+    int64_t mem_limit;           /* SPMM_OPT_MEM_LIMIT (0: none)             */
 };
 
 /*
@@ -215,8 +262,14 @@ spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const fl
  * Asynchronous: it validates its arguments, picks a kernel from the plan's
  * descriptors and N, enqueues the kernels and returns without waiting.  It
  * allocates nothing and enqueues kernels only (no memset or copy), so a call
- * can be captured in a HIP graph on a stream in thread-local capture mode
- * and replayed while the plan, B and C stay alive.  B must not overlap C or argmax.  Runs on one plan must
+ * can be captured in a HIP graph on a stream in thread-local capture mode.
+ * A captured call holds the kernel choice and the device addresses of its
+ * time: it may be replayed while the plan, B and C stay alive AND the plan's
+ * generation (spmm_plan_info) is unchanged.  spmm_plan_set_option calls that
+ * build, rebuild or free a structure (split parameters, piece order, tiles,
+ * window runs, fp16 tiles, panels, merge segments) replace buffers that a
+ * captured kernel would still read or write, and bump the generation;
+ * capture again after them.  B must not overlap C or argmax.  Runs on one plan must
  * be ordered on one stream (the plan's split buffer is shared); use one plan
  * per stream for concurrency.  Kernel faults surface at the caller's next
  * synchronisation, as usual in HIP.
@@ -252,7 +305,10 @@ int spmm_plan_partition(spmm_plan_t plan, int64_t *seg_row, int64_t *seg_begin,
 
 /* Set an option (enum spmm_option).  Changing the split parameters rebuilds
  * the split synchronously; other options apply to later runs.  The caller
- * must not have runs on this plan in flight. */
+ * must not have runs on this plan in flight.  Options that free or replace
+ * device buffers bump the plan's generation, which invalidates HIP graphs
+ * captured from earlier runs on the plan (see spmm_run).  Returns OK,
+ * INVALID_ARG, OOM (see "Device memory"), HIP or UNSUPPORTED. */
 int spmm_plan_set_option(spmm_plan_t plan, int option, int64_t value);
 
 /*
@@ -275,8 +331,8 @@ int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, in
 
 /*
  * Plan of the transpose A^T [K, M] of a plan's matrix (graph-spmm card,
- * "Requirements and limits": the backward of a sum aggregation is the
- * transposed product, from an adjacency on the reversed edge list).  Entry
+ * "Requirements and limits": the card is forward only and points to A^T,
+ * the adjacency with every edge reversed, for the gradient of a sum).  Entry
  * (i, j, a) of A becomes (j, i, a'); within a row of A^T, entries keep A's
  * stored order (rows i ascending).  scale = 0: a' = a (unweighted stays
  * unweighted); scale = 1: a' = a / deg_i in fp32 (1 / deg_i when unweighted),
@@ -286,8 +342,8 @@ int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, in
 spmm_plan_t spmm_plan_transpose(spmm_plan_t plan, int scale);
 
 /*
- * Max-pool backward (graph-spmm card, "Method": the argmax returned by the
- * forward max is what a max-pool backward needs).  plan_t is the transpose
+ * Max-pool backward (graph-spmm card, "Method": the forward max reports its
+ * winning neighbour, and that index routes the gradient back).  plan_t is the transpose
  * (scale 0) of an UNWEIGHTED adjacency A [M, K]; argmax and dC are the
  * forward's argmax [M, N] (int64) and the output gradient [M, N] (fp32):
  *   dB[j][k] = sum of dC[i][k] over rows i with argmax[i][k] == j,

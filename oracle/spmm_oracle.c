@@ -231,9 +231,10 @@ int64_t oracle_mac_gap(int64_t dim, int64_t F, int64_t omega) {
 
 /*
  * Backward pieces and graph construction (graph-spmm kernel card: API table
- * row SparseAdj.from_edge_index; "Requirements and limits": the backward of a
- * sum is the transposed product from a second adjacency on the reversed edge
- * list; "Method": the argmax is what a max-pool backward needs).
+ * row SparseAdj.from_edge_index; "Requirements and limits": the card is forward
+ * only and points to the reversed-edge adjacency A^T for a sum's gradient;
+ * "Method": the forward max reports its winning neighbour, which routes the
+ * max's gradient).
  */
 
 /*

@@ -11,7 +11,8 @@ oracle disagrees with something the pages or the mathematics fix:
 * empty rows reduce to 0 and (0, -1) (graph-spmm card, API table);
 * max / argmax from numpy's max and first-occurrence argmax over the stored
   entries, with ties forced by small-integer features (graph-spmm card,
-  "Correctness": per-row reference built from the CSR entries);
+  "Correctness": max is checked against a walk over each row's stored
+  entries, so duplicates count);
 * val = NULL equals an explicit all-ones weight array bit for bit (card,
   "Correctness");
 * the row split against a hand-enumerated case and its tiling invariants;

@@ -42,7 +42,8 @@ def test_header_compiles_as_c():
     assert r.returncode == 0, r.stderr
 
 
-@pytest.mark.parametrize("struct,cls", [("spmm_plan_info", "_Info"), ("spmm_features", "_Features")])
+@pytest.mark.parametrize("struct,cls", [("spmm_plan_info", "_Info"), ("spmm_features", "_Features"),
+                                        ("spmm_mem_stats", "_MemStats")])
 def test_header_struct_layout_matches_binding(struct, cls, tmp_path):
     import gnn_sparse_dense_amd as G
     py = getattr(G, cls)
@@ -111,8 +112,61 @@ def test_binding_rejects_strided_or_mistyped_tensors():
         G.spmm_run(0, torch.zeros((6, 8)), C, torch.zeros((4, 8), dtype=torch.int32), 8, "max")
     with pytest.raises(ValueError, match="shape"):
         G.spmm_run(0, torch.zeros((6, 8)), C, torch.zeros((5, 8), dtype=torch.int64), 8, "max")
-    with pytest.raises(ValueError, match="GPU"):
-        G.spmm_run(0, torch.zeros((6, 8)), C, None, 8, "sum")
+    G._plan_dims[0x1000] = (4, 6)          # a handle the library never sees
+    try:
+        with pytest.raises(ValueError, match="GPU"):
+            G.spmm_run(0x1000, torch.zeros((6, 8)), C, None, 8, "sum")
+    finally:
+        G._plan_dims.pop(0x1000)
+
+
+def test_binding_rejects_wrong_row_counts():
+    """Row counts of B, C, argmax, dC and dB, and the lengths of the CSR and
+    edge-list arrays, are checked on the host before any address reaches the
+    library (an undersized tensor would otherwise be read or written out of
+    bounds)."""
+    import torch
+
+    import gnn_sparse_dense_amd as G
+    fake = 0x2000                              # never dereferenced: checks come first
+    G._plan_dims[fake] = (4, 6)                # plan of A [4, 6]
+    try:
+        B = torch.zeros((6, 8))
+        C = torch.zeros((4, 8))
+        with pytest.raises(ValueError, match="B has 5 rows, expected 6"):
+            G.spmm_run(fake, torch.zeros((5, 8)), C, None, 8, "sum")
+        with pytest.raises(ValueError, match="C has 3 rows, expected 4"):
+            G.spmm_run(fake, B, torch.zeros((3, 8)), None, 8, "sum")
+        with pytest.raises(ValueError, match="argmax has"):
+            G.spmm_run(fake, B, C, torch.zeros((3, 8), dtype=torch.int64), 8, "max")
+        # max backward over the transpose plan [6, 4]: argmax / dC [4, N], dB [6, N]
+        G._plan_dims[fake] = (6, 4)
+        arg = torch.zeros((4, 8), dtype=torch.int64)
+        with pytest.raises(ValueError, match="dC has 5 rows, expected 4"):
+            G.spmm_max_backward(fake, arg, torch.zeros((5, 8)), torch.zeros((6, 8)), 8)
+        with pytest.raises(ValueError, match="argmax has 3 rows, expected 4"):
+            G.spmm_max_backward(fake, arg[:3], torch.zeros((4, 8)), torch.zeros((6, 8)), 8)
+        with pytest.raises(ValueError, match="dB has 5 rows, expected 6"):
+            G.spmm_max_backward(fake, arg, torch.zeros((4, 8)), torch.zeros((5, 8)), 8)
+        G._plan_dims[fake] = (6, 6)
+        with pytest.raises(ValueError, match="perm has 5 elements, expected 6"):
+            G.spmm_plan_permute(fake, torch.zeros(5, dtype=torch.int64))
+    finally:
+        G._plan_dims.pop(fake)
+    # CSR arrays: rowptr must hold M + 1 entries, col and val at least rowptr[M]
+    rowptr = torch.tensor([0, 2, 3], dtype=torch.int64)
+    with pytest.raises(ValueError, match="rowptr has 3 elements, expected 4"):
+        G.spmm_plan_create(rowptr, torch.zeros(3, dtype=torch.int64), None, 3, 3)
+    with pytest.raises(ValueError, match="col has 2 elements, fewer than the 3"):
+        G.spmm_plan_create(rowptr, torch.zeros(2, dtype=torch.int64), None, 2, 3)
+    with pytest.raises(ValueError, match="val has 1 elements, fewer than the 3"):
+        G.spmm_plan_create(rowptr, torch.zeros(3, dtype=torch.int64), torch.zeros(1), 2, 3)
+    # edge lists: row, col and val of one length
+    with pytest.raises(ValueError, match="col has 3 elements, expected 4"):
+        G.spmm_coo_to_csr(torch.zeros(4, dtype=torch.int64), torch.zeros(3, dtype=torch.int64), None, 2, 2)
+    with pytest.raises(ValueError, match="val has 2 elements, expected 4"):
+        G.spmm_coo_to_csr(torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int64), torch.zeros(2),
+                          2, 2)
 
 
 def test_last_error_truncates():

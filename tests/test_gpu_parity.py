@@ -192,9 +192,12 @@ def test_size_limits(orc):
     # rowptr[M] at the int32 limit is refused from rowptr alone: col is never read
     rp = torch.tensor([0, 2**31 - 1], dtype=torch.int64, device=DEV)
     cl = torch.zeros(1, dtype=torch.int64, device=DEV)
-    with pytest.raises(G.SpmmError) as ei:
+    assert G.lib().spmm_plan_create(rp.data_ptr(), cl.data_ptr(), None, 1, 4) is None
+    st, msg = G.spmm_last_error()
+    assert st == G.SPMM_E_UNSUPPORTED and "nnz" in msg
+    # the binding refuses the same arrays earlier: col is shorter than rowptr[M]
+    with pytest.raises(ValueError, match="col has 1 elements"):
         G.spmm_plan_create(rp, cl, None, 1, 4)
-    assert ei.value.status == G.SPMM_E_UNSUPPORTED and "nnz" in str(ei.value)
     # very wide feature rows: hundreds of column slices with a ragged last one
     rng = np.random.default_rng(12)
     g = W.random_csr(rng, 40, 30, mean_deg=6.0, empty_frac=0.1, heavy_rows=1, heavy_deg=25,
@@ -331,8 +334,11 @@ def test_descriptors_and_errors(orc):
     with pytest.raises(G.SpmmError) as ei:               # and so does the library, given its address
         G.spmm_run(plan, Bh.data_ptr(), C, None, 8, "sum")
     assert ei.value.status == G.SPMM_E_INVALID_ARG
-    with pytest.raises(G.SpmmError):
-        G.spmm_run(plan, C, C, None, 8, "sum")           # B overlaps C
+    with pytest.raises(ValueError):                      # the binding refuses C [M, 8] as B [K, 8]
+        G.spmm_run(plan, C, C, None, 8, "sum")
+    with pytest.raises(G.SpmmError) as ei:               # the library refuses B overlapping C
+        G.spmm_run(plan, C.data_ptr(), C, None, 8, "sum")
+    assert ei.value.status == G.SPMM_E_INVALID_ARG and "overlaps" in str(ei.value)
     G.spmm_plan_destroy(plan)
 
 
