@@ -47,6 +47,7 @@ EXPORTED = (
     "spmm_plan_route", "spmm_plan_partition", "spmm_plan_set_option", "spmm_last_error",
     "spmm_coo_to_csr", "spmm_plan_transpose", "spmm_max_backward", "spmm_plan_features",
     "spmm_plan_reorder", "spmm_plan_permute", "spmm_set_mem_limit", "spmm_mem_stats",
+    "spmm_coo_to_csr_noalloc",
 )
 
 
@@ -136,6 +137,8 @@ def _load() -> ctypes.CDLL:
     lib.spmm_plan_permute.restype = p
     lib.spmm_max_backward.argtypes = [p, p, p, p, i64, p]
     lib.spmm_max_backward.restype = i32
+    lib.spmm_coo_to_csr_noalloc.argtypes = [p, p, p, i64, i64, i64, p, p, p]
+    lib.spmm_coo_to_csr_noalloc.restype = i32
     lib.spmm_set_mem_limit.argtypes = [i64]
     lib.spmm_set_mem_limit.restype = i32
     lib.spmm_mem_stats.argtypes = [ctypes.POINTER(_MemStats)]
@@ -333,6 +336,23 @@ def spmm_coo_to_csr(row, col, val, M: int, K: int):
     _check(_lib.spmm_coo_to_csr(_addr(row), _addr(col), _addr(val), E, int(M), int(K), _addr(rowptr),
                                 _addr(col_out), _addr(val_out)))
     return rowptr, col_out, val_out
+
+
+def spmm_coo_to_csr_noalloc(row, col, val, M: int, K: int, rowptr_out, col_out, val_out=None) -> None:
+    """Edge-list -> CSR into the caller's tensors, with no device allocation
+    in the library (at most 2^20 edges)."""
+    E = int(row.numel())
+    _check_vector("row", row, "int64", exact_len=E)
+    _check_vector("col", col, "int64", exact_len=E)
+    _check_vector("val", val, "float32", exact_len=E)
+    _check_vector("rowptr_out", rowptr_out, "int64", exact_len=int(M) + 1)
+    _check_vector("col_out", col_out, "int64", exact_len=E)
+    _check_vector("val_out", val_out, "float32", exact_len=E if val is not None else None)
+    if val is not None and val_out is None:
+        raise ValueError("val_out is required with val")
+    _check_gpu(row=row, col=col, val=val, rowptr_out=rowptr_out, col_out=col_out, val_out=val_out)
+    _check(_lib.spmm_coo_to_csr_noalloc(_addr(row), _addr(col), _addr(val), E, int(M), int(K), _addr(rowptr_out),
+                                        _addr(col_out), _addr(val_out)))
 
 
 def spmm_plan_transpose(plan: int, scale: int = 0) -> int:

@@ -1414,6 +1414,27 @@ SPMM_API int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float
     return succeed();
 }
 
+SPMM_API int spmm_coo_to_csr_noalloc(const int64_t *row, const int64_t *col, const float *val, int64_t E,
+                                     int64_t M, int64_t K, int64_t *rowptr_out, int64_t *col_out,
+                                     float *val_out) {
+    if (const int st = check_coo_args(row, col, val, E, M, K, rowptr_out, col_out, val_out)) return st;
+    if (E > kNoAllocMaxEdges)
+        return fail(SPMM_E_UNSUPPORTED, "the allocation-free edge-list sort takes at most %lld edges (got %lld)",
+                    (long long)kNoAllocMaxEdges, (long long)E);
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(e, "synchronise before the edge-list sort");
+    int64_t bad = -1;
+    int too_large = 0;
+    e = coo_to_csr_noalloc(row, col, val, E, M, K, rowptr_out, col_out, val ? val_out : nullptr, &bad, &too_large);
+    if (e != hipSuccess) return fail_hip(e, "edge-list sort");
+    if (too_large)
+        return fail(SPMM_E_UNSUPPORTED, "the edge-list sort of %lld edges does not fit the %lld-byte workspace",
+                    (long long)E, (long long)kNoAllocScratchBytes);
+    if (bad >= 0) return fail(SPMM_E_BAD_CSR, "edge %lld has a row outside [0, %lld) or a column outside [0, %lld)",
+                              (long long)bad, (long long)M, (long long)K);
+    return succeed();
+}
+
 SPMM_API spmm_plan_t spmm_plan_transpose(spmm_plan_t p, int scale) {
     if (!p) {
         fail(SPMM_E_INVALID_ARG, "plan is NULL");

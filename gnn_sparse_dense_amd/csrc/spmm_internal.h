@@ -123,6 +123,14 @@ hipError_t coo_sort_storage_bytes(int64_t E, int64_t M, size_t *bytes);
 hipError_t coo_to_csr_in(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
                          int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad,
                          const CooWorkspace &w, hipStream_t s);
+// The allocation-free variant: workspace in a fixed device array of
+// kNoAllocScratchBytes per device, edge lists of at most kNoAllocMaxEdges;
+// *too_large = 1 (and nothing launched) beyond that.
+constexpr int64_t kNoAllocMaxEdges = int64_t(1) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t coo_to_csr_noalloc(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                              int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad,
+                              int *too_large);
 hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
                       int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s);
 hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,

@@ -15,6 +15,7 @@
 #include <hipcub/hipcub.hpp>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include <climits>
@@ -198,6 +199,70 @@ hipError_t coo_to_csr_in(const int64_t *row, const int64_t *col, const float *va
 }
 
 hipError_t coo_sort_storage_bytes(int64_t E, int64_t M, size_t *bytes) { return sort_storage_bytes(E, M, bytes); }
+
+// ---- allocation-free edge-list sort ----
+// The workspace is this file-scope device array; each device holds its own
+// copy from the time the library is loaded on it until the process ends.
+// Host code never passes the array's name to a kernel: it takes the device
+// address from hipGetSymbolAddress, resolved once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu[kMaxDevices];     // one call at a time per device
+unsigned char *g_scratch_ptr[kMaxDevices] = {};
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+hipError_t coo_to_csr_noalloc(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                              int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad,
+                              int *too_large) {
+    *first_bad = -1;
+    *too_large = 0;
+    if (E > kNoAllocMaxEdges) {
+        *too_large = 1;
+        return hipSuccess;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu[dev]);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<unsigned char *>(ptr);
+    }
+    unsigned char *base = g_scratch_ptr[dev];
+    // carve: keys, idx, skeys, perm (int32 [E] each), range records, sort storage
+    CooWorkspace w;
+    const int64_t nb = coo_check_blocks(E);
+    int64_t bad_host[kNoAllocMaxEdges / (kBlock * 4)];
+    w.bad_host = bad_host;
+    const size_t arr = align256(sizeof(int) * (size_t)std::max<int64_t>(E, 1));
+    size_t off = 0;
+    w.keys = reinterpret_cast<int *>(base + off);
+    off += arr;
+    w.idx = reinterpret_cast<int *>(base + off);
+    off += arr;
+    w.skeys = reinterpret_cast<int *>(base + off);
+    off += arr;
+    w.perm = reinterpret_cast<int *>(base + off);
+    off += arr;
+    w.bad = reinterpret_cast<int64_t *>(base + off);
+    off += align256(sizeof(int64_t) * (size_t)std::max<int64_t>(nb, 1));
+    if (E > 0 && (e = coo_sort_storage_bytes(E, M, &w.sort_bytes)) != hipSuccess) return e;
+    if (off + w.sort_bytes > kNoAllocScratchBytes) {
+        *too_large = 1;
+        return hipSuccess;
+    }
+    w.sort = base + off;
+    return coo_to_csr_in(row, col, val, E, M, K, rowptr_out, col_out, val_out, first_bad, w, nullptr);
+}
 
 hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M, int64_t K,
                       int64_t *rowptr_out, int64_t *col_out, float *val_out, int64_t *first_bad, hipStream_t s) {

@@ -330,6 +330,21 @@ int spmm_coo_to_csr(const int64_t *row, const int64_t *col, const float *val, in
                     int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out);
 
 /*
+ * spmm_coo_to_csr without any device allocation, for callers that cannot
+ * allocate (code under HIP graph capture set-up, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and errors as
+ * spmm_coo_to_csr (bit-identical output), but its temporaries live in a fixed
+ * 32 MiB device workspace that the library reserves on every device it is
+ * loaded on, held until the process ends.  Limit: E <= 2^20 edges; larger
+ * edge lists return UNSUPPORTED before anything is launched.  Calls on one
+ * device share that workspace: the library runs them one at a time (a lock
+ * per device), and the workspace keeps the last call's contents, which no
+ * call reads.  Synchronous; calls no hipMalloc or hipFree.
+ */
+int spmm_coo_to_csr_noalloc(const int64_t *row, const int64_t *col, const float *val, int64_t E, int64_t M,
+                            int64_t K, int64_t *rowptr_out, int64_t *col_out, float *val_out);
+
+/*
  * Plan of the transpose A^T [K, M] of a plan's matrix (graph-spmm card,
  * "Requirements and limits": the card is forward only and points to A^T,
  * the adjacency with every edge reversed, for the gradient of a sum).  Entry
