@@ -47,6 +47,8 @@ REGIME_TEXT = {
                  "unweighted, N=16",
     "community": "community M=K=500,000 in 256-node blocks, Bernoulli(0.1) inside + 2 outside, "
                  "weighted, N=512",
+    "mixed": "mixed M=K=1,000,000: a third road-like band, a third 256-node communities, a third "
+             "power-law rows over all columns, weighted, N=128",
 }
 
 
@@ -97,12 +99,27 @@ def read_traffic(family: str, workload: str):
 
 
 class Runner:
+    def set_width(self, N):
+        """Swap in B [K, N] (the regime's feature recipe) and C [M, N]."""
+        import workloads as W
+        torch = self.torch
+        if N == self.w.N:
+            return
+        dev = self.C.device
+        self.B = self.C = self.arg = None
+        torch.cuda.empty_cache()
+        Bh = W.make_features(self.name, self.g.K, N)
+        self.w = W.Workload(graph=self.g, N=N, B=Bh, reduces=self.w.reduces)
+        self.B = torch.from_numpy(Bh).to(dev)
+        self.C = torch.empty((self.g.M, N), dtype=torch.float32, device=dev)
+
     def __init__(self, name, M=None):
         import torch
 
         import gnn_sparse_dense_amd as G
         import workloads as W
         self.torch, self.G = torch, G
+        self.name = name
         t0 = time.time()
         self.w = W.make(name, M=M)
         self.gen_s = time.time() - t0
@@ -200,28 +217,124 @@ def copy_ceiling_gbps(reps=20):
     return 2 * (1 << 30) / (statistics.median(times) * 1e-3) / 1e9
 
 
+def _median_event_ms(fn, reps, flush=None):
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    return statistics.median(times)
+
+
+def ceilings(flush, reps=20, gather_rows=500_000, gather_deg=16, N=128):
+    """Bandwidth ceilings of this GPU, for reading the roofline fractions:
+    * stream read, write and copy of 1 GiB with PyTorch's own kernels
+      (sum, fill_, copy_), bytes moved / median event time;
+    * the random-gather rate of the row kernel against the size of B: a graph
+      of gather_rows rows with gather_deg uniform columns each over K rows of
+      B [K, N=128] (512-byte rows), sum, router's choice, for B from 32 MB to
+      1 GiB; gather bytes nnz * N * 4 / median time, warm (back to back) and
+      with the caches flushed before each run."""
+    import torch
+
+    import gnn_sparse_dense_amd as G
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        src.sum()
+        dst.fill_(1.0)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    gib = n * 4
+    rows2d = src.view(-1, 4096)
+    readers = {"sum": lambda: src.sum(), "amax": lambda: src.amax(), "row sums [65536, 4096]": lambda: rows2d.sum(1),
+               "count_nonzero": lambda: torch.count_nonzero(src)}
+    read = {k: round(gib / (_median_event_ms(f, reps) * 1e-3) / 1e9, 1) for k, f in readers.items()}
+    best = max(read, key=read.get)
+    out = {"stream": {
+        "read_GBps": read[best], "read_by_op": read,
+        "write_GBps": round(gib / (_median_event_ms(lambda: dst.fill_(2.0), reps) * 1e-3) / 1e9, 1),
+        "copy_GBps": round(2 * gib / (_median_event_ms(lambda: dst.copy_(src), reps) * 1e-3) / 1e9, 1),
+        "bytes": gib, "kernels": f"torch {best} (fastest of {', '.join(read)}) / fill_ / copy_ over 1 GiB fp32",
+        "reps": reps}}
+    del src, dst
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    rows = []
+    M = gather_rows
+    nnz = M * gather_deg
+    for b_mb in (32, 64, 128, 256, 512, 1024):
+        K = b_mb * (1 << 20) // (N * 4)
+        rp = torch.arange(0, nnz + 1, gather_deg, dtype=torch.int64, device=dev)
+        cl = torch.randint(0, K, (nnz,), dtype=torch.int64, device=dev, generator=gen)
+        B = torch.randn((K, N), dtype=torch.float32, device=dev, generator=gen)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        plan = G.spmm_plan_create(rp, cl, None, M, K)
+        del rp, cl
+
+        def run():
+            G.spmm_run(plan, B, C, None, N, "sum", None)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            run()
+        e.record()
+        e.synchronize()
+        warm = s.elapsed_time(e) / reps
+        cold = _median_event_ms(run, reps, flush)
+        info = G.spmm_plan_info(plan)
+        gbytes = nnz * N * 4
+        rows.append({"B_MB": b_mb, "K": K, "warm_ms": round(warm, 5), "flushed_ms": round(cold, 5),
+                     "gather_GBps_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
+                     "gather_GBps_flushed": round(gbytes / (cold * 1e-3) / 1e9, 1),
+                     "route": [kernel_family(info), info["route_lanes"], info["route_vec"],
+                               info["route_coarsen"], info["route_slices"]]})
+        print(f"[bench] gather ceiling B={b_mb} MB: {rows[-1]['gather_GBps_warm']} GB/s warm", file=sys.stderr,
+              flush=True)
+        G.spmm_plan_destroy(plan)
+        del B, C
+        torch.cuda.empty_cache()
+    out["gather"] = {"rows": M, "deg": gather_deg, "N": N, "gather_bytes": nnz * N * 4, "by_B_size": rows}
+    return out
+
+
 def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
-    """The CPU oracle (single-threaded C, as built) on the headline workload."""
+    """The CPU oracle (single-threaded C, as built) on the headline workload:
+    median time of repeated whole-graph runs, and the last run's output."""
     import oracle
     g = w.graph
     orc = oracle.default()
     times = []
+    out = None
     t_start = time.perf_counter()
     while len(times) < max_reps:
         t0 = time.perf_counter()
-        orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce)
+        out = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= budget_s:
             break
     t = statistics.median(times)
-    return t, len(times)
+    return t, len(times), out
 
 
-def oracle_regime_timing(w, reduce, budget_elems=1.5e9, reps_small=3):
-    """The single-threaded CPU oracle on one regime, bounded to about
-    budget_elems multiply-adds (about 1.5 s): the whole graph when it fits
-    (median of reps_small runs), else one contiguous block of rows from the
-    middle of the graph, its time scaled to the whole graph by entry count."""
+def oracle_regime_timing(w, reduce, budget_elems=1e10, reps_small=3):
+    """The single-threaded CPU oracle on one regime: the whole graph (median
+    of reps_small runs when it is small, one run otherwise), or, past about
+    budget_elems multiply-adds, one contiguous block of rows from the middle
+    of the graph with its time scaled to the whole graph by entry count.
+    Returns the timing record and the oracle's output (C, or (C, argmax) for
+    max) with the rows it covers (None: all)."""
     import numpy as np
 
     import oracle
@@ -230,8 +343,9 @@ def oracle_regime_timing(w, reduce, budget_elems=1.5e9, reps_small=3):
     N = w.N
     total = g.nnz * N
     if total <= budget_elems:
-        rows, reps, frac = None, reps_small, 1.0
-        what = f"the whole graph, median of {reps_small} runs"
+        reps = reps_small if total <= 2e8 else 1
+        rows, frac = None, 1.0
+        what = f"the whole graph, median of {reps} runs" if reps > 1 else "the whole graph, one run"
     else:
         want = budget_elems / N                         # entries to cover
         deg = np.diff(g.rowptr)
@@ -243,13 +357,66 @@ def oracle_regime_timing(w, reduce, budget_elems=1.5e9, reps_small=3):
         reps, frac = 1, covered / g.nnz
         what = f"rows {rows[0]}..{rows[-1]} ({covered} of {g.nnz} entries), one run, scaled by entry count"
     times = []
+    out = None
     for _ in range(reps):
         t0 = time.perf_counter()
-        orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce, rows=rows)
+        out = orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce, rows=rows)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times) / frac
-    return {"oracle_ms": round(t * 1e3, 2), "oracle_gflops": round(2.0 * total / t / 1e9, 3),
-            "oracle_sample": what}
+    return ({"oracle_ms": round(t * 1e3, 2), "oracle_gflops": round(2.0 * total / t / 1e9, 3),
+             "oracle_sample": what}, out, rows)
+
+
+def parity_against_oracle(w, reduce, info, C, A, ref, rows=None):
+    """The GPU output of the runs just timed against the oracle's output for
+    the same inputs (the CPU-baseline leg's own run), on `rows` (None: all).
+    Max: values and argmax bit for bit on every row.  Sum and mean: rows the
+    row, tile and window kernels walk whole must equal the oracle's fused
+    multiply-add mode bit for bit (same order, one rounding per entry); rows
+    cut into pieces, and every row of the merge-path and panel routes, must
+    lie within 1e-5 * sum|a*b| + 1e-6 (the sum of magnitudes from the oracle,
+    in double, on those rows only)."""
+    import numpy as np
+
+    import oracle
+    g = w.graph
+    orc = oracle.default()
+    sel = np.arange(g.M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    Cg = C[sel] if rows is not None else C
+    rec = {"rows_checked": int(sel.size), "outputs_checked": int(sel.size * w.N)}
+    if reduce == "max":
+        refC, refA = ref
+        bad_v = int((Cg.view(np.uint32) != refC.view(np.uint32)).sum())
+        Ag = A[sel] if rows is not None else A
+        bad_a = int((Ag != refA).sum())
+        rec.update({"rule": "bit-exact values and argmax", "value_mismatches": bad_v, "argmax_mismatches": bad_a,
+                    "status": "ok" if bad_v == 0 and bad_a == 0 else "FAIL"})
+        return rec
+    deg = np.diff(g.rowptr)[sel]
+    pieces = info["route_split"] and info["n_seg"] > 0
+    loose_route = bool(info["route_merge"] or info["route_pairs"] or info["route_mfma"])
+    whole = np.ones(sel.size, bool) if not pieces else deg <= info["split_T"]
+    if loose_route:
+        whole[:] = False
+    fused = ref if g.val is None else orc.spmm(g.rowptr, g.col, g.val, g.M, g.K, w.B, reduce, fused=True,
+                                                rows=rows)
+    wi = np.flatnonzero(whole)
+    bad_exact = int((Cg[wi].view(np.uint32) != fused[wi].view(np.uint32)).sum())
+    li = np.flatnonzero(~whole)
+    worst = 0.0
+    bad_tol = 0
+    if li.size:
+        S = orc.sumabs(g.rowptr, g.col, g.val, g.M, w.B, rows=sel[li])
+        err = np.abs(Cg[li].astype(np.float64) - ref[li].astype(np.float64))
+        bound = 1e-5 * S + 1e-6
+        bad_tol = int((~(err <= bound)).sum())
+        worst = float(np.max(err / bound)) if err.size else 0.0
+    rec.update({"rule": "whole rows bit-exact vs the fused oracle; other rows within 1e-5*sum|a*b| + 1e-6",
+                "rows_bit_exact": int(wi.size), "rows_by_tolerance": int(li.size),
+                "bit_mismatches": bad_exact, "tolerance_failures": bad_tol,
+                "worst_err_over_bound": round(worst, 4),
+                "status": "ok" if bad_exact == 0 and bad_tol == 0 else "FAIL"})
+    return rec
 
 
 def host_cpu() -> str:
@@ -295,9 +462,13 @@ def regime_result(r, reduce, steps, warmup, flush, cpu=False):
         "plan_ms": round(r.info["plan_ms"], 2),
     }
     if cpu:
-        o = oracle_regime_timing(r.w, reduce)
+        C = r.C.cpu().numpy()
+        A = r.arg.cpu().numpy() if reduce == "max" else None
+        o, ref, rows = oracle_regime_timing(r.w, reduce)
         o["gpu_speedup_vs_oracle"] = round(o["oracle_ms"] / med_c, 1)
         res.update(o)
+        res["parity"] = parity_against_oracle(r.w, reduce, r.info, C, A, ref, rows)
+        del C, A, ref
     return res
 
 
@@ -478,6 +649,7 @@ def router_sweep(r, reduce, steps, flush):
                  ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2})]
     rows = []
     for label, opts in variants:
+        print(f"[bench]   {reduce} {label}", file=sys.stderr, flush=True)
         entry = {"variant": label}
         try:
             for k, v in opts.items():
@@ -583,6 +755,11 @@ def main():
                     help="time the JSON-line workload on the matrix-core tiles: 1 fp16, 2 split fp16 (sum/mean)")
     ap.add_argument("--router-sweep", action="store_true",
                     help="only the router evidence: every forced variant per regime against the router's pick")
+    ap.add_argument("--widths", default="",
+                    help="router sweep: feature widths N to sweep per regime (default: each regime's own)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only the bandwidth ceilings: stream read, write and copy of 1 GiB, and the row "
+                         "kernel's random-gather rate against the size of B")
     ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
                     help="set a plan option on the JSON-line workload's plan, e.g. PIECE_ORDER=0 "
                          "(SPMM_OPT_<NAME>; repeatable)")
@@ -600,13 +777,23 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(make_flush(), reps=min(args.steps, 20))}), flush=True)
+        return
+
     if args.router_sweep:
         flush = make_flush()
         evidence = {}
+        widths = [int(x) for x in args.widths.split(",") if x] if args.widths else []
         for name in [x for x in args.regimes.split(",") if x]:
             rr = Runner(name)
-            print(f"[bench] router sweep {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N}", file=sys.stderr, flush=True)
-            evidence[name] = [router_sweep(rr, red, min(args.steps, 30), flush) for red in rr.w.reduces]
+            base_N = rr.w.N
+            for N in (widths or [base_N]):
+                rr.set_width(N)
+                reds = rr.w.reduces if N == base_N else rr.w.reduces[:1]
+                print(f"[bench] router sweep {name}: M={rr.g.M} nnz={rr.g.nnz} N={N} {','.join(reds)}",
+                      file=sys.stderr, flush=True)
+                evidence[f"{name}/N={N}"] = [router_sweep(rr, red, min(args.steps, 30), flush) for red in reds]
             rr.close()
             del rr
             torch.cuda.empty_cache()
@@ -614,7 +801,7 @@ def main():
         geo = 1.0
         for q in ratios:
             geo *= q
-        print(json.dumps({"router_evidence": evidence,
+        print(json.dumps({"router_evidence": evidence, "steps": min(args.steps, 30),
                           "router_speed_vs_best_geomean": round(geo ** (1.0 / len(ratios)), 4),
                           "router_speed_vs_best_min": min(ratios)}), flush=True)
         return
@@ -690,12 +877,21 @@ def main():
     }
 
     if not args.no_cpu:
-        t_cpu, reps = cpu_oracle_baseline(r.w, reduce)
+        # the output of the last timed step, checked against the oracle run
+        # that the CPU baseline times
+        C_gpu = r.C.cpu().numpy()
+        A_gpu = r.arg.cpu().numpy() if reduce == "max" else None
+        t_cpu, reps, ref = cpu_oracle_baseline(r.w, reduce)
         result["cpu_baseline"] = {
             "value": round(flops / t_cpu / 1e9, 3), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {headline} graph and B, {reduce}, median of {reps} single-threaded "
                       f"oracle runs ({t_cpu * 1e3:.1f} ms each) on {host_cpu()}",
         }
+        headline_parity = parity_against_oracle(r.w, reduce, r.info, C_gpu, A_gpu, ref)
+        result["parity"] = headline_parity["status"]
+        result["parity_detail"] = {"headline": headline_parity}
+        del C_gpu, A_gpu, ref
+        print(f"[bench] parity {headline} {reduce}: {headline_parity['status']}", file=sys.stderr, flush=True)
 
     if not args.headline_only:
         flush = make_flush()
@@ -727,6 +923,12 @@ def main():
             del rr
             torch.cuda.empty_cache()
         result["regimes"] = regimes
+        if not args.no_cpu:
+            checks = {f"{name}/{x['reduce']}": x["parity"]["status"] for name, xs in regimes.items() for x in xs
+                      if "parity" in x}
+            result["parity_detail"]["regimes"] = checks
+            if any(v != "ok" for v in checks.values()):
+                result["parity"] = "FAIL"
         result["reuse"] = reuse
         result["vblock"] = vblock_result(min(args.steps, 50), flush)
         result["reorder"] = reorder_result(min(args.steps, 50), flush)

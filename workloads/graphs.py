@@ -60,6 +60,9 @@ CONFIGS = {
     "powerlaw":  dict(M=2_000_000, N=128, seed=3, reduces=("sum",)),
     "diffusion": dict(M=1_000_000, N=16,  seed=4, reduces=("mean", "max")),
     "community": dict(M=500_000,   N=512, seed=5, reduces=("sum",)),
+    # router evaluation only: a third road-like band, a third community
+    # blocks, a third power-law rows over all columns
+    "mixed":     dict(M=1_000_000, N=128, seed=6, reduces=("sum",)),
 }
 
 
@@ -243,12 +246,30 @@ def _gen_community(M: int, rng_s, rng_v, size=256, p=0.1, n_inter=2):
     return rowptr, cols, val
 
 
+def _gen_mixed(M: int, rng_s, rng_v):
+    """Rows [0, M/3): road-like band; [M/3, 2M/3): 256-node communities
+    (columns in that part); the rest: power-law degrees (mean 25) with
+    uniform columns over all M.  Weights U[0, 1)."""
+    m1 = M // 3
+    m2 = M // 3
+    m3 = M - m1 - m2
+    rp1, c1, _ = _gen_road(m1, rng_s, rng_v)
+    rp2, c2, _ = _gen_community(m2, rng_s, rng_v)
+    deg3 = _powerlaw_degrees(rng_s, m3, dmax=min(50_000, M))
+    rp3, c3 = _distinct_columns(rng_s, deg3, M, _uniform_cols(M))
+    rowptr = np.concatenate([rp1, rp1[-1] + rp2[1:], rp1[-1] + rp2[-1] + rp3[1:]]).astype(np.int64)
+    col = np.concatenate([c1, c2 + m1, c3]).astype(np.int64)
+    val = rng_v.random(col.size, dtype=np.float32)
+    return rowptr, col, val
+
+
 _GENERATORS = {
     "tiny": _gen_tiny,
     "road": _gen_road,
     "powerlaw": _gen_powerlaw,
     "diffusion": _gen_diffusion,
     "community": _gen_community,
+    "mixed": _gen_mixed,
 }
 
 
