@@ -49,6 +49,7 @@ REGIME_TEXT = {
                  "weighted, N=512",
     "mixed": "mixed M=K=1,000,000: a third road-like band, a third 256-node communities, a third "
              "power-law rows over all columns, weighted, N=128",
+    "knn": "kNN line M=K=1,000,000, k=10 nearest points on a line, unweighted, N=64",
 }
 
 
@@ -238,9 +239,9 @@ def ceilings(flush, reps=20, gather_rows=500_000, gather_deg=16, N=128):
       (sum, fill_, copy_), bytes moved / median event time;
     * the random-gather rate of the row kernel against the size of B: a graph
       of gather_rows rows with gather_deg uniform columns each over K rows of
-      B [K, N=128] (512-byte rows), sum, router's choice, for B from 32 MB to
-      1 GiB; gather bytes nnz * N * 4 / median time, warm (back to back) and
-      with the caches flushed before each run."""
+      B [K, N=128] (512-byte rows), sum, 16 lanes per row in 64-column
+      slices, for B from 32 MB to 1 GiB; gather bytes nnz * N * 4 / median
+      time, warm (back to back) and with the caches flushed before each run."""
     import torch
 
     import gnn_sparse_dense_amd as G
@@ -267,46 +268,58 @@ def ceilings(flush, reps=20, gather_rows=500_000, gather_deg=16, N=128):
         "reps": reps}}
     del src, dst
     torch.cuda.empty_cache()
-    gen = torch.Generator(device=dev).manual_seed(1234)
-    rows = []
-    M = gather_rows
-    nnz = M * gather_deg
-    for b_mb in (32, 64, 128, 256, 512, 1024):
-        K = b_mb * (1 << 20) // (N * 4)
-        rp = torch.arange(0, nnz + 1, gather_deg, dtype=torch.int64, device=dev)
-        cl = torch.randint(0, K, (nnz,), dtype=torch.int64, device=dev, generator=gen)
-        B = torch.randn((K, N), dtype=torch.float32, device=dev, generator=gen)
-        C = torch.empty((M, N), dtype=torch.float32, device=dev)
-        plan = G.spmm_plan_create(rp, cl, None, M, K)
-        del rp, cl
-
-        def run():
-            G.spmm_run(plan, B, C, None, N, "sum", None)
-        for _ in range(5):
-            run()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            run()
-        e.record()
-        e.synchronize()
-        warm = s.elapsed_time(e) / reps
-        cold = _median_event_ms(run, reps, flush)
-        info = G.spmm_plan_info(plan)
-        gbytes = nnz * N * 4
-        rows.append({"B_MB": b_mb, "K": K, "warm_ms": round(warm, 5), "flushed_ms": round(cold, 5),
-                     "gather_GBps_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
-                     "gather_GBps_flushed": round(gbytes / (cold * 1e-3) / 1e9, 1),
-                     "route": [kernel_family(info), info["route_lanes"], info["route_vec"],
-                               info["route_coarsen"], info["route_slices"]]})
-        print(f"[bench] gather ceiling B={b_mb} MB: {rows[-1]['gather_GBps_warm']} GB/s warm", file=sys.stderr,
-              flush=True)
-        G.spmm_plan_destroy(plan)
-        del B, C
-        torch.cuda.empty_cache()
-    out["gather"] = {"rows": M, "deg": gather_deg, "N": N, "gather_bytes": nnz * N * 4, "by_B_size": rows}
+    rows = [gather_rate(b_mb, flush, reps, gather_rows, gather_deg, N) for b_mb in (32, 64, 128, 256, 512, 1024)]
+    out["gather"] = {"rows": gather_rows, "deg": gather_deg, "N": N, "gather_bytes": gather_rows * gather_deg * N * 4,
+                     "by_B_size": rows}
     return out
+
+
+def gather_rate(b_mb, flush, reps=20, M=500_000, gather_deg=16, N=128, lanes=16):
+    """The row kernel's random-gather rate for B [K, N] of b_mb MB: M rows of
+    gather_deg uniform columns, sum, `lanes` lanes per row (16: 64-column
+    slices, the fastest mapping for uniform gathers from a large B, and the
+    one skewed graphs are routed to; see ceilings())."""
+    import torch
+
+    import gnn_sparse_dense_amd as G
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(1234 + b_mb)
+    nnz = M * gather_deg
+    K = b_mb * (1 << 20) // (N * 4)
+    rp = torch.arange(0, nnz + 1, gather_deg, dtype=torch.int64, device=dev)
+    cl = torch.randint(0, K, (nnz,), dtype=torch.int64, device=dev, generator=gen)
+    B = torch.randn((K, N), dtype=torch.float32, device=dev, generator=gen)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    plan = G.spmm_plan_create(rp, cl, None, M, K)
+    del rp, cl
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_LANES, lanes)
+
+    def run():
+        G.spmm_run(plan, B, C, None, N, "sum", None)
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        run()
+    e.record()
+    e.synchronize()
+    warm = s.elapsed_time(e) / reps
+    cold = _median_event_ms(run, reps, flush)
+    info = G.spmm_plan_info(plan)
+    gbytes = nnz * N * 4
+    row = {"B_MB": b_mb, "K": K, "warm_ms": round(warm, 5), "flushed_ms": round(cold, 5),
+           "gather_GBps_warm": round(gbytes / (warm * 1e-3) / 1e9, 1),
+           "gather_GBps_flushed": round(gbytes / (cold * 1e-3) / 1e9, 1),
+           "route": [kernel_family(info), info["route_lanes"], info["route_vec"],
+                     info["route_coarsen"], info["route_slices"]]}
+    print(f"[bench] gather ceiling B={b_mb} MB: {row['gather_GBps_warm']} GB/s warm", file=sys.stderr,
+          flush=True)
+    G.spmm_plan_destroy(plan)
+    del B, C
+    torch.cuda.empty_cache()
+    return row
 
 
 def cpu_oracle_baseline(w, reduce, budget_s=10.0, max_reps=50):
@@ -437,7 +450,7 @@ def percentile(xs, q):
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
 
-def regime_result(r, reduce, steps, warmup, flush, cpu=False):
+def regime_result(r, reduce, steps, warmup, flush, cpu=False, gather_ceiling=None):
     g, N = r.g, r.w.N
     warm_ms, _ = r.time_back_to_back(reduce, steps, warmup)
     cold, _ = r.time_steps(reduce, steps, 2, flush=flush)
@@ -461,6 +474,15 @@ def regime_result(r, reduce, steps, warmup, flush, cpu=False):
                   "n_seg": r.info["n_seg"]},
         "plan_ms": round(r.info["plan_ms"], 2),
     }
+    if gather_ceiling is not None:
+        # gather-bound regimes: the gathered bytes against the random-gather
+        # rate measured for a B of the same size
+        achieved = gather / (med_c * 1e-3) / 1e9
+        res["roofline_gather"] = {"bound": "gather", "achieved": round(achieved, 1),
+                                  "peak": gather_ceiling["gather_GBps_flushed"], "unit": "GB/s",
+                                  "frac": round(achieved / gather_ceiling["gather_GBps_flushed"], 4),
+                                  "ceiling": f"random 512-byte gathers of the row kernel from a "
+                                             f"{gather_ceiling['B_MB']} MB B, caches flushed"}
     if cpu:
         C = r.C.cpu().numpy()
         A = r.arg.cpu().numpy() if reduce == "max" else None
@@ -576,12 +598,14 @@ def vblock_result(steps, flush):
     B = torch.from_numpy(W.make_features("road", g.K, N)).to(dev)
     C = torch.empty((g.M, N), dtype=torch.float32, device=dev)
     plan = G.spmm_plan_create(rp, cl, None, g.M, g.K)
+    auto_built = G.spmm_plan_info(plan)["pairs_built"]
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_VBLOCK, 0)          # the row kernels
 
     def run():
         G.spmm_run(plan, B, C, None, N, "sum", None)
     t_rows = time_flushed(run, flush, steps)
     t0 = time.perf_counter()
-    G.spmm_plan_set_option(plan, G.SPMM_OPT_VBLOCK, 1)
+    G.spmm_plan_set_option(plan, G.SPMM_OPT_VBLOCK, -1)         # automatic: count, then build
     build = (time.perf_counter() - t0) * 1e3
     t_pan = time_flushed(run, flush, steps)
     info = G.spmm_plan_info(plan)
@@ -589,6 +613,7 @@ def vblock_result(steps, flush):
     comp, _ = byte_model(g, N, "sum")
     return {"workload": "kNN line M=K=1,000,000, k=10, unweighted, N=64, sum", "nnz": g.nnz,
             "padding_ratio": round(info["pair_padding"], 4), "routed_to_panels": info["route_pairs"],
+            "built_at_plan_creation": auto_built,
             "ms_rows": round(t_rows, 5), "ms_panels": round(t_pan, 5), "speedup": round(t_rows / t_pan, 3),
             "effective_GBps_panels": round(comp / (t_pan * 1e-3) / 1e9, 1),
             "build_ms": round(build, 2),
@@ -637,7 +662,7 @@ def router_sweep(r, reduce, steps, flush):
     G = r.G
     auto = {G.SPMM_OPT_LANES: 0, G.SPMM_OPT_COARSEN: 0, G.SPMM_OPT_TILES: -1, G.SPMM_OPT_WINDOW: -1,
             G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1,
-            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: 0}
+            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: -1}
     variants = [("router", {})]
     variants += [(f"lanes={g} coarsen={f}", {G.SPMM_OPT_LANES: g, G.SPMM_OPT_COARSEN: f})
                  for g in (4, 8, 16, 32, 64) for f in (1, 2)]
@@ -646,7 +671,7 @@ def router_sweep(r, reduce, steps, flush):
                  ("window off", {G.SPMM_OPT_WINDOW: 0}), ("XCD remap off", {G.SPMM_OPT_XCD_REMAP: 0}),
                  ("non-temporal C stores", {G.SPMM_OPT_NT_STORE: 1}), ("split on", {G.SPMM_OPT_SPLIT_MODE: 1}),
                  ("split off", {G.SPMM_OPT_SPLIT_MODE: 0}), ("merge-path balancing", {G.SPMM_OPT_BALANCE: 1}),
-                 ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2})]
+                 ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2}), ("V = 2 panels off", {G.SPMM_OPT_VBLOCK: 0})]
     rows = []
     for label, opts in variants:
         print(f"[bench]   {reduce} {label}", file=sys.stderr, flush=True)
@@ -873,6 +898,8 @@ def main():
                 family, r.info["route_lanes"], r.info["route_vec"], r.info["route_coarsen"]),
             "bytes_per_launch": comp, "avg_launch_ms": round(avg_launch_ms, 5),
             "launches_per_step": launches,
+            "timing": "warm: one HIP event pair on the launch stream around the K back-to-back timed steps "
+                      "(synchronize on both sides), divided by K; caches not flushed",
         },
     }
 
@@ -910,8 +937,11 @@ def main():
             rr = Runner(name)
             print(f"[bench] {name}: M={rr.g.M} nnz={rr.g.nnz} N={rr.w.N} gen={rr.gen_s:.1f}s",
                   file=sys.stderr, flush=True)
-            regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush, cpu=not args.no_cpu)
-                             for red in rr.w.reduces]
+            gceil = None
+            if name == "powerlaw":
+                gceil = gather_rate(1024, flush, reps=min(args.steps, 20))
+            regimes[name] = [regime_result(rr, red, args.steps, min(args.warmup, 50), flush, cpu=not args.no_cpu,
+                                           gather_ceiling=gceil) for red in rr.w.reduces]
             if rr.info["route_window"]:
                 regimes[name] += tile_results(rr, args.steps, min(args.warmup, 50), flush, regimes[name])
             reuse[name] = reuse_result(rr, rr.w.reduces[0], min(args.steps, 50), flush)
@@ -923,6 +953,12 @@ def main():
             del rr
             torch.cuda.empty_cache()
         result["regimes"] = regimes
+        same = [x for x in regimes[headline] if x["reduce"] == reduce and "contract" not in x]
+        if same:
+            # the same launch with the caches flushed before each run (the
+            # protocol the per-regime figures use), for comparison
+            result["roofline"]["frac_flushed"] = same[0]["frac_hbm_peak_flushed"]
+            result["roofline"]["avg_launch_ms_flushed"] = same[0]["ms_flushed_median"]
         if not args.no_cpu:
             checks = {f"{name}/{x['reduce']}": x["parity"]["status"] for name, xs in regimes.items() for x in xs
                       if "parity" in x}

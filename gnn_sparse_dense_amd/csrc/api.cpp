@@ -133,7 +133,6 @@ void free_merge(spmm_plan *p) {
 void free_window_runs(spmm_plan *p) {
     dev_free(p->win_lo);
     dev_free(p->win_in);
-    p->win_lo = p->win_in = nullptr;
 }
 
 // Per-row run lengths (entries below / inside the row's window) for the
@@ -436,7 +435,7 @@ int build_pairs(spmm_plan *p) {
     int st = dev_alloc(&p->pair_prow, npanels + 1, "panel rowptr");
     if (st) return st;
     PairOutput out;
-    const hipError_t e = pair_build(p->rowptr, p->col, p->val, p->M, p->K, p->nnz, p->pair_prow, &out);
+    const hipError_t e = pair_build(p->rowptr, p->col, p->val, p->M, p->K, p->nnz, p->rows_sorted, p->pair_prow, &out);
     if (e != hipSuccess) {
         free_pairs(p);
         return fail_hip(e, "V = 2 panel build");
@@ -446,6 +445,25 @@ int build_pairs(spmm_plan *p) {
     p->pair_nvec = out.nvec;
     p->pair_unsorted = out.unsorted != 0;
     return SPMM_OK;
+}
+
+// Automatic V = 2 panels (SPMM_OPT_VBLOCK = -1): for a plan that is not split
+// and whose rows are all stored with ascending columns, count the panels'
+// nonzero vectors with one merge pass, and build the panels when their
+// padding share 1 - nnz / (2 vectors) is at most kPairMaxPadding.  There each
+// gather of a B row serves 1.4 or more entries on average, and the build (two
+// merge passes and a scan, no sort) repays itself within a few hundred
+// products (kNN line graph: 1.5x faster products).
+int auto_pairs(spmm_plan *p) {
+    if (p->opt_vblock != -1 || p->pair_prow || p->split || !p->rows_sorted || p->M < 2 || p->nnz == 0 ||
+        p->K >= (int64_t(1) << 30))
+        return SPMM_OK;
+    int64_t vectors = 0;
+    const hipError_t e = pair_count_sorted(p->rowptr, p->col, p->M, &vectors);
+    if (e != hipSuccess) return fail_hip(e, "V = 2 panel count");
+    const double padding = vectors > 0 ? 1.0 - (double)p->nnz / (2.0 * (double)vectors) : 1.0;
+    if (padding > kPairMaxPadding) return SPMM_OK;
+    return build_pairs(p);
 }
 
 // Merge-path segments (built when SPMM_OPT_BALANCE is 1).
@@ -493,12 +511,13 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //  * low mean degree (< 8, RA-SpMM's sparse-uniform regime): half the lanes
 //    and F = 2, doubling the rows per wave so more rows' gathers are in
 //    flight per wave;
-//  * small graphs (fewer than two waves per CU at 16 rows per wave): 8 rows
-//    per wave, so that twice as many waves share the launch-bound latency;
+//  * small graphs (fewer than two waves per CU at 16 rows per wave):
+//    launch-bound, so as many waves as possible: no coarsening, and 8 lanes
+//    per row (more column slices) up to 128 columns;
 //  * skewed degrees (CV > 1, RA-SpMM's sparse-skewed / extreme-skew regime),
-//    where neighbours carry no locality, with a B wider than 64 floats:
-//    64-column slices, so each pass over the graph touches a quarter-sized
-//    part of B that stays in the Infinity Cache longer;
+//    where neighbours carry no locality, with a B of 128 floats or more:
+//    64-column slices (128-column slices from 512 floats), so each pass over
+//    the graph touches a part of B that stays in the Infinity Cache longer;
 //  * fp16 matrix-core tiles only when the caller enabled them (they follow
 //    the looser fp16 contract) and the run is a sum or mean with 16-byte
 //    aligned float4 access;
@@ -518,14 +537,18 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     int G = std::max(4, pow2_ceil(W));
     int F = W > G ? 2 : 1;
     const bool skewed = p->cv_deg > 1.0;
+    const bool small = p->M * 4 < (int64_t)p->num_cus * 2 * 64;
     if (skewed && W >= 32) {
-        G = 16;
+        G = W >= 128 ? 32 : 16;
         F = 1;
+    } else if (small) {
+        // launch-bound: as many waves as possible, so no coarsening, and 8
+        // lanes per row (more column slices) up to 128 columns
+        F = 1;
+        if (W <= 32) G = 8;
     } else if (p->mean_deg < 8.0 && G >= 16 && W <= G) {
         G /= 2;
         F = 2;
-    } else if (G == 4 && F == 1 && p->M * G < (int64_t)p->num_cus * 2 * 64) {
-        G = 8;   // small graph: 8 rows per wave, so that more waves fill the CUs
     }
     if (p->opt_lanes) G = p->opt_lanes;
     if (p->opt_coarsen) F = p->opt_coarsen;
@@ -538,12 +561,13 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     r.split = p->split;
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
     r.compact = r.tiled && p->tile_compact;
-    // community structure with wide features: stage B's row blocks in LDS
+    // community structure with features of 64 floats or more: stage B's row
+    // blocks in LDS
     // (one dispatch: at most 2^32 / kWinBlock row blocks, about 10^9 rows;
     // larger graphs take the row kernels)
     const bool win_grid = (p->M + kWinRows - 1) / kWinRows <= (int64_t)(UINT32_MAX / kWinBlock);
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 && win_grid &&
-               (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 128));
+               (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 64));
     // fp16 community tiles, when the caller asked for them
     r.mfma = p->opt_mfma > 0 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
     // merge-path balancing, when the caller chose it
@@ -561,7 +585,7 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         return r;
     }
     // V = 2 panels, when built: by padding share (ParamSpMM's PR for V), or forced
-    r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock > 0 &&
+    r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock != 0 &&
               (reduce != SPMM_MAX || !p->pair_unsorted) &&
               (p->opt_vblock == 2 || (!p->split && pair_padding(p) <= kPairMaxPadding));
     if (r.pairs) {
@@ -571,6 +595,10 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         r.coarsen = 1;
         r.slices = (int)((Wp + r.lanes - 1) / r.lanes);
         r.tiled = r.compact = r.window = r.split = false;
+        // panels of neighbouring rows: the plain block order keeps a panel's
+        // neighbours in flight together (kNN line graph, N = 16..512: as fast
+        // or faster than the XCD remap)
+        r.xcd_remap = p->opt_xcd >= 0 ? p->opt_xcd : 0;
         return r;
     }
     if (r.window || r.mfma) {
@@ -827,7 +855,7 @@ SPMM_API spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col,
         p->cv_deg = std::sqrt(std::max(var, 0.0)) / p->mean_deg;
     }
 
-    if ((st = build_split(p)) || (st = build_tiles(p))) {
+    if ((st = build_split(p)) || (st = build_tiles(p)) || (st = auto_pairs(p))) {
         free_plan(p);
         return nullptr;
     }
@@ -943,12 +971,21 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             return succeed();
         }
         case SPMM_OPT_VBLOCK: {
-            if (value < 0 || value > 2) return fail(SPMM_E_INVALID_ARG, "vblock must be 0, 1 or 2");
+            if (value < -1 || value > 2) return fail(SPMM_E_INVALID_ARG, "vblock must be -1, 0, 1 or 2");
             const hipError_t e = hipDeviceSynchronize();
             if (e != hipSuccess) return fail_hip(e, "synchronise before changing the V = 2 panels");
             p->opt_vblock = 0;
             if (value == 0) {
                 free_pairs(p);
+                return succeed();
+            }
+            if (value == -1) {
+                p->opt_vblock = -1;
+                const int st = auto_pairs(p);
+                if (st) {
+                    p->opt_vblock = 0;
+                    return st;
+                }
                 return succeed();
             }
             if (!p->pair_prow) {

@@ -21,6 +21,9 @@
 // no arithmetic and no rounding.
 #include <hipcub/hipcub.hpp>
 
+#include <climits>
+#include <vector>
+
 #include "alloc.h"
 #include "row_kernel_impl.h"
 
@@ -280,12 +283,150 @@ int64_t walk_grid(int64_t n) { return std::max<int64_t>(1, std::min<int64_t>((n 
 
 }  // namespace
 
+namespace {
+
+constexpr int kCountBlocks = 1024;
+
+// Nonzero vectors of the V = 2 panels of a plan whose rows are all stored with
+// ascending columns: one thread per panel merges its two sorted rows (equal
+// columns pair one occurrence of each), so no sort is needed.  One partial
+// count per block, folded on the host.
+__global__ __launch_bounds__(kBlock) void pair_count_sorted_kernel(const int *__restrict__ rowptr,
+                                                                   const int *__restrict__ col, int64_t M,
+                                                                   int64_t *__restrict__ partial) {
+    const int64_t npanels = (M + 1) / 2;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t n = 0;
+    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < npanels; g += stride) {
+        int i = rowptr[2 * g];
+        const int ie = rowptr[2 * g + 1];
+        int j = ie;
+        const int je = rowptr[min(2 * g + 2, M)];
+        while (i < ie && j < je) {
+            const int a = col[i], b = col[j];
+            i += a <= b;
+            j += b <= a;
+            ++n;
+        }
+        n += (ie - i) + (je - j);
+    }
+    __shared__ int64_t sh[kBlock];
+    sh[threadIdx.x] = n;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = sh[0];
+}
+
+// Panels of a plan whose rows are all stored with ascending columns, by a
+// merge of each panel's two rows (the same vectors, in the same order, as the
+// sort-based walk): count writes vectors per panel, write the vectors.
+template <bool WRITE>
+__global__ __launch_bounds__(kBlock) void pair_merge_kernel(const int *__restrict__ rowptr,
+                                                            const int *__restrict__ col,
+                                                            const float *__restrict__ val, int64_t M,
+                                                            int *__restrict__ count, const int *__restrict__ prow,
+                                                            unsigned *__restrict__ pcol, float *__restrict__ pval) {
+    const int64_t npanels = (M + 1) / 2;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < npanels; g += stride) {
+        int i = rowptr[2 * g];
+        const int ie = rowptr[2 * g + 1];
+        int j = ie;
+        const int je = rowptr[min(2 * g + 2, M)];
+        int v = WRITE ? prow[g] : 0;
+        while (i < ie || j < je) {
+            const int a = i < ie ? col[i] : INT_MAX;
+            const int b = j < je ? col[j] : INT_MAX;
+            const bool t0 = i < ie && a <= b;        // row 2g takes part
+            const bool t1 = j < je && b <= a;        // row 2g+1 takes part
+            if constexpr (WRITE) {
+                pcol[v] = (unsigned)(t0 ? a : b) | (t0 ? 0u : kAbsent0) | (t1 ? 0u : kAbsent1);
+                if (pval) {
+                    pval[2 * (int64_t)v] = t0 ? val[i] : 0.0f;
+                    pval[2 * (int64_t)v + 1] = t1 ? val[j] : 0.0f;
+                }
+            }
+            i += t0;
+            j += t1;
+            ++v;
+        }
+        if constexpr (!WRITE) count[g] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t pair_count_sorted(const int *rowptr, const int *col, int64_t M, int64_t *vectors) {
+    *vectors = 0;
+    const int64_t npanels = (M + 1) / 2;
+    if (npanels == 0) return hipSuccess;
+    const int64_t nb = std::max<int64_t>(1, std::min<int64_t>((npanels + kBlock - 1) / kBlock, kCountBlocks));
+    int64_t *partial = nullptr;
+    hipError_t e = dmalloc(&partial, sizeof(int64_t) * (size_t)nb, "panel count records");
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pair_count_sorted_kernel, dim3((unsigned)nb), dim3(kBlock), 0, nullptr, rowptr, col, M,
+                       partial);
+    std::vector<int64_t> h((size_t)nb);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpy(h.data(), partial, sizeof(int64_t) * (size_t)nb, hipMemcpyDeviceToHost);
+    dfree(partial);
+    if (e != hipSuccess) return e;
+    for (int64_t x : h) *vectors += x;
+    return hipSuccess;
+}
+
+// Panels of a plan whose rows are all sorted: per-panel merge counts, their
+// exclusive scan, then the merge again writing the vectors.
+hipError_t pair_build_sorted(const int *rowptr, const int *col, const float *val, int64_t M, int *prow,
+                             PairOutput *out) {
+    const int64_t npanels = (M + 1) / 2;
+    int *cnt = nullptr;
+    void *scan_tmp = nullptr;
+    size_t scan_bytes = 0;
+    hipError_t e = dmalloc(&cnt, sizeof(int) * (size_t)(npanels + 1), "panel counts");
+    if (e == hipSuccess) e = hipMemset(cnt + npanels, 0, sizeof(int));
+    if (e == hipSuccess && npanels > 0) {
+        hipLaunchKernelGGL(pair_merge_kernel<false>, dim3((unsigned)walk_grid(npanels)), dim3(kBlock), 0, nullptr,
+                           rowptr, col, val, M, cnt, nullptr, nullptr, nullptr);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(nullptr, scan_bytes, cnt, prow, (int)(npanels + 1));
+    if (e == hipSuccess) e = dmalloc(&scan_tmp, scan_bytes > 0 ? scan_bytes : 1, "panel scan storage");
+    if (e == hipSuccess) e = hipcub::DeviceScan::ExclusiveSum(scan_tmp, scan_bytes, cnt, prow, (int)(npanels + 1));
+    int nvec = 0;
+    if (e == hipSuccess) e = hipMemcpy(&nvec, prow + npanels, sizeof(int), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && nvec > 0) {
+        e = dmalloc(&out->pcol, sizeof(unsigned) * (size_t)nvec, "panel columns");
+        if (e == hipSuccess && val) e = dmalloc(&out->pval, sizeof(float) * 2 * (size_t)nvec, "panel values");
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(pair_merge_kernel<true>, dim3((unsigned)walk_grid(npanels)), dim3(kBlock), 0,
+                               nullptr, rowptr, col, val, M, nullptr, prow, out->pcol, out->pval);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            dfree(out->pcol);
+            dfree(out->pval);
+            out->pcol = nullptr;
+            out->pval = nullptr;
+        }
+    }
+    out->nvec = nvec;
+    dfree(cnt);
+    dfree(scan_tmp);
+    return e;
+}
+
 hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
-                      int *prow, PairOutput *out) {
+                      bool rows_sorted, int *prow, PairOutput *out) {
     out->nvec = 0;
     out->unsorted = 0;
     out->pcol = nullptr;
     out->pval = nullptr;
+    if (rows_sorted) return pair_build_sorted(rowptr, col, val, M, prow, out);
     const int64_t npanels = (M + 1) / 2;
     uint64_t *ka = nullptr, *kb = nullptr;
     int *pa = nullptr, *pb = nullptr, *cnt = nullptr, *flag = nullptr;

@@ -76,8 +76,12 @@ struct PairOutput {
     int nvec;         // nonzero vectors
     int unsorted;     // some row is not stored with ascending columns
 };
+// rows_sorted: every row is stored with ascending columns (merge build, no sort).
 hipError_t pair_build(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
-                      int *prow, PairOutput *out);
+                      bool rows_sorted, int *prow, PairOutput *out);
+// Nonzero vectors of the V = 2 panels when every row is stored with ascending
+// columns (a merge per panel, no sort; synchronous).
+hipError_t pair_count_sorted(const int *rowptr, const int *col, int64_t M, int64_t *vectors);
 PairKernelFn pair_kernel(int lanes, int vec, bool has_val, bool is_max);
 hipError_t launch_pairs(PairKernelFn fn, PairArgs a, int lanes, int slices, hipStream_t s);
 

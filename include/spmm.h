@@ -75,7 +75,7 @@ enum spmm_option {
     SPMM_OPT_TILES = 9,        /* -1 auto (low, even degrees), 0 off, 1 on, 2 on
                                   with 32-bit records: keep 8-row tile records
                                   holding row bounds + indexes               */
-    SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 128), 0 off,
+    SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 64), 0 off,
                                   1 on: stage each 256-row block of B in LDS
                                   (a faster kernel when every row's columns
                                   are non-decreasing, bit-identical either way;
@@ -85,9 +85,12 @@ enum spmm_option {
     SPMM_OPT_MFMA = 11,        /* matrix-core tiles for community blocks, see
                                   below: 0 off (default), 1 fp16 tiles, 2 split
                                   fp16 tiles (fp32 tolerance)                 */
-    SPMM_OPT_VBLOCK = 12,      /* vectorized blocking V = 2, see below: 0 off
-                                  (default), 1 build, use when padding <= 0.3,
-                                  2 build, always use                          */
+    SPMM_OPT_VBLOCK = 12,      /* vectorized blocking V = 2, see below: -1 auto
+                                  (default): built at plan creation when the
+                                  plan is not split, every row is stored with
+                                  ascending columns and the padding share is
+                                  <= 0.3; 0 off (frees them); 1 build, use when
+                                  padding <= 0.3; 2 build, always use          */
     SPMM_OPT_BALANCE = 13,     /* load balance: 0 row split of heavy rows
                                   (default), 1 merge path, see below          */
     SPMM_OPT_PIECE_ORDER = 14, /* 1 (default): the row split's pieces run in
@@ -158,6 +161,10 @@ int spmm_mem_stats(struct spmm_mem_stats *out);
  * (+ 8 when weighted) + 4 per panel.  With 1, runs use the panels only when
  * the padding share 1 - nnz / (2 * vectors) is at most 0.3; with 2, always.
  * 0 frees them.  Split plans keep their own path unless the value is 2.
+ * With -1 (the default) plan creation counts the vectors of a plan whose rows
+ * are all stored with ascending columns in one merge pass and builds the
+ * panels (two more merge passes and a scan, no sort) when the padding share
+ * is at most 0.3, where each gather of a B row serves 1.4 entries or more.
  */
 
 /*

@@ -115,7 +115,8 @@ OPTION_CASES = [
     ("window runs", "block", "SPMM_OPT_WINDOW", 1, []),
     ("fp16 tiles", "community", "SPMM_OPT_MFMA", 1, []),
     ("split fp16 tiles", "community", "SPMM_OPT_MFMA", 2, []),
-    ("V = 2 panels", "knn", "SPMM_OPT_VBLOCK", 2, []),
+    ("V = 2 panels", "knn", "SPMM_OPT_VBLOCK", 2, [("SPMM_OPT_VBLOCK", 0)]),
+    ("automatic V = 2 panels", "knn", "SPMM_OPT_VBLOCK", -1, [("SPMM_OPT_VBLOCK", 0)]),
     ("merge path", "skewed", "SPMM_OPT_BALANCE", 1, []),
 ]
 

@@ -152,3 +152,46 @@ def test_panels_full_road_sampled(orc):
     rows = np.unique(np.concatenate([np.linspace(0, g.M - 1, 500).astype(np.int64), np.arange(g.M - 30, g.M)]))
     check(orc, g, B, "sum", C[rows], None, rows=rows, exact_rows=np.arange(rows.size), what="road panels")
     G.spmm_plan_destroy(plan)
+
+
+def test_panels_built_automatically(orc):
+    """SPMM_OPT_VBLOCK = -1 (the default): plan creation builds the panels of a
+    plan with sorted rows when their padding share is at most 0.3 (merge
+    count and merge build, no sort); the vectors equal a numpy count and the
+    products stay bit-exact.  Graphs with more padding, unsorted rows or a
+    row split keep the row kernels."""
+    rng = np.random.default_rng(15)
+    cases = [
+        ("knn", W.knn_line(6001, 10), 1),
+        ("knn weighted dups", None, 1),
+        ("random sorted", W.random_csr(rng, 5000, 5000, mean_deg=10.0, weighted=False), 0),
+        ("random unsorted", W.random_csr(rng, 5000, 5000, mean_deg=10.0, shuffle_rows=True), 0),
+    ]
+    # a weighted kNN graph with every row's last column stored twice
+    k = W.knn_line(4001, 8)
+    deg = k.degrees()
+    cols, vals, rp = [], [], [0]
+    for i in range(k.M):
+        c = list(k.col[k.rowptr[i]:k.rowptr[i + 1]])
+        c = c + c[-1:]
+        cols += c
+        vals += list(rng.random(len(c)).astype(np.float32))
+        rp.append(len(cols))
+    cases[1] = ("knn weighted dups", W.Graph("kd", k.M, k.K, np.array(rp, np.int64), np.array(cols, np.int64),
+                                             np.array(vals, np.float32)), 1)
+    for name, g, want in cases:
+        plan = make_plan(g)
+        info = G.spmm_plan_info(plan)
+        log(f"auto panels {name}: built {info['pairs_built']} padding {info['pair_padding']:.3f}")
+        assert info["pairs_built"] == want, name
+        if want:
+            assert info["pair_vectors"] == expected_vectors(g) and info["pair_padding"] <= 0.3
+        for N in (16, 64):
+            B = rng.standard_normal((g.K, N)).astype(np.float32)
+            _, _, _, Bd = to_dev(g, B)
+            for red in ("sum", "mean", "max"):
+                C, arg = gpu_run(plan, g.M, Bd, red)
+                assert G.spmm_plan_info(plan)["route_pairs"] == want, (name, N, red)
+                exact = np.arange(g.M) if name != "random unsorted" else None
+                check(orc, g, B, red, C, arg, exact_rows=exact, what=f"auto {name} N={N} {red}")
+        G.spmm_plan_destroy(plan)

@@ -537,3 +537,27 @@ def test_community_window_matches_row_kernel(orc, shape, order):
             check(orc, g, B, red, C1, a1, exact_rows=np.arange(g.M), what=f"window {shape} N={N} {red}")
         G.spmm_plan_destroy(on)
         G.spmm_plan_destroy(off)
+
+
+def test_router_rules():
+    """Routing decisions measured on the GPU (the router sweep): community
+    structure takes the LDS window kernel from 64 columns; launch-bound small
+    graphs take 8 lanes per row without coarsening up to 128 columns; skewed
+    graphs take 128-column slices from 512 columns."""
+    community = make_plan(W.make_graph("community", M=20_000))
+    for N, win in ((16, 0), (64, 2), (128, 2), (512, 2)):
+        info = G.spmm_plan_route(community, N, "sum")
+        assert (info["route_window"] > 0) == (win > 0), (N, info["route_window"])
+    G.spmm_plan_destroy(community)
+    tiny = make_plan(W.make_graph("tiny"))
+    for N, lanes in ((16, 8), (64, 8), (128, 8), (512, 64)):
+        info = G.spmm_plan_route(tiny, N, "sum")
+        assert (info["route_lanes"], info["route_coarsen"]) == (lanes, 1), (N, info)
+    G.spmm_plan_destroy(tiny)
+    rng = np.random.default_rng(5)
+    skew = make_plan(W.random_csr(rng, 20_000, 20_000, mean_deg=6.0, heavy_rows=20, heavy_deg=5000))
+    assert G.spmm_plan_info(skew)["cv_deg"] > 1.0
+    for N, lanes in ((128, 16), (256, 16), (512, 32), (1024, 32)):
+        info = G.spmm_plan_route(skew, N, "sum")
+        assert (info["route_lanes"], info["route_coarsen"]) == (lanes, 1), (N, info)
+    G.spmm_plan_destroy(skew)

@@ -63,6 +63,9 @@ CONFIGS = {
     # router evaluation only: a third road-like band, a third community
     # blocks, a third power-law rows over all columns
     "mixed":     dict(M=1_000_000, N=128, seed=6, reduces=("sum",)),
+    # router evaluation only: k-nearest-neighbour graph of points on a line
+    # (k = 10, unweighted), where two adjacent rows share most columns
+    "knn":       dict(M=1_000_000, N=64,  seed=7, reduces=("sum",)),
 }
 
 
@@ -263,6 +266,11 @@ def _gen_mixed(M: int, rng_s, rng_v):
     return rowptr, col, val
 
 
+def _gen_knn(M: int, rng_s, rng_v):
+    g = knn_line(M, 10)
+    return g.rowptr, g.col, None
+
+
 _GENERATORS = {
     "tiny": _gen_tiny,
     "road": _gen_road,
@@ -270,6 +278,7 @@ _GENERATORS = {
     "diffusion": _gen_diffusion,
     "community": _gen_community,
     "mixed": _gen_mixed,
+    "knn": _gen_knn,
 }
 
 
