@@ -585,9 +585,12 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         return r;
     }
     // V = 2 panels, when built: by padding share (ParamSpMM's PR for V), or forced
+    // (with community structure as well, the window kernel's LDS reuse beats
+    // the panels from 512 columns: kNN line graph 0.976 vs 1.036 ms)
     r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock != 0 &&
               (reduce != SPMM_MAX || !p->pair_unsorted) &&
-              (p->opt_vblock == 2 || (!p->split && pair_padding(p) <= kPairMaxPadding));
+              (p->opt_vblock == 2 ||
+               (!p->split && pair_padding(p) <= kPairMaxPadding && !(r.window && W >= 128)));
     if (r.pairs) {
         r.vec = vec == 4 ? 4 : 1;
         const int64_t Wp = (N + r.vec - 1) / r.vec;

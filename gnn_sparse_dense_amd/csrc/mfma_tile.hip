@@ -236,6 +236,15 @@ __device__ __forceinline__ void residual_rows(const MfmaArgs &a, int64_t task0, 
     }
 }
 
+// Half offset of 16-byte chunk j (8 k values) of B^T column c in LDS.  The
+// chunk index is XOR-swizzled by h(c) = (c ^ c >> 2) & 15, so that both
+// accesses spread over all 64 banks: the MFMA operand read (16 consecutive
+// columns per 256-byte pass, one chunk each: t -> t ^ t >> 2 is invertible
+// on 4 bits, so h takes 16 values) and the transposing store (16 column quads
+// q of one k range, 8-byte halves of two chunks: c = 4q + e gives
+// h = q ^ ((q & 3) << 2) ^ e, again 16 values).
+__device__ __forceinline__ int bt_off(int c, int j) { return c * kMfmaBtPitch + 8 * (j ^ ((c ^ (c >> 2)) & 15)); }
+
 // LDS of one workgroup: B^T (fp16; high and low halves for split tiles) while
 // the products run, then the fp32 C tile and the residual walk's staging.
 constexpr int kBtBytes = kWinCols * kMfmaBtPitch * 2;
@@ -282,8 +291,12 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)
 
     int bexp = 0;
     {
-        // thread (q, o): rows 4o .. 4o+3 of column quad q, stored as 4 columns of B^T
-        const int q = tid & 15, o = tid >> 4;
+        // thread (q, o): rows 4o .. 4o+3 of column quad q, stored as 4 columns of B^T.
+        // Lanes 0-7 take quads 0-7 of an even o, lanes 8-15 the same quads of
+        // o + 1: each 16-lane group then stores two whole chunks per column
+        // quad (bank-conflict free with bt_off), and every 16 lanes of one o
+        // still read one contiguous 256-byte stretch of a B row.
+        const int q = (tid & 7) | (((tid >> 4) & 1) << 3), o = ((tid >> 3) & 1) | ((tid >> 5) << 1);
         const int64_t cc = c0 + 4 * q;
         f32x4 v[4];
 #pragma unroll
@@ -319,30 +332,30 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)
                     h[r] = (_Float16)x;
                     l[r] = (_Float16)(x - (float)h[r]);
                 }
-                *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
-                *reinterpret_cast<f16x4 *>(sbt_lo + (4 * q + e) * kMfmaBtPitch + 4 * o) = l;
+                *reinterpret_cast<f16x4 *>(sbt + bt_off(4 * q + e, o >> 1) + 4 * (o & 1)) = h;
+                *reinterpret_cast<f16x4 *>(sbt_lo + bt_off(4 * q + e, o >> 1) + 4 * (o & 1)) = l;
             } else {
                 const f16x4 h = {(_Float16)v[0][e], (_Float16)v[1][e], (_Float16)v[2][e], (_Float16)v[3][e]};
-                *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
+                *reinterpret_cast<f16x4 *>(sbt + bt_off(4 * q + e, o >> 1) + 4 * (o & 1)) = h;
             }
         }
     }
     __syncthreads();
 
     f32x16 acc = {};
-    const int boff = (cg * 32 + (lane & 31)) * kMfmaBtPitch + 8 * (lane >> 5);
+    const int bcol = cg * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < kMfmaKSteps; ++ks) {
         const uint4 au = ar[ks % AH];
         if (ks + AH < kMfmaKSteps) ar[ks % AH] = ap[(ks + AH) * 64];
         const f16x8 av = __builtin_bit_cast(f16x8, au);
-        const f16x8 bv = *reinterpret_cast<const f16x8 *>(sbt + boff + ks * 16);
+        const f16x8 bv = *reinterpret_cast<const f16x8 *>(sbt + bt_off(bcol, 2 * ks + (lane >> 5)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
         if constexpr (SPLIT) {
             const uint4 aul = arl[ks % AH];
             if (ks + AH < kMfmaKSteps) arl[ks % AH] = apl[(ks + AH) * 64];
             const f16x8 avl = __builtin_bit_cast(f16x8, aul);
-            const f16x8 bvl = *reinterpret_cast<const f16x8 *>(sbt_lo + boff + ks * 16);
+            const f16x8 bvl = *reinterpret_cast<const f16x8 *>(sbt_lo + bt_off(bcol, 2 * ks + (lane >> 5)));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bvl, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(avl, bv, acc, 0, 0, 0);
         }

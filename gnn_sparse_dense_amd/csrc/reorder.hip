@@ -11,9 +11,11 @@
 // (degree, id) order.  Level by level this is: the nodes of the next level
 // ordered by (position of their earliest-placed neighbour in the current
 // level, degree, id), which is what the GPU computes, one level per step:
-//   expand: every node of the level offers its position to its unplaced
-//           neighbours (atomic minimum: the result does not depend on the
-//           order of the offers) and claims each new node once;
+//   expand: every node of the level offers its position to its neighbours
+//           (atomic minimum: the result does not depend on the order of the
+//           offers); the offer that finds no parent yet claims the node.
+//           Placed nodes always have a parent below the level's positions
+//           (component starts get -1), so offers never change or claim them;
 //   order:  the claimed nodes are sorted by id, then stably by (parent
 //           position, degree), and placed.
 // The permutation is therefore exactly the sequential one.
@@ -90,8 +92,9 @@ __global__ void place_isolated_kernel(const int *__restrict__ order, int64_t n0,
 // First t >= from with order[t] unplaced (one block; the caller guarantees
 // one exists); places it at position `placed` and makes it the frontier.
 __global__ __launch_bounds__(kBlock) void next_start_kernel(const int *__restrict__ order, int64_t from, int64_t M,
-                                                            int *__restrict__ pos, int *__restrict__ frontier,
-                                                            int64_t placed, int64_t *__restrict__ found) {
+                                                            int *__restrict__ pos, int *__restrict__ parent,
+                                                            int *__restrict__ frontier, int64_t placed,
+                                                            int64_t *__restrict__ found) {
     __shared__ int64_t s_best;
     if (threadIdx.x == 0) s_best = INT64_MAX;
     __syncthreads();
@@ -109,6 +112,7 @@ __global__ __launch_bounds__(kBlock) void next_start_kernel(const int *__restric
         if (t != INT64_MAX) {
             const int s = order[t];
             pos[s] = (int)placed;
+            parent[s] = -1;   // below every position: never claimed again
             frontier[0] = s;
         }
     }
@@ -117,9 +121,8 @@ __global__ __launch_bounds__(kBlock) void next_start_kernel(const int *__restric
 // Every frontier node (position base + f) offers its position to its unplaced
 // neighbours and claims each newly reached node once.
 __global__ void expand_kernel(const int *__restrict__ srow, const int *__restrict__ scol,
-                              const int *__restrict__ frontier, int64_t nf, int64_t base, const int *__restrict__ pos,
-                              int *__restrict__ parent, int *__restrict__ claimed, int *__restrict__ next,
-                              int *__restrict__ nnext) {
+                              const int *__restrict__ frontier, int64_t nf, int64_t base,
+                              int *__restrict__ parent, int *__restrict__ next, int *__restrict__ nnext) {
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 64);
     for (int64_t f = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); f < nf; f += stride) {
@@ -127,9 +130,7 @@ __global__ void expand_kernel(const int *__restrict__ srow, const int *__restric
         const int pu = (int)(base + f);
         for (int64_t q = (int64_t)srow[u] + lane; q < srow[u + 1]; q += 64) {
             const int v = scol[q];
-            if (pos[v] >= 0) continue;
-            atomicMin(&parent[v], pu);
-            if (atomicCAS(&claimed[v], 0, 1) == 0) next[atomicAdd(nnext, 1)] = v;
+            if (atomicMin(&parent[v], pu) == INT_MAX) next[atomicAdd(nnext, 1)] = v;
         }
     }
 }
@@ -155,118 +156,218 @@ __global__ void reverse_kernel(const int *__restrict__ pos, int64_t M, int64_t *
 }
 
 // Consecutive levels of one component inside one workgroup, for levels of
-// at most kSmallLevel nodes: expand as above into the global list `next`,
-// then sort the level's nodes by (parent position, degree, id) with a rank
-// count in LDS and place them.  Returns to the host when the component is
-// finished or a level is larger (its claims are then left in `next`,
-// unsorted and unplaced, for the multi-block path).
+// at most kSmallLevel nodes.  The level's edge ranges stay in LDS from one
+// level to the next, so a level costs three dependent trips to memory: the
+// neighbours' ids, the offers (atomic minimum on the parent, which also
+// claims), and the claimed nodes' parent, degree and edge range.  The
+// claimed nodes are ordered by (parent position, degree, id) with a counting
+// sort by parent and a rank among each parent's few children.  Returns to
+// the host when the component is finished or a level is larger than
+// kSmallLevel (its claims are then in `next`, unsorted and unplaced, and the
+// current level in `frontier`, for the multi-block path).
 constexpr int kSmallLevel = 4096;
 constexpr int kSmallBlock = 1024;
+constexpr int kSmallWaves = kSmallBlock / 64;
 
 struct BfsState {
     int64_t base, nf, placed, nn, levels;
     int64_t done;
 };
 
+// Exclusive prefix of x over the workgroup's threads in thread order; *total
+// is the sum.  s_wave holds kSmallWaves + 1 ints.
+__device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) s_wave[wv] = inc;
+    __syncthreads();
+    if (wv == 0) {
+        const int w = lane < kSmallWaves ? s_wave[lane] : 0;
+        int winc = w;
+#pragma unroll
+        for (int o = 1; o < kSmallWaves; o <<= 1) {
+            const int y = __shfl_up(winc, o);
+            if (lane >= o) winc += y;
+        }
+        if (lane < kSmallWaves) s_wave[lane] = winc - w;
+        if (lane == kSmallWaves - 1) s_wave[kSmallWaves] = winc;
+    }
+    __syncthreads();
+    const int ex = s_wave[wv] + inc - x;
+    *total = s_wave[kSmallWaves];
+    __syncthreads();   // s_wave may be reused
+    return ex;
+}
+
 __global__ __launch_bounds__(kSmallBlock) void small_levels_kernel(const int *__restrict__ srow,
                                                                    const int *__restrict__ scol,
                                                                    const int *__restrict__ deg, int *__restrict__ pos,
-                                                                   int *__restrict__ parent, int *__restrict__ claimed,
-                                                                   int *__restrict__ frontier, int *__restrict__ next,
-                                                                   int64_t base, int64_t nf, BfsState *__restrict__ st) {
-    __shared__ int s_par[kSmallLevel], s_deg[kSmallLevel], s_id[kSmallLevel];
-    __shared__ int s_part[kSmallBlock];
+                                                                   int *__restrict__ parent, int *__restrict__ frontier,
+                                                                   int *__restrict__ next, int64_t base, int64_t nf,
+                                                                   BfsState *__restrict__ st) {
+    __shared__ int s_beg[kSmallLevel], s_len[kSmallLevel];                         // edge ranges of the level
+    __shared__ int s_next[kSmallLevel], s_par[kSmallLevel], s_deg[kSmallLevel];    // the claims
+    __shared__ int s_cnt[kSmallLevel], s_grp[kSmallLevel];                         // the counting sort
+    __shared__ int s_wave[kSmallWaves + 1];
     __shared__ int s_count;
-    constexpr int PER = kSmallLevel / kSmallBlock;   // frontier nodes per thread in the scan
+    constexpr int PER = kSmallLevel / kSmallBlock;
+    constexpr int EB = 4;   // edges per thread in flight together
     const int tid = threadIdx.x;
+    for (int64_t f = tid; f < nf; f += kSmallBlock) {
+        const int u = frontier[f];
+        const int b = srow[u];
+        s_beg[f] = b;
+        s_len[f] = srow[u + 1] - b;
+    }
+    if (tid == 0) s_count = 0;
+    __syncthreads();
     int64_t placed = 0, levels = 0;
     int64_t n = 0;
     for (;;) {
-        if (tid == 0) s_count = 0;
-        if (nf <= 64) {
-            // a few frontier nodes: one wave each, lanes over the node's edges
-            __syncthreads();
-            const int lane = tid & 63, wv = tid >> 6;
-            for (int64_t f = wv; f < nf; f += kSmallBlock / 64) {
-                const int u = frontier[f];
-                for (int64_t q = (int64_t)srow[u] + lane; q < srow[u + 1]; q += 64) {
-                    const int v = scol[q];
-                    if (pos[v] >= 0) continue;
-                    atomicMin(&parent[v], (int)(base + f));
-                    if (atomicCAS(&claimed[v], 0, 1) == 0) next[atomicAdd(&s_count, 1)] = v;
+        // expand: the level's edges, flattened (s_par = first edge number of
+        // each level node), each offered its node's position
+        int len[PER];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid * PER + k;
+            len[k] = f < nf ? s_len[f] : 0;
+            sum += len[k];
+        }
+        int edges = 0;
+        int ex = block_exclusive_scan(sum, s_wave, &edges);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid * PER + k;
+            if (f < nf) s_par[f] = ex;
+            ex += len[k];
+        }
+        __syncthreads();
+        for (int e0 = 0; e0 < edges; e0 += EB * kSmallBlock) {
+            int vb[EB], fb[EB];
+#pragma unroll
+            for (int b = 0; b < EB; ++b) {
+                const int e = e0 + b * kSmallBlock + tid;
+                fb[b] = -1;
+                if (e < edges) {
+                    int lo = 0, hi = (int)nf - 1;     // last f with s_par[f] <= e
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (s_par[mid] <= e) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    fb[b] = lo;
+                    vb[b] = scol[s_beg[lo] + (e - s_par[lo])];
                 }
             }
-        } else {
-        // the frontier's edges, flattened: s_par = exclusive prefix of the
-        // frontier nodes' degrees, s_id = their first edge
-        int run = 0;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int f = tid * PER + k;
-            int d = 0;
-            if (f < nf) {
-                const int u = frontier[f];
-                s_id[f] = srow[u];
-                d = srow[u + 1] - s_id[f];
+            for (int b = 0; b < EB; ++b) {
+                if (fb[b] < 0) continue;
+                const int v = vb[b];
+                if (atomicMin(&parent[v], (int)(base + fb[b])) == INT_MAX) {
+                    const int slot = atomicAdd(&s_count, 1);
+                    if (slot < kSmallLevel) s_next[slot] = v;
+                    next[slot] = v;
+                }
             }
-            if (f < kSmallLevel) s_deg[f] = d;
-            run += d;
-        }
-        s_part[tid] = run;
-        __syncthreads();
-        for (int o = 1; o < kSmallBlock; o <<= 1) {   // inclusive scan of the per-thread sums
-            const int x = tid >= o ? s_part[tid - o] : 0;
-            __syncthreads();
-            s_part[tid] += x;
-            __syncthreads();
-        }
-        run = s_part[tid] - run;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int f = tid * PER + k;
-            s_par[f] = run;
-            run += s_deg[f];
-        }
-        const int edges = s_part[kSmallBlock - 1];
-        __syncthreads();
-        for (int e = tid; e < edges; e += kSmallBlock) {
-            int lo = 0, hi = (int)nf - 1;             // last f with s_par[f] <= e
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_par[mid] <= e) lo = mid;
-                else hi = mid - 1;
-            }
-            const int v = scol[s_id[lo] + (e - s_par[lo])];
-            if (pos[v] >= 0) continue;
-            atomicMin(&parent[v], (int)(base + lo));
-            if (atomicCAS(&claimed[v], 0, 1) == 0) next[atomicAdd(&s_count, 1)] = v;
-        }
         }
         __syncthreads();
         n = s_count;
         levels += 1;
         if (n == 0 || n > kSmallLevel) break;
-        for (int64_t i = tid; i < n; i += kSmallBlock) {
-            const int v = next[i];
-            s_id[i] = v;
-            s_par[i] = __hip_atomic_load(&parent[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - (int)base;
-            s_deg[i] = deg[v];
-        }
+        for (int64_t f = tid; f < nf; f += kSmallBlock) s_cnt[f] = 0;
         __syncthreads();
-        for (int64_t i = tid; i < n; i += kSmallBlock) {
-            const int pi = s_par[i], di = s_deg[i], vi = s_id[i];
-            int rank = 0;
-            for (int j = 0; j < (int)n; ++j) {
-                const int pj = s_par[j], dj = s_deg[j];
-                rank += (pj < pi || (pj == pi && (dj < di || (dj == di && s_id[j] < vi)))) ? 1 : 0;
+        // the claims' final parent, degree and edge range; their place in
+        // their parent's group
+        int cv[PER], cp[PER], cd[PER], cs[PER], cb[PER], ce[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * kSmallBlock;
+            if (i < n) {
+                const int v = s_next[i];
+                cv[k] = v;
+                cp[k] = __hip_atomic_load(&parent[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - (int)base;
+                cd[k] = deg[v];
+                cb[k] = srow[v];
+                ce[k] = srow[v + 1];
             }
-            frontier[rank] = vi;
-            pos[vi] = (int)(base + nf + rank);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * kSmallBlock;
+            if (i < n) {
+                s_par[i] = cp[k];
+                s_deg[i] = cd[k];
+                cs[k] = atomicAdd(&s_cnt[cp[k]], 1);
+            }
         }
         __syncthreads();
+        {
+            // group starts: exclusive prefix of the group sizes s_cnt[0 .. nf)
+            int c[PER];
+            sum = 0;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int f = tid * PER + k;
+                c[k] = f < nf ? s_cnt[f] : 0;
+                sum += c[k];
+            }
+            int tot = 0;
+            ex = block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int f = tid * PER + k;
+                if (f < nf) s_cnt[f] = ex;
+                ex += c[k];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * kSmallBlock;
+            if (i < n) s_grp[s_cnt[cp[k]] + cs[k]] = i;
+        }
+        __syncthreads();
+        // rank by (degree, id) inside the parent's group
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * kSmallBlock;
+            if (i < n) {
+                const int pi = cp[k], di = cd[k], vi = cv[k];
+                const int g0 = s_cnt[pi];
+                const int g1 = pi + 1 < nf ? s_cnt[pi + 1] : (int)n;
+                int rank = g0;
+                for (int q = g0; q < g1; ++q) {
+                    const int j = s_grp[q];
+                    const int dj = s_deg[j];
+                    rank += (dj < di || (dj == di && s_next[j] < vi)) ? 1 : 0;
+                }
+                cs[k] = rank;
+            }
+        }
+        __syncthreads();
+        // the new level replaces the old one in LDS (no reader of it is left)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * kSmallBlock;
+            if (i < n) {
+                const int rank = cs[k];
+                s_beg[rank] = cb[k];
+                s_len[rank] = ce[k] - cb[k];
+                frontier[rank] = cv[k];
+                pos[cv[k]] = (int)(base + nf + rank);
+            }
+        }
+        if (tid == 0) s_count = 0;
         base += nf;
         nf = n;
         placed += n;
+        __syncthreads();
     }
     if (tid == 0) {
         st->base = base;
@@ -363,13 +464,12 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
         TRY(hipcub::DeviceRadixSort::SortPairs(tmp, tb, deg, degs_sorted, ids, order, (int)M, 0, db));
     }
     // ---- breadth-first placement ----
-    int *pos, *parent, *claimed, *fa, *fb, *d_nnext;
+    int *pos, *parent, *fa, *fb, *d_nnext;
     uint64_t *lk, *lk2;
     int *li;
     int64_t *d_found;
     TRY(sc.get(&pos, M));
     TRY(sc.get(&parent, M));
-    TRY(sc.get(&claimed, M));
     TRY(sc.get(&fa, M));
     TRY(sc.get(&fb, M));
     TRY(sc.get(&d_nnext, 1));
@@ -380,7 +480,6 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
     const dim3 gM((unsigned)grid_for(M));
     hipLaunchKernelGGL(fill_kernel, gM, dim3(kBlock), 0, nullptr, pos, M, -1);
     hipLaunchKernelGGL(fill_kernel, gM, dim3(kBlock), 0, nullptr, parent, M, INT_MAX);
-    hipLaunchKernelGGL(fill_kernel, gM, dim3(kBlock), 0, nullptr, claimed, M, 0);
     TRY(hipGetLastError());
     // isolated nodes come first in (degree, id) order: each is its own component
     int64_t n0 = 0;
@@ -404,8 +503,8 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
     int64_t placed = n0, from = n0;
     int *frontier = fa, *next = fb;
     while (placed < M) {
-        hipLaunchKernelGGL(next_start_kernel, dim3(1), dim3(kBlock), 0, nullptr, order, from, M, pos, frontier, placed,
-                           d_found);
+        hipLaunchKernelGGL(next_start_kernel, dim3(1), dim3(kBlock), 0, nullptr, order, from, M, pos, parent, frontier,
+                           placed, d_found);
         TRY(hipGetLastError());
         int64_t t = 0;
         TRY(hipMemcpy(&t, d_found, sizeof(int64_t), hipMemcpyDeviceToHost));
@@ -418,7 +517,7 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
             if (nf <= kSmallLevel) {
                 // small levels run on the device until the component ends or a level grows
                 hipLaunchKernelGGL(small_levels_kernel, dim3(1), dim3(kSmallBlock), 0, nullptr, srow, scol, deg, pos,
-                                   parent, claimed, frontier, next, base, nf, d_state);
+                                   parent, frontier, next, base, nf, d_state);
                 TRY(hipGetLastError());
                 BfsState h;
                 TRY(hipMemcpy(&h, d_state, sizeof(BfsState), hipMemcpyDeviceToHost));
@@ -431,7 +530,7 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
             } else {
                 TRY(hipMemset(d_nnext, 0, sizeof(int)));
                 hipLaunchKernelGGL(expand_kernel, dim3((unsigned)grid_for(nf, kWaves)), dim3(kBlock), 0, nullptr, srow,
-                                   scol, frontier, nf, base, pos, parent, claimed, next, d_nnext);
+                                   scol, frontier, nf, base, parent, next, d_nnext);
                 TRY(hipGetLastError());
                 int nn32 = 0;
                 TRY(hipMemcpy(&nn32, d_nnext, sizeof(int), hipMemcpyDeviceToHost));
