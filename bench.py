@@ -662,7 +662,7 @@ def router_sweep(r, reduce, steps, flush):
     G = r.G
     auto = {G.SPMM_OPT_LANES: 0, G.SPMM_OPT_COARSEN: 0, G.SPMM_OPT_TILES: -1, G.SPMM_OPT_WINDOW: -1,
             G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1,
-            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: -1}
+            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: -1, G.SPMM_OPT_SPLIT_FUSED: 1}
     variants = [("router", {})]
     variants += [(f"lanes={g} coarsen={f}", {G.SPMM_OPT_LANES: g, G.SPMM_OPT_COARSEN: f})
                  for g in (4, 8, 16, 32, 64) for f in (1, 2)]
@@ -671,7 +671,8 @@ def router_sweep(r, reduce, steps, flush):
                  ("window off", {G.SPMM_OPT_WINDOW: 0}), ("XCD remap off", {G.SPMM_OPT_XCD_REMAP: 0}),
                  ("non-temporal C stores", {G.SPMM_OPT_NT_STORE: 1}), ("split on", {G.SPMM_OPT_SPLIT_MODE: 1}),
                  ("split off", {G.SPMM_OPT_SPLIT_MODE: 0}), ("merge-path balancing", {G.SPMM_OPT_BALANCE: 1}),
-                 ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2}), ("V = 2 panels off", {G.SPMM_OPT_VBLOCK: 0})]
+                 ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2}), ("V = 2 panels off", {G.SPMM_OPT_VBLOCK: 0}),
+                 ("split in two dispatches", {G.SPMM_OPT_SPLIT_FUSED: 0})]
     rows = []
     for label, opts in variants:
         print(f"[bench]   {reduce} {label}", file=sys.stderr, flush=True)
@@ -682,7 +683,8 @@ def router_sweep(r, reduce, steps, flush):
             ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
             info = G.spmm_plan_info(r.plan)
             entry.update({"ms": round(ms, 5), "path": kernel_family(info) + ("+merge" if info["route_merge"] else "")
-                          + ("+panels" if info["route_pairs"] else ""),
+                          + ("+panels" if info["route_pairs"] else "")
+                          + ("+one dispatch" if info["route_fused_split"] else ""),
                           "route": [info["route_lanes"], info["route_vec"], info["route_coarsen"],
                                     info["route_slices"], info["route_xcd_remap"], info["route_nt_store"],
                                     info["route_split"], info["route_tiled"] * info["tiles"],

@@ -39,6 +39,7 @@ SPMM_OPT_VBLOCK = 12
 SPMM_OPT_BALANCE = 13
 SPMM_OPT_PIECE_ORDER = 14
 SPMM_OPT_MEM_LIMIT = 15
+SPMM_OPT_SPLIT_FUSED = 16
 
 SPMM_REORDER_RCM = 1
 
@@ -81,6 +82,7 @@ class _Info(ctypes.Structure):
         ("pairs_built", ctypes.c_int32), ("route_pairs", ctypes.c_int32),
         ("merge_segments", ctypes.c_int64), ("route_merge", ctypes.c_int32), ("piece_order", ctypes.c_int32),
         ("generation", ctypes.c_int64), ("device_bytes", ctypes.c_int64), ("mem_limit", ctypes.c_int64),
+        ("route_fused_split", ctypes.c_int32),
     ]
 
 

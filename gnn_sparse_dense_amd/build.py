@@ -33,6 +33,7 @@ SOURCES = [
     "pair_kernel.hip",
     "reorder.hip",
     "merge_kernel.hip",
+    "split_fused.hip",
 ]
 
 COMMON = [

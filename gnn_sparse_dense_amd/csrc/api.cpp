@@ -953,6 +953,10 @@ SPMM_API int spmm_plan_set_option(spmm_plan_t p, int option, int64_t value) {
             if (value < 0) return fail(SPMM_E_INVALID_ARG, "memory limit must be >= 0 (0: none)");
             p->mem_limit = value;
             return succeed();
+        case SPMM_OPT_SPLIT_FUSED:
+            if (value < 0 || value > 1) return fail(SPMM_E_INVALID_ARG, "split fused must be 0 or 1");
+            p->opt_split_fused = (int)value;
+            return succeed();
         case SPMM_OPT_NT_STORE:
             if (value < -1 || value > 1) return fail(SPMM_E_INVALID_ARG, "nt store must be -1, 0 or 1");
             p->opt_nt = (int)value;
@@ -1088,6 +1092,7 @@ SPMM_API int spmm_plan_info(spmm_plan_t p, struct spmm_plan_info *out) {
     info.generation = p->generation;
     info.device_bytes = plan_bytes(p);
     info.mem_limit = p->mem_limit;
+    info.route_fused_split = p->route.fused_split ? 1 : 0;
 
     *out = info;
     return succeed();
@@ -1278,37 +1283,56 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     a.nt_store = r.nt_store;
     a.win_lo = p->win_lo;
     a.win_in = p->win_in;
-    hipError_t e = r.window ? launch_window(a, has_val, is_max, r.window_sorted, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
-    if (e != hipSuccess) return fail_hip(e, "row kernel launch");
+    // arguments of the piece kernel for columns [w0, w1)
+    auto piece_args = [&](int64_t w0, int64_t w1) {
+        RowArgs pa;
+        std::memset(&pa, 0, sizeof(pa));
+        pa.seg_begin = p->seg_begin;
+        pa.seg_end = p->seg_end;
+        pa.col = p->col;
+        pa.val = p->val;
+        pa.B = B;
+        pa.out = p->partial;
+        pa.part_arg = p->part_arg;
+        pa.ldo = kPartialWidth;
+        pa.N = N;
+        pa.K = p->K;
+        pa.c_begin = w0;
+        pa.c_end = w1;
+        pa.ntasks = p->n_seg;
+        pa.xcd_remap = 0;
+        pa.nt_store = 0;
+        pa.task_perm = p->seg_order;
+        return pa;
+    };
+    const bool split = p->split && p->n_seg > 0;
+    // a split product of one column pass: light rows and pieces in one dispatch
+    const bool fused = split && p->opt_split_fused != 0 && !r.window && !r.tiled && N <= kPartialWidth &&
+                       split_fused_available(r.lanes, r.vec, r.coarsen);
+    hipError_t e = hipSuccess;
+    bool fused_done = false;
+    if (fused) {
+        e = launch_split_fused(r.lanes, has_val, is_max, a, piece_args(0, N), r.slices, s, &fused_done);
+        if (e != hipSuccess) return fail_hip(e, "split kernel launch");
+    }
+    if (!fused_done) {
+        e = r.window ? launch_window(a, has_val, is_max, r.window_sorted, s) : launch_rows(fn, a, 64 / r.lanes, r.slices, s);
+        if (e != hipSuccess) return fail_hip(e, "row kernel launch");
+    }
+    p->route.fused_split = fused_done;
 
-    if (p->split && p->n_seg > 0) {
+    if (split) {
         for (int64_t w0 = 0; w0 < N; w0 += kPartialWidth) {
             const int64_t w1 = std::min<int64_t>(N, w0 + kPartialWidth);
             const int64_t Wv = (w1 - w0) / r.vec;
             const int F = Wv > 64 ? 2 : 1;
             const int slices = (int)((Wv + 64 * F - 1) / (64 * F));
-            RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true, false, false});
-            if (!pf) return fail(SPMM_E_UNSUPPORTED, "no piece kernel for vec=%d", r.vec);
-            RowArgs pa;
-            std::memset(&pa, 0, sizeof(pa));
-            pa.seg_begin = p->seg_begin;
-            pa.seg_end = p->seg_end;
-            pa.col = p->col;
-            pa.val = p->val;
-            pa.B = B;
-            pa.out = p->partial;
-            pa.part_arg = p->part_arg;
-            pa.ldo = kPartialWidth;
-            pa.N = N;
-            pa.K = p->K;
-            pa.c_begin = w0;
-            pa.c_end = w1;
-            pa.ntasks = p->n_seg;
-            pa.xcd_remap = 0;
-            pa.nt_store = 0;
-            pa.task_perm = p->seg_order;
-            e = launch_rows(pf, pa, 1, slices, s);
-            if (e != hipSuccess) return fail_hip(e, "piece kernel launch");
+            if (!fused_done) {
+                RowKernelFn pf = row_kernel(RowKernelKey{64, r.vec, F, has_val, is_max, true, false, false});
+                if (!pf) return fail(SPMM_E_UNSUPPORTED, "no piece kernel for vec=%d", r.vec);
+                e = launch_rows(pf, piece_args(w0, w1), 1, slices, s);
+                if (e != hipSuccess) return fail_hip(e, "piece kernel launch");
+            }
             CombineArgs ca;
             ca.heavy_rows = p->heavy_rows;
             ca.seg_first = p->seg_first;

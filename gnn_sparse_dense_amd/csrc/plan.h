@@ -18,6 +18,7 @@ struct Route {
     bool mfma = false;
     bool pairs = false;
     bool merge = false;
+    bool fused_split = false;     // light rows and pieces went out in one dispatch
 };
 
 // V = 2 panels are used by default only up to this padding share of vector
@@ -71,7 +72,7 @@ struct spmm_plan {
     int64_t merge_nseg = 0;
     // options (-1 / 0 = automatic)
     int64_t opt_T = -1, opt_L = -1, opt_split = -1, opt_tiles = -1, opt_window = -1;
-    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = -1, opt_balance = 0, opt_piece_order = 1;
+    int opt_lanes = 0, opt_coarsen = 0, opt_vec = 0, opt_xcd = -1, opt_nt = -1, opt_mfma = 0, opt_vblock = -1, opt_balance = 0, opt_piece_order = 1, opt_split_fused = 1;
     // device memory limit of calls on this plan (<= 0: none), and the count
     // of changes to the set of its device buffers
     int64_t mem_limit = 0;

@@ -24,6 +24,12 @@ RowKernelFn row_kernel_v4(const RowKernelKey &k);
 RowKernelFn row_kernel(const RowKernelKey &k);
 
 hipError_t launch_combine(const CombineArgs &a, bool is_max, hipStream_t s);
+// Pieces and light rows of a split product in one dispatch (split_fused.hip);
+// available for the light-row shapes below.  *launched is false (and nothing
+// runs) when the shapes or the grid do not fit one launch: launch separately.
+bool split_fused_available(int lanes, int vec, int coarsen);
+hipError_t launch_split_fused(int lanes, bool has_val, bool is_max, const RowArgs &light, const RowArgs &pieces,
+                              int light_slices, hipStream_t s, bool *launched);
 hipError_t launch_window(const RowArgs &a, bool has_val, bool is_max, bool sorted, hipStream_t s);
 
 // ---- plan-time kernels (plan_kernels.hip) ----

@@ -97,10 +97,14 @@ enum spmm_option {
                                   ascending order of their first entry's
                                   column; 0: in partition order.  Same
                                   partition, same bits; rebuilds the split    */
-    SPMM_OPT_MEM_LIMIT = 15    /* bytes of device memory the plan may hold,
+    SPMM_OPT_MEM_LIMIT = 15,   /* bytes of device memory the plan may hold,
                                   counting the temporaries of a call on it;
                                   0 (default): no limit.  See "Device memory"
                                   below                                       */
+    SPMM_OPT_SPLIT_FUSED = 16  /* 1 (default): a split product of N <= 256
+                                  columns on the row kernel runs its light
+                                  rows and its pieces in one dispatch (pieces
+                                  first); 0: two dispatches.  Same bits      */
 };
 
 /*
@@ -239,6 +243,8 @@ struct spmm_plan_info {
                                     the plan (see spmm_run on graph capture) */
     int64_t device_bytes;        /* device memory the plan holds             */
     int64_t mem_limit;           /* SPMM_OPT_MEM_LIMIT (0: none)             */
+    int32_t route_fused_split;   /* 1 when the last run sent light rows and
+                                    split pieces in one dispatch              */
 };
 
 /*

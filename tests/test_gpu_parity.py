@@ -272,6 +272,66 @@ def test_piece_order_same_bits(orc, shuffled):
     G.spmm_plan_destroy(off)
 
 
+@pytest.mark.parametrize("weighted", [True, False])
+def test_split_fused_same_bits(orc, weighted):
+    """A split product of at most 256 columns on the row kernel runs its light
+    rows and its pieces in one dispatch by default: every output bit equals
+    that of the two dispatches (sum, mean, max and argmax), with the router's
+    launch shape and with forced 16- and 32-lane shapes, XCD remap on and
+    off; wider products keep two dispatches."""
+    rng = np.random.default_rng(4242 + weighted)
+    g = W.random_csr(rng, 20_000, 20_000, mean_deg=6.0, empty_frac=0.05, heavy_rows=40, heavy_deg=5000,
+                     dup_frac=0.01, shuffle_rows=True, weighted=weighted)
+    shapes = [[], [(G.SPMM_OPT_LANES, 16), (G.SPMM_OPT_VEC, 4), (G.SPMM_OPT_COARSEN, 1), (G.SPMM_OPT_XCD_REMAP, 1)],
+              [(G.SPMM_OPT_LANES, 32), (G.SPMM_OPT_VEC, 4), (G.SPMM_OPT_COARSEN, 1), (G.SPMM_OPT_XCD_REMAP, 0)]]
+    light = None
+    for si, shape in enumerate(shapes):
+        on = make_plan(g, shape)
+        off = make_plan(g, shape + [(G.SPMM_OPT_SPLIT_FUSED, 0)])
+        assert G.spmm_plan_info(on)["n_seg"] > 0
+        if light is None:
+            light = _light_rows(on, g.M)
+        for N in (32, 128, 256, 300):
+            B = rng.standard_normal((g.K, N)).astype(np.float32)
+            _, _, _, Bd = to_dev(g, B)
+            for red in ("sum", "mean", "max"):
+                what = f"split fused shape={si} N={N} {red} w={weighted}"
+                log(what)
+                C1, a1 = gpu_run(on, g.M, Bd, red)
+                i1 = G.spmm_plan_info(on)
+                C0, a0 = gpu_run(off, g.M, Bd, red)
+                assert G.spmm_plan_info(off)["route_fused_split"] == 0
+                can = (i1["route_lanes"] in (16, 32) and i1["route_vec"] == 4 and i1["route_coarsen"] == 1
+                       and not i1["route_window"] and not i1["route_tiled"] and N <= 256)
+                assert i1["route_fused_split"] == int(can), (what, i1)
+                if si > 0 and N <= 256:
+                    assert can, (what, i1)
+                assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), what
+                if red == "max":
+                    assert np.array_equal(a1, a0), what
+                if si == 0:
+                    check(orc, g, B, red, C1, a1, exact_rows=light, what=what)
+        G.spmm_plan_destroy(on)
+        G.spmm_plan_destroy(off)
+
+
+def test_split_fused_powerlaw_same_bits(orc):
+    w = _workload("powerlaw", M=200_000)
+    g = w.graph
+    on, off = make_plan(g), make_plan(g, [(G.SPMM_OPT_SPLIT_FUSED, 0)])
+    _, _, _, Bd = to_dev(g, w.B)
+    for red in ("sum", "max"):
+        log(f"split fused powerlaw M={g.M} N={w.N} {red}")
+        C1, a1 = gpu_run(on, g.M, Bd, red)
+        assert G.spmm_plan_info(on)["route_fused_split"] == 1
+        C0, a0 = gpu_run(off, g.M, Bd, red)
+        assert np.array_equal(C1.view(np.uint32), C0.view(np.uint32)), red
+        if red == "max":
+            assert np.array_equal(a1, a0)
+    G.spmm_plan_destroy(on)
+    G.spmm_plan_destroy(off)
+
+
 def test_determinism_bitwise(orc):
     w = _workload("powerlaw", M=200_000)
     g = w.graph
