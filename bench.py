@@ -36,7 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["gnn_sparse_dense_amd/csrc/row_kernel_impl.h", "gnn_sparse_dense_amd/csrc/kernels.h"]
 MFMA_SOURCES = ["gnn_sparse_dense_amd/csrc/mfma_tile.hip", "gnn_sparse_dense_amd/csrc/mfma_args.h"]
-FAMILY_SOURCES = {"mfma_tile_kernel": MFMA_SOURCES, "mfma_split_tile_kernel": MFMA_SOURCES}
+FAMILY_SOURCES = {"mfma_tile_kernel": MFMA_SOURCES, "mfma_split_tile_kernel": MFMA_SOURCES,
+                  "split_fused_kernel": ["gnn_sparse_dense_amd/csrc/split_fused.hip"]}
 
 REGIME_TEXT = {
     "tiny": "tiny random graph M=K=2,000, Poisson(8) degrees, 1% empty rows, weighted, N=16",
@@ -77,6 +78,8 @@ def kernel_family(info) -> str:
         return "window_sorted_kernel" if info.get("route_window") == 2 else "window_kernel"
     if info.get("route_tiled"):
         return "tile_kernel"
+    if info.get("route_fused_split"):
+        return "split_fused_kernel"
     return "row_kernel"
 
 
@@ -683,8 +686,7 @@ def router_sweep(r, reduce, steps, flush):
             ms = statistics.median(r.time_steps(reduce, steps, 2, flush=flush)[0])
             info = G.spmm_plan_info(r.plan)
             entry.update({"ms": round(ms, 5), "path": kernel_family(info) + ("+merge" if info["route_merge"] else "")
-                          + ("+panels" if info["route_pairs"] else "")
-                          + ("+one dispatch" if info["route_fused_split"] else ""),
+                          + ("+panels" if info["route_pairs"] else ""),
                           "route": [info["route_lanes"], info["route_vec"], info["route_coarsen"],
                                     info["route_slices"], info["route_xcd_remap"], info["route_nt_store"],
                                     info["route_split"], info["route_tiled"] * info["tiles"],
@@ -863,7 +865,9 @@ def main():
     # event time per step covers all of them
     launches = 2 if r.info["route_merge"] else 1
     if r.info["route_split"] and r.info["n_seg"] > 0:
-        launches += 2 * (-(-N // 256))
+        # one combine per pass; the pieces share the row kernel's dispatch
+        # when the split runs fused, else add a launch per pass
+        launches += (1 if r.info["route_fused_split"] else 2) * (-(-N // 256))
     comp, gather = byte_model(g, N, reduce)
     flops = 2.0 * g.nnz * N
     value = flops / (ms_per_step * 1e-3) / 1e9

@@ -176,13 +176,34 @@ def _addr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_DTYPES: dict = {}
+
+
+def _dtype_ok(t, dtype: str) -> bool:
+    """t.dtype is torch.<dtype> (the torch dtype object is looked up once)."""
+    d = _DTYPES.get(dtype)
+    if d is None:
+        import torch
+        d = _DTYPES.setdefault(dtype, getattr(torch, dtype))
+    return t.dtype is d
+
+
+def _current_stream(t) -> int:
+    """Raw handle of torch's current stream on the device of tensor t."""
+    import torch
+    get_raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get_raw is not None and t is not None and not isinstance(t, int):
+        return get_raw(t.get_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _check_matrix(name, t, dtype, rows, cols):
     """A tensor passed by address must be what the library will read or write:
     the C ABI sees only the pointer, so a strided view or a wrong dtype would
     be read as packed row-major data without any error."""
     if t is None or isinstance(t, int):
         return
-    if str(t.dtype).split(".")[-1] != dtype:
+    if not _dtype_ok(t, dtype):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major)")
@@ -220,7 +241,7 @@ def _check_rows(name, t, rows):
 def _check_vector(name, t, dtype, min_len=None, exact_len=None):
     if t is None or isinstance(t, int):
         return
-    if str(t.dtype).split(".")[-1] != dtype or not t.is_contiguous() or t.dim() != 1:
+    if not _dtype_ok(t, dtype) or not t.is_contiguous() or t.dim() != 1:
         raise TypeError(f"{name} must be a contiguous 1-D {dtype} tensor")
     if exact_len is not None and t.numel() != exact_len:
         raise ValueError(f"{name} has {t.numel()} elements, expected {exact_len}")
@@ -260,8 +281,7 @@ def spmm_run(plan: int, B, C, argmax, N: int, reduce, stream=None) -> None:
     _check_rows("argmax", argmax, M)
     _check_gpu(B=B, C=C, argmax=argmax)
     if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
+        stream = _current_stream(C)
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     _check(_lib.spmm_run(plan, _addr(B), _addr(C), _addr(argmax), int(N), red, stream))
@@ -398,8 +418,7 @@ def spmm_max_backward(plan_t: int, argmax, dC, dB, N: int, stream=None) -> None:
     _check_rows("dB", dB, Mt)
     _check_gpu(argmax=argmax, dC=dC, dB=dB)
     if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
+        stream = _current_stream(dB)
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     _check(_lib.spmm_max_backward(plan_t, _addr(argmax), _addr(dC), _addr(dB), int(N), stream))
