@@ -83,6 +83,18 @@ __global__ void fill_kernel(int *__restrict__ a, int64_t n, int v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) a[i] = v;
 }
 
+// Number of leading zeros of the ascending degrees (one thread, binary search).
+__global__ void count_isolated_kernel(const int *__restrict__ degs_sorted, int64_t M, int64_t *__restrict__ n0) {
+    if (threadIdx.x != 0) return;
+    int64_t lo = 0, hi = M;   // first index with degree >= 1
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (degs_sorted[mid] < 1) lo = mid + 1;
+        else hi = mid;
+    }
+    *n0 = lo;
+}
+
 // Places order[0 .. n0) (the isolated nodes, degree 0) at positions 0 .. n0-1.
 __global__ void place_isolated_kernel(const int *__restrict__ order, int64_t n0, int *__restrict__ pos) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -155,227 +167,412 @@ __global__ void reverse_kernel(const int *__restrict__ pos, int64_t M, int64_t *
         perm[M - 1 - pos[u]] = u;
 }
 
-// Consecutive levels of one component inside one workgroup, for levels of
-// at most kSmallLevel nodes.  The level's edge ranges stay in LDS from one
-// level to the next, so a level costs three dependent trips to memory: the
-// neighbours' ids, the offers (atomic minimum on the parent, which also
-// claims), and the claimed nodes' parent, degree and edge range.  The
-// claimed nodes are ordered by (parent position, degree, id) with a counting
-// sort by parent and a rank among each parent's few children.  Returns to
-// the host when the component is finished or a level is larger than
-// kSmallLevel (its claims are then in `next`, unsorted and unplaced, and the
-// current level in `frontier`, for the multi-block path).
-constexpr int kSmallLevel = 4096;
-constexpr int kSmallBlock = 1024;
-constexpr int kSmallWaves = kSmallBlock / 64;
-
-struct BfsState {
-    int64_t base, nf, placed, nn, levels;
-    int64_t done;
-};
-
-// Exclusive prefix of x over the workgroup's threads in thread order; *total
-// is the sum.  s_wave holds kSmallWaves + 1 ints.
-__device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
+// Edge records for the level kernel: for every symmetric entry q (u -> v),
+// the edge range start and degree of v beside v itself, so that reaching a
+// node also brings what its own expansion and ordering need.
+__global__ void nbr_records_kernel(const int *__restrict__ srow, const int *__restrict__ scol,
+                                   const int *__restrict__ deg, int64_t nsym, int *__restrict__ nsrow,
+                                   int *__restrict__ ndeg) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nsym; q += stride) {
+        const int v = scol[q];
+        nsrow[q] = srow[v];
+        ndeg[q] = deg[v];
     }
-    if (lane == 63) s_wave[wv] = inc;
-    __syncthreads();
-    if (wv == 0) {
-        const int w = lane < kSmallWaves ? s_wave[lane] : 0;
-        int winc = w;
-#pragma unroll
-        for (int o = 1; o < kSmallWaves; o <<= 1) {
-            const int y = __shfl_up(winc, o);
-            if (lane >= o) winc += y;
-        }
-        if (lane < kSmallWaves) s_wave[lane] = winc - w;
-        if (lane == kSmallWaves - 1) s_wave[kSmallWaves] = winc;
-    }
-    __syncthreads();
-    const int ex = s_wave[wv] + inc - x;
-    *total = s_wave[kSmallWaves];
-    __syncthreads();   // s_wave may be reused
-    return ex;
 }
 
-__global__ __launch_bounds__(kSmallBlock) void small_levels_kernel(const int *__restrict__ srow,
-                                                                   const int *__restrict__ scol,
-                                                                   const int *__restrict__ deg, int *__restrict__ pos,
-                                                                   int *__restrict__ parent, int *__restrict__ frontier,
-                                                                   int *__restrict__ next, int64_t base, int64_t nf,
-                                                                   BfsState *__restrict__ st) {
-    __shared__ int s_beg[kSmallLevel], s_len[kSmallLevel];                         // edge ranges of the level
-    __shared__ int s_next[kSmallLevel], s_par[kSmallLevel], s_deg[kSmallLevel];    // the claims
-    __shared__ int s_cnt[kSmallLevel], s_grp[kSmallLevel];                         // the counting sort
-    __shared__ int s_wave[kSmallWaves + 1];
-    __shared__ int s_count;
+// Consecutive levels of one component inside one workgroup, for levels of
+// at most kSmallLevel nodes.  Breadth first on a symmetric pattern, the
+// neighbours of level L lie in levels L-1, L and L+1 only, so a neighbour is
+// new exactly when it is in neither of the two levels the workgroup already
+// holds: those two levels are LDS hash sets, and the new level's claims go
+// into a third one, keyed by node with the smallest offering position (LDS
+// atomic minimum: independent of the order of the offers).  A level then
+// costs one dependent trip to memory (the level's edge records: neighbour,
+// its edge range start and its degree); the first level after entry, whose
+// previous level is not in LDS, asks the global parent array instead.  The
+// claims are ordered by (parent position, degree, id): one scan over the
+// parents gives each parent's first child and first edge number, a rank
+// among the parent's few children gives the rest, and each new node writes
+// its own edges into an LDS map from edge number to node, so that the next
+// level finds the node of an edge with one read.  Placed nodes get pos,
+// parent and frontier written to memory for the multi-block path.  Returns
+// to the host when the component is finished, or, with the level unexpanded
+// and in `frontier`, when its claims would exceed kSmallLevel.
+constexpr int kSmallLevel = 2048;
+constexpr int kSmallBlock = 1024;
+constexpr int kSmallWaves = kSmallBlock / 64;
+constexpr int kHashBits = 12;
+constexpr int kHashSlots = 1 << kHashBits;   // >= 2 kSmallLevel: load factor at most 1/2
+constexpr int kEdgeMap = 8192;               // levels with more edges search the edge numbers
+static_assert(kHashSlots >= 2 * kSmallLevel, "hash sets hold a level at load <= 1/2");
+static_assert(kSmallLevel <= 65535, "16-bit node numbers in the edge map and group counts");
+
+struct BfsState {
+    int64_t base, nf, placed, levels;
+    int64_t done;   // 1 component finished, 0 a level left to the host, 2 inconsistent
+};
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not
+// for its global stores (nothing in the level kernel reads them back).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the last lane
+// of row 0 (and of row 2) added to row 1 (and row 3), then the last lane of
+// row 1 added to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Exclusive prefixes of x and y over the workgroup's threads in thread
+// order, and their totals, with one barrier: every wave adds up the wave
+// totals itself.  s_wave holds 2 kSmallWaves ints; the caller keeps a
+// barrier between the reads of one call and the writes of the next.
+__device__ __forceinline__ void block_exclusive_scan2(int x, int y, int *s_wave, int *ex_x, int *ex_y, int *tot_x,
+                                                      int *tot_y) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ix = wave_inclusive_scan(x), iy = wave_inclusive_scan(y);
+    if (lane == 63) {
+        s_wave[wv] = ix;
+        s_wave[kSmallWaves + wv] = iy;
+    }
+    lds_barrier();
+    int px = 0, py = 0, tx = 0, ty = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+        const int a = s_wave[w], b = s_wave[kSmallWaves + w];
+        px += w < wv ? a : 0;
+        py += w < wv ? b : 0;
+        tx += a;
+        ty += b;
+    }
+    *ex_x = px + ix - x;
+    *ex_y = py + iy - y;
+    *tot_x = tx;
+    *tot_y = ty;
+}
+
+__device__ __forceinline__ int hash_home(int v) {
+    return (int)(((uint32_t)v * 2654435761u) >> (32 - kHashBits));
+}
+
+// v is a key of set a or of set b (linear probing, -1 marks an empty slot;
+// the two probe sequences advance together).
+__device__ __forceinline__ bool hash_has2(const int *a, const int *b, int v) {
+    int ha = hash_home(v), hb = ha;
+    bool open_a = true, open_b = true, found = false;
+    for (int i = 0; i < kHashSlots && (open_a || open_b); ++i) {
+        const int ka = open_a ? a[ha] : -1;
+        const int kb = open_b ? b[hb] : -1;
+        if (open_a) {
+            if (ka == v) found = true;
+            if (ka == v || ka < 0) open_a = false;
+            ha = (ha + 1) & (kHashSlots - 1);
+        }
+        if (open_b) {
+            if (kb == v) found = true;
+            if (kb == v || kb < 0) open_b = false;
+            hb = (hb + 1) & (kHashSlots - 1);
+        }
+    }
+    return found;
+}
+
+// Slot of v, inserted when absent (*fresh tells which); -1 when the set is full.
+__device__ __forceinline__ int hash_put(int *keys, int v, bool *fresh) {
+    int h = hash_home(v);
+    for (int i = 0; i < kHashSlots; ++i) {
+        const int k = atomicCAS(&keys[h], -1, v);
+        if (k < 0 || k == v) {
+            *fresh = k < 0;
+            return h;
+        }
+        h = (h + 1) & (kHashSlots - 1);
+    }
+    *fresh = false;
+    return -1;
+}
+
+__global__ __launch_bounds__(kSmallBlock) void lds_levels_kernel(
+    const int *__restrict__ srow, const int *__restrict__ scol, const int *__restrict__ nsrow,
+    const int *__restrict__ ndeg, const int *__restrict__ deg, int *__restrict__ pos, int *__restrict__ parent,
+    int *__restrict__ frontier, int64_t M, int64_t nsym, int64_t base, int64_t nf, BfsState *__restrict__ st) {
+    __shared__ int s_beg[kSmallLevel], s_off[kSmallLevel];     // the level's edge ranges, first edge numbers
+    __shared__ uint16_t s_emap[kEdgeMap];                       // edge number -> level node
+    __shared__ int s_keys[3][kHashSlots];                       // two levels + the claims
+    __shared__ int s_hval[kHashSlots];                          // smallest offer per claim
+    __shared__ int s_next[kSmallLevel], s_slot[kSmallLevel];    // claims: node, hash slot,
+    __shared__ int s_csrow[kSmallLevel], s_cdeg[kSmallLevel];   //   edge range start, degree
+    __shared__ int s_gcnt[kSmallLevel], s_gdeg[kSmallLevel];    // per parent: children, their degrees
+    __shared__ int s_grp[kSmallLevel];                          // claims grouped by parent
+    __shared__ int s_wave[2 * kSmallWaves];
+    __shared__ int s_count, s_flag;                             // s_flag: 1 overflow, 2 inconsistent
     constexpr int PER = kSmallLevel / kSmallBlock;
     constexpr int EB = 4;   // edges per thread in flight together
-    const int tid = threadIdx.x;
-    for (int64_t f = tid; f < nf; f += kSmallBlock) {
-        const int u = frontier[f];
-        const int b = srow[u];
-        s_beg[f] = b;
-        s_len[f] = srow[u + 1] - b;
+    const int tid = threadIdx.x, lane = tid & 63;
+    int prv = 0, cur = 1, nxt = 2;
+    for (int i = tid; i < kHashSlots; i += kSmallBlock) {
+        s_keys[0][i] = -1;
+        s_keys[1][i] = -1;
+        s_keys[2][i] = -1;
+        s_hval[i] = INT_MAX;
     }
-    if (tid == 0) s_count = 0;
-    __syncthreads();
+    if (tid == 0) {
+        s_count = 0;
+        s_flag = 0;
+    }
+    lds_barrier();
+    // entry: the level from memory; its first edge numbers by a scan of the degrees
+    int edges = 0;
+    {
+        int ld[PER], dsum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid * PER + k;
+            ld[k] = 0;
+            if (f < nf) {
+                const int u = frontier[f];
+                s_beg[f] = srow[u];
+                ld[k] = deg[u];
+                bool fresh;
+                (void)hash_put(s_keys[cur], u, &fresh);   // nf <= kSmallLevel: always room
+            }
+            dsum += ld[k];
+        }
+        int ex, unused, etot, utot;
+        block_exclusive_scan2(dsum, 0, s_wave, &ex, &unused, &etot, &utot);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int f = tid * PER + k;
+            if (f < nf) {
+                s_off[f] = ex;
+                if (etot <= kEdgeMap)
+                    for (int j = 0; j < ld[k]; ++j) s_emap[ex + j] = (uint16_t)f;
+            }
+            ex += ld[k];
+        }
+        edges = etot;
+    }
+    lds_barrier();
     int64_t placed = 0, levels = 0;
-    int64_t n = 0;
+    bool first = true, finished = false;
     for (;;) {
-        // expand: the level's edges, flattened (s_par = first edge number of
-        // each level node), each offered its node's position
-        int len[PER];
-        int sum = 0;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int f = tid * PER + k;
-            len[k] = f < nf ? s_len[f] : 0;
-            sum += len[k];
+        // expand: each edge of the level offers its node's position
+        for (int64_t f = tid; f < nf; f += kSmallBlock) {
+            s_gcnt[f] = 0;
+            s_gdeg[f] = 0;
         }
-        int edges = 0;
-        int ex = block_exclusive_scan(sum, s_wave, &edges);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int f = tid * PER + k;
-            if (f < nf) s_par[f] = ex;
-            ex += len[k];
-        }
-        __syncthreads();
+        const bool mapped = edges <= kEdgeMap;
         for (int e0 = 0; e0 < edges; e0 += EB * kSmallBlock) {
-            int vb[EB], fb[EB];
+            int vb[EB], sb[EB], db[EB], fb[EB];
 #pragma unroll
             for (int b = 0; b < EB; ++b) {
                 const int e = e0 + b * kSmallBlock + tid;
                 fb[b] = -1;
+                vb[b] = sb[b] = db[b] = 0;
                 if (e < edges) {
-                    int lo = 0, hi = (int)nf - 1;     // last f with s_par[f] <= e
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (s_par[mid] <= e) lo = mid;
-                        else hi = mid - 1;
+                    int f;
+                    if (mapped) {
+                        f = s_emap[e];
+                    } else {
+                        int lo = 0, hi = (int)nf - 1;     // last f with s_off[f] <= e
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if (s_off[mid] <= e) lo = mid;
+                            else hi = mid - 1;
+                        }
+                        f = lo;
                     }
-                    fb[b] = lo;
-                    vb[b] = scol[s_beg[lo] + (e - s_par[lo])];
+                    const int64_t q = f < nf ? (int64_t)s_beg[f] + (e - s_off[f]) : -1;
+                    if (q >= 0 && q < nsym) {
+                        fb[b] = f;
+                        vb[b] = scol[q];
+                        sb[b] = nsrow[q];
+                        db[b] = ndeg[q];
+                    } else {
+                        s_flag = 2;   // cannot happen: the edge map covers the level
+                    }
                 }
+            }
+            if (first) {
+                // placed nodes hold a parent (component starts -1), others INT_MAX
+                int pb[EB];
+#pragma unroll
+                for (int b = 0; b < EB; ++b) pb[b] = fb[b] >= 0 ? parent[vb[b]] : INT_MAX;
+#pragma unroll
+                for (int b = 0; b < EB; ++b)
+                    if (pb[b] != INT_MAX) fb[b] = -1;
             }
 #pragma unroll
             for (int b = 0; b < EB; ++b) {
-                if (fb[b] < 0) continue;
+                if (e0 + b * kSmallBlock >= edges) break;   // uniform
                 const int v = vb[b];
-                if (atomicMin(&parent[v], (int)(base + fb[b])) == INT_MAX) {
-                    const int slot = atomicAdd(&s_count, 1);
-                    if (slot < kSmallLevel) s_next[slot] = v;
-                    next[slot] = v;
+                bool want = fb[b] >= 0;
+                if (want && !first) want = !hash_has2(s_keys[prv], s_keys[cur], v);
+                int h = -1;
+                bool fresh = false;
+                if (want) {
+                    h = hash_put(s_keys[nxt], v, &fresh);
+                    if (h < 0) s_flag = 1;
                 }
+                // claim numbers, one LDS atomic per wave
+                const unsigned long long m = __ballot(fresh);
+                if (m != 0) {
+                    const int leader = __ffsll((long long)m) - 1;
+                    int c0 = 0;
+                    if (lane == leader) c0 = atomicAdd(&s_count, __popcll(m));
+                    c0 = __builtin_amdgcn_readlane(c0, leader);
+                    if (fresh) {
+                        const int c = c0 + __popcll(m & ((1ull << lane) - 1));
+                        if (c < kSmallLevel) {
+                            s_next[c] = v;
+                            s_slot[c] = h;
+                            s_csrow[c] = sb[b];
+                            s_cdeg[c] = db[b];
+                        }
+                    }
+                }
+                if (h >= 0) atomicMin(&s_hval[h], fb[b]);
             }
         }
-        __syncthreads();
-        n = s_count;
+        lds_barrier();
+        const int n = s_count;
+        const int flag = s_flag;
+        if (flag == 0 && base + nf + n > M) {   // cannot happen: every node is placed once
+            s_flag = 2;
+            break;
+        }
+        if (flag != 0 || n > kSmallLevel) break;   // overflow: the host expands this level
         levels += 1;
-        if (n == 0 || n > kSmallLevel) break;
-        for (int64_t f = tid; f < nf; f += kSmallBlock) s_cnt[f] = 0;
-        __syncthreads();
-        // the claims' final parent, degree and edge range; their place in
-        // their parent's group
-        int cv[PER], cp[PER], cd[PER], cs[PER], cb[PER], ce[PER];
+        if (n == 0) {
+            finished = true;
+            break;
+        }
+        // the claims' parent, degree and edge range; their arrival in their
+        // parent's group, and the group's degree sum
+        int cv[PER], cp[PER], cd[PER], cs[PER], cb[PER], co[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * kSmallBlock;
+            cp[k] = -1;
             if (i < n) {
-                const int v = s_next[i];
-                cv[k] = v;
-                cp[k] = __hip_atomic_load(&parent[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - (int)base;
-                cd[k] = deg[v];
-                cb[k] = srow[v];
-                ce[k] = srow[v + 1];
+                cv[k] = s_next[i];
+                cp[k] = s_hval[s_slot[i]];
+                cd[k] = s_cdeg[i];
+                cb[k] = s_csrow[i];
+                cs[k] = atomicAdd(&s_gcnt[cp[k]], 1);
+                atomicAdd(&s_gdeg[cp[k]], cd[k]);
             }
         }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = tid + k * kSmallBlock;
-            if (i < n) {
-                s_par[i] = cp[k];
-                s_deg[i] = cd[k];
-                cs[k] = atomicAdd(&s_cnt[cp[k]], 1);
-            }
-        }
-        __syncthreads();
+        lds_barrier();
         {
-            // group starts: exclusive prefix of the group sizes s_cnt[0 .. nf)
-            int c[PER];
-            sum = 0;
+            // group starts and first edge numbers: exclusive prefixes over the parents
+            int c[PER], d[PER], csum = 0, dsum = 0;
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const int f = tid * PER + k;
-                c[k] = f < nf ? s_cnt[f] : 0;
-                sum += c[k];
+                c[k] = f < nf ? s_gcnt[f] : 0;
+                d[k] = f < nf ? s_gdeg[f] : 0;
+                csum += c[k];
+                dsum += d[k];
             }
-            int tot = 0;
-            ex = block_exclusive_scan(sum, s_wave, &tot);
+            int exc, exd, ctot, dtot;
+            block_exclusive_scan2(csum, dsum, s_wave, &exc, &exd, &ctot, &dtot);
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const int f = tid * PER + k;
-                if (f < nf) s_cnt[f] = ex;
-                ex += c[k];
+                if (f < nf) {
+                    s_gcnt[f] = exc;
+                    s_gdeg[f] = exd;
+                }
+                exc += c[k];
+                exd += d[k];
             }
+            edges = dtot;   // edges of the new level
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * kSmallBlock;
-            if (i < n) s_grp[s_cnt[cp[k]] + cs[k]] = i;
+            if (i < n) {
+                const int at = s_gcnt[cp[k]] + cs[k];
+                if (at < n) s_grp[at] = i;
+            }
         }
-        __syncthreads();
-        // rank by (degree, id) inside the parent's group
+        lds_barrier();
+        // rank by (degree, id) inside the parent's group; the degrees of the
+        // children ranked before give the first edge number
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * kSmallBlock;
             if (i < n) {
                 const int pi = cp[k], di = cd[k], vi = cv[k];
-                const int g0 = s_cnt[pi];
-                const int g1 = pi + 1 < nf ? s_cnt[pi + 1] : (int)n;
-                int rank = g0;
+                const int g0 = s_gcnt[pi];
+                const int g1 = min(pi + 1 < nf ? s_gcnt[pi + 1] : n, n);
+                int rank = g0, off = s_gdeg[pi];
                 for (int q = g0; q < g1; ++q) {
                     const int j = s_grp[q];
-                    const int dj = s_deg[j];
-                    rank += (dj < di || (dj == di && s_next[j] < vi)) ? 1 : 0;
+                    const int dj = s_cdeg[j];
+                    const bool before = dj < di || (dj == di && s_next[j] < vi);
+                    rank += before ? 1 : 0;
+                    off += before ? dj : 0;
                 }
                 cs[k] = rank;
+                co[k] = off;
             }
         }
-        __syncthreads();
-        // the new level replaces the old one in LDS (no reader of it is left)
+        // the new level replaces the old one in LDS (no reader of it is
+        // left); the claims' set becomes the current level's, the previous
+        // level's set is emptied for the next claims
+        const bool map_next = edges <= kEdgeMap;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * kSmallBlock;
             if (i < n) {
                 const int rank = cs[k];
-                s_beg[rank] = cb[k];
-                s_len[rank] = ce[k] - cb[k];
-                frontier[rank] = cv[k];
+                if (rank < n) {
+                    s_beg[rank] = cb[k];
+                    s_off[rank] = co[k];
+                    if (map_next && co[k] >= 0 && co[k] + cd[k] <= kEdgeMap)
+                        for (int j = 0; j < cd[k]; ++j) s_emap[co[k] + j] = (uint16_t)rank;
+                    frontier[rank] = cv[k];
+                }
                 pos[cv[k]] = (int)(base + nf + rank);
+                parent[cv[k]] = (int)(base + cp[k]);
             }
+        }
+        const int freed = prv;
+        prv = cur;
+        cur = nxt;
+        nxt = freed;
+        for (int i = tid; i < kHashSlots; i += kSmallBlock) {
+            s_keys[nxt][i] = -1;
+            s_hval[i] = INT_MAX;
         }
         if (tid == 0) s_count = 0;
         base += nf;
         nf = n;
         placed += n;
-        __syncthreads();
+        first = false;
+        lds_barrier();
     }
     if (tid == 0) {
         st->base = base;
         st->nf = nf;
         st->placed = placed;
-        st->nn = n;
         st->levels = levels;
-        st->done = n == 0 ? 1 : 0;
+        st->done = s_flag == 2 ? 2 : finished ? 1 : 0;
     }
 }
 
@@ -454,6 +651,14 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
     hipLaunchKernelGGL(sym_col_deg_kernel, dim3((unsigned)grid_for(std::max(nsym, M))), dim3(kBlock), 0, nullptr,
                        ukeys, nsym, M, srow, scol, deg, ids);
     TRY(hipGetLastError());
+    int *nsrow, *ndeg;
+    TRY(sc.get(&nsrow, nsym));
+    TRY(sc.get(&ndeg, nsym));
+    if (nsym > 0) {
+        hipLaunchKernelGGL(nbr_records_kernel, dim3((unsigned)grid_for(nsym)), dim3(kBlock), 0, nullptr, srow, scol,
+                           deg, nsym, nsrow, ndeg);
+        TRY(hipGetLastError());
+    }
     // ---- (degree, id) order: a stable sort by degree of ids in ascending order ----
     {
         size_t tb = 0;
@@ -483,11 +688,9 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
     TRY(hipGetLastError());
     // isolated nodes come first in (degree, id) order: each is its own component
     int64_t n0 = 0;
-    {
-        std::vector<int> hd((size_t)M);
-        TRY(hipMemcpy(hd.data(), degs_sorted, sizeof(int) * M, hipMemcpyDeviceToHost));
-        n0 = std::lower_bound(hd.begin(), hd.end(), 1) - hd.begin();
-    }
+    hipLaunchKernelGGL(count_isolated_kernel, dim3(1), dim3(64), 0, nullptr, degs_sorted, M, d_found);
+    TRY(hipGetLastError());
+    TRY(hipMemcpy(&n0, d_found, sizeof(int64_t), hipMemcpyDeviceToHost));
     if (n0 > 0) {
         hipLaunchKernelGGL(place_isolated_kernel, dim3((unsigned)grid_for(n0)), dim3(kBlock), 0, nullptr, order, n0,
                            pos);
@@ -513,11 +716,11 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
         int64_t base = placed, nf = 1;
         placed += 1;
         while (nf > 0) {
-            int64_t nn = 0;
             if (nf <= kSmallLevel) {
-                // small levels run on the device until the component ends or a level grows
-                hipLaunchKernelGGL(small_levels_kernel, dim3(1), dim3(kSmallBlock), 0, nullptr, srow, scol, deg, pos,
-                                   parent, frontier, next, base, nf, d_state);
+                // small levels run on the device until the component ends or
+                // a level's claims outgrow the workgroup
+                hipLaunchKernelGGL(lds_levels_kernel, dim3(1), dim3(kSmallBlock), 0, nullptr, srow, scol, nsrow, ndeg,
+                                   deg, pos, parent, frontier, M, nsym, base, nf, d_state);
                 TRY(hipGetLastError());
                 BfsState h;
                 TRY(hipMemcpy(&h, d_state, sizeof(BfsState), hipMemcpyDeviceToHost));
@@ -525,19 +728,19 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
                 placed += h.placed;
                 base = h.base;
                 nf = h.nf;
+                if (h.done == 2) return hipErrorUnknown;
                 if (h.done) break;
-                nn = h.nn;
-            } else {
-                TRY(hipMemset(d_nnext, 0, sizeof(int)));
-                hipLaunchKernelGGL(expand_kernel, dim3((unsigned)grid_for(nf, kWaves)), dim3(kBlock), 0, nullptr, srow,
-                                   scol, frontier, nf, base, parent, next, d_nnext);
-                TRY(hipGetLastError());
-                int nn32 = 0;
-                TRY(hipMemcpy(&nn32, d_nnext, sizeof(int), hipMemcpyDeviceToHost));
-                nn = nn32;
-                *levels += 1;
-                if (nn == 0) break;
             }
+            // a level with many claims: expanded by the whole device
+            TRY(hipMemset(d_nnext, 0, sizeof(int)));
+            hipLaunchKernelGGL(expand_kernel, dim3((unsigned)grid_for(nf, kWaves)), dim3(kBlock), 0, nullptr, srow,
+                               scol, frontier, nf, base, parent, next, d_nnext);
+            TRY(hipGetLastError());
+            int nn32 = 0;
+            TRY(hipMemcpy(&nn32, d_nnext, sizeof(int), hipMemcpyDeviceToHost));
+            const int64_t nn = nn32;
+            *levels += 1;
+            if (nn == 0) break;
             // ids ascending, then stably by (parent position - base, degree)
             size_t b1 = sort1, b2 = sort2;
             TRY(hipcub::DeviceRadixSort::SortKeys(stmp, b1, next, frontier, (int)nn, 0, bits_for((uint64_t)M)));

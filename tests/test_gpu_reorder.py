@@ -65,7 +65,48 @@ def test_reorder_golden(orc):
     G.spmm_plan_destroy(plan)
 
 
+def _alternating_levels(seed):
+    """Breadth-first levels that alternate between a few nodes and thousands:
+    short chains joined through wide layers (5,000 then 3,000 nodes, each
+    wide node linked to both chain ends around it), one direction per entry,
+    under random ids, so that the level kernel hands wide levels to the
+    multi-block path and takes the chains back up after them."""
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    nid = 0
+
+    def new(n):
+        nonlocal nid
+        ids = np.arange(nid, nid + n)
+        nid += n
+        return ids
+
+    def link(a, b):
+        rows.append(np.asarray(a).ravel())
+        cols.append(np.asarray(b).ravel())
+
+    chain = new(3)
+    link(chain[:-1], chain[1:])
+    for width in (5000, 3000, 1500):
+        wide = new(width)
+        nxt = new(3)
+        link(np.full(width, chain[-1]), wide)
+        link(wide, np.full(width, nxt[0]))
+        # a few links inside the wide layer
+        a = rng.choice(wide, 200)
+        link(a, rng.choice(wide, 200))
+        link(nxt[:-1], nxt[1:])
+        chain = nxt
+    M = nid
+    r, c = np.concatenate(rows), np.concatenate(cols)
+    keep = r != c
+    rowptr, col, _ = W.csr_from_pairs(M, r[keep], c[keep])
+    g = W.Graph("alternating", M, M, rowptr, col, None)
+    return W.relabel(g, seed)
+
+
 CASES = [
+    ("alternating-levels", lambda: _alternating_levels(75)),
     ("irregular", lambda: W.random_csr(np.random.default_rng(70), 3000, 3000, mean_deg=2.5, empty_frac=0.2,
                                        dup_frac=0.2, shuffle_rows=True)),
     ("road-relabelled", lambda: W.relabel(W.make_graph("road", M=60_000), 71)),
