@@ -638,10 +638,14 @@ def reorder_result(steps, flush):
     C = torch.empty((g.M, N), dtype=torch.float32, device=dev)
     plan = G.spmm_plan_create(rp, cl, None, g.M, g.K)
     t_before = time_flushed(lambda: G.spmm_run(plan, B, C, None, N, "sum", None), flush, steps)
-    t0 = time.perf_counter()
-    perm = G.spmm_plan_reorder(plan)
-    torch.cuda.synchronize()
-    t_rcm = (time.perf_counter() - t0) * 1e3
+    # the first call in a process also loads the reordering kernels and the
+    # library sorts; a second call on the same graph shows the steady cost
+    t_rcm = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        perm = G.spmm_plan_reorder(plan)
+        torch.cuda.synchronize()
+        t_rcm.append((time.perf_counter() - t0) * 1e3)
     t0 = time.perf_counter()
     pp = G.spmm_plan_permute(plan, perm)
     t_perm = (time.perf_counter() - t0) * 1e3
@@ -649,11 +653,13 @@ def reorder_result(steps, flush):
     t_after = time_flushed(lambda: G.spmm_run(pp, Bp, C, None, N, "sum", None), flush, steps)
     G.spmm_plan_destroy(pp)
     G.spmm_plan_destroy(plan)
-    once = t_rcm + t_perm
+    gain = t_before - t_after
     return {"workload": "road-like graph under random node ids (M=K=1,000,000, N=64, sum)",
             "ms_before": round(t_before, 5), "ms_after": round(t_after, 5),
-            "speedup": round(t_before / t_after, 3), "rcm_ms": round(t_rcm, 1), "permute_ms": round(t_perm, 1),
-            "break_even_runs": round(once / (t_before - t_after)) if t_before > t_after else None}
+            "speedup": round(t_before / t_after, 3), "rcm_first_call_ms": round(t_rcm[0], 1),
+            "rcm_ms": round(t_rcm[1], 1), "permute_ms": round(t_perm, 1),
+            "break_even_runs": round((t_rcm[1] + t_perm) / gain) if gain > 0 else None,
+            "break_even_runs_first_call": round((t_rcm[0] + t_perm) / gain) if gain > 0 else None}
 
 
 def router_sweep(r, reduce, steps, flush):

@@ -6,7 +6,8 @@ profiles/ (each summary records the command that produced its input).
   python bench_report.py trace    KERNEL_STATS_CSV [--cmd CMD] [--top N]
   python bench_report.py traffic  --fetch CSV --write CSV --kernel SUBSTR --algorithmic BYTES
                                   --workload TEXT --source-sha SHA [--cmd CMD ...]
-  python bench_report.py counters COUNTER_CSV --kernel SUBSTR [--cmd CMD ...]
+  python bench_report.py counters COUNTER_CSV [COUNTER_CSV ...] --kernel SUBSTR [--title T] [--workload W]
+                                  [--source-sha SHA] [--cmd CMD ...]
 
 ROUTER_JSON / CEILINGS_JSON are the JSON lines printed by `bench.py
 --router-sweep` and `bench.py --ceilings`; the CSVs are rocprofv3's
@@ -181,28 +182,74 @@ def traffic(args):
 
 
 def counters(args):
-    rows = _rows(args.file)
-    vals = defaultdict(lambda: defaultdict(float))
-    names = {}
-    for r in rows:
-        kn = _col(r, "Kernel_Name")
-        if not any(s in kn for s in args.kernel):
-            continue
-        key = _col(r, "Dispatch_Id", "Correlation_Id")
-        vals[key][_col(r, "Counter_Name")] += float(_col(r, "Counter_Value"))
-        names[key] = kn
-    by_kernel = defaultdict(list)
-    for key, cv in vals.items():
-        by_kernel[names[key]].append(cv)
-    out = ["# Hardware counters", ""]
+    # per file: mean per dispatch of each counter, per kernel; passes of the
+    # same kernel (one file each) are merged by kernel name
+    merged = defaultdict(lambda: defaultdict(list))
+    ndisp = defaultdict(int)
+    for path in args.file:
+        vals = defaultdict(lambda: defaultdict(float))
+        names = {}
+        for r in _rows(path):
+            kn = _col(r, "Kernel_Name")
+            if not any(sub in kn for sub in args.kernel):
+                continue
+            key = _col(r, "Dispatch_Id", "Correlation_Id")
+            vals[key][_col(r, "Counter_Name")] += float(_col(r, "Counter_Value"))
+            names[key] = kn
+        by_kernel = defaultdict(list)
+        for key, cv in vals.items():
+            by_kernel[names[key]].append(cv)
+        for kn, ds in by_kernel.items():
+            ndisp[kn] = max(ndisp[kn], len(ds))
+            for c in ds[0]:
+                merged[kn][c].append(statistics.mean(d.get(c, 0.0) for d in ds))
+    out = [f"# Hardware counters{': ' + args.title if args.title else ''}", ""]
+    if args.workload:
+        out += [f"Workload: {args.workload}", ""]
     if args.cmd:
-        out += ["Command:", "", "```", *args.cmd, "```", ""]
-    for kn, ds in by_kernel.items():
-        out += [f"`{kn[:120]}`: {len(ds)} dispatches, mean per dispatch:", "", "| counter | value |", "|---|---|"]
-        for c in sorted(ds[0]):
-            out.append(f"| {c} | {statistics.mean(d.get(c, 0.0) for d in ds):.6g} |")
+        out += ["Commands (from /tmp, repository at `$R`):", "", "```", *args.cmd, "```", ""]
+    for kn, cs in merged.items():
+        mean = {c: statistics.mean(v) for c, v in sorted(cs.items())}
+        out += [f"`{kn[:120]}`: {ndisp[kn]} dispatches per pass, mean per dispatch:", "", "| counter | value |",
+                "|---|---|"]
+        for c, v in mean.items():
+            out.append(f"| {c} | {v:.6g} |")
         out.append("")
+        der = derived(mean)
+        if der:
+            out += ["Derived (256 CUs with one TA and one TD each, 1024 SIMDs; GRBM_GUI_ACTIVE is summed over "
+                    "the 8 XCDs):", ""]
+            out += [f"- {k}: {v}" for k, v in der]
+            out.append("")
+    if args.source_sha:
+        out.append(f"kernel_source_sha: {args.source_sha}")
     print("\n".join(out))
+
+
+def derived(m):
+    """Shares and ratios from the raw counter means that are present."""
+    d = []
+    gui = m.get("GRBM_GUI_ACTIVE")
+    per_xcd = gui / 8 if gui else None
+    if per_xcd:
+        for c, name in (("TA_TA_BUSY_sum", "TA busy share per CU"), ("TD_TD_BUSY_sum", "TD busy share per CU")):
+            if c in m:
+                d.append((name, f"{100 * m[c] / 256 / per_xcd:.1f} %"))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            d.append(("MFMA busy share per SIMD", f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (per_xcd * 1024):.2f} %"))
+        if "SQ_INSTS_VALU" in m:
+            d.append(("VALU issue share per SIMD (4 cycles per wave64 instruction)",
+                      f"{100 * 4 * m['SQ_INSTS_VALU'] / (per_xcd * 1024):.1f} %"))
+    if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and m["TCC_HIT_sum"] + m["TCC_MISS_sum"] > 0:
+        d.append(("L2 hit rate", f"{100 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f} %"))
+    if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m and m["SQ_LDS_IDX_ACTIVE"] > m["SQ_LDS_BANK_CONFLICT"]:
+        d.append(("LDS bank conflict ratio (conflict cycles / conflict-free active cycles)",
+                  f"{m['SQ_LDS_BANK_CONFLICT'] / (m['SQ_LDS_IDX_ACTIVE'] - m['SQ_LDS_BANK_CONFLICT']):.3f}"))
+    if "SQ_WAIT_INST_ANY" in m and m.get("SQ_WAVE_CYCLES"):
+        d.append(("share of wave time waiting on memory", f"{100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %"))
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
+        d.append(("MFMA work per dispatch", f"{m['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / 1e9:.1f} GFLOP"))
+    return d
 
 
 def main():
@@ -210,12 +257,15 @@ def main():
     sub = ap.add_subparsers(dest="what", required=True)
     for name in ("router", "ceilings", "trace", "counters"):
         p = sub.add_parser(name)
-        p.add_argument("file")
+        p.add_argument("file", nargs="+" if name == "counters" else None)
         p.add_argument("--cmd", action="append", default=[])
         if name == "trace":
             p.add_argument("--top", type=int, default=30)
         if name == "counters":
             p.add_argument("--kernel", action="append", required=True)
+            p.add_argument("--title", default="")
+            p.add_argument("--workload", default="")
+            p.add_argument("--source-sha", default="")
     p = sub.add_parser("traffic")
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)

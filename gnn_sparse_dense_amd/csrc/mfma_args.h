@@ -7,7 +7,7 @@
 namespace gspmm {
 
 constexpr int kMfmaKSteps = kWinRows / 16;   // k-steps of 16 per 256-wide community tile
-constexpr int kMfmaBtPitch = kWinRows;       // fp16 per staged B^T row (16-byte chunks XOR-swizzled)
+constexpr int kMfmaBtPitch = kWinRows + 8;   // fp16 per staged B^T row of fp16 tiles (16-byte skew per row)
 
 // Tile t covers rows and columns [t*kWinRows, (t+1)*kWinRows).  Its dense
 // fp16 values are stored in the operand order of v_mfma_f32_32x32x16_f16: for

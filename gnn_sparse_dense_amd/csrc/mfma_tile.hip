@@ -236,14 +236,20 @@ __device__ __forceinline__ void residual_rows(const MfmaArgs &a, int64_t task0, 
     }
 }
 
-// Half offset of 16-byte chunk j (8 k values) of B^T column c in LDS.  The
-// chunk index is XOR-swizzled by h(c) = (c ^ c >> 2) & 15, so that both
-// accesses spread over all 64 banks: the MFMA operand read (16 consecutive
-// columns per 256-byte pass, one chunk each: t -> t ^ t >> 2 is invertible
-// on 4 bits, so h takes 16 values) and the transposing store (16 column quads
-// q of one k range, 8-byte halves of two chunks: c = 4q + e gives
-// h = q ^ ((q & 3) << 2) ^ e, again 16 values).
-__device__ __forceinline__ int bt_off(int c, int j) { return c * kMfmaBtPitch + 8 * (j ^ ((c ^ (c >> 2)) & 15)); }
+// B^T in LDS, two layouts.  Split tiles (three products per k-step: the
+// operand reads bind) store 16-byte chunk j (8 k values) of column c at half
+// bt_off(c, j): rows of kWinRows halves, chunk index XOR-swizzled by
+// h(c) = (c ^ c >> 2) & 15, so that both accesses spread over all 64 banks:
+// the MFMA operand read (16 consecutive columns per 256-byte pass, one chunk
+// each: t -> t ^ t >> 2 is invertible on 4 bits, so h takes 16 values) and
+// the transposing store (16 column quads q of one k range, 8-byte halves of
+// two chunks: c = 4q + e gives h = q ^ ((q & 3) << 2) ^ e, again 16 values).
+// fp16 tiles (one product per k-step: the staging of B binds) keep rows of
+// kMfmaBtPitch = kWinRows + 8 halves (a 16-byte skew per row), written by
+// the staging map that reads 256 contiguous bytes of a B row per 16 lanes.
+// Measured on the community graph (N = 512, flushed): the swizzle takes split
+// tiles from 1.121 to 1.044 ms; on fp16 tiles it cost 0.858 -> 0.966 ms.
+__device__ __forceinline__ int bt_off(int c, int j) { return c * kWinRows + 8 * (j ^ ((c ^ (c >> 2)) & 15)); }
 
 // LDS of one workgroup: B^T (fp16; high and low halves for split tiles) while
 // the products run, then the fp32 C tile and the residual walk's staging.
@@ -292,11 +298,13 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)
     int bexp = 0;
     {
         // thread (q, o): rows 4o .. 4o+3 of column quad q, stored as 4 columns of B^T.
-        // Lanes 0-7 take quads 0-7 of an even o, lanes 8-15 the same quads of
-        // o + 1: each 16-lane group then stores two whole chunks per column
-        // quad (bank-conflict free with bt_off), and every 16 lanes of one o
-        // still read one contiguous 256-byte stretch of a B row.
-        const int q = (tid & 7) | (((tid >> 4) & 1) << 3), o = ((tid >> 3) & 1) | ((tid >> 5) << 1);
+        // Split tiles: lanes 0-7 take quads 0-7 of an even o, lanes 8-15 the
+        // same quads of o + 1, so that each 16-lane group stores two whole
+        // chunks per column quad (bank-conflict free with the swizzle); every
+        // 16 lanes of one o still read one contiguous 256-byte stretch of a
+        // B row.  fp16 tiles: lanes 0-15 take quads 0-15 of one o.
+        const int q = SPLIT ? (tid & 7) | (((tid >> 4) & 1) << 3) : tid & 15;
+        const int o = SPLIT ? ((tid >> 3) & 1) | ((tid >> 5) << 1) : tid >> 4;
         const int64_t cc = c0 + 4 * q;
         f32x4 v[4];
 #pragma unroll
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)
                 *reinterpret_cast<f16x4 *>(sbt_lo + bt_off(4 * q + e, o >> 1) + 4 * (o & 1)) = l;
             } else {
                 const f16x4 h = {(_Float16)v[0][e], (_Float16)v[1][e], (_Float16)v[2][e], (_Float16)v[3][e]};
-                *reinterpret_cast<f16x4 *>(sbt + bt_off(4 * q + e, o >> 1) + 4 * (o & 1)) = h;
+                *reinterpret_cast<f16x4 *>(sbt + (4 * q + e) * kMfmaBtPitch + 4 * o) = h;
             }
         }
     }
@@ -344,12 +352,14 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(8, 8)
 
     f32x16 acc = {};
     const int bcol = cg * 32 + (lane & 31);
+    const int boff = bcol * kMfmaBtPitch + 8 * (lane >> 5);   // fp16 tiles
 #pragma unroll
     for (int ks = 0; ks < kMfmaKSteps; ++ks) {
         const uint4 au = ar[ks % AH];
         if (ks + AH < kMfmaKSteps) ar[ks % AH] = ap[(ks + AH) * 64];
         const f16x8 av = __builtin_bit_cast(f16x8, au);
-        const f16x8 bv = *reinterpret_cast<const f16x8 *>(sbt + bt_off(bcol, 2 * ks + (lane >> 5)));
+        const f16x8 bv = *reinterpret_cast<const f16x8 *>(
+            sbt + (SPLIT ? bt_off(bcol, 2 * ks + (lane >> 5)) : boff + ks * 16));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
         if constexpr (SPLIT) {
             const uint4 aul = arl[ks % AH];
