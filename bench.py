@@ -192,6 +192,19 @@ class Runner:
         self.G.spmm_plan_destroy(self.plan)
 
 
+def library_load_ms() -> float:
+    import torch
+    import gnn_sparse_dense_amd as G
+    dev = torch.device("cuda:0")
+    rp = torch.tensor([0, 1, 2], dtype=torch.int64, device=dev)
+    cl = torch.tensor([1, 0], dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    G.spmm_plan_destroy(G.spmm_plan_create(rp, cl, None, 2, 2))
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
+
+
 def make_flush():
     import torch
     buf = torch.ones(512 * 1024 * 1024 // 4 * 2, dtype=torch.float32, device="cuda:0")   # 1 GiB
@@ -747,14 +760,22 @@ def backward_result(r, flush, steps):
     import torch
     G, g, N = r.G, r.g, r.w.N
     dev = r.C.device
-    t0 = time.perf_counter()
-    pt = G.spmm_plan_transpose(r.plan, 0)
-    t_plan = (time.perf_counter() - t0) * 1e3
+    # the process's first transpose also sets up the library sorts it uses:
+    # the second build of the same transpose is the per-graph cost
+    t_plans = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        pt = G.spmm_plan_transpose(r.plan, 0)
+        t_plans.append((time.perf_counter() - t0) * 1e3)
+        if len(t_plans) == 1:
+            G.spmm_plan_destroy(pt)
+    t_plan = t_plans[1]
     dC = torch.randn((g.M, N), dtype=torch.float32, device=dev)
     dB = torch.empty((g.K, N), dtype=torch.float32, device=dev)
     ms = time_flushed(lambda: G.spmm_run(pt, dC, dB, None, N, "sum", None), flush, steps)
     comp_t = (g.K + 1) * 4 + g.nnz * (4 + (4 if g.val is not None else 0)) + g.M * N * 4 + g.K * N * 4
-    out = {"transpose_plan_ms": round(t_plan, 2), "sum_backward_ms": round(ms, 5),
+    out = {"transpose_plan_ms": round(t_plan, 2), "transpose_plan_first_ms": round(t_plans[0], 2),
+           "sum_backward_ms": round(ms, 5),
            "sum_backward_GBps": round(comp_t / (ms * 1e-3) / 1e9, 1)}
     if "max" in r.w.reduces and g.val is None:
         arg = torch.empty((g.M, N), dtype=torch.int64, device=dev)
@@ -841,6 +862,10 @@ def main():
                           "router_speed_vs_best_min": min(ratios)}), flush=True)
         return
 
+    # the process's first library call loads the library's code object onto
+    # the GPU (about 13 ms); a throwaway plan on a 2-node graph pays it here,
+    # so that each graph's plan creation below is its own cost
+    load_ms = library_load_ms()
     headline = args.workload
     r = Runner(headline)
     reduce = args.reduce or r.w.reduces[0]
@@ -977,7 +1002,7 @@ def main():
             result["parity_detail"]["regimes"] = checks
             if any(v != "ok" for v in checks.values()):
                 result["parity"] = "FAIL"
-        result["reuse"] = reuse
+        result["reuse"] = dict(reuse, library_load_ms=round(load_ms, 2))
         result["vblock"] = vblock_result(min(args.steps, 50), flush)
         result["reorder"] = reorder_result(min(args.steps, 50), flush)
         if backward:
