@@ -54,15 +54,16 @@ def router(args):
     geo = math.exp(sum(math.log(q) for q in ratios) / len(ratios))
     out += ["", f"Geometric mean of router / best over {len(ratios)} configurations: **{geo:.4f}**; "
             f"minimum **{min(ratios):.4f}**.", ""]
+    out += [f"Per configuration: the router's pick and the {args.top} fastest other variants "
+            "(the JSON line holds all of them).", ""]
     for cfg, entries in ev.items():
         for e in entries:
             out += [f"## {cfg}, {e['reduce']}", "", "| variant | ms | path | route (lanes, vec, F, slices, xcd, nt, "
                     "split, tiles, window) |", "|---|---|---|---|"]
-            for v in e["variants"]:
-                if "ms" in v:
-                    out.append(f"| {v['variant']} | {v['ms']:.4f} | {v['path']} | {v['route']} |")
-                else:
-                    out.append(f"| {v['variant']} | - | unsupported | {v.get('unsupported', '')[:80]} |")
+            timed = [v for v in e["variants"] if "ms" in v]
+            rest = sorted((v for v in timed if v["variant"] != "router"), key=lambda v: v["ms"])[:args.top]
+            for v in [x for x in timed if x["variant"] == "router"] + rest:
+                out.append(f"| {v['variant']} | {v['ms']:.4f} | {v['path']} | {v['route']} |")
             out.append("")
     print("\n".join(out))
 
@@ -261,6 +262,8 @@ def main():
         p.add_argument("--cmd", action="append", default=[])
         if name == "trace":
             p.add_argument("--top", type=int, default=30)
+        if name == "router":
+            p.add_argument("--top", type=int, default=3)
         if name == "counters":
             p.add_argument("--kernel", action="append", required=True)
             p.add_argument("--title", default="")
