@@ -95,7 +95,7 @@ def test_ragged_widths(orc, N):
     G.spmm_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("route", ["rows", "tiles", "split", "window"])
+@pytest.mark.parametrize("route", ["rows", "tiles", "split", "split_fused", "window"])
 def test_max_with_infinite_products(orc, route):
     """Finite inputs whose products overflow to -inf: weights 1e30 times B
     entries of -1e30 in half of B's columns.  Some rows hold only such
@@ -105,7 +105,8 @@ def test_max_with_infinite_products(orc, route):
     an all -inf output its first entry: the oracle's stored-order rule."""
     rng = np.random.default_rng(71)
     g = W.random_csr(rng, 3000, 2048, mean_deg=9.0, empty_frac=0.05, dup_frac=0.1,
-                     shuffle_rows=route != "window", weighted=True, heavy_rows=6 if route == "split" else 0,
+                     shuffle_rows=route != "window", weighted=True,
+                     heavy_rows=6 if route.startswith("split") else 0,
                      heavy_deg=700)
     deg = g.degrees()
     all_inf = rng.choice(np.flatnonzero(deg > 0), size=300, replace=False)
@@ -115,11 +116,14 @@ def test_max_with_infinite_products(orc, route):
         g.val[g.rowptr[i]:g.rowptr[i + 1]] = 1e30
     for i in lead_inf:
         g.val[g.rowptr[i]:g.rowptr[i] + 2] = 1e30
-    N = 128 if route == "window" else 24
+    N = {"window": 128, "split_fused": 64}.get(route, 24)
     B = rng.standard_normal((g.K, N)).astype(np.float32)
     B[:, ::2] = -1e30
     opts = {"rows": [(G.SPMM_OPT_TILES, 0)], "tiles": [(G.SPMM_OPT_TILES, 1)],
             "split": [(G.SPMM_OPT_SPLIT_T, 64), (G.SPMM_OPT_SPLIT_L, 50), (G.SPMM_OPT_SPLIT_MODE, 1)],
+            "split_fused": [(G.SPMM_OPT_SPLIT_T, 64), (G.SPMM_OPT_SPLIT_L, 50), (G.SPMM_OPT_SPLIT_MODE, 1),
+                            (G.SPMM_OPT_TILES, 0), (G.SPMM_OPT_LANES, 16), (G.SPMM_OPT_VEC, 4),
+                            (G.SPMM_OPT_COARSEN, 1)],
             "window": [(G.SPMM_OPT_WINDOW, 1)]}[route]
     plan = make_plan(g, opts)
     _, _, _, Bd = to_dev(g, B)
@@ -127,6 +131,7 @@ def test_max_with_infinite_products(orc, route):
     info = G.spmm_plan_info(plan)
     routed = {"rows": info["route_tiled"] == 0 and info["route_window"] == 0,
               "tiles": info["route_tiled"] == 1, "split": info["n_heavy"] > 0,
+              "split_fused": info["n_heavy"] > 0 and info["route_fused_split"] == 1,
               "window": info["route_window"] > 0}[route]
     assert routed, f"{route} not taken: {info}"
     assert np.isneginf(C[all_inf][:, ::2]).all()
