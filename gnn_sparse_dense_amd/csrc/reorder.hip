@@ -582,13 +582,34 @@ int bits_for(uint64_t vmax) {
     return b;
 }
 
-// Device scratch freed on scope exit.
+// Device scratch freed on scope exit.  With reserve(), the buffers are
+// slices of one allocation (an allocation and a free per call instead of
+// one per buffer: device frees cost about 0.2 ms each); a request beyond the
+// reserve gets its own allocation.
 struct Scratch {
     std::vector<void *> ptrs;
+    char *pool = nullptr;
+    size_t used = 0, cap = 0;
+    static size_t round_up(size_t b) { return (b + 255) & ~size_t(255); }
+    hipError_t reserve(size_t bytes) {
+        void *q = nullptr;
+        const hipError_t e = dmalloc(&q, std::max<size_t>(bytes, 1), "reordering scratch");
+        if (e != hipSuccess) return e;
+        ptrs.push_back(q);
+        pool = static_cast<char *>(q);
+        cap = bytes;
+        return hipSuccess;
+    }
     template <typename T>
     hipError_t get(T **p, size_t count) {
+        const size_t b = round_up(std::max<size_t>(count, 1) * sizeof(T));
+        if (pool && used + b <= cap) {
+            *p = reinterpret_cast<T *>(pool + used);
+            used += b;
+            return hipSuccess;
+        }
         *p = nullptr;
-        hipError_t e = dmalloc(reinterpret_cast<void **>(p), std::max<size_t>(count, 1) * sizeof(T), "reordering scratch");
+        hipError_t e = dmalloc(reinterpret_cast<void **>(p), b, "reordering scratch");
         if (e == hipSuccess) ptrs.push_back(*p);
         return e;
     }
@@ -611,6 +632,28 @@ hipError_t rcm_order(const int *rowptr, const int *col, int64_t M, int64_t nnz, 
     Scratch sc;
     // ---- symmetric pattern ----
     const int64_t nk = 2 * nnz;
+    {
+        // one reserve for every buffer below, sized from upper bounds (the
+        // symmetric pattern has at most nk entries; sort storage for the
+        // widest keys)
+        size_t tb_keys = 0, tb_unique = 0, tb_deg = 0, tb_ids = 0, tb_level = 0;
+        hipcub::DoubleBuffer<uint64_t> nb(nullptr, nullptr);
+        TRY(hipcub::DeviceRadixSort::SortKeys(nullptr, tb_keys, nb, (int)nk, 0, 64));
+        TRY(hipcub::DeviceSelect::Unique(nullptr, tb_unique, (uint64_t *)nullptr, (uint64_t *)nullptr,
+                                         (int64_t *)nullptr, (int)nk));
+        TRY(hipcub::DeviceRadixSort::SortPairs(nullptr, tb_deg, (int *)nullptr, (int *)nullptr, (int *)nullptr,
+                                               (int *)nullptr, (int)M, 0, 32));
+        TRY(hipcub::DeviceRadixSort::SortKeys(nullptr, tb_ids, (int *)nullptr, (int *)nullptr, (int)M, 0,
+                                              bits_for((uint64_t)M)));
+        TRY(hipcub::DeviceRadixSort::SortPairs(nullptr, tb_level, (uint64_t *)nullptr, (uint64_t *)nullptr,
+                                               (int *)nullptr, (int *)nullptr, (int)M, 0, 64));
+        const size_t n1 = (size_t)std::max<int64_t>(nk, 1), m1 = (size_t)M + 1;
+        auto r = Scratch::round_up;
+        const size_t total = 3 * r(n1 * 8) + r(8) + r(tb_keys) + r(tb_unique) + r(m1 * 4) + 3 * r(n1 * 4) +
+                             9 * r((size_t)M * 4) + r(tb_deg) + 2 * r(4) + 2 * r((size_t)M * 8) + r(8) +
+                             r(std::max(tb_ids, tb_level)) + r(sizeof(BfsState)) + 4 * 256;
+        TRY(sc.reserve(total));
+    }
     uint64_t *ka, *kb, *ukeys;
     int64_t *d_count;
     TRY(sc.get(&ka, nk));
@@ -820,6 +863,21 @@ hipError_t permute_csr(const int *rowptr, const int *col, const float *val, int6
                        const int64_t *perm, int64_t *rowptr_p, int64_t *col_p, float *val_p, bool *bad_perm) {
     *bad_perm = false;
     Scratch sc;
+    {
+        // one reserve for the buffers below (sort storage for the widest keys)
+        size_t tb_scan = 0, tb_sort = 0;
+        TRY(hipcub::DeviceScan::ExclusiveSum(nullptr, tb_scan, (int64_t *)nullptr, (int64_t *)nullptr,
+                                             (int)(M + 1)));
+        if (nnz > 0) {
+            hipcub::DoubleBuffer<uint64_t> nk(nullptr, nullptr);
+            hipcub::DoubleBuffer<int> ni(nullptr, nullptr);
+            TRY(hipcub::DeviceRadixSort::SortPairs(nullptr, tb_sort, nk, ni, (int)nnz, 0, 64));
+        }
+        auto r = Scratch::round_up;
+        const size_t n1 = (size_t)std::max<int64_t>(nnz, 1);
+        TRY(sc.reserve(r((size_t)M * 4) + r(4) + r(((size_t)M + 1) * 8) + r(tb_scan) + 2 * r(n1 * 8) +
+                       2 * r(n1 * 4) + r(tb_sort) + 2 * 256));
+    }
     int *inv, *d_bad;
     TRY(sc.get(&inv, M));
     TRY(sc.get(&d_bad, 1));
