@@ -153,13 +153,26 @@ hipError_t stable_sort(const int *keys, const int *idx, int *skeys, int *perm, i
     return e != hipSuccess ? e : e2;
 }
 
-// Device buffers of a transpose, freed on scope exit.
-struct Scratch {
-    int *keys = nullptr, *idx = nullptr, *skeys = nullptr, *perm = nullptr, *rowid = nullptr;
-    void *sort = nullptr;
-    ~Scratch() {
-        for (void *q : {(void *)keys, (void *)idx, (void *)skeys, (void *)perm, (void *)rowid, sort}) dfree(q);
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Scratch of one call as slices of a single allocation (one allocation and
+// one free per call instead of one per buffer), freed on scope exit.
+struct Pool {
+    unsigned char *base = nullptr;
+    size_t off = 0;
+    hipError_t alloc(size_t bytes, const char *what) {
+        void *q = nullptr;
+        const hipError_t e = dmalloc(&q, std::max<size_t>(bytes, 1), what);
+        base = static_cast<unsigned char *>(q);
+        return e;
     }
+    template <typename T>
+    T *take(size_t count) {
+        T *p = reinterpret_cast<T *>(base + off);
+        off += align256(sizeof(T) * std::max<size_t>(count, 1));
+        return p;
+    }
+    ~Pool() { dfree(base); }
 };
 
 }  // namespace
@@ -212,8 +225,6 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu[kMaxDevices];     // one call at a time per device
 unsigned char *g_scratch_ptr[kMaxDevices] = {};
-
-size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -272,30 +283,46 @@ hipError_t coo_to_csr(const int64_t *row, const int64_t *col, const float *val, 
     std::vector<int64_t> bad_host((size_t)std::max<int64_t>(nb, 1));
     w.bad_host = bad_host.data();
     hipError_t e = E > 0 ? coo_sort_storage_bytes(E, M, &w.sort_bytes) : hipSuccess;
-    if (e == hipSuccess) e = dmalloc_n(&w.keys, E, "edge keys");
-    if (e == hipSuccess) e = dmalloc_n(&w.idx, E, "edge positions");
-    if (e == hipSuccess) e = dmalloc_n(&w.skeys, E, "sorted edge keys");
-    if (e == hipSuccess) e = dmalloc_n(&w.perm, E, "sorted edge positions");
-    if (e == hipSuccess) e = dmalloc_n(&w.bad, nb, "edge range records");
-    if (e == hipSuccess) e = dmalloc(&w.sort, std::max<size_t>(w.sort_bytes, 1), "edge sort storage");
-    if (e == hipSuccess)
-        e = coo_to_csr_in(row, col, val, E, M, K, rowptr_out, col_out, val_out, first_bad, w, s);
-    for (void *q : {(void *)w.keys, (void *)w.idx, (void *)w.skeys, (void *)w.perm, (void *)w.bad, w.sort}) dfree(q);
-    return e;
+    if (e != hipSuccess) return e;
+    // edge keys, positions, sorted keys and positions (int32 [E] each), range
+    // records, sort storage
+    const size_t arr = align256(sizeof(int) * (size_t)std::max<int64_t>(E, 1));
+    Pool pool;
+    e = pool.alloc(4 * arr + align256(sizeof(int64_t) * (size_t)std::max<int64_t>(nb, 1)) +
+                       align256(std::max<size_t>(w.sort_bytes, 1)),
+                   "edge-list sort scratch");
+    if (e != hipSuccess) return e;
+    w.keys = pool.take<int>(E);
+    w.idx = pool.take<int>(E);
+    w.skeys = pool.take<int>(E);
+    w.perm = pool.take<int>(E);
+    w.bad = pool.take<int64_t>(nb);
+    w.sort = pool.take<unsigned char>(w.sort_bytes);
+    return coo_to_csr_in(row, col, val, E, M, K, rowptr_out, col_out, val_out, first_bad, w, s);
 }
 
 hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, int64_t M, int64_t K, int64_t nnz,
                          bool scale, int64_t *rowptr_t, int64_t *col_t, float *val_t, hipStream_t s) {
-    Scratch t;
     size_t sort_bytes = 0;
     hipError_t e = nnz > 0 ? sort_storage_bytes(nnz, K, &sort_bytes) : hipSuccess;
-    if (e == hipSuccess) e = dmalloc_n(&t.keys, nnz, "transpose keys");
-    if (e == hipSuccess) e = dmalloc_n(&t.idx, nnz, "transpose positions");
-    if (e == hipSuccess) e = dmalloc_n(&t.skeys, nnz, "sorted transpose keys");
-    if (e == hipSuccess) e = dmalloc_n(&t.perm, nnz, "sorted transpose positions");
-    if (e == hipSuccess) e = dmalloc_n(&t.rowid, nnz, "transpose row ids");
-    if (e == hipSuccess) e = dmalloc(&t.sort, std::max<size_t>(sort_bytes, 1), "transpose sort storage");
     if (e != hipSuccess) return e;
+    // keys, positions, sorted keys and positions, row ids (int32 [nnz] each),
+    // sort storage
+    Pool pool;
+    e = pool.alloc(5 * align256(sizeof(int) * (size_t)std::max<int64_t>(nnz, 1)) +
+                       align256(std::max<size_t>(sort_bytes, 1)),
+                   "transpose scratch");
+    if (e != hipSuccess) return e;
+    struct {
+        int *keys, *idx, *skeys, *perm, *rowid;
+        void *sort;
+    } t;
+    t.keys = pool.take<int>(nnz);
+    t.idx = pool.take<int>(nnz);
+    t.skeys = pool.take<int>(nnz);
+    t.perm = pool.take<int>(nnz);
+    t.rowid = pool.take<int>(nnz);
+    t.sort = pool.take<unsigned char>(sort_bytes);
     if (nnz > 0) {
         hipLaunchKernelGGL(transpose_prepare_kernel, dim3((unsigned)((M + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
                            rowptr, col, M, t.keys, t.idx, t.rowid);
