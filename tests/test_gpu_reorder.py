@@ -186,3 +186,34 @@ def test_sparse_adj_reordered_roundtrip(orc):
     assert f["mean_bandwidth"] < adj.features(2)["mean_bandwidth"] / 10
     radj.close()
     adj.close()
+
+
+def _random_square(rng):
+    """A random square graph of one of several structures, under random ids
+    or not: irregular CSR (components, duplicates, self loops, empty rows),
+    communities, a band, a kNN line, or chains joined through wide layers."""
+    kind = int(rng.integers(5))
+    if kind == 0:
+        M = int(rng.integers(1, 6000))
+        g = W.random_csr(rng, M, M, mean_deg=float(rng.uniform(0.3, 12.0)), empty_frac=float(rng.uniform(0, 0.4)),
+                         dup_frac=float(rng.uniform(0, 0.3)), shuffle_rows=bool(rng.random() < 0.5))
+    elif kind == 1:
+        g = W.make_graph("community", M=int(rng.integers(256, 6000)))
+    elif kind == 2:
+        g = W.make_graph("road", M=int(rng.integers(600, 30_000)))
+    elif kind == 3:
+        g = W.knn_line(int(rng.integers(20, 20_000)), int(rng.integers(1, 12)))
+    else:
+        return _alternating_levels(int(rng.integers(1 << 30)))
+    return W.relabel(g, int(rng.integers(1 << 30))) if rng.random() < 0.6 else g
+
+
+def test_reorder_random_sweep(orc):
+    """40 seeded random square graphs: the permutation bit-exact against the
+    oracle every time (level sizes from 1 to thousands, so both the LDS level
+    kernel and the multi-block path run, and hand levels to each other)."""
+    rng = np.random.default_rng(4096)
+    for case in range(40):
+        g = _random_square(rng)
+        plan, perm, ref = rcm_and_check(orc, g, f"random square graph {case}")
+        G.spmm_plan_destroy(plan)
