@@ -149,3 +149,54 @@ def test_autograd_layer(orc, reduce):
         gt = W.Graph("t", g.K, g.M, rt, ct, vt)
         check(orc, gt, dC, "sum", dB, None, exact_rows=np.arange(g.K), what=f"autograd {reduce}")
     adj.close()
+
+
+def test_backward_random_sweep(orc):
+    """30 seeded random graphs (random shapes, duplicates, empty and heavy
+    rows, weighted or not): edge list -> CSR bit-exact, the transposed plan
+    (plain and 1/deg-scaled) through its products, and, for unweighted
+    graphs, the max-pool backward bit-exact."""
+    rng = np.random.default_rng(777)
+    for case in range(30):
+        M, K = int(rng.integers(1, 5000)), int(rng.integers(1, 5000))
+        weighted = bool(rng.random() < 0.5)
+        heavy = int(rng.integers(0, 4))
+        g = W.random_csr(rng, M, K, mean_deg=float(rng.uniform(0.5, 20.0)), empty_frac=float(rng.uniform(0, 0.3)),
+                         dup_frac=float(rng.uniform(0, 0.3)), shuffle_rows=bool(rng.random() < 0.5),
+                         weighted=weighted, heavy_rows=heavy, heavy_deg=int(rng.integers(200, 2000)) if heavy else 0)
+        N = int(rng.choice([1, 3, 16, 33, 64, 130]))
+        what = f"backward case {case}: M={M} K={K} nnz={g.nnz} N={N} weighted={weighted}"
+        log(what)
+        # edge list -> CSR: the CSR's entries as an edge list, shuffled
+        rows = np.repeat(np.arange(M), g.degrees())
+        sh = rng.permutation(g.nnz)
+        r, c = rows[sh], g.col[sh]
+        v = None if g.val is None else g.val[sh]
+        rp, co, vo = G.spmm_coo_to_csr(torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV),
+                                       None if v is None else torch.from_numpy(v).to(DEV), M, K)
+        ref = orc.coo_to_csr(r, c, v, M, K)
+        assert np.array_equal(rp.cpu().numpy(), ref[0]) and np.array_equal(co.cpu().numpy(), ref[1]), what
+        if v is not None:
+            assert np.array_equal(vo.cpu().numpy().view(np.uint32), ref[2].view(np.uint32)), what
+        plan = make_plan(g)
+        for scale in (0, 1):
+            pt = G.spmm_plan_transpose(plan, scale)
+            rt, ct, vt = orc.transpose(g.rowptr, g.col, g.val, g.M, g.K, scale=bool(scale))
+            gt = W.Graph("t", g.K, g.M, rt, ct, vt if (g.val is not None or scale) else None)
+            Gm = rng.standard_normal((g.M, N)).astype(np.float32)
+            _, _, _, Gd = to_dev(gt, Gm)
+            C, _ = gpu_run(pt, g.K, Gd, "sum")
+            light = G.spmm_plan_partition(pt)["light"]
+            check(orc, gt, Gm, "sum", C, None, exact_rows=light, what=f"{what} transpose scale={scale}")
+            if scale == 0 and not weighted:
+                B = rng.integers(0, 4, size=(g.K, N)).astype(np.float32)
+                _, _, _, Bd = to_dev(g, B)
+                Cm, arg = gpu_run(plan, g.M, Bd, "max")
+                dC = rng.standard_normal((g.M, N)).astype(np.float32)
+                dB = torch.full((g.K, N), float("nan"), dtype=torch.float32, device=DEV)
+                G.spmm_max_backward(pt, torch.from_numpy(arg).to(DEV), torch.from_numpy(dC).to(DEV), dB, N)
+                torch.cuda.synchronize()
+                refb = orc.max_backward(arg, dC, g.M, g.K)
+                assert np.array_equal(dB.cpu().numpy().view(np.uint32), refb.view(np.uint32)), what
+            G.spmm_plan_destroy(pt)
+        G.spmm_plan_destroy(plan)
