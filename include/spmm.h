@@ -432,9 +432,10 @@ enum spmm_reorder_method { SPMM_REORDER_RCM = 1 };
  * breadth first with every node appending its unplaced neighbours in
  * ascending (degree, id) order; the order is then reversed.  Deterministic.
  *   perm : device int64 [M], written: perm[i] = the node placed at position i.
- * Needs a square plan (M == K).  Synchronous; allocates and frees temporary
- * device memory (about 40 bytes per entry).  Returns OK, INVALID_ARG
- * (non-square plan, unknown method, bad pointer), OOM or HIP.
+ * Needs a square plan (M == K).  Synchronous; allocates and frees one block
+ * of temporary device memory (about 72 bytes per entry of A and 60 per
+ * node).  Returns OK, INVALID_ARG (non-square plan, unknown method, bad
+ * pointer), OOM or HIP.
  */
 int spmm_plan_reorder(spmm_plan_t plan, int method, int64_t *perm);
 
