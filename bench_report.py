@@ -54,10 +54,12 @@ def router(args):
     geo = math.exp(sum(math.log(q) for q in ratios) / len(ratios))
     out += ["", f"Geometric mean of router / best over {len(ratios)} configurations: **{geo:.4f}**; "
             f"minimum **{min(ratios):.4f}**.", ""]
-    out += [f"Per configuration: the router's pick and the {args.top} fastest other variants "
-            "(the JSON line holds all of them).", ""]
+    out += [f"Configurations where the router is below {args.detail_below} of the best: the router's pick and "
+            f"the {args.top} fastest other variants (the JSON line holds all of them).", ""]
     for cfg, entries in ev.items():
         for e in entries:
+            if e["router_speed_vs_best"] >= args.detail_below:
+                continue
             out += [f"## {cfg}, {e['reduce']}", "", "| variant | ms | path | route (lanes, vec, F, slices, xcd, nt, "
                     "split, tiles, window) |", "|---|---|---|---|"]
             timed = [v for v in e["variants"] if "ms" in v]
@@ -264,6 +266,7 @@ def main():
             p.add_argument("--top", type=int, default=30)
         if name == "router":
             p.add_argument("--top", type=int, default=3)
+            p.add_argument("--detail-below", type=float, default=0.99)
         if name == "counters":
             p.add_argument("--kernel", action="append", required=True)
             p.add_argument("--title", default="")

@@ -538,17 +538,31 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     int F = W > G ? 2 : 1;
     const bool skewed = p->cv_deg > 1.0;
     const bool small = p->M * 4 < (int64_t)p->num_cus * 2 * 64;
+    // widths that are a multiple of 8 vectors but not a power of two (96,
+    // 160, 192 floats): rounding G up to a power of two leaves lanes idle
+    const bool odd8 = !skewed && W % 8 == 0 && (W & (W - 1)) != 0 && W < 64;
     if (skewed && W >= 32) {
-        G = W >= 128 ? 32 : 16;
+        // skewed graphs: column slices of 32 lanes from 64 to 128 vectors, of
+        // 16 lanes otherwise (each pass over the graph touches a part of every
+        // B row, which keeps more of B in the Infinity Cache)
+        G = (W >= 64 && W <= 128) ? 32 : 16;
         F = 1;
     } else if (small) {
         // launch-bound: as many waves as possible, so no coarsening, and 8
         // lanes per row (more column slices) up to 128 columns
         F = 1;
         if (W <= 32) G = 8;
+    } else if (odd8) {
+        // low degree: row tiles of 8 lanes x 2 vectors, in 64-column slices;
+        // else half the lanes, coarsened, in one slice
+        G = p->mean_deg < 8.0 ? 8 : G / 2;
+        F = 2;
     } else if (p->mean_deg < 8.0 && G >= 16 && W <= G) {
         G /= 2;
         F = 2;
+    } else if (p->mean_deg >= 8.0 && W > 64 && W % 64 == 0) {
+        // wide features at higher degree: 64-lane slices without coarsening
+        F = 1;
     }
     if (p->opt_lanes) G = p->opt_lanes;
     if (p->opt_coarsen) F = p->opt_coarsen;
@@ -585,16 +599,26 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         return r;
     }
     // V = 2 panels, when built: by padding share (ParamSpMM's PR for V), or forced
-    // (with community structure as well, the window kernel's LDS reuse beats
-    // the panels from 512 columns: kNN line graph 0.976 vs 1.036 ms)
+    // (with community structure as well, the window kernel's 64-column
+    // slices beat the panels from 512 columns, and above 256 columns when the
+    // width is not a power of two: kNN line graph 0.976 vs 1.036 ms at 512
+    // columns, 0.633 vs 0.924 ms at 300)
     r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock != 0 &&
               (reduce != SPMM_MAX || !p->pair_unsorted) &&
               (p->opt_vblock == 2 ||
-               (!p->split && pair_padding(p) <= kPairMaxPadding && !(r.window && W >= 128)));
+               (!p->split && pair_padding(p) <= kPairMaxPadding &&
+                !(r.window && (W >= 128 || (W > 64 && (W & (W - 1)) != 0)))));
     if (r.pairs) {
         r.vec = vec == 4 ? 4 : 1;
         const int64_t Wp = (N + r.vec - 1) / r.vec;
-        r.lanes = p->opt_lanes ? p->opt_lanes : std::min(64, std::max(4, pow2_ceil(Wp)));
+        // at most 32 lanes: two 128-column slices beat one of 256 (kNN line
+        // graph, 256 columns: 0.497 vs 0.519 ms); a width that is not a power
+        // of two takes its largest power-of-two factor, so that no lane idles
+        // (kNN, 96 and 160 columns: 8 lanes; 192: 16)
+        int lanes = std::min(32, std::max(4, pow2_ceil(Wp)));
+        const int64_t factor = Wp & -Wp;
+        if ((Wp & (Wp - 1)) != 0 && factor >= 4) lanes = (int)std::min<int64_t>(32, factor);
+        r.lanes = p->opt_lanes ? p->opt_lanes : lanes;
         r.coarsen = 1;
         r.slices = (int)((Wp + r.lanes - 1) / r.lanes);
         r.tiled = r.compact = r.window = r.split = false;

@@ -608,7 +608,14 @@ def test_router_rules():
     """Routing decisions measured on the GPU (the router sweep): community
     structure takes the LDS window kernel from 64 columns; launch-bound small
     graphs take 8 lanes per row without coarsening up to 128 columns; skewed
-    graphs take 128-column slices from 512 columns."""
+    graphs take 64-column slices from 128 columns, 128-column slices from 256
+    to 512 and 64-column slices above; widths of a multiple of 8 vectors that
+    are not powers of two (96, 160, 192 floats) take 8 lanes x 2 vectors at
+    low degree and half the lanes coarsened otherwise; wide features at
+    higher degree take 64 lanes without coarsening; V = 2 panels take the
+    largest power-of-two factor of a width that is not a power of two as
+    their lane count, and community-structured graphs take the window kernel
+    instead of panels for such widths above 256 floats."""
     community = make_plan(W.make_graph("community", M=20_000))
     for N, win in ((16, 0), (64, 2), (128, 2), (512, 2)):
         info = G.spmm_plan_route(community, N, "sum")
@@ -622,7 +629,26 @@ def test_router_rules():
     rng = np.random.default_rng(5)
     skew = make_plan(W.random_csr(rng, 20_000, 20_000, mean_deg=6.0, heavy_rows=20, heavy_deg=5000))
     assert G.spmm_plan_info(skew)["cv_deg"] > 1.0
-    for N, lanes in ((128, 16), (256, 16), (512, 32), (1024, 32)):
+    for N, lanes in ((96, 32), (128, 16), (192, 16), (256, 32), (512, 32), (1024, 16)):
         info = G.spmm_plan_route(skew, N, "sum")
         assert (info["route_lanes"], info["route_coarsen"]) == (lanes, 1), (N, info)
     G.spmm_plan_destroy(skew)
+    road = make_plan(W.make_graph("road", M=100_000))
+    for N, lg in ((64, (8, 2)), (96, (8, 2)), (100, (16, 2)), (160, (8, 2)), (192, (8, 2))):
+        info = G.spmm_plan_route(road, N, "sum")
+        assert (info["route_lanes"], info["route_coarsen"]) == lg, (N, info)
+    G.spmm_plan_destroy(road)
+    diffusion = make_plan(W.make_graph("diffusion", M=100_000))
+    for N, lg in ((96, (16, 2)), (100, (32, 1)), (160, (32, 2)), (192, (32, 2)), (300, (64, 2)),
+                  (512, (64, 1)), (1024, (64, 1))):
+        info = G.spmm_plan_route(diffusion, N, "mean")
+        assert (info["route_lanes"], info["route_coarsen"]) == lg, (N, info)
+    G.spmm_plan_destroy(diffusion)
+    knn = make_plan(W.knn_line(50_000, 10))
+    assert G.spmm_plan_info(knn)["pairs_built"] == 1
+    for N, panels, lanes in ((96, 1, 8), (100, 1, 32), (128, 1, 32), (160, 1, 8), (192, 1, 16), (256, 1, 32),
+                             (300, 0, 16), (512, 0, 16)):
+        info = G.spmm_plan_route(knn, N, "sum")
+        assert info["route_pairs"] == panels and (panels or info["route_window"] > 0), (N, info)
+        assert info["route_lanes"] == lanes, (N, info)
+    G.spmm_plan_destroy(knn)
