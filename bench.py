@@ -684,7 +684,7 @@ def router_sweep(r, reduce, steps, flush):
     G = r.G
     auto = {G.SPMM_OPT_LANES: 0, G.SPMM_OPT_COARSEN: 0, G.SPMM_OPT_TILES: -1, G.SPMM_OPT_WINDOW: -1,
             G.SPMM_OPT_XCD_REMAP: -1, G.SPMM_OPT_NT_STORE: -1, G.SPMM_OPT_SPLIT_MODE: -1,
-            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: -1, G.SPMM_OPT_SPLIT_FUSED: 1}
+            G.SPMM_OPT_BALANCE: 0, G.SPMM_OPT_VBLOCK: -1, G.SPMM_OPT_SPLIT_FUSED: 1, G.SPMM_OPT_VEC: 0}
     variants = [("router", {})]
     variants += [(f"lanes={g} coarsen={f}", {G.SPMM_OPT_LANES: g, G.SPMM_OPT_COARSEN: f})
                  for g in (4, 8, 16, 32, 64) for f in (1, 2)]
@@ -694,7 +694,8 @@ def router_sweep(r, reduce, steps, flush):
                  ("non-temporal C stores", {G.SPMM_OPT_NT_STORE: 1}), ("split on", {G.SPMM_OPT_SPLIT_MODE: 1}),
                  ("split off", {G.SPMM_OPT_SPLIT_MODE: 0}), ("merge-path balancing", {G.SPMM_OPT_BALANCE: 1}),
                  ("V = 2 panels", {G.SPMM_OPT_VBLOCK: 2}), ("V = 2 panels off", {G.SPMM_OPT_VBLOCK: 0}),
-                 ("split in two dispatches", {G.SPMM_OPT_SPLIT_FUSED: 0})]
+                 ("split in two dispatches", {G.SPMM_OPT_SPLIT_FUSED: 0}),
+                 ("float2 lanes", {G.SPMM_OPT_VEC: 2}), ("float1 lanes", {G.SPMM_OPT_VEC: 1})]
     rows = []
     for label, opts in variants:
         print(f"[bench]   {reduce} {label}", file=sys.stderr, flush=True)

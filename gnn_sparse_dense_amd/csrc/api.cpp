@@ -518,6 +518,10 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 //    where neighbours carry no locality, with a B of 128 floats or more:
 //    64-column slices (128-column slices from 512 floats), so each pass over
 //    the graph touches a part of B that stays in the Infinity Cache longer;
+//    that holds at power-of-two widths: at other widths past 32 vectors a
+//    half-width lane group, coarsened, covers the row in one slice and wins
+//    (33 floats on the power-law graph: 1.83 vs 2.77 ms; 300 floats: 11.8
+//    vs 12.4 ms), the same rule as on the other graphs;
 //  * fp16 matrix-core tiles only when the caller enabled them (they follow
 //    the looser fp16 contract) and the run is a sum or mean with 16-byte
 //    aligned float4 access;
@@ -529,22 +533,53 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     Route r;
     const bool a16 = aligned(B, 16) && aligned(C, 16) && (!argmax || aligned(argmax, 16));
     const bool a8 = aligned(B, 8) && aligned(C, 8) && (!argmax || aligned(argmax, 16));
-    int vec = (N % 4 == 0 && a16) ? 4 : (N % 2 == 0 && a8) ? 2 : 1;
-    if (p->opt_vec == 4 && N % 4 == 0 && a16) vec = 4;
+    const bool a4 = aligned(B, 4) && aligned(C, 4) && (!argmax || aligned(argmax, 8));
+    const bool skewed = p->cv_deg > 1.0;
+    const bool small = p->M * 4 < (int64_t)p->num_cus * 2 * 64;
+    // whole float4 vectors: 16-byte aligned rows
+    const bool whole4 = N % 4 == 0 && a16;
+    // float4 lanes also where rows are only 4-byte aligned or N is not a
+    // multiple of 4 (the last vector of a row ends at column N): one 16-byte
+    // access per lane instead of two or four narrower ones (road graph, 33
+    // floats: 0.094 vs 0.198 ms in float1 lanes; 602 floats: 1.38 vs 1.60 ms
+    // in float2 lanes)
+    const bool ragged4 = N >= 4 && a4;
+    int vec = (whole4 || ragged4) ? 4 : (N % 2 == 0 && a8) ? 2 : 1;
+    // Float1 lanes instead where a row spans only a few float4 lanes and the
+    // rate of gathers, not DRAM, bounds the product: rows of at most 8
+    // floats at mean degree 16 and above, whose B rows stay in cache
+    // (community graph, 8 floats: 0.071 vs 0.095 ms; 7 floats: 0.072 vs
+    // 0.095 ms), and at most 16 floats on split skewed graphs, where a wave's
+    // rows then number fewer and end closer together (power-law graph, 16
+    // floats: 1.09 vs 1.34 ms; mixed graph, 8 floats: 0.317 vs 0.372 ms)
+    if (vec == 4 && ((N <= 8 && p->mean_deg >= 16.0) || (N <= 16 && p->split))) vec = 1;
+    if (p->opt_vec == 4 && (whole4 || ragged4)) vec = 4;
     else if (p->opt_vec == 2 && N % 2 == 0 && a8) vec = 2;
     else if (p->opt_vec == 1) vec = 1;
     const int64_t W = (N + vec - 1) / vec;
     int G = std::max(4, pow2_ceil(W));
     int F = W > G ? 2 : 1;
-    const bool skewed = p->cv_deg > 1.0;
-    const bool small = p->M * 4 < (int64_t)p->num_cus * 2 * 64;
+    const bool pow2 = (W & (W - 1)) == 0;
     // widths that are a multiple of 8 vectors but not a power of two (96,
     // 160, 192 floats): rounding G up to a power of two leaves lanes idle
-    const bool odd8 = !skewed && W % 8 == 0 && (W & (W - 1)) != 0 && W < 64;
-    if (skewed && W >= 32) {
+    const bool odd8 = !skewed && W % 8 == 0 && !pow2 && W < 64;
+    // other widths of 17 to 63 vectors that leave a quarter or more of their
+    // power-of-two lane group idle (66, 130, 140 floats): at mean degree below
+    // 16, half the group, coarsened, so that a row's second vector slot takes
+    // the remainder and each wave holds twice the rows (diffusion graph, 66
+    // floats: 0.292 vs 0.328 ms; 130 floats: 0.505 vs 0.556 ms); at higher or
+    // skewed degrees the whole group stays faster (community graph, 130
+    // floats: 0.539 vs 0.570 ms)
+    int pc = 1;
+    while (pc < W) pc <<= 1;
+    const bool ragged = !pow2 && W > 16 && W < 64 && 4 * W <= 3 * pc && p->mean_deg < 16.0 && !skewed;
+    if (skewed && W >= 32 && W % 8 == 0) {
         // skewed graphs: column slices of 32 lanes from 64 to 128 vectors, of
         // 16 lanes otherwise (each pass over the graph touches a part of every
-        // B row, which keeps more of B in the Infinity Cache)
+        // B row, which keeps more of B in the Infinity Cache); measured at
+        // widths of a multiple of 32 floats: at other widths a nearly empty
+        // last slice costs a whole pass (power-law graph, 130 floats: one
+        // 64-lane slice 4.92 ms, three 16-lane slices 6.01 ms)
         G = (W >= 64 && W <= 128) ? 32 : 16;
         F = 1;
     } else if (small) {
@@ -556,6 +591,9 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         // low degree: row tiles of 8 lanes x 2 vectors, in 64-column slices;
         // else half the lanes, coarsened, in one slice
         G = p->mean_deg < 8.0 ? 8 : G / 2;
+        F = 2;
+    } else if (ragged) {
+        G = (int)pc / 2;
         F = 2;
     } else if (p->mean_deg < 8.0 && G >= 16 && W <= G) {
         G /= 2;
@@ -575,13 +613,14 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     r.split = p->split;
     r.tiled = p->tiles != nullptr && !p->split && (G == 4 || G == 8);
     r.compact = r.tiled && p->tile_compact;
-    // community structure with features of 64 floats or more: stage B's row
-    // blocks in LDS
+    // community structure with features of more than 32 floats: stage B's
+    // row blocks in LDS (community graph, 33 floats: 0.114 vs 0.184 ms in
+    // 16-lane rows; at 32 floats and below 8-lane rows are as fast or faster)
     // (one dispatch: at most 2^32 / kWinBlock row blocks, about 10^9 rows;
     // larger graphs take the row kernels)
     const bool win_grid = (p->M + kWinRows - 1) / kWinRows <= (int64_t)(UINT32_MAX / kWinBlock);
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 && win_grid &&
-               (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N >= 64));
+               (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N > 32));
     // fp16 community tiles, when the caller asked for them
     r.mfma = p->opt_mfma > 0 && p->mfma_tiles != nullptr && reduce != SPMM_MAX && N % 4 == 0 && a16;
     // merge-path balancing, when the caller chose it
@@ -603,10 +642,13 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     // slices beat the panels from 512 columns, and above 256 columns when the
     // width is not a power of two: kNN line graph 0.976 vs 1.036 ms at 512
     // columns, 0.633 vs 0.924 ms at 300)
+    // The panels have float4 and float1 forms only: a float2 width of 128
+    // floats or more keeps the float2 row kernel (kNN line graph, 130 floats:
+    // 0.745 vs 0.789 ms; 602 floats: 2.51 vs 3.36 ms).
     r.pairs = !r.mfma && p->pair_prow != nullptr && p->opt_vblock != 0 &&
               (reduce != SPMM_MAX || !p->pair_unsorted) &&
               (p->opt_vblock == 2 ||
-               (!p->split && pair_padding(p) <= kPairMaxPadding &&
+               (!p->split && pair_padding(p) <= kPairMaxPadding && !(vec == 2 && N >= 128) &&
                 !(r.window && (W >= 128 || (W > 64 && (W & (W - 1)) != 0)))));
     if (r.pairs) {
         r.vec = vec == 4 ? 4 : 1;
@@ -618,6 +660,10 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
         int lanes = std::min(32, std::max(4, pow2_ceil(Wp)));
         const int64_t factor = Wp & -Wp;
         if ((Wp & (Wp - 1)) != 0 && factor >= 4) lanes = (int)std::min<int64_t>(32, factor);
+        // other widths past 32 vectors that are not a power of two: 64 lanes,
+        // the fewest slices (kNN line graph, 130 floats: 0.358 vs 0.444 ms at
+        // 32 lanes; 1026 floats: 2.84 vs 3.20 ms)
+        else if ((Wp & (Wp - 1)) != 0 && Wp > 32) lanes = 64;
         r.lanes = p->opt_lanes ? p->opt_lanes : lanes;
         r.coarsen = 1;
         r.slices = (int)((Wp + r.lanes - 1) / r.lanes);
@@ -1346,9 +1392,13 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     p->route.fused_split = fused_done;
 
     if (split) {
-        for (int64_t w0 = 0; w0 < N; w0 += kPartialWidth) {
-            const int64_t w1 = std::min<int64_t>(N, w0 + kPartialWidth);
-            const int64_t Wv = (w1 - w0) / r.vec;
+        for (int64_t p0 = 0; p0 < N; p0 += kPartialWidth) {
+            const int64_t w1 = std::min<int64_t>(N, p0 + kPartialWidth);
+            // a last pass narrower than one vector starts earlier, so that its
+            // vectors stay inside the pass (the overlap is recomputed with the
+            // same bits)
+            const int64_t w0 = std::min(p0, std::max<int64_t>(0, w1 - r.vec));
+            const int64_t Wv = (w1 - w0 + r.vec - 1) / r.vec;
             const int F = Wv > 64 ? 2 : 1;
             const int slices = (int)((Wv + 64 * F - 1) / (64 * F));
             if (!fused_done) {

@@ -173,7 +173,10 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
     const int sub = lane / G;
     const int64_t c0 = by * SL + (int64_t)g * VEC;
     const bool ok = c0 < a.N;
-    const int colf = (int)c0;
+    // a vector that would run past column N ends there instead (the launch
+    // guarantees N >= VEC); its lower columns are also its neighbour's, with
+    // the same bits
+    const int colf = (int)(VEC > 1 && c0 > a.N - VEC ? a.N - VEC : c0);
 
     const int64_t v = task0 + sub;
     const bool live = v < a.npanels;

@@ -33,6 +33,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
+// The same vectors at their element alignment: a row of B or C starts at a
+// multiple of 4 bytes only when N is not a multiple of 4 (or the caller's
+// pointer is offset), and global loads and stores of 2 or 4 dwords need dword
+// alignment only, so such rows still take one 8- or 16-byte access per lane.
+typedef float f32x2a __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef int i32x2a __attribute__((ext_vector_type(2), aligned(4)));
+typedef int i32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef long long i64x2a __attribute__((ext_vector_type(2), aligned(8)));
 
 // Block id permutation for the 8 XCDs.  The hardware hands consecutive block
 // ids to the XCDs round-robin, each XCD with its own L2.  Within every run of
@@ -73,10 +82,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int VEC>
 __device__ __forceinline__ void load_vec(const float *p, float (&x)[VEC]) {
     if constexpr (VEC == 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 v = *reinterpret_cast<const f32x4a *>(p);
         x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
     } else if constexpr (VEC == 2) {
-        const f32x2 v = *reinterpret_cast<const f32x2 *>(p);
+        const f32x2 v = *reinterpret_cast<const f32x2a *>(p);
         x[0] = v.x; x[1] = v.y;
     } else {
         x[0] = *p;
@@ -86,13 +95,13 @@ __device__ __forceinline__ void load_vec(const float *p, float (&x)[VEC]) {
 template <int VEC>
 __device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool nt) {
     if constexpr (VEC == 4) {
-        const f32x4 v = {x[0], x[1], x[2], x[3]};
-        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
-        else *reinterpret_cast<f32x4 *>(p) = v;
+        const f32x4a v = {x[0], x[1], x[2], x[3]};
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x4a *>(p));
+        else *reinterpret_cast<f32x4a *>(p) = v;
     } else if constexpr (VEC == 2) {
-        const f32x2 v = {x[0], x[1]};
-        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(p));
-        else *reinterpret_cast<f32x2 *>(p) = v;
+        const f32x2a v = {x[0], x[1]};
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x2a *>(p));
+        else *reinterpret_cast<f32x2a *>(p) = v;
     } else {
         if (nt) __builtin_nontemporal_store(x[0], p);
         else *p = x[0];
@@ -102,10 +111,10 @@ __device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool 
 template <int VEC>
 __device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC]) {
     if constexpr (VEC == 4) {
-        reinterpret_cast<i64x2 *>(p)[0] = i64x2{x[0], x[1]};
-        reinterpret_cast<i64x2 *>(p)[1] = i64x2{x[2], x[3]};
+        reinterpret_cast<i64x2a *>(p)[0] = i64x2a{x[0], x[1]};
+        reinterpret_cast<i64x2a *>(p)[1] = i64x2a{x[2], x[3]};
     } else if constexpr (VEC == 2) {
-        *reinterpret_cast<i64x2 *>(p) = i64x2{x[0], x[1]};
+        *reinterpret_cast<i64x2a *>(p) = i64x2a{x[0], x[1]};
     } else {
         *p = x[0];
     }
@@ -113,8 +122,8 @@ __device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC]) {
 
 template <int VEC>
 __device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
-    if constexpr (VEC == 4) *reinterpret_cast<i32x4 *>(p) = i32x4{x[0], x[1], x[2], x[3]};
-    else if constexpr (VEC == 2) *reinterpret_cast<i32x2 *>(p) = i32x2{x[0], x[1]};
+    if constexpr (VEC == 4) *reinterpret_cast<i32x4a *>(p) = i32x4a{x[0], x[1], x[2], x[3]};
+    else if constexpr (VEC == 2) *reinterpret_cast<i32x2a *>(p) = i32x2a{x[0], x[1]};
     else *p = x[0];
 }
 
@@ -245,12 +254,20 @@ __device__ __forceinline__ void store_out(const RowArgs &a, int64_t orow, int de
 }
 
 // Column ownership of lane g within its row group for the slice starting at c0.
+// When the launch's width is not a multiple of VEC, the one vector that would
+// run past c_end is moved back to end there: it reads and writes the last VEC
+// columns, the lower ones of which its neighbour lane also computes.  Both
+// fold the same entries in the same order, so both write the same bits, and
+// every access stays inside the row (the launch guarantees c_end - c_begin
+// >= VEC).
 template <int G, int VEC, int F>
 __device__ __forceinline__ void lane_columns(const RowArgs &a, int64_t c0, int g, int (&colf)[F], bool (&ok)[F]) {
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-        colf[f] = (int)(c0 + (f * G + g) * VEC);
-        ok[f] = (c0 + (int64_t)(f * G + g) * VEC) < a.c_end;
+        const int64_t c = c0 + (int64_t)(f * G + g) * VEC;
+        ok[f] = c < a.c_end;
+        const int64_t last = a.c_end - VEC;   // first column of the last whole vector
+        colf[f] = (int)(VEC > 1 && c > last ? last : c);
     }
 }
 
@@ -510,14 +527,19 @@ __device__ __forceinline__ void window_coords(const RowArgs &a, int64_t *w0, int
 }
 
 // The window: B rows w0 .. w0 + kWinRows - 1, columns c0 .. c0 + kWinCols - 1,
-// zero past the edges of B.
+// zero past the edges of B.  Slot q holds the vector that lane q of a row
+// reads: when N is not a multiple of 4, the vector that would run past column
+// N ends there instead (as in lane_columns; N >= 4).
 __device__ __forceinline__ void load_window(const RowArgs &a, f32x4 *s_B, int64_t w0, int64_t c0) {
     constexpr int Q = kWinCols / 4;                 // float4 per window row
     for (int i = threadIdx.x; i < kWinRows * Q; i += kWinBlock) {
         const int r = i / Q, q = i - (i / Q) * Q;
         const int64_t brow = w0 + r, bcol = c0 + q * 4;
         f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (brow < a.K && bcol < a.N) v = *reinterpret_cast<const f32x4 *>(a.B + brow * a.N + bcol);
+        if (brow < a.K && bcol < a.N) {
+            const int64_t bc = bcol > a.N - 4 ? a.N - 4 : bcol;
+            v = *reinterpret_cast<const f32x4a *>(a.B + brow * a.N + bc);
+        }
         s_B[i] = v;
     }
     __syncthreads();
@@ -597,7 +619,7 @@ __device__ __forceinline__ void win_hbm_run(const E *se, int lo, int hi, const R
         for (int u = 0; u < U; ++u) {
             ent[u] = se[k + u < hi ? k + u : lo];
             b[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4 *>(a.B + elem_off(ent_key(ent[u]), a.N, colf));
+            if (k + u < hi && ok) b[u] = *reinterpret_cast<const f32x4a *>(a.B + elem_off(ent_key(ent[u]), a.N, colf));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -671,8 +693,8 @@ void window_sorted_kernel_t(RowArgs a) {
     load_window(a, s_B, w0, c0);
     const int wlo = (int)w0;
     const int g16m1 = g * 16 - 1;
-    const int colf = (int)(c0 + g * 4);
     const bool ok = c0 + g * 4 < a.c_end;
+    const int colf = (int)(c0 + g * 4 > a.c_end - 4 ? a.c_end - 4 : c0 + g * 4);   // as in lane_columns
     E *se = s_e[wv];
 
     for (int pass = 0; pass < kWinRows / (WW * R); ++pass) {

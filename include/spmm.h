@@ -69,13 +69,16 @@ enum spmm_option {
                                   are split, and T and L are capped at 2^24   */
     SPMM_OPT_LANES = 4,        /* lanes per row G in {4,8,16,32,64}; 0 auto       */
     SPMM_OPT_COARSEN = 5,      /* vectors per lane F in {1,2}; 0 auto             */
-    SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto            */
+    SPMM_OPT_VEC = 6,          /* floats per vector in {1,2,4}; 0 auto.  4 also
+                                  serves any N >= 4 and rows that are only
+                                  4-byte aligned: the last vector of a row
+                                  ends at column N                           */
     SPMM_OPT_XCD_REMAP = 7,    /* -1 auto, 0 off, 1 on: contiguous rows per XCD  */
     SPMM_OPT_NT_STORE = 8,     /* -1 auto, 0 off, 1 on: non-temporal C stores    */
     SPMM_OPT_TILES = 9,        /* -1 auto (low, even degrees), 0 off, 1 on, 2 on
                                   with 32-bit records: keep 8-row tile records
                                   holding row bounds + indexes               */
-    SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N >= 64), 0 off,
+    SPMM_OPT_WINDOW = 10,      /* -1 auto (community structure, N > 32), 0 off,
                                   1 on: stage each 256-row block of B in LDS
                                   (a faster kernel when every row's columns
                                   are non-decreasing, bit-identical either way;
@@ -272,6 +275,9 @@ spmm_plan_t spmm_plan_create(const int64_t *rowptr, const int64_t *col, const fl
  *   argmax : device int64 [M, N] or NULL; only allowed with SPMM_MAX, where it
  *            receives the column id of each maximum (-1 for empty rows).
  *   N      : feature width, N >= 1.
+ * B, C and argmax need only their element alignment: for N >= 4 the kernels
+ * read and write 16 bytes per lane at any 4-byte aligned address (a row's
+ * last vector ends at column N), and write no byte outside C and argmax.
  * Asynchronous: it validates its arguments, picks a kernel from the plan's
  * descriptors and N, enqueues the kernels and returns without waiting.  It
  * allocates nothing and enqueues kernels only (no memset or copy), so a call

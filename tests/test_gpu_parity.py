@@ -48,13 +48,13 @@ def test_forced_variants_agree_bitwise(orc, weighted):
     rng = np.random.default_rng(101)
     g = W.random_csr(rng, 3001, 2500, mean_deg=9.0, empty_frac=0.05, dup_frac=0.1,
                      shuffle_rows=True, weighted=weighted, zero_frac=0.05)
-    for N in (16, 64, 100):
+    for N in (16, 64, 100, 37):
         B = rng.standard_normal((g.K, N)).astype(np.float32)
         _, _, _, Bd = to_dev(g, B)
         for red in ("sum", "mean", "max"):
             ref_out = None
             for lanes, coarsen, vec in VARIANTS:
-                if N % vec:
+                if vec == 2 and N % 2:   # float4 lanes also serve widths that are not a multiple of 4
                     continue
                 what = f"N={N} {red} lanes={lanes} F={coarsen} vec={vec} w={weighted}"
                 log(what)
@@ -84,13 +84,14 @@ def test_ragged_widths(orc, N):
         log(f"ragged N={N} {red}")
         C, arg = gpu_run(plan, g.M, Bd, red)
         check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=f"N={N} {red}")
-    # an offset (8-byte but not 16-byte aligned) view of B forces narrower vectors
+    # an offset (8-byte but not 16-byte aligned) view of B keeps float4 lanes
+    # on 4-byte aligned rows
     if N % 4 == 0:
         Bbig = torch.empty(g.K * N + 2, dtype=torch.float32, device=DEV)
         Bv = Bbig[2:].view(g.K, N)
         Bv.copy_(Bd)
         C, _ = gpu_run(plan, g.M, Bv, "sum")
-        assert G.spmm_plan_info(plan)["route_vec"] == 2
+        assert G.spmm_plan_info(plan)["route_vec"] == 4
         check(orc, g, B, "sum", C, None, exact_rows=np.arange(g.M), what=f"N={N} misaligned B")
     G.spmm_plan_destroy(plan)
 
