@@ -344,11 +344,15 @@ hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, in
 // col_t: they are staged kChunk at a time in LDS with coalesced loads (as in
 // the forward row kernel), then lane g of row j's group gathers dC[i][c..] and
 // argmax[i][c..] in predicated batches and adds dC where argmax == j, in
-// ascending i.  A repeated i (a duplicated edge) is counted once.
+// ascending i.  A repeated i (a duplicated edge) is counted once.  With VEC =
+// 4 the rows need only element alignment (16-byte accesses at 4-byte aligned
+// addresses), and when N is not a multiple of 4 the lane whose vector would
+// run past column N takes the last four columns: the columns it shares with
+// its neighbour lane get the same sums, in the same order, from both.
 template <int G, int VEC>
 __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    typedef long long l2 __attribute__((ext_vector_type(2)));
+    typedef float f4 __attribute__((ext_vector_type(4), aligned(4)));
+    typedef long long l2 __attribute__((ext_vector_type(2), aligned(8)));
     constexpr int R = 64 / G;
     constexpr int U = 4;
     constexpr int NT = kChunk / 64;
@@ -361,8 +365,9 @@ __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
     if (j0 >= a.rows) return;                               // uniform per wave
     const int64_t j = j0 + sub;
     const bool live = j < a.rows;
-    const int64_t c = (int64_t)blockIdx.y * (G * VEC) + g * VEC;
-    const bool ok = c < a.N;
+    const int64_t c0 = (int64_t)blockIdx.y * (G * VEC) + g * VEC;
+    const bool ok = c0 < a.N;
+    const int64_t c = (VEC > 1 && c0 > a.N - VEC) ? a.N - VEC : c0;   // a.N >= VEC
     const int beg = live ? a.rowptr_t[j] : 0;
     const int deg = live ? a.rowptr_t[j + 1] - beg : 0;
     const int beg0 = __builtin_amdgcn_readfirstlane(beg);
@@ -449,9 +454,11 @@ __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
 
 hipError_t launch_maxgrad(const MaxGradArgs &a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
-    const bool a16 = ((uintptr_t)a.dC % 16 == 0) && ((uintptr_t)a.argmax % 16 == 0) && ((uintptr_t)a.dB % 16 == 0);
-    const int vec = (a.N % 4 == 0 && a16) ? 4 : 1;
-    const int64_t W = a.N / vec;
+    // float4 lanes for any N >= 4 (element-aligned rows, the last vector of a
+    // row ending at column N), float1 below
+    const bool a4 = ((uintptr_t)a.dC % 4 == 0) && ((uintptr_t)a.argmax % 8 == 0) && ((uintptr_t)a.dB % 4 == 0);
+    const int vec = (a.N >= 4 && a4) ? 4 : 1;
+    const int64_t W = (a.N + vec - 1) / vec;
     int G = 4;
     while (G < W && G < 64) G <<= 1;
     const int64_t per_block = (int64_t)(64 / G) * kWaves;

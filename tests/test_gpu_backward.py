@@ -95,7 +95,7 @@ def test_transposed_plan_product(orc, name, M, scale):
     G.spmm_plan_destroy(plan)
 
 
-@pytest.mark.parametrize("N", [16, 13, 64])
+@pytest.mark.parametrize("N", [16, 13, 64, 5, 130])
 def test_max_backward_bit_exact(orc, N):
     rng = np.random.default_rng(N)
     g = W.random_csr(rng, 6000, 4500, mean_deg=7.0, empty_frac=0.1, dup_frac=0.2, shuffle_rows=True,
@@ -200,3 +200,32 @@ def test_backward_random_sweep(orc):
                 assert np.array_equal(dB.cpu().numpy().view(np.uint32), refb.view(np.uint32)), what
             G.spmm_plan_destroy(pt)
         G.spmm_plan_destroy(plan)
+
+
+def test_max_backward_offset_pointers(orc):
+    """dC, argmax and dB one element past a 16-byte boundary: float4 lanes on
+    4-byte aligned rows, the same bits as the oracle, guards untouched."""
+    rng = np.random.default_rng(77)
+    N = 33
+    g = W.random_csr(rng, 3000, 2500, mean_deg=6.0, empty_frac=0.1, weighted=False)
+    B = rng.integers(0, 4, size=(g.K, N)).astype(np.float32)
+    plan = make_plan(g)
+    _, _, _, Bd = to_dev(g, B)
+    _, arg = gpu_run(plan, g.M, Bd, "max")
+    dC = rng.standard_normal((g.M, N)).astype(np.float32)
+    pt = G.spmm_plan_transpose(plan, 0)
+    abig = torch.empty(g.M * N + 1, dtype=torch.int64, device=DEV)
+    av = abig[1:].view(g.M, N)
+    av.copy_(torch.from_numpy(arg))
+    cbig = torch.empty(g.M * N + 1, dtype=torch.float32, device=DEV)
+    cv = cbig[1:].view(g.M, N)
+    cv.copy_(torch.from_numpy(dC))
+    dbig = torch.full((g.K * N + 2,), float("nan"), dtype=torch.float32, device=DEV)
+    dv = dbig[1:-1].view(g.K, N)
+    G.spmm_max_backward(pt, av, cv, dv, N)
+    torch.cuda.synchronize()
+    ref = orc.max_backward(arg, dC, g.M, g.K)
+    assert np.array_equal(dv.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(dbig[0].item()) and np.isnan(dbig[-1].item())
+    G.spmm_plan_destroy(pt)
+    G.spmm_plan_destroy(plan)
