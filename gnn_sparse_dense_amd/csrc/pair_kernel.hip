@@ -174,9 +174,9 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
     const int64_t c0 = by * SL + (int64_t)g * VEC;
     const bool ok = c0 < a.N;
     // a vector that would run past column N ends there instead (the launch
-    // guarantees N >= VEC); its lower columns are also its neighbour's, with
-    // the same bits
+    // guarantees N >= VEC); it writes only the columns past its neighbour's
     const int colf = (int)(VEC > 1 && c0 > a.N - VEC ? a.N - VEC : c0);
+    const int skip = (int)(c0 - colf);
 
     const int64_t v = task0 + sub;
     const bool live = v < a.npanels;
@@ -258,9 +258,9 @@ __global__ __launch_bounds__(kBlock) void pair_kernel_t(PairArgs a) {
             }
         }
         if constexpr (!IS_MAX) mean_divide<VEC>(a.mean != 0, d, res);
-        store_vec<VEC>(a.C + row * a.N + colf, res, false);
+        store_vec<VEC>(a.C + row * a.N + colf, res, false, skip);
         if constexpr (IS_MAX)
-            if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar);
+            if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar, skip);
     }
 }
 

@@ -92,9 +92,19 @@ __device__ __forceinline__ void load_vec(const float *p, float (&x)[VEC]) {
     }
 }
 
+// Stores of one lane's vector.  skip > 0 marks a row's last vector moved back
+// to end at the launch's last column (lane_columns): it writes only its
+// elements skip .. VEC-1, the columns no other lane writes.  The wave-wide
+// test comes first, so that waves without such a lane (every wave when N is
+// a multiple of VEC) take one scalar branch; it also keeps the window
+// kernels within their 64 registers.
 template <int VEC>
-__device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool nt) {
-    if constexpr (VEC == 4) {
+__device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool nt, int skip = 0) {
+    if (VEC > 1 && __builtin_amdgcn_ballot_w64(skip > 0) != 0 && skip > 0) {
+#pragma unroll
+        for (int e = 1; e < VEC; ++e)
+            if (e >= skip) p[e] = x[e];   // at most 3 elements per row: plain stores
+    } else if constexpr (VEC == 4) {
         const f32x4a v = {x[0], x[1], x[2], x[3]};
         if (nt) __builtin_nontemporal_store(v, reinterpret_cast<f32x4a *>(p));
         else *reinterpret_cast<f32x4a *>(p) = v;
@@ -109,8 +119,12 @@ __device__ __forceinline__ void store_vec(float *p, const float (&x)[VEC], bool 
 }
 
 template <int VEC>
-__device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC]) {
-    if constexpr (VEC == 4) {
+__device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC], int skip = 0) {
+    if (VEC > 1 && __builtin_amdgcn_ballot_w64(skip > 0) != 0 && skip > 0) {
+#pragma unroll
+        for (int e = 1; e < VEC; ++e)
+            if (e >= skip) p[e] = x[e];
+    } else if constexpr (VEC == 4) {
         reinterpret_cast<i64x2a *>(p)[0] = i64x2a{x[0], x[1]};
         reinterpret_cast<i64x2a *>(p)[1] = i64x2a{x[2], x[3]};
     } else if constexpr (VEC == 2) {
@@ -121,8 +135,12 @@ __device__ __forceinline__ void store_arg64(int64_t *p, const int (&x)[VEC]) {
 }
 
 template <int VEC>
-__device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC]) {
-    if constexpr (VEC == 4) *reinterpret_cast<i32x4a *>(p) = i32x4a{x[0], x[1], x[2], x[3]};
+__device__ __forceinline__ void store_arg32(int *p, const int (&x)[VEC], int skip = 0) {
+    if (VEC > 1 && __builtin_amdgcn_ballot_w64(skip > 0) != 0 && skip > 0) {
+#pragma unroll
+        for (int e = 1; e < VEC; ++e)
+            if (e >= skip) p[e] = x[e];
+    } else if constexpr (VEC == 4) *reinterpret_cast<i32x4a *>(p) = i32x4a{x[0], x[1], x[2], x[3]};
     else if constexpr (VEC == 2) *reinterpret_cast<i32x2a *>(p) = i32x2a{x[0], x[1]};
     else *p = x[0];
 }
@@ -233,6 +251,9 @@ __device__ __forceinline__ void store_out(const RowArgs &a, int64_t orow, int de
     for (int f = 0; f < F; ++f) {
         if (!ok[f]) continue;
         const int64_t cc = (int64_t)colf[f] - a.c_begin;
+        // lanes own columns c_begin + k*VEC ..; a vector moved back to end at
+        // c_end starts off that grid, and its first elements are a neighbour's
+        const int skip = (VEC - ((colf[f] - (int)a.c_begin) & (VEC - 1))) & (VEC - 1);   // VEC a power of two
         float res[VEC];
         int ar[VEC];
 #pragma unroll
@@ -245,21 +266,21 @@ __device__ __forceinline__ void store_out(const RowArgs &a, int64_t orow, int de
             }
         }
         if constexpr (!IS_MAX && !PIECES) mean_divide<VEC>(a.mean != 0, deg, res);
-        store_vec<VEC>(orow_p + cc, res, a.nt_store != 0);
+        store_vec<VEC>(orow_p + cc, res, a.nt_store != 0, skip);
         if constexpr (IS_MAX) {
-            if constexpr (PIECES) store_arg32<VEC>(a.part_arg + orow * a.ldo + cc, ar);
-            else if (a.argmax) store_arg64<VEC>(a.argmax + orow * a.ldo + cc, ar);
+            if constexpr (PIECES) store_arg32<VEC>(a.part_arg + orow * a.ldo + cc, ar, skip);
+            else if (a.argmax) store_arg64<VEC>(a.argmax + orow * a.ldo + cc, ar, skip);
         }
     }
 }
 
 // Column ownership of lane g within its row group for the slice starting at c0.
 // When the launch's width is not a multiple of VEC, the one vector that would
-// run past c_end is moved back to end there: it reads and writes the last VEC
-// columns, the lower ones of which its neighbour lane also computes.  Both
-// fold the same entries in the same order, so both write the same bits, and
-// every access stays inside the row (the launch guarantees c_end - c_begin
-// >= VEC).
+// run past c_end is moved back to end there: it reads the last VEC columns,
+// the lower ones of which its neighbour lane also reads, and writes only the
+// columns past its neighbour's (store_out), so every access stays inside the
+// row (the launch guarantees c_end - c_begin >= VEC) and no two lanes write
+// the same element.
 template <int G, int VEC, int F>
 __device__ __forceinline__ void lane_columns(const RowArgs &a, int64_t c0, int g, int (&colf)[F], bool (&ok)[F]) {
 #pragma unroll

@@ -347,8 +347,8 @@ hipError_t transpose_csr(const int *rowptr, const int *col, const float *val, in
 // ascending i.  A repeated i (a duplicated edge) is counted once.  With VEC =
 // 4 the rows need only element alignment (16-byte accesses at 4-byte aligned
 // addresses), and when N is not a multiple of 4 the lane whose vector would
-// run past column N takes the last four columns: the columns it shares with
-// its neighbour lane get the same sums, in the same order, from both.
+// run past column N reads the last four columns and writes only those past
+// its neighbour lane's.
 template <int G, int VEC>
 __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
     typedef float f4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -446,7 +446,13 @@ __global__ __launch_bounds__(kBlock) void maxgrad_kernel_t(MaxGradArgs a) {
     }
     if (!live || !ok) return;
     if constexpr (VEC == 4) {
-        *reinterpret_cast<f4 *>(a.dB + j * a.N + c) = f4{acc[0], acc[1], acc[2], acc[3]};
+        if (c == c0) {
+            *reinterpret_cast<f4 *>(a.dB + j * a.N + c) = f4{acc[0], acc[1], acc[2], acc[3]};
+        } else {
+#pragma unroll
+            for (int e = 1; e < VEC; ++e)
+                if (c + e >= c0) a.dB[j * a.N + c + e] = acc[e];
+        }
     } else {
         for (int e = 0; e < VEC; ++e) a.dB[j * a.N + c + e] = acc[e];
     }
