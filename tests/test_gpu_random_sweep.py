@@ -2,8 +2,10 @@
 plan options (every router decision forced on, off or left automatic, in
 random combinations), through the C ABI, against the oracle: sum and mean
 within the tolerance, max and argmax bit-exact, rows walked whole bit-exact
-against the fused oracle.  Combinations the library refuses as unsupported
-are counted, not failed."""
+against the fused oracle.  B, C and argmax start one element past an
+allocation's start in about half the cases (rows only 4- or 8-byte
+aligned), and the elements next to C and argmax must stay untouched.
+Combinations the library refuses as unsupported are counted, not failed."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import gnn_sparse_dense_amd as G
-    from tests.gpu_helpers import check, gpu_run, log, make_plan, to_dev
+    from tests.gpu_helpers import DEV, check, gpu_run, log, make_plan, to_dev
 
 CASES = 300
 
@@ -58,7 +60,7 @@ def test_random_sweep(orc):
     routes = {}
     for case in range(CASES):
         g = _graph(rng)
-        N = int(rng.choice([1, 2, 3, 4, 7, 16, 33, 64, 100, 128, 200, 256, 300]))
+        N = int(rng.choice([1, 3, 4, 5, 6, 7, 9, 13, 16, 17, 33, 50, 64, 66, 100, 130, 200, 257, 258, 259, 300, 513]))
         red = ["sum", "mean", "max"][int(rng.integers(3))]
         opts = _options(rng)
         what = f"case {case}: M={g.M} K={g.K} nnz={g.nnz} N={N} {red} opts={opts}"
@@ -70,9 +72,31 @@ def test_random_sweep(orc):
             refused += 1
             continue
         B = rng.standard_normal((g.K, N)).astype(np.float32)
-        _, _, _, Bd = to_dev(g, B)
+        _, _, _, Bd0 = to_dev(g, B)
+        ob, oc = int(rng.integers(2)), int(rng.integers(2))
+        log(f"  offsets B {ob} C {oc}")
+        Bbig = torch.empty(g.K * N + 1, dtype=torch.float32, device=DEV)
+        Bd = Bbig[ob:ob + g.K * N].view(g.K, N)
+        Bd.copy_(Bd0)
         try:
-            C, arg = gpu_run(plan, g.M, Bd, red)
+            Cbig = torch.full((g.M * N + 2,), float("nan"), dtype=torch.float32, device=DEV)
+            Cv = Cbig[oc:oc + g.M * N].view(g.M, N)
+            Abig = None
+            Av = None
+            if red == "max":
+                Abig = torch.full((g.M * N + 2,), 0x7F7F7F7F7F7F7F7F, dtype=torch.int64, device=DEV)
+                Av = Abig[oc:oc + g.M * N].view(g.M, N)
+            G.spmm_run(plan, Bd, Cv, Av, N, red, None)
+            torch.cuda.synchronize()
+            C = Cv.cpu().numpy()
+            arg = None if Av is None else Av.cpu().numpy()
+            tail = Cbig[oc + g.M * N:].cpu().numpy()
+            assert np.isnan(tail).all(), f"{what}: write past C"
+            if oc:
+                assert np.isnan(Cbig[0].item()), f"{what}: write before C"
+            if Abig is not None:
+                atail = Abig[oc + g.M * N:].cpu().numpy()
+                assert (atail == 0x7F7F7F7F7F7F7F7F).all(), f"{what}: write past argmax"
         except G.SpmmError as e:
             assert e.status == G.SPMM_E_UNSUPPORTED, f"{what}: {e}"
             refused += 1
@@ -82,7 +106,7 @@ def test_random_sweep(orc):
         key = ("merge" if info["route_merge"] else "panels" if info["route_pairs"] else
                "window" if info["route_window"] else "tiles" if info["route_tiled"] else "rows") + \
               ("+split" if info["route_split"] and info["n_seg"] > 0 else "") + \
-              ("+one dispatch" if info["route_fused_split"] else "")
+              ("+one dispatch" if info["route_fused_split"] else "") + f"/v{info['route_vec']}"
         routes[key] = routes.get(key, 0) + 1
         # rows walked whole: all of them, less the split rows; none certified
         # on the merge path (a row may span segments) or on V = 2 panels over
