@@ -84,14 +84,14 @@ def test_ragged_widths(orc, N):
         log(f"ragged N={N} {red}")
         C, arg = gpu_run(plan, g.M, Bd, red)
         check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=f"N={N} {red}")
-    # an offset (8-byte but not 16-byte aligned) view of B keeps float4 lanes
-    # on 4-byte aligned rows
+    # an offset (8-byte but not 16-byte aligned) view of B: float4 lanes on
+    # 4-byte aligned rows (float1 below 128 floats on this small graph)
     if N % 4 == 0:
         Bbig = torch.empty(g.K * N + 2, dtype=torch.float32, device=DEV)
         Bv = Bbig[2:].view(g.K, N)
         Bv.copy_(Bd)
         C, _ = gpu_run(plan, g.M, Bv, "sum")
-        assert G.spmm_plan_info(plan)["route_vec"] == 4
+        assert G.spmm_plan_info(plan)["route_vec"] == (1 if N < 128 else 4)
         check(orc, g, B, "sum", C, None, exact_rows=np.arange(g.M), what=f"N={N} misaligned B")
     G.spmm_plan_destroy(plan)
 
@@ -608,7 +608,8 @@ def test_community_window_matches_row_kernel(orc, shape, order):
 def test_router_rules():
     """Routing decisions measured on the GPU (the router sweep): community
     structure takes the LDS window kernel from 64 columns; launch-bound small
-    graphs take 8 lanes per row without coarsening up to 128 columns; skewed
+    graphs take float1 lanes below 128 columns, 8 lanes per row up to 32
+    vectors, and no coarsening; skewed
     graphs take 64-column slices from 128 columns, 128-column slices from 256
     to 512 and 64-column slices above; widths of a multiple of 8 vectors that
     are not powers of two (96, 160, 192 floats) take 8 lanes x 2 vectors at
@@ -623,9 +624,9 @@ def test_router_rules():
         assert (info["route_window"] > 0) == (win > 0), (N, info["route_window"])
     G.spmm_plan_destroy(community)
     tiny = make_plan(W.make_graph("tiny"))
-    for N, lanes in ((16, 8), (64, 8), (128, 8), (512, 64)):
+    for N, vec, lanes in ((16, 1, 8), (64, 1, 64), (128, 4, 8), (512, 4, 64)):
         info = G.spmm_plan_route(tiny, N, "sum")
-        assert (info["route_lanes"], info["route_coarsen"]) == (lanes, 1), (N, info)
+        assert (info["route_vec"], info["route_lanes"], info["route_coarsen"]) == (vec, lanes, 1), (N, info)
     G.spmm_plan_destroy(tiny)
     rng = np.random.default_rng(5)
     skew = make_plan(W.random_csr(rng, 20_000, 20_000, mean_deg=6.0, heavy_rows=20, heavy_deg=5000))

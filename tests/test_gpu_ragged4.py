@@ -151,8 +151,8 @@ def test_split_last_pass_narrower_than_a_vector(orc, N):
 def test_router_ragged_rules():
     """Routing at widths that are not a multiple of 4 (measured with the
     router sweep): float4 lanes by default; float1 lanes for rows of at most
-    8 floats at mean degree 16 and above, and of at most 16 floats on split
-    skewed graphs; half the lane group, coarsened, for 17 to 63 vectors that leave a quarter of it
+    8 floats at mean degree 16 and above, of at most 16 floats on split
+    skewed graphs and below 128 floats on small graphs; half the lane group, coarsened, for 17 to 63 vectors that leave a quarter of it
     idle at mean degree below 16; skewed graphs without column slices at such
     widths; V = 2 panels with 64 lanes past 32 vectors; the window kernel for
     community structure from 33 floats."""
@@ -168,6 +168,10 @@ def test_router_ragged_rules():
         assert G.spmm_plan_route(community, N, "sum")["route_window"] > 0, N
     assert G.spmm_plan_route(community, 17, "sum")["route_window"] == 0
     G.spmm_plan_destroy(community)
+    tiny = make_plan(W.make_graph("tiny"))
+    assert G.spmm_plan_route(tiny, 33, "sum")["route_vec"] == 1
+    assert G.spmm_plan_route(tiny, 130, "sum")["route_vec"] == 4
+    G.spmm_plan_destroy(tiny)
     rng = np.random.default_rng(5)
     skew = make_plan(W.random_csr(rng, 20_000, 20_000, mean_deg=6.0, heavy_rows=20, heavy_deg=5000))
     assert G.spmm_plan_info(skew)["n_heavy"] > 0
