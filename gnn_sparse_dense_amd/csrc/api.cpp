@@ -502,33 +502,38 @@ int pow2_ceil(int64_t x) {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Rule router (first matching rule per decision; forced options override):
-//  * vector width: 4 floats when N and the pointers allow 16-byte accesses,
-//    else 2, else 1;
+//  * vector width: 4 floats for any N >= 4 (16-byte accesses at element
+//    alignment, a row's last vector moved back to end at column N); float1
+//    where a row spans only a few float4 lanes and gathers, not DRAM, bound
+//    the product, and on small graphs below 128 floats; below 4 floats 2
+//    (aligned, N = 2) or 1;
 //  * lanes per row: one pass of the row's group spans the W = N / vec vector
 //    columns (several rows per wave when W < 64; coarsening F = 2 when
 //    W > 64), following ParamSpMM's thread-coarsening analysis (section 3.3)
 //    with the MAC-job gap kept at zero wherever N allows;
 //  * low mean degree (< 8, RA-SpMM's sparse-uniform regime): half the lanes
 //    and F = 2, doubling the rows per wave so more rows' gathers are in
-//    flight per wave;
+//    flight per wave; widths that leave a quarter of the covering lane group
+//    idle take the same shape below mean degree 16;
 //  * small graphs (fewer than two waves per CU at 16 rows per wave):
 //    launch-bound, so as many waves as possible: no coarsening, and 8 lanes
-//    per row (more column slices) up to 128 columns;
+//    per row (more column slices) up to 32 vectors;
 //  * skewed degrees (CV > 1, RA-SpMM's sparse-skewed / extreme-skew regime),
-//    where neighbours carry no locality, with a B of 128 floats or more:
-//    64-column slices (128-column slices from 512 floats), so each pass over
-//    the graph touches a part of B that stays in the Infinity Cache longer;
-//    that holds at power-of-two widths: at other widths past 32 vectors a
-//    half-width lane group, coarsened, covers the row in one slice and wins
-//    (33 floats on the power-law graph: 1.83 vs 2.77 ms; 300 floats: 11.8
-//    vs 12.4 ms), the same rule as on the other graphs;
+//    where neighbours carry no locality, with a B of 128 floats or more in a
+//    multiple of 32 floats: 64-column slices (128-column slices from 512
+//    floats), so each pass over the graph touches a part of B that stays in
+//    the Infinity Cache longer; at other widths one slice of the covering
+//    lane group;
+//  * the LDS window kernels for community structure above 32 floats; V = 2
+//    panels where the plan built them;
 //  * fp16 matrix-core tiles only when the caller enabled them (they follow
 //    the looser fp16 contract) and the run is a sum or mean with 16-byte
 //    aligned float4 access;
 //  * XCD remap in chunks of 256 blocks (rows sharing B rows meet in one L2,
 //    all XCDs sweep one region together): measured neutral or better on
 //    every regime, and better than chunks of 64 or 1024.
-// The thresholds come from rocprofv3-timed sweeps on the five regimes.
+// The thresholds come from rocprofv3-timed sweeps over seven graphs and 25
+// widths (the router sweep of the benchmark).
 Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const void *C, const void *argmax) {
     Route r;
     const bool a16 = aligned(B, 16) && aligned(C, 16) && (!argmax || aligned(argmax, 16));
@@ -617,9 +622,9 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     r.compact = r.tiled && p->tile_compact;
     // community structure with features of more than 32 floats: stage B's
     // row blocks in LDS (community graph, 33 floats: 0.114 vs 0.184 ms in
-    // 16-lane rows; at 32 floats and below 8-lane rows are as fast or faster)
-    // (one dispatch: at most 2^32 / kWinBlock row blocks, about 10^9 rows;
-    // larger graphs take the row kernels)
+    // 16-lane rows; at 32 floats and below 8-lane rows are as fast or
+    // faster).  One dispatch holds at most 2^32 / kWinBlock row blocks,
+    // about 10^9 rows; larger graphs take the row kernels.
     const bool win_grid = (p->M + kWinRows - 1) / kWinRows <= (int64_t)(UINT32_MAX / kWinBlock);
     r.window = !p->split && vec == 4 && p->opt_lanes == 0 && p->opt_coarsen == 0 && win_grid &&
                (p->opt_window == 1 || (p->opt_window == -1 && p->win_frac >= 0.5 && N > 32));
