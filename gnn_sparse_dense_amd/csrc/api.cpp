@@ -559,7 +559,10 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     // floats: 1.09 vs 1.34 ms; mixed graph, 8 floats: 0.317 vs 0.372 ms),
     // and below 128 floats on launch-bound small graphs, where float1 lanes
     // give more waves (2,000-node graph, 16 floats: 8.1 vs 8.5 us)
-    if (vec == 4 && ((N <= 8 && p->mean_deg >= 16.0) || (N <= 16 && p->split) || (small && N < 128))) vec = 1;
+    // (not when the caller forced the window kernels on: they need float4)
+    if (vec == 4 && p->opt_window != 1 &&
+        ((N <= 8 && p->mean_deg >= 16.0) || (N <= 16 && p->split) || (small && N < 128)))
+        vec = 1;
     if (p->opt_vec == 4 && (whole4 || ragged4)) vec = 4;
     else if (p->opt_vec == 2 && N % 2 == 0 && a8) vec = 2;
     else if (p->opt_vec == 1) vec = 1;

@@ -186,3 +186,25 @@ def test_router_ragged_rules():
     assert (info["route_pairs"], info["route_lanes"]) == (1, 64), info
     assert G.spmm_plan_route(knn, 602, "sum")["route_window"] > 0
     G.spmm_plan_destroy(knn)
+
+
+@pytest.mark.parametrize("N", [33, 64])
+def test_forced_window_keeps_float4_on_small_graphs(orc, N):
+    """The window kernels need float4 lanes: forcing them on a graph small
+    enough for the router's float1 rule still routes them, with the oracle's
+    results."""
+    g = W.make_graph("community", M=3072)
+    rng = np.random.default_rng(900 + N)
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    plan = make_plan(g, [(G.SPMM_OPT_WINDOW, 1)])
+    _, _, _, Bd = to_dev(g, B)
+    for red in ("sum", "max"):
+        log(f"forced window, small graph, N={N} {red}")
+        C, arg = gpu_run(plan, g.M, Bd, red)
+        info = G.spmm_plan_info(plan)
+        assert info["route_window"] == 2 and info["route_vec"] == 4, info
+        check(orc, g, B, red, C, arg, exact_rows=np.arange(g.M), what=f"forced window N={N} {red}")
+    auto = make_plan(g)
+    assert G.spmm_plan_route(auto, N, "sum")["route_vec"] == 1   # the small-graph rule
+    G.spmm_plan_destroy(auto)
+    G.spmm_plan_destroy(plan)
