@@ -208,3 +208,35 @@ def test_forced_window_keeps_float4_on_small_graphs(orc, N):
     assert G.spmm_plan_route(auto, N, "sum")["route_vec"] == 1   # the small-graph rule
     G.spmm_plan_destroy(auto)
     G.spmm_plan_destroy(plan)
+
+
+FULL_RAGGED = [("road", 33, "sum"), ("diffusion", 17, "max"), ("community", 130, "sum"), ("powerlaw", 130, "sum")]
+
+
+@pytest.mark.parametrize("name,N,red", FULL_RAGGED, ids=[f[0] for f in FULL_RAGGED])
+def test_full_size_ragged_widths_sampled(orc, name, N, red):
+    """The full-size graphs at widths that are not a multiple of 4, in the
+    router's own launch configuration: every output written, sampled rows
+    against the oracle (evenly spaced, first and last, the longest rows and
+    split rows; whole rows bit-exact)."""
+    g = W.make_graph(name)
+    rng = np.random.default_rng(1000 + N)
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    log(f"full {name}: M={g.M} nnz={g.nnz} N={N} {red}")
+    plan = make_plan(g)
+    part = G.spmm_plan_partition(plan)
+    _, _, _, Bd = to_dev(g, B)
+    C, arg = gpu_run(plan, g.M, Bd, red, poison=True)
+    info = G.spmm_plan_info(plan)
+    assert info["route_vec"] == 4, info
+    assert not np.isnan(C).any(), "unwritten output"
+    deg = g.degrees()
+    sample = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(g.M - 64, g.M), rng.choice(g.M, size=2000, replace=False),
+        np.argsort(deg)[-200:], np.unique(part["seg_row"])[:1000],
+    ])).astype(np.int64)
+    light_set = np.setdiff1d(sample, np.unique(part["seg_row"]))
+    exact_idx = np.searchsorted(sample, light_set)
+    check(orc, g, B, red, C[sample], None if arg is None else arg[sample], rows=sample, exact_rows=exact_idx,
+          what=f"full {name} N={N} {red}")
+    G.spmm_plan_destroy(plan)
