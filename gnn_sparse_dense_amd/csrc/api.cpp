@@ -636,10 +636,11 @@ Route route_for(const spmm_plan *p, int64_t N, int reduce, const void *B, const 
     // merge-path balancing, when the caller chose it
     r.merge = !r.mfma && p->opt_balance == 1 && p->merge_seg_row != nullptr;
     if (r.merge) {
-        const bool al4 = N % 4 == 0 && a16, al2 = N % 2 == 0 && a8;
+        const bool al2 = N % 2 == 0 && a8;
         // skewed graphs: 64-column slices (each pass over the graph touches a
-        // quarter of a 256-byte B row), as for the row kernels
-        r.vec = p->cv_deg > 1.0 ? 1 : (N >= 256 && al4) ? 4 : (N >= 128 && al2) ? 2 : 1;
+        // quarter of a 256-byte B row), as for the row kernels; float4 lanes
+        // at any width from 256 floats (whole4 or ragged4)
+        r.vec = p->cv_deg > 1.0 ? 1 : (N >= 256 && (whole4 || ragged4)) ? 4 : (N >= 128 && al2) ? 2 : 1;
         r.lanes = 64;
         r.coarsen = 1;
         const int64_t w = std::min<int64_t>(N, kPartialWidth);
@@ -1301,9 +1302,11 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
         ma.N = N;
         ma.nseg = p->merge_nseg;
         ma.mean = reduce == SPMM_MEAN;
-        for (int64_t w0 = 0; w0 < N; w0 += kPartialWidth) {
-            ma.c_begin = w0;
-            ma.c_end = std::min<int64_t>(N, w0 + kPartialWidth);
+        for (int64_t p0 = 0; p0 < N; p0 += kPartialWidth) {
+            // a last pass narrower than one vector starts earlier (as for the
+            // split's passes; the overlap is recomputed with the same bits)
+            ma.c_end = std::min<int64_t>(N, p0 + kPartialWidth);
+            ma.c_begin = std::min(p0, std::max<int64_t>(0, ma.c_end - r.vec));
             const hipError_t e = launch_merge(mf, ma, r.vec, is_max, s);
             if (e != hipSuccess) return fail_hip(e, "merge kernel launch");
         }

@@ -49,7 +49,7 @@ __global__ void merge_coords_kernel(const int *__restrict__ rowptr, int64_t M, i
 
 template <int VEC, bool IS_MAX>
 __device__ __forceinline__ void merge_emit(const MergeArgs &a, int64_t row, int deg, bool complete, int colf,
-                                           bool ok, const float (&acc)[VEC], const int (&arg)[VEC]) {
+                                           int skip, bool ok, const float (&acc)[VEC], const int (&arg)[VEC]) {
     if (!ok) return;
     float res[VEC];
     int ar[VEC];
@@ -63,9 +63,9 @@ __device__ __forceinline__ void merge_emit(const MergeArgs &a, int64_t row, int 
         }
     }
     if constexpr (!IS_MAX) mean_divide<VEC>(a.mean != 0, complete ? deg : 0, res);
-    store_vec<VEC>(a.C + row * a.N + colf, res, false);
+    store_vec<VEC>(a.C + row * a.N + colf, res, false, skip);
     if constexpr (IS_MAX)
-        if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar);
+        if (a.argmax) store_arg64<VEC>(a.argmax + row * a.N + colf, ar, skip);
 }
 
 template <int VEC, bool HAS_VAL, bool IS_MAX>
@@ -79,7 +79,10 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_t(MergeArgs a) {
     if (w >= a.nseg) return;                            // uniform per wave
     const int64_t c = a.c_begin + (int64_t)blockIdx.y * 64 * VEC + (int64_t)lane * VEC;
     const bool ok = c < a.c_end;
-    const int colf = (int)c;
+    // a vector that would run past the pass's last column ends there instead
+    // (the pass is at least VEC wide) and writes only its own columns
+    const int colf = (int)(VEC > 1 && c > a.c_end - VEC ? a.c_end - VEC : c);
+    const int skip = (int)(c - colf);
 
     const int i0 = a.seg_row[w], p0 = a.seg_entry[w];
     const int i1 = a.seg_row[w + 1], p1 = a.seg_entry[w + 1];
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_t(MergeArgs a) {
     int end_i = nr > 0 ? s_end[wv][0] : INT_MAX;        // end of row i if it ends in this segment
     bool touched = false;
     auto finish_row = [&]() {
-        merge_emit<VEC, IS_MAX>(a, i, end_i - row_start, !(i == i0 && carried_in), colf, ok, acc, arg);
+        merge_emit<VEC, IS_MAX>(a, i, end_i - row_start, !(i == i0 && carried_in), colf, skip, ok, acc, arg);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             acc[e] = IS_MAX ? -INFINITY : 0.0f;
@@ -162,9 +165,9 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_t(MergeArgs a) {
     const bool carry = i1 < a.M && touched;
     if (lane == 0) a.carry_row[w] = carry ? i1 : -1;
     if (carry && ok) {
-        const int64_t off = w * kPartialWidth + (c - a.c_begin);
-        store_vec<VEC>(a.carry + off, acc, false);
-        if constexpr (IS_MAX) store_arg32<VEC>(a.carry_arg + off, arg);
+        const int64_t off = w * kPartialWidth + (colf - a.c_begin);
+        store_vec<VEC>(a.carry + off, acc, false, skip);
+        if constexpr (IS_MAX) store_arg32<VEC>(a.carry_arg + off, arg, skip);
     }
 }
 

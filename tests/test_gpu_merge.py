@@ -102,3 +102,35 @@ def test_merge_full_powerlaw_sampled(orc):
                                      np.argsort(deg)[-40:], np.arange(g.M - 20, g.M)]))
     check(orc, g, B, "sum", C[rows], None, rows=rows, what="full power-law (sampled rows)")
     G.spmm_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("N", [257, 259, 302, 513, 602])
+def test_merge_float4_at_any_width(orc, N):
+    """Merge path on float4 lanes at widths that are not a multiple of 4 (a
+    row's last vector moved back to end at column N; a last 256-column pass of
+    fewer than 4 columns starts earlier), and with B and C one element past an
+    allocation's start: sum and mean in tolerance (whole rows bit-exact), max
+    and argmax bit-exact."""
+    rng = np.random.default_rng(N + 11)
+    g = W.make_graph("road", M=30_000)
+    plan = merge_plan(g)
+    exact = whole_rows(g)
+    B = rng.standard_normal((g.K, N)).astype(np.float32)
+    _, _, _, Bd = to_dev(g, B)
+    for red in ("sum", "mean", "max"):
+        log(f"merge float4 N={N} {red}")
+        C, arg = gpu_run(plan, g.M, Bd, red)
+        info = G.spmm_plan_info(plan)
+        assert info["route_merge"] == 1 and info["route_vec"] == 4, info
+        check(orc, g, B, red, C, arg, exact_rows=exact, what=f"merge N={N} {red}")
+    Bbig = torch.empty(g.K * N + 1, dtype=torch.float32, device=DEV)
+    Bv = Bbig[1:].view(g.K, N)
+    Bv.copy_(Bd)
+    Cbig = torch.full((g.M * N + 2,), float("nan"), dtype=torch.float32, device=DEV)
+    Cv = Cbig[1:-1].view(g.M, N)
+    G.spmm_run(plan, Bv, Cv, None, N, "sum", None)
+    torch.cuda.synchronize()
+    assert G.spmm_plan_info(plan)["route_vec"] == 4
+    assert np.isnan(Cbig[0].item()) and np.isnan(Cbig[-1].item())
+    check(orc, g, B, "sum", Cv.cpu().numpy(), None, exact_rows=exact, what=f"merge offset N={N}")
+    G.spmm_plan_destroy(plan)
