@@ -78,6 +78,7 @@ struct RowKernelKey {
     bool pieces;  // piece mode (split rows) instead of row mode
     bool tiled;   // row-tile records instead of CSR row bounds
     bool compact; // compact (16-bit) row-tile records
+    bool batch4;  // row tiles of 4 lanes x float4: entries in batches of 4 instead of 8
 };
 
 typedef void (*RowKernelFn)(RowArgs);

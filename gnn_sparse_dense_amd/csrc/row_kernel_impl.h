@@ -447,7 +447,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel_t(RowArgs a) {
 //                   offsets from the base;
 // then, when weighted, tile_cap fp32 values.  Overflow tiles (more entries
 // than tile_cap, or a column span beyond 16 bits) go through the CSR path.
-template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool COMPACT>
+// UB: entries per batch (0: the consume loop's default).
+template <int G, int VEC, int F, bool HAS_VAL, bool IS_MAX, bool COMPACT, int UB = 0>
 __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     static_assert(G == 4 || G == 8, "a wave holds one or two row tiles");
     constexpr int R = 64 / G;
@@ -515,10 +516,10 @@ __global__ __launch_bounds__(kBlock) void tile_kernel_t(RowArgs a) {
     init_acc<F, VEC, IS_MAX>(acc, arg);
     if constexpr (COMPACT) {
         const unsigned short *cp16 = reinterpret_cast<const unsigned short *>(hdr + HDR) + b;
-        consume<F, VEC, HAS_VAL, IS_MAX, false, 0, true>(cp16, vp, 0, deg, a.B, a.N, colf, ok, acc, arg, nullptr,
-                                                       0, 0, base);
+        consume<F, VEC, HAS_VAL, IS_MAX, false, UB, true>(cp16, vp, 0, deg, a.B, a.N, colf, ok, acc, arg, nullptr,
+                                                        0, 0, base);
     } else {
-        consume<F, VEC, HAS_VAL, IS_MAX>(hdr + HDR + b, vp, 0, deg, a.B, a.N, colf, ok, acc, arg);
+        consume<F, VEC, HAS_VAL, IS_MAX, false, UB>(hdr + HDR + b, vp, 0, deg, a.B, a.N, colf, ok, acc, arg);
     }
     if (live) store_out<F, VEC, IS_MAX, false>(a, orow, deg, colf, ok, acc, arg);
 }
@@ -802,6 +803,19 @@ RowKernelFn pick_row_kernel(const RowKernelKey &k) {
     if (k.tiled) {
         if constexpr (G == 4 || G == 8) {
             if (k.pieces) return nullptr;
+            if (k.batch4) {
+                // sum and mean only (max measured no faster in batches of 4)
+                if constexpr (G == 4 && VEC == 4 && F == 1) {
+                    if (k.is_max) return nullptr;
+                    if (k.compact)
+                        return k.has_val ? tile_kernel_t<G, VEC, F, true, false, true, 4>
+                                         : tile_kernel_t<G, VEC, F, false, false, true, 4>;
+                    return k.has_val ? tile_kernel_t<G, VEC, F, true, false, false, 4>
+                                     : tile_kernel_t<G, VEC, F, false, false, false, 4>;
+                } else {
+                    return nullptr;
+                }
+            }
             if (k.compact) {
                 if (k.is_max)
                     return k.has_val ? tile_kernel_t<G, VEC, F, true, true, true>
