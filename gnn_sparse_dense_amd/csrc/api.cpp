@@ -1339,7 +1339,7 @@ SPMM_API int spmm_run(spmm_plan_t p, const float *B, float *C, int64_t *argmax, 
     // 4-lane float4 row tiles at mean degree 8 and above: entries in batches
     // of 4, not 8 (fewer idle slots in a row's last batch: rows of exactly 10
     // entries fill 10 of 12 slots instead of 10 of 16; diffusion graph, 16
-    // floats, mean: 0.0726 vs 0.0751 ms; at mean degree 3 the batches of 8
+    // floats, mean: 0.0732 vs 0.0752 ms; at mean degree 3 the batches of 8
     // stay faster, road graph 16 floats: 0.0400 vs 0.0420 ms)
     const bool batch4 = r.tiled && r.lanes == 4 && r.vec == 4 && r.coarsen == 1 && !is_max && p->mean_deg >= 8.0;
     RowKernelKey key{r.lanes, r.vec, r.coarsen, has_val, is_max, false, r.tiled, r.compact, batch4};
